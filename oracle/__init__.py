@@ -1,0 +1,8 @@
+"""fp64 CPU oracle for the fused attention forward pass (test infrastructure only).
+
+Only tests, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg may
+import this package. The product path never does.
+"""
+from .attention import attention, attention_rows, visible_count, visible_mask
+
+__all__ = ["attention", "attention_rows", "visible_count", "visible_mask"]

@@ -1,0 +1,142 @@
+"""fp64 CPU oracle for the fused attention forward pass.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path imports, links or runs
+this module: only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` call it. It shares no code with the HIP kernels.
+
+What it computes (the plain definition, not the tiled recurrence):
+
+    O   = softmax(scale * Q K^T + mask) V
+    LSE = log(sum_j exp(scale * q_i . k_j))   over the visible keys j
+
+Sources (four web pages on fused attention; cited by page and section):
+  * rustytorch ``flash_attention_forward.metal``, kernel
+    ``flash_attention_forward``: the operation "O = softmax(Q @ K^T * scale) @ V",
+    the dot-then-scale score, the top-left causal test (key index greater
+    than query index is skipped), and the per-row log-sum-exp output kept for
+    the backward pass.
+  * spb/forge ``src/kernels/flash_attention.metal``, header comment and the
+    forward kernel ``flash_attn_fwd``: the online-softmax identity whose
+    end result is the plain softmax, the GQA head map hkv = h / (H / HKV),
+    the sliding window (keys j >= i - window + 1, self included, 0 = full
+    attention), and the stored L = m + log(l).
+  * boostr ``flash.wgsl``, ``flash_attention_fwd_f32``: [B, H, S, D] layout,
+    separate query/key lengths, the visible key range [start_k, end_k) with
+    end_k = min(i + 1, S_k) under causal masking, and the safe (max-shifted)
+    softmax evaluated in two passes.
+
+Readings taken where the pages are silent or disagree (each is stated again in
+the design notes):
+  * a row with no visible key gets O = 0 (every page) and LSE = -inf (the
+    rustytorch kernel yields -inf, the boostr shader's comment says "use
+    -inf"; forge stores 0);
+  * causal masking is top-left aligned (j <= i) also when Sq != Sk;
+  * the window without causal is one-sided (only the lower bound applies);
+  * inputs are taken exactly as stored (bf16 values upcast exactly), scale is
+    the caller's float32 value upcast to fp64.
+
+Pinned by tests/test_oracle.py against closed forms, brute-force exact sums,
+invariants and torch's float64 scaled_dot_product_attention.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def visible_mask(i: np.ndarray, Sk: int, causal: bool, window: int) -> np.ndarray:
+    """Boolean [len(i), Sk]: key j is visible to query row i.
+
+    causal: j <= i (top-left aligned, rustytorch causal test / boostr end_k).
+    window > 0: j >= i - window + 1 (forge FlashParams.window, boostr start_k).
+    """
+    i = np.asarray(i, dtype=np.int64)[:, None]
+    j = np.arange(Sk, dtype=np.int64)[None, :]
+    vis = np.ones((i.shape[0], Sk), dtype=bool)
+    if causal:
+        vis &= j <= i
+    if window > 0:
+        vis &= j >= i - window + 1
+    return vis
+
+
+def _softmax_rows(S: np.ndarray, vis: np.ndarray, Vh: np.ndarray):
+    """Masked softmax of score rows S [n, Sk] (fp64) applied to Vh [Sk, D].
+
+    Max-shifted as in boostr's first pass; the shift cancels exactly in the
+    ratio, and m + log(l) is the log-sum-exp of the visible scores."""
+    S = np.where(vis, S, -np.inf)
+    nonempty = vis.any(axis=1)
+    m = np.where(nonempty, S.max(axis=1, initial=-np.inf), 0.0)
+    P = np.exp(S - m[:, None])                 # masked entries -> exp(-inf) = 0
+    l = P.sum(axis=1)
+    O = np.zeros((S.shape[0], Vh.shape[1]), dtype=np.float64)
+    lse = np.full(S.shape[0], -np.inf, dtype=np.float64)
+    if nonempty.any():
+        ne = nonempty
+        O[ne] = (P[ne] @ Vh) / l[ne, None]
+        lse[ne] = m[ne] + np.log(l[ne])
+        # Internal consistency: every normalised softmax row sums to 1 and the
+        # max term alone contributes exp(0) = 1 to l.
+        rs = (P[ne] / l[ne, None]).sum(axis=1)
+        assert np.all(np.abs(rs - 1.0) <= 1e-12), "softmax row does not sum to 1"
+        assert np.all(l[ne] >= 1.0), "row sum below the max term"
+    return O, lse
+
+
+def attention(Q, K, V, scale: float, causal: bool = False, window: int = 0):
+    """Full forward: returns (O [B,H,Sq,D] fp64, LSE [B,H,Sq] fp64).
+
+    Materialises the full Sq x Sk score matrix for one (b, h) at a time."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, H, Sq, D = Q.shape
+    HKV, Sk = K.shape[1], K.shape[2]
+    assert H % HKV == 0, "H must be a multiple of HKV"
+    g = H // HKV
+    scale = float(np.float64(scale))
+    O = np.zeros((B, H, Sq, D), dtype=np.float64)
+    LSE = np.zeros((B, H, Sq), dtype=np.float64)
+    rows = np.arange(Sq)
+    vis = visible_mask(rows, Sk, causal, window)
+    for b in range(B):
+        for h in range(H):
+            hk = h // g                       # GQA head map
+            S = scale * (Q[b, h] @ K[b, hk].T)
+            O[b, h], LSE[b, h] = _softmax_rows(S, vis, V[b, hk])
+    return O, LSE
+
+
+def attention_rows(Q, K, V, scale: float, causal: bool, window: int, rows):
+    """Forward for selected query rows only.
+
+    rows: int array [n, 3] of (b, h, i). Returns (O [n, D], LSE [n]) in the
+    order given. Materialises the score rows [n_bh, Sk] per (b, h)."""
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+    H = Q.shape[1]
+    HKV, Sk, D = K.shape[1], K.shape[2], K.shape[3]
+    assert H % HKV == 0
+    g = H // HKV
+    scale = float(np.float64(scale))
+    O = np.zeros((rows.shape[0], D), dtype=np.float64)
+    LSE = np.zeros(rows.shape[0], dtype=np.float64)
+    key = rows[:, 0] * H + rows[:, 1]
+    for bh in np.unique(key):
+        sel = np.nonzero(key == bh)[0]
+        b, h = int(bh // H), int(bh % H)
+        hk = h // g
+        ii = rows[sel, 2]
+        q = np.asarray(Q[b, h, ii], dtype=np.float64)
+        Kh = np.asarray(K[b, hk], dtype=np.float64)
+        Vh = np.asarray(V[b, hk], dtype=np.float64)
+        S = scale * (q @ Kh.T)
+        O[sel], LSE[sel] = _softmax_rows(S, visible_mask(ii, Sk, causal, window), Vh)
+    return O, LSE
+
+
+def visible_count(Sq: int, Sk: int, causal: bool, window: int) -> np.ndarray:
+    """|visible(i)| for every query row i (int64 [Sq])."""
+    i = np.arange(Sq, dtype=np.int64)
+    hi = np.minimum(i + 1, Sk) if causal else np.full(Sq, Sk, dtype=np.int64)
+    lo = np.maximum(i - window + 1, 0) if window > 0 else np.zeros(Sq, dtype=np.int64)
+    return np.maximum(hi - lo, 0)

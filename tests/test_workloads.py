@@ -1,0 +1,51 @@
+"""Seeded input generation: bf16 rounding, determinism, row sampling. CPU only."""
+import numpy as np
+
+import workloads as W
+
+
+def test_bf16_round_to_nearest_even():
+    one = np.float32(1.0)
+    ulp = np.float32(2.0 ** -7)          # bf16 spacing at 1.0
+    x = np.array([1.0,
+                  one + ulp / 2,          # tie -> even (1.0)
+                  one + ulp + ulp / 2,    # tie -> even (1 + 2 ulp)
+                  one + ulp / 2 + np.float32(2.0 ** -20),   # just above tie -> up
+                  -2.5, 3.0e-3, 65504.0], dtype=np.float32)
+    bits = W.round_to_bf16_bits(x)
+    assert bits[0] == 0x3F80
+    assert bits[1] == 0x3F80
+    assert bits[2] == 0x3F82
+    assert bits[3] == 0x3F81
+    assert bits[4] == 0xC020
+    back = W.bf16_bits_to_f32(bits)
+    assert np.all(np.abs(back - x) <= np.abs(x) * 2.0 ** -8)
+
+
+def test_inputs_are_deterministic_and_rounded():
+    wl = W.small(W.CONFIGS[2], B=1, H=4, HKV=1, Sq=64, Sk=64)
+    a, b = W.make_inputs(wl), W.make_inputs(wl)
+    np.testing.assert_array_equal(a.q, b.q)
+    np.testing.assert_array_equal(a.v_bits, b.v_bits)
+    np.testing.assert_array_equal(W.bf16_bits_to_f32(a.k_bits), a.k)
+    assert a.q.shape == (1, 4, 64, 128) and a.k.shape == (1, 1, 64, 128)
+    # amplitude 0.5 N(0,1): sample std near 0.5
+    assert 0.45 < float(a.q.std()) < 0.55
+
+
+def test_uniform_v_range():
+    wl = W.small(W.CONFIGS[4], Sq=16, Sk=512)
+    inp = W.make_inputs(wl)
+    assert inp.v.min() >= -1.0 and inp.v.max() <= 1.0 and inp.v.std() > 0.5
+
+
+def test_sampled_rows_union_of_random_and_edges():
+    wl = W.small(W.CONFIGS[3], Sq=512, Sk=512, n_random_rows=40, edge_rows=8)
+    rows = W.check_rows(W.make_inputs(wl))
+    assert rows.shape[1] == 3
+    keys = {tuple(r) for r in rows.tolist()}
+    assert len(keys) == len(rows)
+    for h in range(wl.H):
+        assert (0, h, 0) in keys and (0, h, 511) in keys and (0, h, 7) in keys
+    assert len(rows) <= 40 + wl.H * 16
+    assert W.check_rows(W.make_inputs(W.CONFIGS[0])) is None

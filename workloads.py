@@ -1,0 +1,170 @@
+"""Seeded synthetic workloads for the fused attention forward pass.
+
+This module only *generates inputs*: shapes, seeded random tensors, bf16
+rounding of the drawn values, and seeded samples of which query rows a check
+looks at. It holds none of the attention arithmetic, so both the fp64 oracle
+(under ``oracle/``) and the GPU path can consume the same buffers without
+sharing any code of the method.
+
+Workload shapes follow the five synthetic configurations of the benchmark
+(small reference case, fp32 causal MHA, bf16 causal GQA, fp32 sliding-window
+GQA, bf16 long non-square single head). Layout is [B, H, S, D] contiguous for
+Q and O, [B, HKV, S, D] for K and V, as in the boostr ``flash.wgsl`` header
+comment and the rustytorch ``flash_attention_forward.metal`` buffer comments.
+
+Recipe (stated once, used everywhere):
+  * generator: ``numpy.random.default_rng`` on a ``SeedSequence(seed)`` spawned
+    into four independent streams (Q, K, V, row sample);
+  * seed = 20261202 + config index (0-based);
+  * values are drawn in float32; for bf16 workloads they are rounded to the
+    nearest bf16 (ties to even) and both sides read the rounded values.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+
+BASE_SEED = 20261202
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    HKV: int
+    Sq: int
+    Sk: int
+    D: int
+    dtype: str            # "f32" or "bf16"
+    causal: int
+    window: int
+    q_dist: str = "normal"     # "normal" | "uniform"
+    k_dist: str = "normal"
+    v_dist: str = "normal"
+    amplitude: float = 1.0      # multiplies every drawn value (before rounding)
+    check: str = "all"          # "all" | "sampled"
+    n_random_rows: int = 0      # for "sampled": distinct (b,h,i) drawn uniformly
+    edge_rows: int = 0          # for "sampled": first/last rows of every (b,h)
+    seed_index: int = 0
+
+    @property
+    def group(self) -> int:
+        return self.H // self.HKV
+
+    @property
+    def seed(self) -> int:
+        return BASE_SEED + self.seed_index
+
+    def scale(self) -> float:
+        """1/sqrt(D) rounded to float32 (the value both sides use)."""
+        return float(np.float32(1.0 / math.sqrt(self.D)))
+
+
+CONFIGS = [
+    Workload("tiny_f32_128", 1, 1, 1, 128, 128, 64, "f32", 0, 0,
+             check="all", seed_index=0),
+    Workload("mha_causal_f32_b4h8_s1024_d64", 4, 8, 8, 1024, 1024, 64, "f32", 1, 0,
+             check="all", seed_index=1),
+    Workload("gqa_causal_bf16_b2h32kv8_s4096_d128", 2, 32, 8, 4096, 4096, 128, "bf16", 1, 0,
+             amplitude=0.5, check="sampled", n_random_rows=4096, edge_rows=64,
+             seed_index=2),
+    Workload("swa_gqa_f32_b1h16kv4_s16384_d128_w4096", 1, 16, 4, 16384, 16384, 128, "f32", 1, 4096,
+             check="sampled", n_random_rows=512, edge_rows=64, seed_index=3),
+    Workload("long_bf16_sq8192_sk65536_d256", 1, 1, 1, 8192, 65536, 256, "bf16", 0, 0,
+             v_dist="uniform", check="sampled", n_random_rows=256, edge_rows=0,
+             seed_index=4),
+]
+
+# The configuration the throughput metric is quoted on (bf16 causal GQA).
+HEADLINE = 2
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 array -> uint16 bf16 bit patterns, round to nearest, ties to even.
+
+    Inputs here are finite, so no NaN special case is needed."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    bias = 0x7FFF + ((u >> 16) & 1)
+    return ((u + bias) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _draw(rng: np.random.Generator, shape, dist: str) -> np.ndarray:
+    if dist == "normal":
+        return rng.standard_normal(shape, dtype=np.float32)
+    if dist == "uniform":
+        return rng.uniform(-1.0, 1.0, size=shape).astype(np.float32)
+    raise ValueError(dist)
+
+
+@dataclass
+class Inputs:
+    """Host copies of one workload's inputs.
+
+    ``q``/``k``/``v`` are float32 arrays holding exactly the values the GPU
+    reads (for bf16 workloads they are the rounded values); ``*_bits`` are the
+    bf16 bit patterns (uint16) for bf16 workloads, else None."""
+    wl: Workload
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    q_bits: np.ndarray | None = None
+    k_bits: np.ndarray | None = None
+    v_bits: np.ndarray | None = None
+    rows_rng: np.random.Generator | None = field(default=None, repr=False)
+
+
+def make_inputs(wl: Workload, seed: int | None = None) -> Inputs:
+    seed = wl.seed if seed is None else seed
+    sq, sk, sv, srow = np.random.SeedSequence(seed).spawn(4)
+    q = _draw(np.random.default_rng(sq), (wl.B, wl.H, wl.Sq, wl.D), wl.q_dist)
+    k = _draw(np.random.default_rng(sk), (wl.B, wl.HKV, wl.Sk, wl.D), wl.k_dist)
+    v = _draw(np.random.default_rng(sv), (wl.B, wl.HKV, wl.Sk, wl.D), wl.v_dist)
+    if wl.amplitude != 1.0:
+        a = np.float32(wl.amplitude)
+        q, k, v = q * a, k * a, v * a
+    out = Inputs(wl, q, k, v, rows_rng=np.random.default_rng(srow))
+    if wl.dtype == "bf16":
+        out.q_bits = round_to_bf16_bits(q)
+        out.k_bits = round_to_bf16_bits(k)
+        out.v_bits = round_to_bf16_bits(v)
+        out.q = bf16_bits_to_f32(out.q_bits)
+        out.k = bf16_bits_to_f32(out.k_bits)
+        out.v = bf16_bits_to_f32(out.v_bits)
+    return out
+
+
+def check_rows(inp: Inputs) -> np.ndarray | None:
+    """Rows (b, h, i) a parity check compares, as an int64 array [n, 3].
+
+    None means every row. For "sampled" workloads: ``n_random_rows`` distinct
+    rows drawn uniformly from all B*H*Sq rows, united with the first and last
+    ``edge_rows`` rows of every (b, h)."""
+    wl = inp.wl
+    if wl.check == "all":
+        return None
+    rng = inp.rows_rng if inp.rows_rng is not None else np.random.default_rng(wl.seed)
+    total = wl.B * wl.H * wl.Sq
+    pick = rng.choice(total, size=min(wl.n_random_rows, total), replace=False)
+    flat = set(int(x) for x in pick)
+    if wl.edge_rows:
+        e = min(wl.edge_rows, wl.Sq)
+        for bh in range(wl.B * wl.H):
+            for i in list(range(e)) + list(range(wl.Sq - e, wl.Sq)):
+                flat.add(bh * wl.Sq + i)
+    flat = np.array(sorted(flat), dtype=np.int64)
+    b = flat // (wl.H * wl.Sq)
+    h = (flat // wl.Sq) % wl.H
+    i = flat % wl.Sq
+    return np.stack([b, h, i], axis=1)
+
+
+def small(wl: Workload, **kw) -> Workload:
+    """A copy of a workload with some fields replaced (for reduced-size tests)."""
+    return replace(wl, **kw)
