@@ -1,0 +1,98 @@
+"""Fused attention forward pass for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/fa.h`` (``libfa.so``). Every
+step of the computation runs in the library's HIP kernels; this module only
+checks and marshals arguments. torch provides device memory and streams.
+
+    o, lse = fwd(q, k, v, causal=True, window=0)
+
+q: [B, H, Sq, D], k and v: [B, HKV, Sk, D], contiguous CUDA (HIP) tensors of
+dtype float32 or bfloat16; o has q's shape and dtype, lse is float32
+[B, H, Sq] in natural-log units. A row with no visible key gets o = 0 and
+lse = -inf.
+"""
+from __future__ import annotations
+
+import math
+
+from ._lib import FA_BF16, FA_F32, FA_MAX_SPLITS, FaError, lib, library_path
+
+__all__ = ["fwd", "fwd_into", "plan_splits", "release", "FaError", "library_path",
+           "default_scale", "FA_F32", "FA_BF16", "FA_MAX_SPLITS"]
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return FA_F32
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def default_scale(D: int) -> float:
+    """1/sqrt(D) rounded to float32, the value the library receives."""
+    import numpy as np
+    return float(np.float32(1.0 / math.sqrt(D)))
+
+
+def _check(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, heads, S, D]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3]:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+
+
+def fwd_into(q, k, v, o, lse, *, causal=False, window=0, scale=None, num_splits=0, stream=None):
+    """Run the forward pass into caller-provided o and lse. Returns (o, lse)."""
+    import torch
+    _check(q, k, v)
+    B, H, Sq, D = q.shape
+    HKV, Sk = k.shape[1], k.shape[2]
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
+        raise ValueError("o must be contiguous with q's shape and dtype")
+    if tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, Sq]")
+    if scale is None:
+        scale = default_scale(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = lib().fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         B, H, HKV, Sq, Sk, D, float(scale), int(bool(causal)), int(window),
+                         _dtype_code(q), int(num_splits), stream.cuda_stream)
+    if st != 0:
+        raise FaError(st)
+    return o, lse
+
+
+def fwd(q, k, v, *, causal=False, window=0, scale=None, num_splits=0, stream=None):
+    """Forward pass; allocates o and lse with torch. Returns (o, lse)."""
+    import torch
+    _check(q, k, v)
+    B, H, Sq, _ = q.shape
+    with torch.cuda.device(q.device):
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    return fwd_into(q, k, v, o, lse, causal=causal, window=window, scale=scale,
+                    num_splits=num_splits, stream=stream)
+
+
+def plan_splits(B, H, HKV, Sq, Sk, D, *, causal=False, window=0, dtype="bf16") -> int:
+    """Key-axis split count the library picks for this problem on the current device."""
+    code = FA_BF16 if dtype in ("bf16", FA_BF16) else FA_F32
+    r = lib().fa_plan_splits(B, H, HKV, Sq, Sk, D, int(bool(causal)), int(window), code)
+    if r < 0:
+        raise FaError(-r)
+    return r
+
+
+def release():
+    """Return the split-K workspace pools to the HIP runtime."""
+    lib().fa_release()

@@ -1,0 +1,59 @@
+"""Ahead-of-time build of libfa.so for gfx950 with hipcc.
+
+The library is built in-tree (next to this file) so that it travels with the
+source tree; nothing is JIT-compiled at run time.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+SOURCES = [os.path.join(CSRC, "fa_fwd.hip"), os.path.join(CSRC, "fa_api.cpp")]
+
+ARCH = "gfx950"
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # Keep the compiler from forming packed fp32 VALU instructions.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP library cannot be built")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libfa.so (always recompiles). Returns the path."""
+    tmp = LIB_PATH + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if verbose or res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+    if res.returncode != 0:
+        if os.path.exists(tmp):
+            os.remove(tmp)
+        raise RuntimeError(f"hipcc failed with status {res.returncode}: {' '.join(cmd)}")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def ensure_built() -> str:
+    """Build only if no library exists yet."""
+    if not os.path.exists(LIB_PATH):
+        build()
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

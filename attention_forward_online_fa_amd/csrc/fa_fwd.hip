@@ -1,0 +1,644 @@
+// Fused attention forward pass for gfx950 (MI355X): tiled QK^T and PV on
+// MFMA with an online softmax between them, one query tile per workgroup.
+//
+// Method (the online-softmax recurrence of the forge flash_attention.metal
+// header comment, applied per key tile instead of per key): for each K/V tile
+//   S     = scale * Q K^T                (MFMA, fp32 accumulate)
+//   m_new = max(m, rowmax(S))
+//   P     = exp(S - m_new),  corr = exp(m - m_new)
+//   l     = l * corr + rowsum(P),  O = O * corr + P V   (MFMA)
+// and at the end O /= l, LSE = m + log(l) (the log-sum-exp output of the
+// rustytorch flash_attention_forward.metal kernel). Scores are carried in
+// base-2 units (scale * log2 e folded into one multiply) so every exponential
+// is a single v_exp_f32. m starts at -inf; a row whose keys so far are all
+// masked uses 0 as the shift so that exp(-inf - (-inf)) never appears (the
+// NaN hazard named in the forge header comment). Rows that never see a key
+// end with l = 0 and are written as O = 0, LSE = -inf.
+//
+// Whole K/V tiles above the causal diagonal or before the sliding window are
+// never visited; only tiles that straddle a mask edge (or the end of the key
+// axis) pay the per-element test, as the forge forward kernel does with its
+// kb_lim / jb_begin bounds.
+//
+// Work decomposition (gfx950): a workgroup is 4 wavefronts x 32 query rows =
+// 128 rows of one (batch, head). Each wavefront keeps its 32 query rows in
+// registers as the MFMA B operand and computes S^T = K Q^T, so a lane owns one
+// query row (column of S^T) and half of the tile's keys: row max and row sum
+// are in-lane plus one exchange with lane ^ 32. The P tile then feeds the
+// second MFMA (O^T = V^T P^T) straight from registers; V is transposed once
+// into LDS when it is staged. K/V tiles are double-buffered in LDS: the next
+// tile's global loads are in flight while the current tile is computed.
+//
+// Workgroup order: heaviest query tiles (latest rows under a causal mask)
+// first; when the number of (batch, head, split) units is a multiple of 8 the
+// blocks are remapped so that the query heads sharing one K/V head land on the
+// same XCD (MI355X dispatches workgroups round-robin over its 8 XCDs, each
+// with its own L2).
+#include "fa_kernels.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;   // 4 wavefronts of 64
+constexpr float kLn2 = 0.693147180559945309f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------------ work mapping
+struct Tile {
+  int b, h, hkv, qblk, split;
+};
+
+__device__ __forceinline__ Tile map_tile(const Params& p) {
+  const int i = blockIdx.x;
+  int t, u;
+  if (p.xcd_remap) {
+    // Block i runs on XCD i % 8 as that XCD's (i / 8)-th block. Give XCD x
+    // the contiguous unit range [x U/8, (x+1) U/8), heaviest tiles first.
+    const int upx = p.units >> 3;
+    const int k = i >> 3;
+    t = k / upx;
+    u = (i & 7) * upx + k % upx;
+  } else {
+    t = i / p.units;
+    u = i % p.units;
+  }
+  Tile w;
+  w.qblk = p.n_qblk - 1 - t;
+  const int hg = u % p.group;
+  int r = u / p.group;
+  w.split = r % p.nsplit;
+  r /= p.nsplit;
+  w.hkv = r % p.HKV;
+  w.b = r / p.HKV;
+  w.h = w.hkv * p.group + hg;
+  return w;
+}
+
+// Key range [lo, hi) a workgroup with rows [q0, q0 + kBlockM) must visit.
+__device__ __forceinline__ void key_range(const Params& p, int q0, int split, int& lo, int& hi) {
+  lo = split * p.split_len;
+  hi = min(p.Sk, lo + p.split_len);
+  const int last = min(q0 + kBlockM, p.Sq) - 1;
+  if (p.causal) hi = min(hi, last + 1);
+  if (p.window > 0) lo = max(lo, q0 - p.window + 1);
+}
+
+__device__ __forceinline__ bool visible(const Params& p, int i, int j) {
+  return j < p.Sk && (!p.causal || j <= i) && (p.window <= 0 || j > i - p.window);
+}
+
+// Finish one query row: combine the two lane halves' row sums, then write
+// LSE and hand 1/l to `store(partial, row, split, inv)`, which writes O (or
+// the fp32 partial of this key split).
+template <typename StoreFn>
+__device__ __forceinline__ void finish_row(const Params& p, int b, int h, int split, int i,
+                                           int g, float m, float l_lane, StoreFn store) {
+  const float l = l_lane + __shfl_xor(l_lane, 32);
+  const bool any = l > 0.f;
+  const float inv = any ? 1.f / l : 0.f;
+  const float lse = any ? (m + __log2f(l)) * kLn2 : -INFINITY;
+  if (i >= p.Sq) return;
+  const size_t row = (size_t)(b * p.H + h) * p.Sq + i;
+  const bool partial = p.nsplit > 1;
+  store(partial, row, split, inv);
+  if (g == 0) {
+    if (partial)
+      p.Lpart[(size_t)split * p.B * p.H * p.Sq + row] = lse;
+    else
+      p.LSE[row] = lse;
+  }
+}
+
+// ====================================================================== bf16
+// S^T tile = K Q^T with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims from
+// LDS, B = 16 dims x 32 query rows from registers. In the accumulator, lane
+// (q = lane % 32, g = lane / 32) holds rows 8(v/4) + 4g + v%4 of S^T. Loading
+// A row r from key pi(r) (bits 2 and 3 of r swapped) makes element v of that
+// lane hold key 16(v/8) + 8g + v%8: eight consecutive keys per lane half,
+// which is exactly the k-slot order the PV MFMA wants for its B operand.
+__device__ __forceinline__ int perm_row(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+template <int D, int BN>
+struct Bf16Tile {
+  static constexpr int DC = D / 16;      // k-steps of the S MFMA
+  static constexpr int DB = D / 32;      // 32-dim blocks of the O^T accumulator
+  static constexpr int KB = BN / 32;     // 32-key blocks of S^T
+  static constexpr int KROW = D * 2;     // bytes per K row in LDS
+  static constexpr int CPR = D / 8;      // 16-byte chunks per K row
+  static constexpr int VROW = BN * 2;    // bytes per V^T row in LDS
+  static constexpr int CPV = BN / 8;     // 16-byte chunks per V^T row
+  static constexpr int KBYTES = BN * KROW;
+  static constexpr int VBYTES = D * VROW;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int K_IT = BN * CPR / kThreads;                  // K chunks per thread
+  static constexpr int VBLK = (BN / 4) * (D / 8);                   // 4-key x 8-dim blocks
+  static constexpr int V_IT = (VBLK + kThreads - 1) / kThreads;
+  static_assert(BN * CPR % kThreads == 0, "K tile must split evenly over the workgroup");
+
+  // XOR swizzles on 16-byte chunks: a wavefront's 16-lane groups read 16
+  // distinct bank quads for both the K reads (16 keys, one chunk) and the V^T
+  // reads (16 dims, one chunk).
+  __device__ static __forceinline__ int swz_k(int key) {
+    return CPR >= 16 ? (key & 15) : ((key >> 1) & 7);
+  }
+  __device__ static __forceinline__ int swz_v(int d) {
+    return (d / (16 / CPV)) % CPV;
+  }
+};
+
+template <int D, int BN>
+__global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1))
+void fwd_bf16_kernel(Params p) {
+  using T = Bf16Tile<D, BN>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const Tile w = map_tile(p);
+  const int q0 = w.qblk * kBlockM;
+  const int qw = q0 + wave * 32;
+  const int i = qw + l32;
+
+  const __bf16* Qp = (const __bf16*)p.Q + (size_t)(w.b * p.H + w.h) * p.Sq * D;
+  const __bf16* Kp = (const __bf16*)p.K + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
+  const __bf16* Vp = (const __bf16*)p.V + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
+
+  int lo, hi;
+  key_range(p, q0, w.split, lo, hi);
+  const int t0 = (lo / BN) * BN;
+  const int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
+
+  // Query rows as the B operand: k-slot (g, e) of step t is dim 16t + 8g + e.
+  bf16x8 qf[T::DC];
+#pragma unroll
+  for (int t = 0; t < T::DC; ++t) {
+    if (i < p.Sq)
+      qf[t] = *(const bf16x8*)(Qp + (size_t)i * D + 16 * t + 8 * g);
+    else
+      qf[t] = bf16x8{};
+  }
+
+  f32x16 o[T::DB];
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db) o[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  u32x4 kreg[T::K_IT];
+  u32x4 vreg[T::V_IT][4];
+
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int it = 0; it < T::K_IT; ++it) {
+      const int c = tid + it * kThreads;
+      const int row = c / T::CPR, ch = c % T::CPR;
+      const int key = kt + row;
+      kreg[it] = key < p.Sk ? *(const u32x4*)(Kp + (size_t)key * D + ch * 8) : u32x4{};
+    }
+#pragma unroll
+    for (int it = 0; it < T::V_IT; ++it) {
+      const int blk = tid + it * kThreads;
+      const int db8 = blk % (D / 8), kb4 = blk / (D / 8);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kt + 4 * kb4 + r;
+        vreg[it][r] = (blk < T::VBLK && key < p.Sk)
+                          ? *(const u32x4*)(Vp + (size_t)key * D + db8 * 8)
+                          : u32x4{};
+      }
+    }
+  };
+
+  auto store_tile = [&](char* st) {
+    char* Ks = st;
+    char* Vs = st + T::KBYTES;
+#pragma unroll
+    for (int it = 0; it < T::K_IT; ++it) {
+      const int c = tid + it * kThreads;
+      const int row = c / T::CPR, ch = c % T::CPR;
+      *(u32x4*)(Ks + row * T::KROW + ((ch ^ T::swz_k(row)) << 4)) = kreg[it];
+    }
+#pragma unroll
+    for (int it = 0; it < T::V_IT; ++it) {
+      const int blk = tid + it * kThreads;
+      if (blk >= T::VBLK) continue;
+      const int db8 = blk % (D / 8), kb4 = blk / (D / 8);
+      // vreg[it][r] = V[key 4 kb4 + r][dims 8 db8 .. +7]; write V^T rows.
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int wd = c >> 1;
+        unsigned x0 = vreg[it][0][wd], x1 = vreg[it][1][wd];
+        unsigned x2 = vreg[it][2][wd], x3 = vreg[it][3][wd];
+        unsigned lo2, hi2;
+        if ((c & 1) == 0) {
+          lo2 = (x0 & 0xffffu) | (x1 << 16);
+          hi2 = (x2 & 0xffffu) | (x3 << 16);
+        } else {
+          lo2 = (x0 >> 16) | (x1 & 0xffff0000u);
+          hi2 = (x2 >> 16) | (x3 & 0xffff0000u);
+        }
+        const int d = 8 * db8 + c;
+        char* dst = Vs + d * T::VROW + (((kb4 >> 1) ^ T::swz_v(d)) << 4) + (kb4 & 1) * 8;
+        *(u32x2*)dst = u32x2{lo2, hi2};
+      }
+    }
+  };
+
+  if (n_tiles > 0) {
+    load_tile(t0);
+    store_tile(smem);
+  }
+  __syncthreads();
+
+  const int krow = perm_row(l32);
+  for (int it = 0; it < n_tiles; ++it) {
+    const int kt = t0 + it * BN;
+    const char* Ks = smem + (it & 1) * T::STAGE;
+    const char* Vs = Ks + T::KBYTES;
+    if (it + 1 < n_tiles) load_tile(kt + BN);
+
+    const bool skip = qw >= p.Sq || (p.causal && kt > qw + 31) ||
+                      (p.window > 0 && kt + BN - 1 < qw - p.window + 1);
+    if (!skip) {
+      // ---- S^T = K Q^T
+      f32x16 s[T::KB];
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < T::DC; ++t) {
+#pragma unroll
+        for (int kb = 0; kb < T::KB; ++kb) {
+          const int key = kb * 32 + krow;
+          const int ch = 2 * t + g;
+          const bf16x8 a = *(const bf16x8*)(Ks + key * T::KROW + ((ch ^ T::swz_k(key)) << 4));
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb], 0, 0, 0);
+        }
+      }
+      // ---- scale to base-2 units, mask edge tiles
+      const bool edge = (kt + BN > p.Sk) || (p.causal && kt + BN - 1 > qw) ||
+                        (p.window > 0 && kt < qw + 31 - p.window + 1);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float x = s[kb][v] * p.sl;
+          if (edge) {
+            const int j = kt + 32 * kb + 16 * (v >> 3) + 8 * g + (v & 7);
+            x = visible(p, i, j) ? x : -INFINITY;
+          }
+          s[kb][v] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float corr = fast_exp2(m - m_use);
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float e = fast_exp2(s[kb][v] - m_use);
+          s[kb][v] = e;
+          rs += e;
+        }
+      }
+      l = l * corr + rs;
+      m = m_new;
+      if (__any(corr != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) o[db] *= corr;
+      }
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          bf16x8 pf;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pf[e] = (__bf16)s[kb][8 * c2 + e];
+          const int ch = 2 * (2 * kb + c2) + g;
+#pragma unroll
+          for (int db = 0; db < T::DB; ++db) {
+            const int d = 32 * db + l32;
+            const bf16x8 a = *(const bf16x8*)(Vs + d * T::VROW + ((ch ^ T::swz_v(d)) << 4));
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, o[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    if (it + 1 < n_tiles) store_tile((char*)smem + ((it + 1) & 1) * T::STAGE);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds dims 32 db + 8 a + 4 g + (0..3) of row i.
+  finish_row(p, w.b, w.h, w.split, i, g, m, l,
+             [&](bool partial, size_t row, int split, float inv) {
+               if (partial) {
+                 const size_t rows = (size_t)p.B * p.H * p.Sq;
+                 float* dst = p.Opart + ((size_t)split * rows + row) * D;
+#pragma unroll
+                 for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+                   for (int a = 0; a < 4; ++a) {
+                     f32x4 v4 = {o[db][4 * a] * inv, o[db][4 * a + 1] * inv,
+                                 o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv};
+                     *(f32x4*)(dst + 32 * db + 8 * a + 4 * g) = v4;
+                   }
+               } else {
+                 __bf16* dst = (__bf16*)p.O + row * D;
+#pragma unroll
+                 for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+                   for (int a = 0; a < 4; ++a) {
+                     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                     bf16x4 v4 = {(__bf16)(o[db][4 * a] * inv), (__bf16)(o[db][4 * a + 1] * inv),
+                                  (__bf16)(o[db][4 * a + 2] * inv), (__bf16)(o[db][4 * a + 3] * inv)};
+                     *(bf16x4*)(dst + 32 * db + 8 * a + 4 * g) = v4;
+                   }
+               }
+             });
+}
+
+// ====================================================================== fp32
+// S^T tile = K Q^T with v_mfma_f32_32x32x2_f32 (true fp32 products). Step t
+// pairs k-slot g with dim t + (D/2) g, so a lane reads four consecutive steps
+// of its K row with one 16-byte LDS load. The PV MFMA step u takes, in lane
+// half g, the key 8(u/4) + 4g + u%4 that the S accumulator element u holds,
+// and O^T row m of d-block db is dim (D/32) m + db, so one 16-byte LDS load of
+// a V row feeds four d-blocks and the epilogue stores 16-byte runs.
+template <int D>
+struct F32Tile {
+  static constexpr int BN = 32;
+  static constexpr int DH = D / 2;        // k-steps of the S MFMA
+  static constexpr int DB = D / 32;       // d-blocks of the O^T accumulator
+  static constexpr int LD = D + 4;        // LDS row stride (floats): conflict-free K reads
+  static constexpr int TILE_F = BN * LD;  // floats per K or V tile
+  static constexpr int STAGE_F = 2 * TILE_F;
+  static constexpr int C4 = D / 4;        // float4 chunks per row
+  static constexpr int IT = BN * C4 / kThreads;
+  static_assert(BN * C4 % kThreads == 0, "tile must split evenly over the workgroup");
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1))
+void fwd_f32_kernel(Params p) {
+  using T = F32Tile<D>;
+  constexpr int BN = T::BN;
+  __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE_F];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const Tile w = map_tile(p);
+  const int q0 = w.qblk * kBlockM;
+  const int qw = q0 + wave * 32;
+  const int i = qw + l32;
+
+  const float* Qp = (const float*)p.Q + (size_t)(w.b * p.H + w.h) * p.Sq * D;
+  const float* Kp = (const float*)p.K + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
+  const float* Vp = (const float*)p.V + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
+
+  int lo, hi;
+  key_range(p, q0, w.split, lo, hi);
+  const int t0 = (lo / BN) * BN;
+  const int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
+
+  float qf[T::DH];
+#pragma unroll
+  for (int t4 = 0; t4 < T::DH / 4; ++t4) {
+    f32x4 v = i < p.Sq ? *(const f32x4*)(Qp + (size_t)i * D + T::DH * g + 4 * t4) : f32x4{};
+    qf[4 * t4 + 0] = v[0];
+    qf[4 * t4 + 1] = v[1];
+    qf[4 * t4 + 2] = v[2];
+    qf[4 * t4 + 3] = v[3];
+  }
+
+  f32x16 o[T::DB];
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db) o[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  f32x4 kreg[T::IT], vreg[T::IT];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int it = 0; it < T::IT; ++it) {
+      const int c = tid + it * kThreads;
+      const int row = c / T::C4, c4 = c % T::C4;
+      const int key = kt + row;
+      const bool ok = key < p.Sk;
+      kreg[it] = ok ? *(const f32x4*)(Kp + (size_t)key * D + 4 * c4) : f32x4{};
+      vreg[it] = ok ? *(const f32x4*)(Vp + (size_t)key * D + 4 * c4) : f32x4{};
+    }
+  };
+  auto store_tile = [&](float* st) {
+#pragma unroll
+    for (int it = 0; it < T::IT; ++it) {
+      const int c = tid + it * kThreads;
+      const int row = c / T::C4, c4 = c % T::C4;
+      *(f32x4*)(st + row * T::LD + 4 * c4) = kreg[it];
+      *(f32x4*)(st + T::TILE_F + row * T::LD + 4 * c4) = vreg[it];
+    }
+  };
+
+  if (n_tiles > 0) {
+    load_tile(t0);
+    store_tile(smem);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const int kt = t0 + it * BN;
+    const float* Ks = smem + (it & 1) * T::STAGE_F;
+    const float* Vs = Ks + T::TILE_F;
+    if (it + 1 < n_tiles) load_tile(kt + BN);
+
+    const bool skip = qw >= p.Sq || (p.causal && kt > qw + 31) ||
+                      (p.window > 0 && kt + BN - 1 < qw - p.window + 1);
+    if (!skip) {
+      f32x16 s = f32x16{};
+      const float* krow = Ks + l32 * T::LD + T::DH * g;
+#pragma unroll
+      for (int t4 = 0; t4 < T::DH / 4; ++t4) {
+        const f32x4 a = *(const f32x4*)(krow + 4 * t4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf[4 * t4 + e], s, 0, 0, 0);
+      }
+      const bool edge = (kt + BN > p.Sk) || (p.causal && kt + BN - 1 > qw) ||
+                        (p.window > 0 && kt < qw + 31 - p.window + 1);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float x = s[v] * p.sl;
+        if (edge) {
+          const int j = kt + 8 * (v >> 2) + 4 * g + (v & 3);
+          x = visible(p, i, j) ? x : -INFINITY;
+        }
+        s[v] = x;
+        mx = fmaxf(mx, x);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float corr = fast_exp2(m - m_use);
+      float rs = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float e = fast_exp2(s[v] - m_use);
+        s[v] = e;
+        rs += e;
+      }
+      l = l * corr + rs;
+      m = m_new;
+      if (__any(corr != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) o[db] *= corr;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int key = 8 * (u >> 2) + 4 * g + (u & 3);
+        const float* vrow = Vs + key * T::LD + T::DB * l32;
+        float va[T::DB];
+        if constexpr (T::DB >= 4) {
+#pragma unroll
+          for (int c4 = 0; c4 < T::DB / 4; ++c4) {
+            const f32x4 x = *(const f32x4*)(vrow + 4 * c4);
+            va[4 * c4 + 0] = x[0];
+            va[4 * c4 + 1] = x[1];
+            va[4 * c4 + 2] = x[2];
+            va[4 * c4 + 3] = x[3];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < T::DB; ++e) va[e] = vrow[e];
+        }
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[db], s[u], o[db], 0, 0, 0);
+      }
+    }
+
+    if (it + 1 < n_tiles) store_tile(smem + ((it + 1) & 1) * T::STAGE_F);
+    __syncthreads();
+  }
+
+  // ---- epilogue: element v of block db is dim (D/32)(8(v/4) + 4g + v%4) + db.
+  finish_row(p, w.b, w.h, w.split, i, g, m, l,
+             [&](bool partial, size_t row, int split, float inv) {
+               float* dst;
+               if (partial) {
+                 const size_t rows = (size_t)p.B * p.H * p.Sq;
+                 dst = p.Opart + ((size_t)split * rows + row) * D;
+               } else {
+                 dst = (float*)p.O + row * D;
+               }
+#pragma unroll
+               for (int v = 0; v < 16; ++v) {
+                 const int mrow = 8 * (v >> 2) + 4 * g + (v & 3);
+                 float* d0 = dst + T::DB * mrow;
+                 if (T::DB % 4 == 0) {
+#pragma unroll
+                   for (int c4 = 0; c4 < T::DB / 4; ++c4) {
+                     f32x4 x = {o[4 * c4][v] * inv, o[4 * c4 + 1][v] * inv,
+                                o[4 * c4 + 2][v] * inv, o[4 * c4 + 3][v] * inv};
+                     *(f32x4*)(d0 + 4 * c4) = x;
+                   }
+                 } else {
+#pragma unroll
+                   for (int db = 0; db < T::DB; ++db) d0[db] = o[db][v] * inv;
+                 }
+               }
+             });
+}
+
+// ============================================================ split merge
+// O = sum_s exp(LSE_s - LSE) O_s and LSE = log sum_s exp(LSE_s): the block
+// form of the online-softmax rescale. A split that saw no key has
+// LSE_s = -inf and weight 0; a row with no key in any split gets O = 0 and
+// LSE = -inf.
+template <typename OutT, int D>
+__global__ __launch_bounds__(kThreads)
+void merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpart,
+                  OutT* __restrict__ O, float* __restrict__ LSE, long rows, int nsplit) {
+  constexpr int TPR = D / 4;               // threads per row, 4 dims each
+  constexpr int RPB = kThreads / TPR;
+  const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  if (row >= rows) return;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, Lpart[(size_t)s * rows + row]);
+  f32x4 acc = f32x4{};
+  float den = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < nsplit; ++s) {
+      const float ls = Lpart[(size_t)s * rows + row];
+      const float wgt = __expf(ls - M);
+      den += wgt;
+      const f32x4 x = *(const f32x4*)(Opart + ((size_t)s * rows + row) * D + 4 * c);
+      acc += wgt * x;
+    }
+    acc *= 1.f / den;
+  }
+  OutT* dst = O + (size_t)row * D + 4 * c;
+  if constexpr (sizeof(OutT) == 2) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    *(bf16x4*)dst = bf16x4{(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
+  } else {
+    *(f32x4*)dst = acc;
+  }
+  if (c == 0) LSE[row] = M == -INFINITY ? -INFINITY : M + __logf(den);
+}
+
+// ================================================================ launch
+int key_tile(int dtype, int D) {
+  if (dtype == 1) return D == 256 ? 32 : 64;
+  return F32Tile<64>::BN;
+}
+
+template <typename OutT, int D>
+static hipError_t launch_merge(const Params& p, hipStream_t stream) {
+  const long rows = (long)p.B * p.H * p.Sq;
+  constexpr int RPB = kThreads / (D / 4);
+  const long blocks = (rows + RPB - 1) / RPB;
+  hipLaunchKernelGGL((merge_kernel<OutT, D>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                     p.Opart, p.Lpart, (OutT*)p.O, p.LSE, rows, p.nsplit);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_d(const Params& p, int dtype, hipStream_t stream) {
+  const long blocks = (long)p.units * p.n_qblk;
+  if (dtype == 1) {
+    constexpr int BN = D == 256 ? 32 : 64;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BN>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nsplit == 1) return e;
+  return dtype == 1 ? launch_merge<__bf16, D>(p, stream) : launch_merge<float, D>(p, stream);
+}
+
+hipError_t launch_forward(const Params& p, int dtype, int D, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_d<64>(p, dtype, stream);
+    case 128: return launch_d<128>(p, dtype, stream);
+    case 256: return launch_d<256>(p, dtype, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa

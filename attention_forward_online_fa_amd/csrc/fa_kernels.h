@@ -1,0 +1,37 @@
+// Internal interface between the C ABI (fa_api.cpp) and the kernels
+// (fa_fwd.hip). Not installed; callers use include/fa.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstddef>
+
+namespace fa {
+
+// Everything one forward launch needs. Built and checked on the host.
+struct Params {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* LSE;
+  float* Opart;      // [nsplit][B*H*Sq][D] fp32 partial outputs (nsplit > 1)
+  float* Lpart;      // [nsplit][B*H*Sq]    partial log-sum-exp    (nsplit > 1)
+  int B, H, HKV, Sq, Sk;
+  int group;         // H / HKV
+  float sl;          // scale * log2(e): scores are kept in base-2 units
+  int causal;
+  int window;
+  int nsplit;        // key-axis splits (1 = none)
+  int split_len;     // keys per split, a multiple of the key tile
+  int n_qblk;        // ceil(Sq / BM)
+  int units;         // B * H * nsplit
+  int xcd_remap;     // 1: group work so units sharing K/V stay on one XCD
+};
+
+// Tile shape per (dtype, D): query rows per workgroup and keys per K/V tile.
+constexpr int kBlockM = 128;
+int key_tile(int dtype, int D);
+
+// Queue the forward kernel (and the merge kernel when p.nsplit > 1).
+hipError_t launch_forward(const Params& p, int dtype, int D, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config IDX]
+
+A step is one fa_fwd call (every kernel of the forward pass, including the
+key-split merge when the library splits) over one batch of synthetic inputs
+that are resident in HBM before timing starts. The default workload is the
+bf16 causal GQA configuration (B=2, H=32, HKV=8, S=4096, D=128), the one the
+headline metric is quoted on. Prints one JSON line.
+
+Metric: TFLOP/s counting 4*B*H*D*sum_i |visible keys of row i| (masked
+pairs are not counted), i.e. the two matrix products of attention restricted
+to the mask.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as W  # noqa: E402
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (published)
+KERNEL_SOURCES = [os.path.join(ROOT, "attention_forward_online_fa_amd", "csrc", f)
+                  for f in ("fa_fwd.hip", "fa_api.cpp", "fa_kernels.h")]
+
+
+def visible_pairs(wl: W.Workload) -> int:
+    """sum_i |visible(i)| for one (b, h), in closed form per row."""
+    i = np.arange(wl.Sq, dtype=np.int64)
+    hi = np.minimum(i + 1, wl.Sk) if wl.causal else np.full(wl.Sq, wl.Sk, np.int64)
+    lo = np.maximum(i - wl.window + 1, 0) if wl.window > 0 else np.zeros(wl.Sq, np.int64)
+    return int(np.maximum(hi - lo, 0).sum())
+
+
+def counted_flops(wl: W.Workload) -> float:
+    return 4.0 * wl.B * wl.H * wl.D * visible_pairs(wl)
+
+
+def algorithmic_bytes(wl: W.Workload) -> int:
+    esz = 2 if wl.dtype == "bf16" else 4
+    q = wl.B * wl.H * wl.Sq * wl.D * esz
+    kv = 2 * wl.B * wl.HKV * wl.Sk * wl.D * esz
+    return q + kv + q + wl.B * wl.H * wl.Sq * 4
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(wl: W.Workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
+    none exist or the kernel sources changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def device_inputs(inp, torch):
+    if inp.wl.dtype == "bf16":
+        conv = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+        return conv(inp.q_bits), conv(inp.k_bits), conv(inp.v_bits)
+    return tuple(torch.from_numpy(a).cuda() for a in (inp.q, inp.k, inp.v))
+
+
+def cpu_baseline(wl: W.Workload, inp, target_rows: int):
+    """The fp64 oracle on a bounded row sample of the same workload."""
+    from oracle import attention_rows
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(wl.seed + 7)
+    total = wl.B * wl.H * wl.Sq
+    flat = np.sort(rng.choice(total, size=min(target_rows, total), replace=False))
+    rows = np.stack([flat // (wl.H * wl.Sq), (flat // wl.Sq) % wl.H, flat % wl.Sq], axis=1)
+    i = rows[:, 2]
+    hi = np.minimum(i + 1, wl.Sk) if wl.causal else np.full(len(i), wl.Sk)
+    lo = np.maximum(i - wl.window + 1, 0) if wl.window > 0 else np.zeros(len(i), np.int64)
+    flops = 4.0 * wl.D * float(np.maximum(hi - lo, 0).sum())
+    t0 = time.perf_counter()
+    attention_rows(inp.q, inp.k, inp.v, wl.scale(), bool(wl.causal), wl.window, rows)
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{len(rows)} random query rows of {total} (all heads), fp64 numpy, "
+                      f"{dt:.2f} s; value counts the same unmasked FLOPs per row"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=W.HEADLINE)
+    ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's choice")
+    ap.add_argument("--cpu-rows", type=int, default=32768,
+                    help="rows of the CPU-oracle sample (0 = skip the CPU leg)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              f"multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_forward_online_fa_amd as fa
+
+    wl = W.CONFIGS[args.config]
+    inp = W.make_inputs(wl)
+    q, k, v = device_inputs(inp, torch)
+    o = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, wl.Sq), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+    scale = wl.scale()
+    splits = fa.plan_splits(wl.B, wl.H, wl.HKV, wl.Sq, wl.Sk, wl.D, causal=bool(wl.causal),
+                            window=wl.window, dtype=wl.dtype) if args.num_splits == 0 else args.num_splits
+
+    def step():
+        fa.fwd_into(q, k, v, o, lse, causal=bool(wl.causal), window=wl.window, scale=scale,
+                    num_splits=args.num_splits, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1) / args.steps          # HIP events on the launch stream
+    ms_per_step = wall * 1e3 / args.steps
+
+    flops = counted_flops(wl)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (ev_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+    traffic = measured_traffic(wl)
+
+    rec = {
+        "metric": "attention fwd TFLOP/s (unmasked FLOPs) + % of MFMA peak, 1xMI355X",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "HKV": wl.HKV, "Sq": wl.Sq,
+                   "Sk": wl.Sk, "D": wl.D, "causal": wl.causal, "window": wl.window,
+                   "num_splits": splits, "counted_flops": flops,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic,
+                     "kernel_ms": round(ev_ms, 5),
+                     "algorithmic_bytes": algorithmic_bytes(wl)},
+    }
+    if args.cpu_rows > 0:
+        rec["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_rows)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,119 @@
+/*
+ * fa.h - fused attention forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * Computes, for every query row i of every (batch b, query head h):
+ *
+ *   O[b,h,i,:] = sum_j p_ij V[b,hk,j,:] / sum_j p_ij,   p_ij = exp(s_ij - max_j s_ij)
+ *   LSE[b,h,i] = log(sum_j exp(s_ij)),                  s_ij = scale * (Q[b,h,i,:] . K[b,hk,j,:])
+ *
+ * with hk = h / (H / HKV) (grouped-query attention) and j running over the
+ * keys visible to row i:
+ *   causal != 0  keeps j <= i (top-left aligned, also when Sq != Sk);
+ *   window  > 0  keeps j >= i - window + 1 (self included); 0 = no window.
+ * A row with no visible key gets O = 0 and LSE = -inf.
+ *
+ * Sources: the operation and the log-sum-exp output follow the rustytorch
+ * flash_attention_forward.metal kernel (online softmax, "log-sum-exp for
+ * backward" output); the GQA head map and the sliding window follow the
+ * forge flash_attention.metal forward kernel (FlashParams.window, hkv =
+ * h / (H / HKV)); the argument set (B, H, HKV, Sq, Sk, D, scale, causal,
+ * window) and the [B, H, S, D] layout follow the FlashParams uniform and
+ * header comment of the boostr flash.wgsl shader. The online-softmax
+ * recurrence (running max m, running sum l, rescale by exp(m_old - m_new))
+ * is the one in the forge header comment; nothing of size Sq x Sk is stored.
+ *
+ * The library is plain C ABI: no HIP or torch types in any signature.
+ */
+#ifndef FA_H
+#define FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of Q, K, V and O. LSE is always float32. */
+enum fa_dtype {
+  FA_F32 = 0,   /* float32 in and out, float32 MFMA arithmetic            */
+  FA_BF16 = 1   /* bfloat16 in and out, float32 accumulate and softmax    */
+};
+
+/* Status codes. Every argument error is detected on the host before any
+ * device work is queued; nothing is written in that case. */
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULLPTR = 1,   /* a required pointer is NULL                          */
+  FA_ERR_SHAPE = 2,     /* a dimension < 1, or a tensor larger than 2^62 bytes */
+  FA_ERR_GQA = 3,       /* H is not a multiple of HKV                          */
+  FA_ERR_HEAD_DIM = 4,  /* D not in {64, 128, 256}                             */
+  FA_ERR_DTYPE = 5,     /* dtype not an fa_dtype value                         */
+  FA_ERR_WINDOW = 6,    /* window < 0 or causal not 0/1                        */
+  FA_ERR_ALIGN = 7,     /* a buffer is not 16-byte aligned                     */
+  FA_ERR_HIP = 8,       /* the HIP runtime reported an error                   */
+  FA_ERR_WORKSPACE = 9, /* split-K workspace could not be allocated            */
+  FA_ERR_SPLITS = 10    /* num_splits < 0 or above FA_MAX_SPLITS               */
+};
+
+#define FA_MAX_SPLITS 64
+
+/*
+ * fa_fwd - forward pass.
+ *
+ *   Q    device pointer, [B, H,   Sq, D] contiguous, element type `dtype`
+ *   K    device pointer, [B, HKV, Sk, D] contiguous, element type `dtype`
+ *   V    device pointer, [B, HKV, Sk, D] contiguous, element type `dtype`
+ *   O    device pointer, [B, H,   Sq, D] contiguous, element type `dtype` (written)
+ *   LSE  device pointer, [B, H,   Sq]    contiguous, float32, natural log (written)
+ *   scale  multiplies q.k after the dot product (callers usually pass 1/sqrt(D))
+ *   causal 0 or 1; window >= 0 (0 = none)
+ *   stream hipStream_t to queue the work on, NULL = the null stream
+ *
+ * The caller owns all five buffers; all must be 16-byte aligned and must not
+ * overlap O or LSE with the inputs. Every element of O and LSE is written,
+ * including rows with no visible key. The call is asynchronous with respect
+ * to the host; it keeps no reference to the buffers after the queued work
+ * completes. Returns an fa_status code.
+ *
+ * Long key ranges with few query tiles are split across workgroups along the
+ * key axis and merged by log-sum-exp weights; the partial results live in a
+ * library-owned, stream-ordered workspace (see fa_release).
+ */
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+           int B, int H, int HKV, int Sq, int Sk, int D,
+           float scale, int causal, int window, int dtype, void* stream);
+
+/*
+ * fa_fwd_ex - fa_fwd with an explicit number of key-axis splits.
+ *
+ *   num_splits 0 = choose automatically (what fa_fwd does), 1 = never split,
+ *              n = split the key range into n contiguous chunks (n is capped
+ *              to the number of key tiles). At most FA_MAX_SPLITS.
+ * Same arguments, ownership and errors as fa_fwd otherwise.
+ */
+int fa_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE,
+              int B, int H, int HKV, int Sq, int Sk, int D,
+              float scale, int causal, int window, int dtype,
+              int num_splits, void* stream);
+
+/*
+ * fa_plan_splits - the number of key-axis splits fa_fwd would use for this
+ * problem on the current device (1 = no split). Returns a negative fa_status
+ * on argument errors. Queries the device once (HIP call), queues no work.
+ */
+int fa_plan_splits(int B, int H, int HKV, int Sq, int Sk, int D,
+                   int causal, int window, int dtype);
+
+/* fa_status_string - static, human-readable text for a status code. */
+const char* fa_status_string(int status);
+
+/*
+ * fa_release - return the split-K workspace pool of every device this
+ * library has used to the HIP runtime. Must not be called while work queued
+ * by fa_fwd is still running. Later calls allocate again as needed.
+ */
+void fa_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

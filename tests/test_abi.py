@@ -1,0 +1,116 @@
+"""The C ABI library loads, exports every function include/fa.h declares, and
+rejects bad arguments on the host before any device work. CPU only: every
+call here fails validation before the library touches the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_forward_online_fa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _header_text():
+    with open(HEADER) as fh:
+        text = fh.read()
+    return re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+
+
+def declared_functions():
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", _header_text())))
+
+
+def declared_enum():
+    vals = {}
+    for name, val in re.findall(r"\b(FA_[A-Z0-9_]+)\s*=\s*(\d+)", _header_text()):
+        vals[name] = int(val)
+    return vals
+
+
+def test_header_declares_the_expected_api():
+    assert declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libfa.so does not export {name}"
+    out = os.popen(f"nm -D --defined-only {_lib.library_path()}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", out), f"{name} not a defined text symbol"
+
+
+def test_enum_values_match_binding():
+    e = declared_enum()
+    assert e["FA_F32"] == _lib.FA_F32 and e["FA_BF16"] == _lib.FA_BF16
+    for code, name in _lib.STATUS.items():
+        assert e[name] == code
+    m = re.search(r"#define\s+FA_MAX_SPLITS\s+(\d+)", _header_text())
+    assert int(m.group(1)) == _lib.FA_MAX_SPLITS
+
+
+def test_status_strings():
+    lib = _lib.lib()
+    assert lib.fa_status_string(0) == b"ok"
+    for code in range(1, 11):
+        s = lib.fa_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.fa_status_string(999) == b"unknown status"
+
+
+A = 0x10000          # a 16-byte aligned fake address; never dereferenced
+GOOD = dict(B=1, H=4, HKV=2, Sq=64, Sk=64, D=128, scale=0.125, causal=1, window=0, dtype=1)
+
+
+def call(ptrs=(A, A, A, A, A), splits=0, **over):
+    a = dict(GOOD, **over)
+    return _lib.lib().fa_fwd_ex(*ptrs, a["B"], a["H"], a["HKV"], a["Sq"], a["Sk"], a["D"],
+                                a["scale"], a["causal"], a["window"], a["dtype"], splits, None)
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_null_pointer(which):
+    ptrs = [A] * 5
+    ptrs[which] = None
+    assert call(tuple(ptrs)) == 1
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(B=0), 2), (dict(H=0), 2), (dict(HKV=0), 2), (dict(Sq=0), 2), (dict(Sk=-3), 2),
+    (dict(H=6, HKV=4), 3), (dict(H=4, HKV=3), 3),
+    (dict(D=96), 4), (dict(D=32), 4), (dict(D=512), 4),
+    (dict(dtype=2), 5), (dict(dtype=-1), 5),
+    (dict(window=-1), 6), (dict(causal=2), 6),
+    (dict(B=1 << 20, H=1 << 10, Sq=1 << 10), 2),
+])
+def test_argument_errors(over, code):
+    assert call(**over) == code
+
+
+def test_split_count_errors():
+    assert call(splits=-1) == 10
+    assert call(splits=65) == 10
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_misaligned_buffer(which):
+    ptrs = [A] * 5
+    ptrs[which] = A + 4
+    assert call(tuple(ptrs)) == 7
+
+
+def test_plan_splits_rejects_bad_args_without_device():
+    lib = _lib.lib()
+    assert lib.fa_plan_splits(1, 4, 3, 64, 64, 128, 0, 0, 1) == -3
+    assert lib.fa_plan_splits(1, 4, 4, 64, 64, 80, 0, 0, 1) == -4
+
+
+def test_python_binding_fails_loudly_on_cpu_tensors():
+    import torch
+    import attention_forward_online_fa_amd as fa
+    q = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q)

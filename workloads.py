@@ -86,9 +86,12 @@ def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """float32 array -> uint16 bf16 bit patterns, round to nearest, ties to even.
 
     Inputs here are finite, so no NaN special case is needed."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    bias = 0x7FFF + ((u >> 16) & 1)
-    return ((u + bias) >> 16).astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    assert np.all(np.isfinite(x)), "bf16 rounding expects finite inputs"
+    # For finite inputs u + 0x8000 stays below 2**32, so uint32 arithmetic is exact.
+    r = u + np.uint32(0x7FFF)
+    r += (u >> np.uint32(16)) & np.uint32(1)
+    return (r >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
