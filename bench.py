@@ -113,8 +113,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=W.HEADLINE)
     ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's choice")
-    ap.add_argument("--cpu-rows", type=int, default=32768,
+    ap.add_argument("--cpu-rows", type=int, default=262144,
                     help="rows of the CPU-oracle sample (0 = skip the CPU leg)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of attention, run a plain device-to-device copy of MIB "
+                         "MiB (reference for scaling HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -124,6 +127,17 @@ def main():
 
     import torch
     import attention_forward_online_fa_amd as fa
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n,
+                          "launches": max(args.steps, 1)}), flush=True)
+        return
 
     wl = W.CONFIGS[args.config]
     inp = W.make_inputs(wl)
