@@ -125,6 +125,15 @@ __device__ __forceinline__ void finish_row(const Params& p, int b, int h, int sp
 // A row r from key pi(r) (bits 2 and 3 of r swapped) makes element v of that
 // lane hold key 16(v/8) + 8g + v%8: eight consecutive keys per lane half,
 // which is exactly the k-slot order the PV MFMA wants for its B operand.
+//
+// K and V tiles are copied HBM -> LDS by the buffer unit (buffer_load_dwordx4
+// ... lds): no VGPRs and no VALU work, and rows past the end of the key axis
+// come back as zeros from the buffer range check. Both tiles stay row-major
+// ([key][dim]) with a 16-byte-chunk XOR swizzle. The PV MFMA needs V^T as its
+// A operand (eight consecutive keys of one dim per lane); ds_read_b64_tr_b16
+// delivers exactly that from the row-major V tile: within each 16-lane block,
+// lane 4r + c reads 4 dims of key row r and the hardware hands lane j the
+// 4 keys of dim j.
 __device__ __forceinline__ int perm_row(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
@@ -134,34 +143,63 @@ struct Bf16Tile {
   static constexpr int DC = D / 16;      // k-steps of the S MFMA
   static constexpr int DB = D / 32;      // 32-dim blocks of the O^T accumulator
   static constexpr int KB = BN / 32;     // 32-key blocks of S^T
-  static constexpr int KROW = D * 2;     // bytes per K row in LDS
-  static constexpr int CPR = D / 8;      // 16-byte chunks per K row
-  static constexpr int VROW = BN * 2;    // bytes per V^T row in LDS
-  static constexpr int CPV = BN / 8;     // 16-byte chunks per V^T row
-  static constexpr int KBYTES = BN * KROW;
-  static constexpr int VBYTES = D * VROW;
-  static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int K_IT = BN * CPR / kThreads;                  // K chunks per thread
-  static constexpr int VBLK = (BN / 4) * (D / 8);                   // 4-key x 8-dim blocks
-  static constexpr int V_IT = (VBLK + kThreads - 1) / kThreads;
-  static_assert(BN * CPR % kThreads == 0, "K tile must split evenly over the workgroup");
+  static constexpr int KC = BN / 16;     // 16-key chunks of the PV MFMA
+  static constexpr int ROW = D * 2;      // bytes per K or V row in LDS
+  static constexpr int CPR = D / 8;      // 16-byte chunks per row
+  static constexpr int TILE = BN * ROW;  // bytes per K or V tile
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int NI = BN * CPR / 64;       // 1 KB DMA wave-instructions per tile
+  static constexpr int NIW = NI / 4;             // ... per wavefront
+  static_assert(NI % 4 == 0, "each wavefront issues the same number of DMA instructions");
 
-  // XOR swizzles on 16-byte chunks: a wavefront's 16-lane groups read 16
-  // distinct bank quads for both the K reads (16 keys, one chunk) and the V^T
-  // reads (16 dims, one chunk).
+  // K reads: 16 lanes read one chunk of 16 different keys -> XOR with the key.
   __device__ static __forceinline__ int swz_k(int key) {
     return CPR >= 16 ? (key & 15) : ((key >> 1) & 7);
   }
-  __device__ static __forceinline__ int swz_v(int d) {
-    return (d / (16 / CPV)) % CPV;
+  // V transpose reads: 32 lanes read 4 chunks of 4 consecutive keys -> move
+  // each key of the group of 4 to its own group of 4 chunks.
+  __device__ static __forceinline__ int swz_v(int key) {
+    return CPR >= 16 ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
   }
 };
 
-template <int D, int BN>
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ bf16x8 read_v_pair(const char* base, int off0, int off1) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_char*)(base + off0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_char*)(base + off1));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// One 16-byte-per-lane HBM -> LDS copy: lane l's 16 bytes at base + voff land
+// at lds + 16 l (bytes past `bytes` read as zero).
+__device__ __forceinline__ void dma16(const void* base, unsigned bytes, int voff, char* lds) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_char*)lds, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_dma_and_sync() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+__device__ __forceinline__ float half_max(float x) {
+  // max over lane and lane ^ 32 (the two halves of one query row's keys)
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+constexpr float kRescaleSlack = 8.f;   // log2 units: P stays <= 2^8 between rescales
+
+template <int D, int BN, bool kPosScale>
 __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1))
 void fwd_bf16_kernel(Params p) {
   using T = Bf16Tile<D, BN>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -179,6 +217,28 @@ void fwd_bf16_kernel(Params p) {
   const int t0 = (lo / BN) * BN;
   const int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
 
+  // DMA: LDS chunk P = 64 (wave NIW + k) + lane of a tile holds logical chunk
+  // (P % CPR) ^ swz(row) of row P / CPR.
+  int voff_k[T::NIW], voff_v[T::NIW];
+#pragma unroll
+  for (int k = 0; k < T::NIW; ++k) {
+    const int P = 64 * (wave * T::NIW + k) + lane;
+    const int row = P / T::CPR, pc = P % T::CPR;
+    voff_k[k] = row * T::ROW + ((pc ^ T::swz_k(row)) << 4);
+    voff_v[k] = row * T::ROW + ((pc ^ T::swz_v(row)) << 4);
+  }
+  auto issue_tile = [&](char* st, int kt) {
+    const unsigned bytes = (unsigned)min((long)(p.Sk - kt) * T::ROW, 0x7fffffffL);
+    const __bf16* kb = Kp + (size_t)kt * D;
+    const __bf16* vb = Vp + (size_t)kt * D;
+#pragma unroll
+    for (int k = 0; k < T::NIW; ++k) {
+      char* dk = st + (wave * T::NIW + k) * 1024;
+      dma16(kb, bytes, voff_k[k], dk);
+      dma16(vb, bytes, voff_v[k], dk + T::TILE);
+    }
+  };
+
   // Query rows as the B operand: k-slot (g, e) of step t is dim 16t + 8g + e.
   bf16x8 qf[T::DC];
 #pragma unroll
@@ -189,163 +249,128 @@ void fwd_bf16_kernel(Params p) {
       qf[t] = bf16x8{};
   }
 
+  // Per-lane LDS read offsets (tile-relative).
+  const int krow = perm_row(l32);
+  int koff[T::DC];
+#pragma unroll
+  for (int t = 0; t < T::DC; ++t) koff[t] = krow * T::ROW + (((2 * t + g) ^ T::swz_k(krow)) << 4);
+  const int blk = lane >> 4, li = lane & 15;
+  const int vrow = 8 * g + (li >> 2);                       // + 16 C + 4 h
+  int voff[T::DB];
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db) {
+    const int chunk = 4 * db + 2 * (blk & 1) + ((li & 3) >> 1);
+    voff[db] = vrow * T::ROW + ((chunk ^ T::swz_v(vrow)) << 4) + 8 * (li & 1);
+  }
+
   f32x16 o[T::DB];
 #pragma unroll
   for (int db = 0; db < T::DB; ++db) o[db] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  float m_ref = -INFINITY, l = 0.f;
+  const float sl = p.sl;
 
-  u32x4 kreg[T::K_IT];
-  u32x4 vreg[T::V_IT][4];
-
-  auto load_tile = [&](int kt) {
+  auto compute_tile = [&](const char* Ks, int kt) {
+    const char* Vs = Ks + T::TILE;
+    // ---- S^T = K Q^T
+    f32x16 s[T::KB];
 #pragma unroll
-    for (int it = 0; it < T::K_IT; ++it) {
-      const int c = tid + it * kThreads;
-      const int row = c / T::CPR, ch = c % T::CPR;
-      const int key = kt + row;
-      kreg[it] = key < p.Sk ? *(const u32x4*)(Kp + (size_t)key * D + ch * 8) : u32x4{};
-    }
+    for (int kb = 0; kb < T::KB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-    for (int it = 0; it < T::V_IT; ++it) {
-      const int blk = tid + it * kThreads;
-      const int db8 = blk % (D / 8), kb4 = blk / (D / 8);
+    for (int t = 0; t < T::DC; ++t) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kt + 4 * kb4 + r;
-        vreg[it][r] = (blk < T::VBLK && key < p.Sk)
-                          ? *(const u32x4*)(Vp + (size_t)key * D + db8 * 8)
-                          : u32x4{};
+      for (int kb = 0; kb < T::KB; ++kb) {
+        const bf16x8 a = *(const bf16x8*)(Ks + koff[t] + kb * 32 * T::ROW);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb], 0, 0, 0);
       }
     }
-  };
-
-  auto store_tile = [&](char* st) {
-    char* Ks = st;
-    char* Vs = st + T::KBYTES;
+    // ---- mask edge tiles; row max
+    const bool edge = (kt + BN > p.Sk) || (p.causal && kt + BN - 1 > qw) ||
+                      (p.window > 0 && kt < qw + 31 - p.window + 1);
+    if (!kPosScale) {
 #pragma unroll
-    for (int it = 0; it < T::K_IT; ++it) {
-      const int c = tid + it * kThreads;
-      const int row = c / T::CPR, ch = c % T::CPR;
-      *(u32x4*)(Ks + row * T::KROW + ((ch ^ T::swz_k(row)) << 4)) = kreg[it];
+      for (int kb = 0; kb < T::KB; ++kb) s[kb] *= sl;
     }
+    if (edge) {
 #pragma unroll
-    for (int it = 0; it < T::V_IT; ++it) {
-      const int blk = tid + it * kThreads;
-      if (blk >= T::VBLK) continue;
-      const int db8 = blk % (D / 8), kb4 = blk / (D / 8);
-      // vreg[it][r] = V[key 4 kb4 + r][dims 8 db8 .. +7]; write V^T rows.
+      for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int wd = c >> 1;
-        unsigned x0 = vreg[it][0][wd], x1 = vreg[it][1][wd];
-        unsigned x2 = vreg[it][2][wd], x3 = vreg[it][3][wd];
-        unsigned lo2, hi2;
-        if ((c & 1) == 0) {
-          lo2 = (x0 & 0xffffu) | (x1 << 16);
-          hi2 = (x2 & 0xffffu) | (x3 << 16);
-        } else {
-          lo2 = (x0 >> 16) | (x1 & 0xffff0000u);
-          hi2 = (x2 >> 16) | (x3 & 0xffff0000u);
+        for (int v = 0; v < 16; ++v) {
+          const int j = kt + 32 * kb + 16 * (v >> 3) + 8 * g + (v & 7);
+          if (!visible(p, i, j)) s[kb][v] = -INFINITY;
         }
-        const int d = 8 * db8 + c;
-        char* dst = Vs + d * T::VROW + (((kb4 >> 1) ^ T::swz_v(d)) << 4) + (kb4 & 1) * 8;
-        *(u32x2*)dst = u32x2{lo2, hi2};
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+    mx = half_max(mx);
+    const float mt = kPosScale ? mx * sl : mx;     // tile max in base-2 units
+    // ---- lazy rescale: move the reference max only when it grows by more
+    // than kRescaleSlack; exact, since O and l always share the reference.
+    const bool grow = mt > m_ref + kRescaleSlack;
+    if (__any(grow)) {
+      const float corr = grow ? fast_exp2(m_ref - mt) : 1.f;
+      m_ref = grow ? mt : m_ref;
+      l *= corr;
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) o[db] *= corr;
+    }
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    // ---- P = exp2(S - m), packed to bf16 for the PV MFMA; l += rowsum(P)
+    bf16x8 pf[T::KC];
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = s[kb][8 * c2 + e];
+          const float pe = kPosScale ? fast_exp2(fmaf(x, sl, -m_use)) : fast_exp2(x - m_use);
+          pf[2 * kb + c2][e] = (__bf16)pe;
+        }
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    float rs = 0.f;
+#pragma unroll
+    for (int c = 0; c < T::KC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 two = {pf[c][e], pf[c][e + 1]};
+        rs = __builtin_amdgcn_fdot2_f32_bf16(two, ones, rs, false);
+      }
+    l += rs;
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int c = 0; c < T::KC; ++c) {
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        const int base = 16 * c * T::ROW;
+        const bf16x8 a = read_v_pair(Vs, voff[db] + base, voff[db] + base + 4 * T::ROW);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c], o[db], 0, 0, 0);
       }
     }
   };
 
-  if (n_tiles > 0) {
-    load_tile(t0);
-    store_tile(smem);
-  }
-  __syncthreads();
+  auto wave_skips = [&](int kt) {
+    return qw >= p.Sq || (p.causal && kt > qw + 31) ||
+           (p.window > 0 && kt + BN - 1 < qw - p.window + 1);
+  };
 
-  const int krow = perm_row(l32);
-  for (int it = 0; it < n_tiles; ++it) {
+  if (n_tiles > 0) issue_tile(smem, t0);
+  for (int it = 0; it < n_tiles; it += 2) {
     const int kt = t0 + it * BN;
-    const char* Ks = smem + (it & 1) * T::STAGE;
-    const char* Vs = Ks + T::KBYTES;
-    if (it + 1 < n_tiles) load_tile(kt + BN);
-
-    const bool skip = qw >= p.Sq || (p.causal && kt > qw + 31) ||
-                      (p.window > 0 && kt + BN - 1 < qw - p.window + 1);
-    if (!skip) {
-      // ---- S^T = K Q^T
-      f32x16 s[T::KB];
-#pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-      for (int t = 0; t < T::DC; ++t) {
-#pragma unroll
-        for (int kb = 0; kb < T::KB; ++kb) {
-          const int key = kb * 32 + krow;
-          const int ch = 2 * t + g;
-          const bf16x8 a = *(const bf16x8*)(Ks + key * T::KROW + ((ch ^ T::swz_k(key)) << 4));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb], 0, 0, 0);
-        }
-      }
-      // ---- scale to base-2 units, mask edge tiles
-      const bool edge = (kt + BN > p.Sk) || (p.causal && kt + BN - 1 > qw) ||
-                        (p.window > 0 && kt < qw + 31 - p.window + 1);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = s[kb][v] * p.sl;
-          if (edge) {
-            const int j = kt + 32 * kb + 16 * (v >> 3) + 8 * g + (v & 7);
-            x = visible(p, i, j) ? x : -INFINITY;
-          }
-          s[kb][v] = x;
-          mx = fmaxf(mx, x);
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float corr = fast_exp2(m - m_use);
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float e = fast_exp2(s[kb][v] - m_use);
-          s[kb][v] = e;
-          rs += e;
-        }
-      }
-      l = l * corr + rs;
-      m = m_new;
-      if (__any(corr != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < T::DB; ++db) o[db] *= corr;
-      }
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          bf16x8 pf;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pf[e] = (__bf16)s[kb][8 * c2 + e];
-          const int ch = 2 * (2 * kb + c2) + g;
-#pragma unroll
-          for (int db = 0; db < T::DB; ++db) {
-            const int d = 32 * db + l32;
-            const bf16x8 a = *(const bf16x8*)(Vs + d * T::VROW + ((ch ^ T::swz_v(d)) << 4));
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, o[db], 0, 0, 0);
-          }
-        }
-      }
-    }
-
-    if (it + 1 < n_tiles) store_tile((char*)smem + ((it + 1) & 1) * T::STAGE);
-    __syncthreads();
+    wait_dma_and_sync();
+    if (it + 1 < n_tiles) issue_tile(smem + T::STAGE, kt + BN);
+    if (!wave_skips(kt)) compute_tile(smem, kt);
+    if (it + 1 >= n_tiles) break;
+    wait_dma_and_sync();
+    if (it + 2 < n_tiles) issue_tile(smem, kt + 2 * BN);
+    if (!wave_skips(kt + BN)) compute_tile(smem + T::STAGE, kt + BN);
   }
 
   // ---- epilogue: lane holds dims 32 db + 8 a + 4 g + (0..3) of row i.
-  finish_row(p, w.b, w.h, w.split, i, g, m, l,
+  finish_row(p, w.b, w.h, w.split, i, g, m_ref, l,
              [&](bool partial, size_t row, int split, float inv) {
                if (partial) {
                  const size_t rows = (size_t)p.B * p.H * p.Sq;
@@ -623,7 +648,10 @@ static hipError_t launch_d(const Params& p, int dtype, hipStream_t stream) {
   const long blocks = (long)p.units * p.n_qblk;
   if (dtype == 1) {
     constexpr int BN = D == 256 ? 32 : 64;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BN>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    if (p.sl > 0.f)
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   } else {
     hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   }

@@ -43,6 +43,14 @@ def test_library_exports_every_declared_symbol():
         assert re.search(rf"\bT {name}\b", out), f"{name} not a defined text symbol"
 
 
+def test_library_has_no_undefined_symbols_of_its_own():
+    # A kernel whose host-side launch stub was not emitted shows up as an
+    # undefined fa:: symbol; the library would then fail to load on any box.
+    out = os.popen(f"nm -D --undefined-only {_lib.library_path()}").read()
+    own = [ln for ln in out.splitlines() if "_ZN2fa" in ln or " fa_" in ln]
+    assert not own, f"unresolved library symbols: {own}"
+
+
 def test_enum_values_match_binding():
     e = declared_enum()
     assert e["FA_F32"] == _lib.FA_F32 and e["FA_BF16"] == _lib.FA_BF16
