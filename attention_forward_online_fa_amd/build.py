@@ -33,17 +33,56 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
+# Kernels allowed to use private (scratch) memory. Every other kernel must keep
+# all its state in registers and LDS; scratch traffic would dominate its time.
+SCRATCH_ALLOWED = ("fwd_f32_kernelILi256E",)
+
+
+def parse_resource_usage(remarks: str) -> dict:
+    """Per-kernel {name: {"vgpr":, "agpr":, "scratch":, "vgpr_spill":, "lds":}} from
+    hipcc's -Rpass-analysis=kernel-resource-usage remarks."""
+    out, cur = {}, None
+    keys = {"VGPRs": "vgpr", "AGPRs": "agpr", "ScratchSize [bytes/lane]": "scratch",
+            "VGPRs Spill": "vgpr_spill", "LDS Size [bytes/block]": "lds"}
+    for line in remarks.splitlines():
+        if "remark:" not in line:
+            continue
+        body = line.split("remark:", 1)[1].split(" [-Rpass", 1)[0].strip()
+        if body.startswith("Function Name:"):
+            cur = body.split(":", 1)[1].strip()
+            out[cur] = {}
+        elif cur is not None and ":" in body:
+            k, v = body.rsplit(":", 1)
+            if k.strip() in keys:
+                try:
+                    out[cur][keys[k.strip()]] = int(v.strip())
+                except ValueError:
+                    pass
+    return out
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source into libfa.so (always recompiles). Returns the path."""
+    """Compile every source into libfa.so (always recompiles). Returns the path.
+
+    Fails if a kernel outside SCRATCH_ALLOWED uses scratch memory."""
     tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
+    cmd = [hipcc(), *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-I", INCLUDE,
+           "-I", CSRC, *SOURCES, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
-    if verbose or res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
     if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
         if os.path.exists(tmp):
             os.remove(tmp)
         raise RuntimeError(f"hipcc failed with status {res.returncode}: {' '.join(cmd)}")
+    usage = parse_resource_usage(res.stderr)
+    bad = [k for k, u in usage.items()
+           if u.get("scratch", 0) > 0 and not any(a in k for a in SCRATCH_ALLOWED)]
+    if verbose:
+        for k, u in sorted(usage.items()):
+            sys.stderr.write(f"{k}: {u}\n")
+    if bad:
+        os.remove(tmp)
+        raise RuntimeError(f"kernels use scratch memory: {bad}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

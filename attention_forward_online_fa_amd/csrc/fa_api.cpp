@@ -86,7 +86,7 @@ int check_args(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int win
 // GPU (fewer tiles than compute units), and never below 4 key tiles per split.
 int auto_splits(int B, int H, int Sq, int Sk, int D, int causal, int window, int dtype,
                 int num_cus) {
-  const int BM = fa::kBlockM, BN = fa::key_tile(dtype, D);
+  const int BM = fa::block_m(dtype, D), BN = fa::key_tile(dtype, D);
   const long n_qblk = (Sq + BM - 1) / BM;
   const long work = (long)B * H * n_qblk;
   if (work >= num_cus) return 1;
@@ -129,7 +129,7 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   st = device_state(&ds);
   if (st != FA_OK) return st;
 
-  const int BM = fa::kBlockM;
+  const int BM = fa::block_m(dtype, D);
   int ns = 1, split_len = 0;
   resolve_splits(num_splits, B, H, Sq, Sk, D, causal, window, dtype, ds->num_cus, &ns,
                  &split_len);

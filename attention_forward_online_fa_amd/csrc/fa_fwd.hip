@@ -62,7 +62,10 @@ __device__ __forceinline__ Tile map_tile(const Params& p) {
   int t, u;
   if (p.xcd_remap) {
     // Block i runs on XCD i % 8 as that XCD's (i / 8)-th block. Give XCD x
-    // the contiguous unit range [x U/8, (x+1) U/8), heaviest tiles first.
+    // the contiguous unit range [x U/8, (x+1) U/8).
+    // Within an XCD: query tile major (heaviest first), then unit; the units
+    // of one XCD are consecutive, so query heads sharing a K/V head run there
+    // together. (Ordering kv-head-group major instead measured ~1.5% slower.)
     const int upx = p.units >> 3;
     const int k = i >> 3;
     t = k / upx;
@@ -83,11 +86,12 @@ __device__ __forceinline__ Tile map_tile(const Params& p) {
   return w;
 }
 
-// Key range [lo, hi) a workgroup with rows [q0, q0 + kBlockM) must visit.
-__device__ __forceinline__ void key_range(const Params& p, int q0, int split, int& lo, int& hi) {
+// Key range [lo, hi) a workgroup with rows [q0, q0 + bm) must visit.
+__device__ __forceinline__ void key_range(const Params& p, int q0, int bm, int split, int& lo,
+                                          int& hi) {
   lo = split * p.split_len;
   hi = min(p.Sk, lo + p.split_len);
-  const int last = min(q0 + kBlockM, p.Sq) - 1;
+  const int last = min(q0 + bm, p.Sq) - 1;
   if (p.causal) hi = min(hi, last + 1);
   if (p.window > 0) lo = max(lo, q0 - p.window + 1);
 }
@@ -193,15 +197,22 @@ __device__ __forceinline__ float half_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-constexpr float kRescaleSlack = 8.f;   // log2 units: P stays <= 2^8 between rescales
+constexpr float kRowSumLimit = 1.8446744e19f;   // 2^64: row-sum bound that triggers a rescale
 
 template <int D, int BN, bool kPosScale>
 __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1))
 void fwd_bf16_kernel(Params p) {
   using T = Bf16Tile<D, BN>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
+  // K and V tiles double-buffered; four separate objects let the compiler see
+  // that the copy filling one buffer never aliases the reads of another (it
+  // would otherwise wait for the in-flight copy before reading).
+  __shared__ __attribute__((aligned(1024))) char kbuf0[T::TILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[T::TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[T::TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[T::TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
   const int l32 = lane & 31, g = lane >> 5;
   const Tile w = map_tile(p);
   const int q0 = w.qblk * kBlockM;
@@ -213,7 +224,7 @@ void fwd_bf16_kernel(Params p) {
   const __bf16* Vp = (const __bf16*)p.V + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
 
   int lo, hi;
-  key_range(p, q0, w.split, lo, hi);
+  key_range(p, q0, kBlockM, w.split, lo, hi);
   const int t0 = (lo / BN) * BN;
   const int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
 
@@ -227,15 +238,15 @@ void fwd_bf16_kernel(Params p) {
     voff_k[k] = row * T::ROW + ((pc ^ T::swz_k(row)) << 4);
     voff_v[k] = row * T::ROW + ((pc ^ T::swz_v(row)) << 4);
   }
-  auto issue_tile = [&](char* st, int kt) {
+  auto issue = [&](int kt, char* kdst, char* vdst) {
     const unsigned bytes = (unsigned)min((long)(p.Sk - kt) * T::ROW, 0x7fffffffL);
     const __bf16* kb = Kp + (size_t)kt * D;
     const __bf16* vb = Vp + (size_t)kt * D;
 #pragma unroll
     for (int k = 0; k < T::NIW; ++k) {
-      char* dk = st + (wave * T::NIW + k) * 1024;
-      dma16(kb, bytes, voff_k[k], dk);
-      dma16(vb, bytes, voff_v[k], dk + T::TILE);
+      const int off = (wave * T::NIW + k) * 1024;
+      dma16(kb, bytes, voff_k[k], kdst + off);
+      dma16(vb, bytes, voff_v[k], vdst + off);
     }
   };
 
@@ -268,11 +279,11 @@ void fwd_bf16_kernel(Params p) {
   for (int db = 0; db < T::DB; ++db) o[db] = f32x16{};
   float m_ref = -INFINITY, l = 0.f;
   const float sl = p.sl;
+  f32x16 s[T::KB];
+  bf16x8 pf[T::KC];
 
-  auto compute_tile = [&](const char* Ks, int kt) {
-    const char* Vs = Ks + T::TILE;
-    // ---- S^T = K Q^T
-    f32x16 s[T::KB];
+  // ---- S^T = K Q^T for one tile
+  auto qk = [&](const char* Ks) {
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb) s[kb] = f32x16{};
 #pragma unroll
@@ -283,42 +294,40 @@ void fwd_bf16_kernel(Params p) {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb], 0, 0, 0);
       }
     }
-    // ---- mask edge tiles; row max
-    const bool edge = (kt + BN > p.Sk) || (p.causal && kt + BN - 1 > qw) ||
-                      (p.window > 0 && kt < qw + 31 - p.window + 1);
+  };
+
+  // ---- mask the keys of an edge tile this row cannot see
+  auto mask = [&](int kt) {
     if (!kPosScale) {
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb) s[kb] *= sl;
     }
+    const bool edge = (kt + BN > p.Sk) || (p.causal && kt + BN - 1 > qw) ||
+                      (p.window > 0 && kt < qw + 31 - p.window + 1);
     if (edge) {
+      // Element v of block kb holds key kt + 8g + c with c = 32kb + 16(v/8) + v%8,
+      // a compile-time constant: compare it with this row's visible range.
+      const int base = kt + 8 * g;
+      const int hi_c = (p.causal ? min(i, p.Sk - 1) : p.Sk - 1) - base;   // c <= hi_c
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int j = kt + 32 * kb + 16 * (v >> 3) + 8 * g + (v & 7);
-          if (!visible(p, i, j)) s[kb][v] = -INFINITY;
-        }
+        for (int v = 0; v < 16; ++v)
+          if (32 * kb + 16 * (v >> 3) + (v & 7) > hi_c) s[kb][v] = -INFINITY;
+      if (p.window > 0) {
+        const int lo_c = i - p.window + 1 - base;                           // c >= lo_c
+#pragma unroll
+        for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (32 * kb + 16 * (v >> 3) + (v & 7) < lo_c) s[kb][v] = -INFINITY;
+      }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < T::KB; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-    mx = half_max(mx);
-    const float mt = kPosScale ? mx * sl : mx;     // tile max in base-2 units
-    // ---- lazy rescale: move the reference max only when it grows by more
-    // than kRescaleSlack; exact, since O and l always share the reference.
-    const bool grow = mt > m_ref + kRescaleSlack;
-    if (__any(grow)) {
-      const float corr = grow ? fast_exp2(m_ref - mt) : 1.f;
-      m_ref = grow ? mt : m_ref;
-      l *= corr;
-#pragma unroll
-      for (int db = 0; db < T::DB; ++db) o[db] *= corr;
-    }
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    // ---- P = exp2(S - m), packed to bf16 for the PV MFMA; l += rowsum(P)
-    bf16x8 pf[T::KC];
+  };
+
+  // ---- P = exp2(S - m_sub) packed to bf16; returns this lane's row sum of P
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  auto exp_pack_sum = [&](float m_sub) {
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
@@ -326,10 +335,9 @@ void fwd_bf16_kernel(Params p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float x = s[kb][8 * c2 + e];
-          const float pe = kPosScale ? fast_exp2(fmaf(x, sl, -m_use)) : fast_exp2(x - m_use);
+          const float pe = kPosScale ? fast_exp2(fmaf(x, sl, -m_sub)) : fast_exp2(x - m_sub);
           pf[2 * kb + c2][e] = (__bf16)pe;
         }
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
     float rs = 0.f;
 #pragma unroll
@@ -339,8 +347,38 @@ void fwd_bf16_kernel(Params p) {
         const bf16x2 two = {pf[c][e], pf[c][e + 1]};
         rs = __builtin_amdgcn_fdot2_f32_bf16(two, ones, rs, false);
       }
+    return rs;
+  };
+
+  // ---- softmax of one tile against the running reference max m_ref. The
+  // exact tile max is only needed when the reference is too stale (or still
+  // -inf): then some lane's row sum exceeds 2^64 (or is +inf), and the wave
+  // takes the slow path: true row max, rescale O and l, recompute P. Exact in
+  // every case, since O and l always share one reference; between rescales
+  // every P stays below 2^64, far inside the float32 and bfloat16 range.
+  auto softmax = [&]() {
+    float rs = exp_pack_sum(m_ref == -INFINITY ? -1e30f : m_ref);
+    if (__any(!(rs <= kRowSumLimit))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+      mx = half_max(mx);
+      const float mt = kPosScale ? mx * sl : mx;   // tile max in base-2 units
+      const float m_new = fmaxf(m_ref, mt);
+      const float corr = fast_exp2(m_ref - (m_new == -INFINITY ? 0.f : m_new));
+      m_ref = m_new;
+      l *= corr;
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) o[db] *= corr;
+      rs = exp_pack_sum(m_ref == -INFINITY ? 0.f : m_ref);
+    }
     l += rs;
-    // ---- O^T += V^T P^T
+  };
+
+  // ---- O^T += V^T P^T
+  auto pv = [&](const char* Vs) {
 #pragma unroll
     for (int c = 0; c < T::KC; ++c) {
 #pragma unroll
@@ -357,16 +395,23 @@ void fwd_bf16_kernel(Params p) {
            (p.window > 0 && kt + BN - 1 < qw - p.window + 1);
   };
 
-  if (n_tiles > 0) issue_tile(smem, t0);
-  for (int it = 0; it < n_tiles; it += 2) {
-    const int kt = t0 + it * BN;
+  // One tile: K(t), V(t) in (Kc, Vc); the copy of tile t+1 goes to (Kn, Vn).
+  auto step = [&](int t, const char* Kc, const char* Vc, char* Kn, char* Vn) {
+    const int kt = t0 + t * BN;
     wait_dma_and_sync();
-    if (it + 1 < n_tiles) issue_tile(smem + T::STAGE, kt + BN);
-    if (!wave_skips(kt)) compute_tile(smem, kt);
-    if (it + 1 >= n_tiles) break;
-    wait_dma_and_sync();
-    if (it + 2 < n_tiles) issue_tile(smem, kt + 2 * BN);
-    if (!wave_skips(kt + BN)) compute_tile(smem + T::STAGE, kt + BN);
+    if (t + 1 < n_tiles) issue(kt + BN, Kn, Vn);
+    if (wave_skips(kt)) return;
+    qk(Kc);
+    mask(kt);
+    softmax();
+    pv(Vc);
+  };
+
+  if (n_tiles > 0) issue(t0, kbuf0, vbuf0);
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, kbuf0, vbuf0, kbuf1, vbuf1);
+    if (t + 1 >= n_tiles) break;
+    step(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
   }
 
   // ---- epilogue: lane holds dims 32 db + 8 a + 4 g + (0..3) of row i.
@@ -437,7 +482,7 @@ void fwd_f32_kernel(Params p) {
   const float* Vp = (const float*)p.V + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
 
   int lo, hi;
-  key_range(p, q0, w.split, lo, hi);
+  key_range(p, q0, kBlockM, w.split, lo, hi);
   const int t0 = (lo / BN) * BN;
   const int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
 
@@ -457,7 +502,7 @@ void fwd_f32_kernel(Params p) {
   float m = -INFINITY, l = 0.f;
 
   f32x4 kreg[T::IT], vreg[T::IT];
-  auto load_tile = [&](int kt) {
+  auto load_tile = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < T::IT; ++it) {
       const int c = tid + it * kThreads;
@@ -468,7 +513,7 @@ void fwd_f32_kernel(Params p) {
       vreg[it] = ok ? *(const f32x4*)(Vp + (size_t)key * D + 4 * c4) : f32x4{};
     }
   };
-  auto store_tile = [&](float* st) {
+  auto store_tile = [&](float* st) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < T::IT; ++it) {
       const int c = tid + it * kThreads;
@@ -562,7 +607,7 @@ void fwd_f32_kernel(Params p) {
 
   // ---- epilogue: element v of block db is dim (D/32)(8(v/4) + 4g + v%4) + db.
   finish_row(p, w.b, w.h, w.split, i, g, m, l,
-             [&](bool partial, size_t row, int split, float inv) {
+             [&](bool partial, size_t row, int split, float inv) __attribute__((always_inline)) {
                float* dst;
                if (partial) {
                  const size_t rows = (size_t)p.B * p.H * p.Sq;
@@ -632,6 +677,8 @@ int key_tile(int dtype, int D) {
   if (dtype == 1) return D == 256 ? 32 : 64;
   return F32Tile<64>::BN;
 }
+
+int block_m(int dtype, int D) { return kBlockM; }
 
 template <typename OutT, int D>
 static hipError_t launch_merge(const Params& p, hipStream_t stream) {

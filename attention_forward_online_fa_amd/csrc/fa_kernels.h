@@ -30,6 +30,7 @@ struct Params {
 // Tile shape per (dtype, D): query rows per workgroup and keys per K/V tile.
 constexpr int kBlockM = 128;
 int key_tile(int dtype, int D);
+int block_m(int dtype, int D);
 
 // Queue the forward kernel (and the merge kernel when p.nsplit > 1).
 hipError_t launch_forward(const Params& p, int dtype, int D, hipStream_t stream);
