@@ -147,6 +147,14 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   p.Sk = Sk;
   p.group = H / HKV;
   p.sl = (float)((double)scale * 1.4426950408889634);
+  if (dtype == FA_BF16) {
+    // The bf16 kernel needs a positive multiplier: q.k * scale = (-q).k * |scale|
+    // exactly, and for scale = 0 a multiplier of 1e-30 leaves every exp2
+    // argument within 1e-20 of 0, where exp2 rounds to exactly 1.
+    p.neg_q = scale < 0.f ? 1 : 0;
+    const double mag = std::fabs((double)scale) * 1.4426950408889634;
+    p.sl = mag > 0.0 ? (float)mag : 1e-30f;
+  }
   p.causal = causal;
   p.window = window;
   p.nsplit = ns;

@@ -199,7 +199,7 @@ __device__ __forceinline__ float half_max(float x) {
 
 constexpr float kRowSumLimit = 1.8446744e19f;   // 2^64: row-sum bound that triggers a rescale
 
-template <int D, int BN, bool kPosScale>
+template <int D, int BN>
 __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1))
 void fwd_bf16_kernel(Params p) {
   using T = Bf16Tile<D, BN>;
@@ -258,6 +258,10 @@ void fwd_bf16_kernel(Params p) {
       qf[t] = *(const bf16x8*)(Qp + (size_t)i * D + 16 * t + 8 * g);
     else
       qf[t] = bf16x8{};
+    if (p.neg_q) {   // negative scale: use -Q and |scale| (exact sign flips)
+      u32x4 bits = __builtin_bit_cast(u32x4, qf[t]) ^ 0x80008000u;
+      qf[t] = __builtin_bit_cast(bf16x8, bits);
+    }
   }
 
   // Per-lane LDS read offsets (tile-relative).
@@ -298,10 +302,6 @@ void fwd_bf16_kernel(Params p) {
 
   // ---- mask the keys of an edge tile this row cannot see
   auto mask = [&](int kt) {
-    if (!kPosScale) {
-#pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) s[kb] *= sl;
-    }
     const bool edge = (kt + BN > p.Sk) || (p.causal && kt + BN - 1 > qw) ||
                       (p.window > 0 && kt < qw + 31 - p.window + 1);
     if (edge) {
@@ -335,7 +335,7 @@ void fwd_bf16_kernel(Params p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float x = s[kb][8 * c2 + e];
-          const float pe = kPosScale ? fast_exp2(fmaf(x, sl, -m_sub)) : fast_exp2(x - m_sub);
+          const float pe = fast_exp2(fmaf(x, sl, -m_sub));
           pf[2 * kb + c2][e] = (__bf16)pe;
         }
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
@@ -365,7 +365,7 @@ void fwd_bf16_kernel(Params p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
       mx = half_max(mx);
-      const float mt = kPosScale ? mx * sl : mx;   // tile max in base-2 units
+      const float mt = mx * sl;   // tile max in base-2 units (sl > 0)
       const float m_new = fmaxf(m_ref, mt);
       const float corr = fast_exp2(m_ref - (m_new == -INFINITY ? 0.f : m_new));
       m_ref = m_new;
@@ -695,10 +695,7 @@ static hipError_t launch_d(const Params& p, int dtype, hipStream_t stream) {
   const long blocks = (long)p.units * p.n_qblk;
   if (dtype == 1) {
     constexpr int BN = D == 256 ? 32 : 64;
-    if (p.sl > 0.f)
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BN>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   } else {
     hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   }

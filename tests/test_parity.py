@@ -157,10 +157,12 @@ def test_deterministic(dtype):
     assert torch.equal(c[0], d[0]) and torch.equal(c[1], d[1])
 
 
-def test_scale_passed_through():
-    wl = wl_small("f32", 1, 2, 1, 130, 130, 64, 1, 0, seed=9)
-    check_full(wl, scale=0.37)
-    check_full(wl, scale=-0.2)
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 64), ("bf16", 128), ("bf16", 256)])
+@pytest.mark.parametrize("scale", [0.37, -0.2, 0.0])
+def test_scale_passed_through(dtype, D, scale):
+    # negative scale flips the softmax; zero scale gives the mean of the visible V
+    wl = wl_small(dtype, 1, 2, 1, 130, 150, D, 1, 0, seed=9)
+    check_full(wl, scale=scale)
 
 
 # ------------------------------------------------------- benchmark workloads
