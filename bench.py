@@ -5,7 +5,9 @@
 
 A step is one fa_fwd call (every kernel of the forward pass, including the
 key-split merge when the library splits) over one batch of synthetic inputs
-that are resident in HBM before timing starts. The default workload is the
+that are resident in HBM before timing starts. W untimed warm-up steps run
+first, then more untimed steps for --warmup-seconds (clock ramp-up), then
+exactly K timed steps. The default workload is the
 bf16 causal GQA configuration (B=2, H=32, HKV=8, S=4096, D=128), the one the
 headline metric is quoted on. Prints one JSON line.
 
@@ -109,8 +111,11 @@ def cpu_baseline(wl: W.Workload, inp, target_rows: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-seconds", type=float, default=2.0,
+                    help="after the W warm-up steps, keep running untimed steps until this "
+                         "much time has passed (the GPU clock ramps up for about a second)")
     ap.add_argument("--config", type=int, default=W.HEADLINE)
     ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's choice")
     ap.add_argument("--cpu-rows", type=int, default=262144,
@@ -156,6 +161,11 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    t_warm = time.perf_counter() + args.warmup_seconds
+    while time.perf_counter() < t_warm:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
