@@ -157,14 +157,20 @@ struct Bf16Tile {
   static_assert(NI % 4 == 0, "each wavefront issues the same number of DMA instructions");
 
   // K reads: 16 lanes read one chunk of 16 different keys -> XOR with the key.
-  __device__ static __forceinline__ int swz_k(int key) {
-    return CPR >= 16 ? (key & 15) : ((key >> 1) & 7);
-  }
+  static constexpr int swz_k(int key) { return CPR >= 16 ? (key & 15) : ((key >> 1) & 7); }
   // V transpose reads: 32 lanes read 4 chunks of 4 consecutive keys -> move
   // each key of the group of 4 to its own group of 4 chunks.
-  __device__ static __forceinline__ int swz_v(int key) {
-    return CPR >= 16 ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
+  static constexpr int swz_v(int key) { return CPR >= 16 ? 4 * (key & 3) : 4 * ((key >> 1) & 1); }
+  // Tile byte offset that LDS chunk P of a copy reads: logical chunk
+  // (P % CPR) ^ swz(row) of row P / CPR.
+  static constexpr int dma_off(int P, bool v) {
+    return (P / CPR) * ROW + (((P % CPR) ^ (v ? swz_v(P / CPR) : swz_k(P / CPR))) << 4);
   }
+  // The offsets of copy instruction k (chunks 64k.. of a wavefront's share)
+  // differ from those of instruction 0 by the same XOR in every lane: the row
+  // step and the swizzle touch disjoint bits. One register per buffer then
+  // holds a lane's offsets.
+  static constexpr int dma_xor(int k, bool v) { return dma_off(64 * k, v) ^ dma_off(0, v); }
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -200,7 +206,7 @@ __device__ __forceinline__ float half_max(float x) {
 constexpr float kRowSumLimit = 1.8446744e19f;   // 2^64: row-sum bound that triggers a rescale
 
 template <int D, int BN>
-__global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1))
+__global__ __launch_bounds__(kThreads, 2)
 void fwd_bf16_kernel(Params p) {
   using T = Bf16Tile<D, BN>;
   // K and V tiles double-buffered; four separate objects let the compiler see
@@ -230,14 +236,8 @@ void fwd_bf16_kernel(Params p) {
 
   // DMA: LDS chunk P = 64 (wave NIW + k) + lane of a tile holds logical chunk
   // (P % CPR) ^ swz(row) of row P / CPR.
-  int voff_k[T::NIW], voff_v[T::NIW];
-#pragma unroll
-  for (int k = 0; k < T::NIW; ++k) {
-    const int P = 64 * (wave * T::NIW + k) + lane;
-    const int row = P / T::CPR, pc = P % T::CPR;
-    voff_k[k] = row * T::ROW + ((pc ^ T::swz_k(row)) << 4);
-    voff_v[k] = row * T::ROW + ((pc ^ T::swz_v(row)) << 4);
-  }
+  const int voff_k = T::dma_off(64 * wave * T::NIW + lane, false);
+  const int voff_v = T::dma_off(64 * wave * T::NIW + lane, true);
   auto issue = [&](int kt, char* kdst, char* vdst) {
     const unsigned bytes = (unsigned)min((long)(p.Sk - kt) * T::ROW, 0x7fffffffL);
     const __bf16* kb = Kp + (size_t)kt * D;
@@ -245,8 +245,8 @@ void fwd_bf16_kernel(Params p) {
 #pragma unroll
     for (int k = 0; k < T::NIW; ++k) {
       const int off = (wave * T::NIW + k) * 1024;
-      dma16(kb, bytes, voff_k[k], kdst + off);
-      dma16(vb, bytes, voff_v[k], vdst + off);
+      dma16(kb, bytes, voff_k ^ T::dma_xor(k, false), kdst + off);
+      dma16(vb, bytes, voff_v ^ T::dma_xor(k, true), vdst + off);
     }
   };
 
@@ -264,19 +264,30 @@ void fwd_bf16_kernel(Params p) {
     }
   }
 
-  // Per-lane LDS read offsets (tile-relative).
+  // Per-lane LDS read offsets (tile-relative). The swizzles only touch the low
+  // four chunk-index bits, so chunks 16..31 of a row (D = 256) sit a fixed 256
+  // bytes from chunks 0..15, and within those the offsets of K step t and of V
+  // block db are the step-0 / block-0 offsets XOR 32 t and XOR 64 db in every
+  // lane. D <= 128 keeps them in registers; D = 256, short of registers at two
+  // wavefronts per SIMD, forms them with one XOR each.
   const int krow = perm_row(l32);
-  int koff[T::DC];
+  constexpr int KO = T::DC < 8 ? T::DC : 8;
+  constexpr int KR = D == 256 ? 1 : KO;
+  int koff[KR];
 #pragma unroll
-  for (int t = 0; t < T::DC; ++t) koff[t] = krow * T::ROW + (((2 * t + g) ^ T::swz_k(krow)) << 4);
+  for (int t = 0; t < KR; ++t) koff[t] = krow * T::ROW + (((2 * t + g) ^ T::swz_k(krow)) << 4);
+  auto k_off = [&](int t) { return (KR == 1 ? koff[0] ^ (32 * (t % KO)) : koff[t % KO]) + (t / KO) * 256; };
   const int blk = lane >> 4, li = lane & 15;
   const int vrow = 8 * g + (li >> 2);                       // + 16 C + 4 h
-  int voff[T::DB];
+  constexpr int VO = T::DB < 4 ? T::DB : 4;
+  constexpr int VR = D == 256 ? 1 : VO;
+  int voff[VR];
 #pragma unroll
-  for (int db = 0; db < T::DB; ++db) {
+  for (int db = 0; db < VR; ++db) {
     const int chunk = 4 * db + 2 * (blk & 1) + ((li & 3) >> 1);
     voff[db] = vrow * T::ROW + ((chunk ^ T::swz_v(vrow)) << 4) + 8 * (li & 1);
   }
+  auto v_off = [&](int db) { return (VR == 1 ? voff[0] ^ (64 * (db % VO)) : voff[db % VO]) + (db / VO) * 256; };
 
   f32x16 o[T::DB];
 #pragma unroll
@@ -288,13 +299,15 @@ void fwd_bf16_kernel(Params p) {
 
   // ---- S^T = K Q^T for one tile
   auto qk = [&](const char* Ks) {
+    // keep the XOR-derived offsets inside the loop (not hoisted into registers)
+    if constexpr (KR == 1) asm volatile("" : "+v"(koff[0]));
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int t = 0; t < T::DC; ++t) {
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb) {
-        const bf16x8 a = *(const bf16x8*)(Ks + koff[t] + kb * 32 * T::ROW);
+        const bf16x8 a = *(const bf16x8*)(Ks + k_off(t) + kb * 32 * T::ROW);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb], 0, 0, 0);
       }
     }
@@ -379,12 +392,14 @@ void fwd_bf16_kernel(Params p) {
 
   // ---- O^T += V^T P^T
   auto pv = [&](const char* Vs) {
+    if constexpr (VR == 1) asm volatile("" : "+v"(voff[0]));
 #pragma unroll
     for (int c = 0; c < T::KC; ++c) {
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) {
         const int base = 16 * c * T::ROW;
-        const bf16x8 a = read_v_pair(Vs, voff[db] + base, voff[db] + base + 4 * T::ROW);
+        const int vo = v_off(db) + base;
+        const bf16x8 a = read_v_pair(Vs, vo, vo + 4 * T::ROW);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c], o[db], 0, 0, 0);
       }
     }
