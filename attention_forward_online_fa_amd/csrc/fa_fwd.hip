@@ -238,8 +238,9 @@ void fwd_bf16_kernel(Params p) {
   // (P % CPR) ^ swz(row) of row P / CPR.
   const int voff_k = T::dma_off(64 * wave * T::NIW + lane, false);
   const int voff_v = T::dma_off(64 * wave * T::NIW + lane, true);
-  auto issue = [&](int kt, char* kdst, char* vdst) {
-    const unsigned bytes = (unsigned)min((long)(p.Sk - kt) * T::ROW, 0x7fffffffL);
+  auto issue = [&](int kt, char* kdst, char* vdst, bool full = false) {
+    // a full tile needs no bound: BN rows are in range
+    const unsigned bytes = full ? (unsigned)(BN * T::ROW) : (unsigned)min((long)(p.Sk - kt) * T::ROW, 0x7fffffffL);
     const __bf16* kb = Kp + (size_t)kt * D;
     const __bf16* vb = Vp + (size_t)kt * D;
 #pragma unroll
@@ -411,7 +412,7 @@ void fwd_bf16_kernel(Params p) {
   };
 
   // One tile: K(t), V(t) in (Kc, Vc); the copy of tile t+1 goes to (Kn, Vn).
-  auto step = [&](int t, const char* Kc, const char* Vc, char* Kn, char* Vn) {
+  auto step = [&](int t, const char* Kc, const char* Vc, char* Kn, char* Vn) __attribute__((always_inline)) {
     const int kt = t0 + t * BN;
     wait_dma_and_sync();
     if (t + 1 < n_tiles) issue(kt + BN, Kn, Vn);
@@ -422,12 +423,49 @@ void fwd_bf16_kernel(Params p) {
     pv(Vc);
   };
 
-  if (n_tiles > 0) issue(t0, kbuf0, vbuf0);
-  for (int t = 0; t < n_tiles; t += 2) {
-    step(t, kbuf0, vbuf0, kbuf1, vbuf1);
-    if (t + 1 >= n_tiles) break;
-    step(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
+  // Interior tiles: every row of the block sees every key of the tile and the
+  // next tile exists with BN keys below Sk, so the step needs no skip, mask or
+  // bounds decisions.
+  auto step_in = [&](int t, const char* Kc, const char* Vc, char* Kn, char* Vn) __attribute__((always_inline)) {
+    const int kt = t0 + t * BN;
+    wait_dma_and_sync();
+    issue(kt + BN, Kn, Vn, true);
+    qk(Kc);
+    softmax();
+    pv(Vc);
+  };
+  // Tiles [0, full_hi) exist and hold BN keys below Sk; tiles [u_lo, u_hi)
+  // are also fully visible to every row of the block.
+  const int full_hi = min(n_tiles, (p.Sk - t0) / BN);
+  int u_lo = 0, u_hi = 0;
+  if (q0 + kBlockM <= p.Sq) {
+    u_hi = full_hi;
+    if (p.causal) u_hi = min(u_hi, max(0, (q0 - t0 + 1) / BN));
+    if (p.window > 0) {
+      const int need = q0 + kBlockM - p.window - t0;       // kt - t0 >= need
+      u_lo = need > 0 ? (need + BN - 1) / BN : 0;
+    }
   }
+  // steps t and t+1 both interior, and the tiles they copy (t+1, t+2) full
+  auto in2 = [&](int t) __attribute__((always_inline)) {
+    return t >= u_lo && t + 1 < u_hi && t + 2 < full_hi;
+  };
+  auto gen2 = [&](int t) __attribute__((always_inline)) {   // generic steps t, t+1; true when the loop is over
+    step(t, kbuf0, vbuf0, kbuf1, vbuf1);
+    if (t + 1 >= n_tiles) return true;
+    step(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
+    return t + 2 >= n_tiles;
+  };
+
+  if (n_tiles > 0) issue(t0, kbuf0, vbuf0);
+  int t = 0;
+  bool done = n_tiles == 0;
+  for (; !done && !in2(t); t += 2) done = gen2(t);
+  for (; !done && in2(t); t += 2) {
+    step_in(t, kbuf0, vbuf0, kbuf1, vbuf1);
+    step_in(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
+  }
+  for (; !done; t += 2) done = gen2(t);
 
   // ---- epilogue: lane holds dims 32 db + 8 a + 4 g + (0..3) of row i.
   finish_row(p, w.b, w.h, w.split, i, g, m_ref, l,

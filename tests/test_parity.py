@@ -94,6 +94,11 @@ SMALL = [
     ("bf16", 1, 4, 1, 384, 500, 128, 1, 100),
     ("bf16", 1, 2, 1, 150, 170, 256, 1, 0),
     ("bf16", 1, 1, 1, 96, 1000, 256, 0, 0),
+    # long enough for the interior-tile path, entered after window-edge tiles
+    # and left before a partial last tile
+    ("bf16", 1, 2, 1, 1024, 1024, 128, 1, 300),
+    ("bf16", 1, 2, 2, 512, 1000, 64, 0, 0),
+    ("bf16", 1, 2, 1, 640, 2100, 256, 0, 0),
 ]
 
 
