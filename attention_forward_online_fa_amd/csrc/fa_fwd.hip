@@ -602,7 +602,6 @@ void fwd_f32_kernel(Params p) {
       }
       const bool edge = (kt + BN > p.Sk) || (p.causal && kt + BN - 1 > qw) ||
                         (p.window > 0 && kt < qw + 31 - p.window + 1);
-      float mx = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float x = s[v] * p.sl;
@@ -611,25 +610,36 @@ void fwd_f32_kernel(Params p) {
           x = visible(p, i, j) ? x : -INFINITY;
         }
         s[v] = x;
-        mx = fmaxf(mx, x);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float corr = fast_exp2(m - m_use);
-      float rs = 0.f;
+      // P against the running reference max m (base-2 units); the exact tile
+      // max is needed only when some lane's row sum exceeds 2^64 (which
+      // includes the first tile, m = -inf): then O and l are rescaled and P
+      // recomputed. O and l always share the reference: the same softmax.
+      f32x16 e;
+      auto exps = [&](float m_sub) __attribute__((always_inline)) {
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float e = fast_exp2(s[v] - m_use);
-        s[v] = e;
-        rs += e;
-      }
-      l = l * corr + rs;
-      m = m_new;
-      if (__any(corr != 1.f)) {
+        for (int v = 0; v < 16; ++v) {
+          e[v] = fast_exp2(s[v] - m_sub);
+          part[v & 3] += e[v];
+        }
+        return (part[0] + part[1]) + (part[2] + part[3]);
+      };
+      float rs = exps(m == -INFINITY ? -1e30f : m);
+      if (__any(!(rs <= kRowSumLimit))) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx);
+        const float corr = fast_exp2(m - (m_new == -INFINITY ? 0.f : m_new));
+        m = m_new;
+        l *= corr;
 #pragma unroll
         for (int db = 0; db < T::DB; ++db) o[db] *= corr;
+        rs = exps(m == -INFINITY ? 0.f : m);
       }
+      l += rs;
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int key = 8 * (u >> 2) + 4 * g + (u & 3);
@@ -650,7 +660,7 @@ void fwd_f32_kernel(Params p) {
         }
 #pragma unroll
         for (int db = 0; db < T::DB; ++db)
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[db], s[u], o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[db], e[u], o[db], 0, 0, 0);
       }
     }
 
