@@ -206,7 +206,7 @@ __device__ __forceinline__ float half_max(float x) {
 constexpr float kRowSumLimit = 1.8446744e19f;   // 2^64: row-sum bound that triggers a rescale
 
 template <int D, int BN>
-__global__ __launch_bounds__(kThreads, 2)
+__global__ __launch_bounds__(kThreads, (D == 128 ? 3 : 2))
 void fwd_bf16_kernel(Params p) {
   using T = Bf16Tile<D, BN>;
   // K and V tiles double-buffered; four separate objects let the compiler see
@@ -737,7 +737,7 @@ void merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpa
 
 // ================================================================ launch
 int key_tile(int dtype, int D) {
-  if (dtype == 1) return D == 256 ? 32 : 64;
+  if (dtype == 1) return D >= 128 ? 32 : 64;
   return F32Tile<64>::BN;
 }
 
@@ -757,7 +757,7 @@ template <int D>
 static hipError_t launch_d(const Params& p, int dtype, hipStream_t stream) {
   const long blocks = (long)p.units * p.n_qblk;
   if (dtype == 1) {
-    constexpr int BN = D == 256 ? 32 : 64;
+    constexpr int BN = D >= 128 ? 32 : 64;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, BN>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   } else {
     hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
