@@ -251,6 +251,10 @@ void fwd_bf16_kernel(Params p) {
     }
   };
 
+  // The first K/V copy goes out before the query rows are loaded, so the two
+  // latencies overlap.
+  if (n_tiles > 0) issue(t0, kbuf0, vbuf0);
+
   // Query rows as the B operand: k-slot (g, e) of step t is dim 16t + 8g + e.
   bf16x8 qf[T::DC];
 #pragma unroll
@@ -457,7 +461,6 @@ void fwd_bf16_kernel(Params p) {
     return t + 2 >= n_tiles;
   };
 
-  if (n_tiles > 0) issue(t0, kbuf0, vbuf0);
   int t = 0;
   bool done = n_tiles == 0;
   for (; !done && !in2(t); t += 2) done = gen2(t);
