@@ -99,6 +99,11 @@ SMALL = [
     ("bf16", 1, 2, 1, 1024, 1024, 128, 1, 300),
     ("bf16", 1, 2, 2, 512, 1000, 64, 0, 0),
     ("bf16", 1, 2, 1, 640, 2100, 256, 0, 0),
+    # 32-key tiles at D = 128: long causal interior run (odd tile count per pair
+    # loop), non-causal with a partial last tile, one-sided window with ragged ends
+    ("bf16", 1, 4, 1, 1536, 1536, 128, 1, 0),
+    ("bf16", 1, 2, 2, 256, 1500, 128, 0, 0),
+    ("bf16", 2, 2, 1, 333, 1111, 128, 0, 500),
 ]
 
 
