@@ -343,29 +343,53 @@ void fwd_bf16_kernel(Params p) {
     }
   };
 
-  // ---- P = exp2(S - m_sub) packed to bf16; returns this lane's row sum of P
+  // ---- P = exp2(S - m_sub) packed to bf16; returns this lane's row sum of P.
+  // D <= 128 sums the fp32 values with VALU adds (v_dot2c_f32_bf16 issues to
+  // the matrix pipe, where it waits behind the other wavefronts' MFMAs);
+  // D = 256, at two wavefronts per SIMD and short of registers, sums the
+  // rounded bf16 values with dot2.
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   auto exp_pack_sum = [&](float m_sub) {
+    if constexpr (D == 256) {
 #pragma unroll
-    for (int kb = 0; kb < T::KB; ++kb)
+      for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
+        for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = s[kb][8 * c2 + e];
-          const float pe = fast_exp2(fmaf(x, sl, -m_sub));
-          pf[2 * kb + c2][e] = (__bf16)pe;
+          for (int e = 0; e < 8; ++e)
+            pf[2 * kb + c2][e] = (__bf16)fast_exp2(fmaf(s[kb][8 * c2 + e], sl, -m_sub));
+      const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+      float rs = 0.f;
+#pragma unroll
+      for (int c = 0; c < T::KC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 two = {pf[c][e], pf[c][e + 1]};
+          rs = __builtin_amdgcn_fdot2_f32_bf16(two, ones, rs, false);
         }
-    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-    float rs = 0.f;
+      return rs;
+    } else {
+      f32x4 ps = {0.f, 0.f, 0.f, 0.f};   // four partial sums
 #pragma unroll
-    for (int c = 0; c < T::KC; ++c)
+      for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2 two = {pf[c][e], pf[c][e + 1]};
-        rs = __builtin_amdgcn_fdot2_f32_bf16(two, ones, rs, false);
-      }
-    return rs;
+        for (int c2 = 0; c2 < 2; ++c2) {
+          f32x4 lo, hi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lo[e] = fast_exp2(fmaf(s[kb][8 * c2 + e], sl, -m_sub));
+            hi[e] = fast_exp2(fmaf(s[kb][8 * c2 + 4 + e], sl, -m_sub));
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pf[2 * kb + c2][e] = (__bf16)lo[e];
+            pf[2 * kb + c2][4 + e] = (__bf16)hi[e];
+          }
+          ps += lo;
+          ps += hi;
+        }
+      return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    }
   };
 
   // ---- softmax of one tile against the running reference max m_ref. The
