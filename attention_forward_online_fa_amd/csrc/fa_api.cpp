@@ -55,7 +55,9 @@ int workspace_pool(int dev_index, DeviceState& s, hipMemPool_t* pool) {
       return FA_ERR_WORKSPACE;
     }
     uint64_t thr = UINT64_MAX;
-    hipMemPoolSetAttribute(s.pool, hipMemPoolAttrReleaseThreshold, &thr);
+    // Best effort: without the threshold the pool still works, it only hands
+    // memory back at synchronisation points.
+    (void)hipMemPoolSetAttribute(s.pool, hipMemPoolAttrReleaseThreshold, &thr);
   }
   *pool = s.pool;
   return FA_OK;
@@ -182,9 +184,9 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
     p.Opart = static_cast<float*>(ws);
     p.Lpart = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
   }
-  hipError_t e = fa::launch_forward(p, dtype, D, stream);
-  if (ws) hipFreeAsync(ws, stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  const hipError_t e = fa::launch_forward(p, dtype, D, stream);
+  const hipError_t f = ws ? hipFreeAsync(ws, stream) : hipSuccess;
+  return (e == hipSuccess && f == hipSuccess) ? FA_OK : FA_ERR_HIP;
 }
 
 }  // namespace
@@ -236,7 +238,7 @@ const char* fa_status_string(int status) {
 void fa_release(void) {
   std::lock_guard<std::mutex> lk(g_mu);
   for (int d = 0; d < kMaxDevices; ++d) {
-    if (g_dev[d].pool) hipMemPoolTrimTo(g_dev[d].pool, 0);
+    if (g_dev[d].pool) (void)hipMemPoolTrimTo(g_dev[d].pool, 0);   // nothing to report
   }
 }
 
