@@ -13,6 +13,7 @@ lse = -inf.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 
 from ._lib import FA_BF16, FA_F32, FA_MAX_SPLITS, FaError, lib, library_path
@@ -91,6 +92,21 @@ def plan_splits(B, H, HKV, Sq, Sk, D, *, causal=False, window=0, dtype="bf16") -
     if r < 0:
         raise FaError(-r)
     return r
+
+
+def schedule_table(B, H, HKV, Sq, Sk, D, nslot, *, causal=False, window=0, dtype="f32"):
+    """Persistent-launch item lists for nslot workgroups (host only): returns
+    (num_splits, offsets[nslot + 1], items)."""
+    code = FA_BF16 if dtype in ("bf16", FA_BF16) else FA_F32
+    args = (B, H, HKV, Sq, Sk, D, int(bool(causal)), int(window), code, nslot)
+    n = lib().fa_schedule_table(*args, None, 0, None)
+    if n < 0:
+        raise FaError(-n)
+    buf = (ctypes.c_int * n)()
+    ns = ctypes.c_int(0)
+    lib().fa_schedule_table(*args, ctypes.cast(buf, ctypes.c_void_p), n, ctypes.byref(ns))
+    table = list(buf)
+    return ns.value, table[:nslot + 1], table[nslot + 1:]
 
 
 def release():

@@ -4,9 +4,14 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdint>
+#include <map>
 #include <mutex>
+#include <queue>
+#include <vector>
 
 #include "fa_kernels.h"
 
@@ -14,10 +19,20 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
+// A persistent-launch schedule: [nslot + 1] offsets, then item ids, on the
+// host and (uploaded once) on the device.
+struct Sched {
+  std::vector<int> host;
+  int* dev = nullptr;
+};
+using SchedKey = std::array<int, 12>;
+
 struct DeviceState {
   bool init = false;
   int num_cus = 0;
+  int f32_bpc[3] = {-1, -1, -1};   // fp32 workgroups per CU for D = 64, 128, 256
   hipMemPool_t pool = nullptr;
+  std::map<SchedKey, Sched> scheds;
 };
 
 std::mutex g_mu;
@@ -102,6 +117,141 @@ int auto_splits(int B, int H, int Sq, int Sk, int D, int causal, int window, int
   return ns < 1 ? 1 : (int)ns;
 }
 
+// ---- persistent schedules for the fp32 kernel on small causal / windowed grids
+// Query tiles of a causal or windowed problem see very different numbers of
+// keys. With too few tiles to give every CU several, the longest tile sets
+// the kernel time and most CUs idle at the end. Such launches split the key
+// axis so that no piece is much longer than the average load of a workgroup
+// slot, and run one persistent workgroup per slot (as many slots as the
+// kernel's occupancy allows) over a host-computed list of pieces whose total
+// cost is balanced: longest first onto the least loaded slot, then moves and
+// swaps out of the most loaded slot while they lower the maximum.
+constexpr int kItemCost2 = 5;   // fixed cost per piece (start-up, epilogue), in half key tiles
+
+// Key tiles a workgroup visits: the host twin of key_range in the kernels.
+int item_tiles(int q0, int BM, int BN, int split, int split_len, int Sq, int Sk, int causal,
+               int window) {
+  int lo = split * split_len;
+  int hi = std::min(Sk, lo + split_len);
+  const int last = std::min(q0 + BM, Sq) - 1;
+  if (causal) hi = std::min(hi, last + 1);
+  if (window > 0) lo = std::max(lo, q0 - window + 1);
+  const int t0 = (lo / BN) * BN;
+  return hi > lo ? (hi - t0 + BN - 1) / BN : 0;
+}
+
+// Slots of a persistent launch for this problem, or 0 when it runs one
+// workgroup per item.
+int persistent_slots(DeviceState& s, int B, int H, int Sq, int D, int causal, int window,
+                     int dtype) {
+  if (dtype != FA_F32 || (!causal && window <= 0)) return 0;
+  const int BM = fa::block_m(dtype, D);
+  const long qtiles = (long)B * H * ((Sq + BM - 1) / BM);
+  if (qtiles >= 2L * s.num_cus) return 0;
+  const int di = D == 64 ? 0 : D == 128 ? 1 : 2;
+  if (s.f32_bpc[di] < 0) s.f32_bpc[di] = fa::f32_blocks_per_cu(D);
+  return s.f32_bpc[di] > 0 ? s.f32_bpc[di] * s.num_cus : 0;
+}
+
+// Key splits for a persistent launch: the longest query tile cut into pieces
+// of about the average slot load.
+int persistent_splits(int B, int H, int Sq, int Sk, int D, int causal, int window, int dtype,
+                      int nslot) {
+  const int BM = fa::block_m(dtype, D), BN = fa::key_tile(dtype, D);
+  const int n_qblk = (Sq + BM - 1) / BM;
+  long total = 0;
+  int longest = 0;
+  for (int qb = 0; qb < n_qblk; ++qb) {
+    const int t = item_tiles(qb * BM, BM, BN, 0, Sk, Sq, Sk, causal, window);
+    total += t;
+    longest = std::max(longest, t);
+  }
+  total *= (long)B * H;
+  const double avg = (double)total / nslot + kItemCost2 / 2.0;
+  const int sk_tiles = (Sk + BN - 1) / BN;
+  int ns = (int)std::ceil(longest / avg);
+  return std::max(1, std::min({ns, FA_MAX_SPLITS, sk_tiles}));
+}
+
+// Balanced item lists for nslot workgroups: [nslot + 1] offsets, then the
+// item ids (item = qblk * units + unit, unit = ((b HKV + hkv) ns + split)
+// group + head-in-group, as the kernel decodes it).
+std::vector<int> build_schedule(int B, int H, int HKV, int Sq, int Sk, int D, int causal,
+                                int window, int dtype, int ns, int split_len, int nslot) {
+  const int BM = fa::block_m(dtype, D), BN = fa::key_tile(dtype, D);
+  const int n_qblk = (Sq + BM - 1) / BM;
+  const int group = H / HKV, units = B * H * ns;
+  const int n = n_qblk * units;
+  std::vector<int> tiles(n), cost(n);
+  for (int it = 0; it < n; ++it) {
+    const int qb = it / units, split = (it % units / group) % ns;
+    tiles[it] = item_tiles(qb * BM, BM, BN, split, split_len, Sq, Sk, causal, window);
+    cost[it] = 2 * tiles[it] + kItemCost2;
+  }
+  // longest first onto the least loaded slot
+  std::vector<int> order(n);
+  for (int i = 0; i < n; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cost[a] > cost[b]; });
+  std::vector<std::vector<int>> slot(nslot);
+  std::vector<long> load(nslot, 0);
+  using LS = std::pair<long, int>;
+  std::priority_queue<LS, std::vector<LS>, std::greater<LS>> heap;
+  for (int sl = 0; sl < nslot; ++sl) heap.push({0, sl});
+  for (int it : order) {
+    const LS top = heap.top();
+    heap.pop();
+    slot[top.second].push_back(it);
+    load[top.second] = top.first + cost[it];
+    heap.push({load[top.second], top.second});
+  }
+  // moves and swaps out of the most loaded slot while they lower its load
+  // below the old maximum without raising the other slot to it
+  for (int iter = 0; iter < 2000; ++iter) {
+    const int mx = (int)(std::max_element(load.begin(), load.end()) - load.begin());
+    long best_gain = 0;
+    int bi = -1, bs = -1, bj = -1;
+    for (int a = 0; a < (int)slot[mx].size(); ++a) {
+      const int ci = cost[slot[mx][a]];
+      for (int sl = 0; sl < nslot; ++sl) {
+        if (sl == mx) continue;
+        if (load[sl] + ci < load[mx]) {
+          const long gain = load[mx] - std::max(load[sl] + ci, load[mx] - ci);
+          if (gain > best_gain) { best_gain = gain; bi = a; bs = sl; bj = -1; }
+        }
+        for (int b = 0; b < (int)slot[sl].size(); ++b) {
+          const int d = ci - cost[slot[sl][b]];
+          if (d > 0 && load[sl] + d < load[mx]) {
+            const long gain = load[mx] - std::max(load[sl] + d, load[mx] - d);
+            if (gain > best_gain) { best_gain = gain; bi = a; bs = sl; bj = b; }
+          }
+        }
+      }
+    }
+    if (bi < 0) break;
+    const int it = slot[mx][bi];
+    slot[mx].erase(slot[mx].begin() + bi);
+    load[mx] -= cost[it];
+    if (bj >= 0) {
+      const int jt = slot[bs][bj];
+      slot[bs].erase(slot[bs].begin() + bj);
+      load[bs] -= cost[jt];
+      slot[mx].push_back(jt);
+      load[mx] += cost[jt];
+    }
+    slot[bs].push_back(it);
+    load[bs] += cost[it];
+  }
+  std::vector<int> table;
+  table.reserve(nslot + 1 + n);
+  table.push_back(0);
+  for (int sl = 0; sl < nslot; ++sl) table.push_back(table.back() + (int)slot[sl].size());
+  for (int sl = 0; sl < nslot; ++sl) {
+    std::stable_sort(slot[sl].begin(), slot[sl].end(), [&](int a, int b) { return tiles[a] > tiles[b]; });
+    table.insert(table.end(), slot[sl].begin(), slot[sl].end());
+  }
+  return table;
+}
+
 // Final split count and keys per split for a requested count (0 = auto).
 void resolve_splits(int requested, int B, int H, int Sq, int Sk, int D, int causal, int window,
                     int dtype, int num_cus, int* ns_out, int* split_len_out) {
@@ -115,6 +265,40 @@ void resolve_splits(int requested, int B, int H, int Sq, int Sk, int D, int caus
   const int split_len = ((sk_tiles + ns - 1) / ns) * BN;
   *ns_out = (Sk + split_len - 1) / split_len;
   *split_len_out = split_len;
+}
+
+// Splits, keys per split and persistent slots (0 = none) for one call.
+void plan(DeviceState& s, int requested, int B, int H, int Sq, int Sk, int D, int causal,
+          int window, int dtype, int* ns, int* split_len, int* nslot) {
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    *nslot = persistent_slots(s, B, H, Sq, D, causal, window, dtype);
+  }
+  if (*nslot > 0 && requested == 0)
+    requested = persistent_splits(B, H, Sq, Sk, D, causal, window, dtype, *nslot);
+  resolve_splits(requested, B, H, Sq, Sk, D, causal, window, dtype, s.num_cus, ns, split_len);
+}
+
+// The device copy of a persistent schedule, built and uploaded on first use
+// (a synchronous copy, so every stream sees it) and kept until fa_release.
+int schedule_for(DeviceState& s, int B, int H, int HKV, int Sq, int Sk, int D, int causal,
+                 int window, int dtype, int ns, int split_len, int nslot, const int** out) {
+  const SchedKey key = {B, H, HKV, Sq, Sk, D, causal, window, dtype, ns, split_len, nslot};
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto found = s.scheds.find(key);
+  if (found == s.scheds.end()) {
+    Sched sc;
+    sc.host = build_schedule(B, H, HKV, Sq, Sk, D, causal, window, dtype, ns, split_len, nslot);
+    const size_t bytes = sc.host.size() * sizeof(int);
+    if (hipMalloc(reinterpret_cast<void**>(&sc.dev), bytes) != hipSuccess) return FA_ERR_WORKSPACE;
+    if (hipMemcpy(sc.dev, sc.host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+      (void)hipFree(sc.dev);
+      return FA_ERR_HIP;
+    }
+    found = s.scheds.emplace(key, std::move(sc)).first;
+  }
+  *out = found->second.dev;
+  return FA_OK;
 }
 
 int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
@@ -132,9 +316,8 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   if (st != FA_OK) return st;
 
   const int BM = fa::block_m(dtype, D);
-  int ns = 1, split_len = 0;
-  resolve_splits(num_splits, B, H, Sq, Sk, D, causal, window, dtype, ds->num_cus, &ns,
-                 &split_len);
+  int ns = 1, split_len = 0, nslot = 0;
+  plan(*ds, num_splits, B, H, Sq, Sk, D, causal, window, dtype, &ns, &split_len, &nslot);
 
   fa::Params p = {};
   p.Q = Q;
@@ -167,6 +350,12 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   if (blocks < 1 || blocks > 2147483647L) return FA_ERR_SHAPE;
   p.units = (int)units;
   p.xcd_remap = (p.units % 8 == 0) ? 1 : 0;
+  if (nslot > 0) {
+    st = schedule_for(*ds, B, H, HKV, Sq, Sk, D, causal, window, dtype, ns, split_len, nslot,
+                      &p.sched);
+    if (st != FA_OK) return st;
+    p.nslot = nslot;
+  }
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
   void* ws = nullptr;
@@ -213,9 +402,27 @@ int fa_plan_splits(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int
   DeviceState* ds = nullptr;
   st = device_state(&ds);
   if (st != FA_OK) return -st;
-  int ns = 1, split_len = 0;
-  resolve_splits(0, B, H, Sq, Sk, D, causal, window, dtype, ds->num_cus, &ns, &split_len);
+  int ns = 1, split_len = 0, nslot = 0;
+  plan(*ds, 0, B, H, Sq, Sk, D, causal, window, dtype, &ns, &split_len, &nslot);
   return ns;
+}
+
+int fa_schedule_table(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int window,
+                      int dtype, int nslot, int* table, int capacity, int* num_splits) {
+  const int st = check_args(B, H, HKV, Sq, Sk, D, causal, window, dtype);
+  if (st != FA_OK) return -st;
+  if (nslot < 1 || capacity < 0 || (capacity > 0 && !table)) return -FA_ERR_SHAPE;
+  const int BM = fa::block_m(dtype, D);
+  const long items = (long)B * H * FA_MAX_SPLITS * ((Sq + BM - 1) / BM);
+  if (items + nslot + 1 > 2147483647L) return -FA_ERR_SHAPE;
+  int ns = 1, split_len = 0;
+  resolve_splits(persistent_splits(B, H, Sq, Sk, D, causal, window, dtype, nslot), B, H, Sq, Sk,
+                 D, causal, window, dtype, 1, &ns, &split_len);
+  const std::vector<int> t =
+      build_schedule(B, H, HKV, Sq, Sk, D, causal, window, dtype, ns, split_len, nslot);
+  if (num_splits) *num_splits = ns;
+  for (int i = 0; i < (int)t.size() && i < capacity; ++i) table[i] = t[i];
+  return (int)t.size();
 }
 
 const char* fa_status_string(int status) {
@@ -237,9 +444,19 @@ const char* fa_status_string(int status) {
 
 void fa_release(void) {
   std::lock_guard<std::mutex> lk(g_mu);
+  int cur = -1;
+  (void)hipGetDevice(&cur);
   for (int d = 0; d < kMaxDevices; ++d) {
-    if (g_dev[d].pool) (void)hipMemPoolTrimTo(g_dev[d].pool, 0);   // nothing to report
+    DeviceState& s = g_dev[d];
+    if (s.pool) (void)hipMemPoolTrimTo(s.pool, 0);   // nothing to report
+    if (!s.scheds.empty() && hipSetDevice(d) == hipSuccess) {
+      // schedules may still be read by queued kernels: wait for the device first
+      (void)hipDeviceSynchronize();
+      for (auto& kv : s.scheds) (void)hipFree(kv.second.dev);
+      s.scheds.clear();
+    }
   }
+  if (cur >= 0) (void)hipSetDevice(cur);
 }
 
 }  // extern "C"

@@ -86,6 +86,22 @@ __device__ __forceinline__ Tile map_tile(const Params& p) {
   return w;
 }
 
+// Work tile of item qblk * units + unit in a persistent launch (the unit
+// decomposition of map_tile, without its XCD grouping).
+__device__ __forceinline__ Tile item_tile(const Params& p, int item) {
+  Tile w;
+  w.qblk = item / p.units;
+  const int u = item % p.units;
+  const int hg = u % p.group;
+  int r = u / p.group;
+  w.split = r % p.nsplit;
+  r /= p.nsplit;
+  w.hkv = r % p.HKV;
+  w.b = r / p.HKV;
+  w.h = w.hkv * p.group + hg;
+  return w;
+}
+
 // Key range [lo, hi) a workgroup with rows [q0, q0 + bm) must visit.
 __device__ __forceinline__ void key_range(const Params& p, int q0, int bm, int split, int& lo,
                                           int& hi) {
@@ -113,7 +129,8 @@ __device__ __forceinline__ void finish_row(const Params& p, int b, int h, int sp
   if (i >= p.Sq) return;
   const size_t row = (size_t)(b * p.H + h) * p.Sq + i;
   const bool partial = p.nsplit > 1;
-  store(partial, row, split, inv);
+  // A split row that saw no key needs only its LSE (-inf): the merge skips it.
+  if (!partial || any) store(partial, row, split, inv);
   if (g == 0) {
     if (partial)
       p.Lpart[(size_t)split * p.B * p.H * p.Sq + row] = lse;
@@ -552,7 +569,10 @@ void fwd_f32_kernel(Params p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const Tile w = map_tile(p);
+  // One item per workgroup, or (persistent launch) this slot's item list.
+  const int k_end = p.sched ? p.sched[blockIdx.x + 1] : 1;
+  for (int kk = p.sched ? p.sched[blockIdx.x] : 0; kk < k_end; ++kk) {
+  const Tile w = p.sched ? item_tile(p, p.sched[p.nslot + 1 + kk]) : map_tile(p);
   const int q0 = w.qblk * kBlockM;
   const int qw = q0 + wave * 32;
   const int i = qw + l32;
@@ -722,6 +742,8 @@ void fwd_f32_kernel(Params p) {
                  }
                }
              });
+  __syncthreads();   // LDS is reused by the next item
+  }
 }
 
 // ============================================================ split merge
@@ -745,6 +767,7 @@ void merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpa
   if (M != -INFINITY) {
     for (int s = 0; s < nsplit; ++s) {
       const float ls = Lpart[(size_t)s * rows + row];
+      if (ls == -INFINITY) continue;   // no key in this split (its O part is not written)
       const float wgt = __expf(ls - M);
       den += wgt;
       const f32x4 x = *(const f32x4*)(Opart + ((size_t)s * rows + row) * D + 4 * c);
@@ -770,6 +793,15 @@ int key_tile(int dtype, int D) {
 
 int block_m(int dtype, int D) { return kBlockM; }
 
+int f32_blocks_per_cu(int D) {
+  int n = 0;
+  hipError_t e = hipErrorInvalidValue;
+  if (D == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<64>, kThreads, 0);
+  if (D == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<128>, kThreads, 0);
+  if (D == 256) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<256>, kThreads, 0);
+  return e == hipSuccess ? n : 0;
+}
+
 template <typename OutT, int D>
 static hipError_t launch_merge(const Params& p, hipStream_t stream) {
   const long rows = (long)p.B * p.H * p.Sq;
@@ -783,11 +815,12 @@ static hipError_t launch_merge(const Params& p, hipStream_t stream) {
 template <int D>
 static hipError_t launch_d(const Params& p, int dtype, hipStream_t stream) {
   const long blocks = (long)p.units * p.n_qblk;
-  if (dtype == 1) {
+  if (dtype == 1) {   // (the bf16 kernel has no persistent form; sched is ignored)
     constexpr int BN = D >= 128 ? 32 : 64;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, BN>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    const long grid = p.sched ? (long)p.nslot : blocks;
+    hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;

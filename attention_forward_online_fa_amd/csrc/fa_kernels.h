@@ -27,12 +27,19 @@ struct Params {
   int n_qblk;        // ceil(Sq / BM)
   int units;         // B * H * nsplit
   int xcd_remap;     // 1: group work so units sharing K/V stay on one XCD
+  // Persistent launch (fp32 kernel): nslot workgroups, workgroup s runs the
+  // items sched[nslot + 1 + k] for k in [sched[s], sched[s + 1]), item =
+  // qblk * units + unit. Null: one workgroup per item in the default order.
+  const int* sched;
+  int nslot;
 };
 
 // Tile shape per (dtype, D): query rows per workgroup and keys per K/V tile.
 constexpr int kBlockM = 128;
 int key_tile(int dtype, int D);
 int block_m(int dtype, int D);
+// Workgroups of the fp32 kernel that fit on one CU at head dim D (0 on error).
+int f32_blocks_per_cu(int D);
 
 // Queue the forward kernel (and the merge kernel when p.nsplit > 1).
 hipError_t launch_forward(const Params& p, int dtype, int D, hipStream_t stream);

@@ -76,6 +76,12 @@ enum fa_status {
  * Long key ranges with few query tiles are split across workgroups along the
  * key axis and merged by log-sum-exp weights; the partial results live in a
  * library-owned, stream-ordered workspace (see fa_release).
+ *
+ * float32 causal or windowed problems with few query tiles (fewer than two
+ * per CU) run persistent workgroups over a balanced list of key-split pieces.
+ * The list depends only on the shape; the first call with a new shape builds
+ * it on the host and uploads it with a synchronous copy (so that call must not
+ * be made during stream capture), later calls reuse it until fa_release.
  */
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
            int B, int H, int HKV, int Sq, int Sk, int D,
@@ -102,13 +108,30 @@ int fa_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE,
 int fa_plan_splits(int B, int H, int HKV, int Sq, int Sk, int D,
                    int causal, int window, int dtype);
 
+/*
+ * fa_schedule_table - the item lists of a persistent launch with nslot
+ * workgroups for this problem (host computation only; no HIP call, so it
+ * also runs without a GPU). Writes min(length, capacity) ints to `table`:
+ * nslot + 1 offsets, then item ids (item = q_tile * units + unit, units =
+ * B * H * splits; slot s runs items table[nslot + 1 + k] for k in
+ * [table[s], table[s + 1])). Stores the key-split count in *num_splits when
+ * that pointer is not NULL. Returns the full length, or a negative fa_status
+ * on argument errors (nslot < 1, or capacity > 0 with a NULL table, gives
+ * -FA_ERR_SHAPE).
+ */
+int fa_schedule_table(int B, int H, int HKV, int Sq, int Sk, int D,
+                      int causal, int window, int dtype, int nslot,
+                      int* table, int capacity, int* num_splits);
+
 /* fa_status_string - static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 
 /*
  * fa_release - return the split-K workspace pool of every device this
- * library has used to the HIP runtime. Must not be called while work queued
- * by fa_fwd is still running. Later calls allocate again as needed.
+ * library has used to the HIP runtime and free the cached persistent-launch
+ * schedules (after a device synchronisation on each device that holds some).
+ * Must not be called while other threads call fa_fwd. Later calls allocate
+ * again as needed.
  */
 void fa_release(void);
 
