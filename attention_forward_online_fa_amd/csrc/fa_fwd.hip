@@ -415,8 +415,9 @@ void fwd_bf16_kernel(Params p) {
   // takes the slow path: true row max, rescale O and l, recompute P. Exact in
   // every case, since O and l always share one reference; between rescales
   // every P stays below 2^64, far inside the float32 and bfloat16 range.
+  float m_sub = -1e30f;   // m_ref, or -1e30 while m_ref is -inf
   auto softmax = [&]() {
-    float rs = exp_pack_sum(m_ref == -INFINITY ? -1e30f : m_ref);
+    float rs = exp_pack_sum(m_sub);
     if (__any(!(rs <= kRowSumLimit))) {
       float mx = -INFINITY;
 #pragma unroll
@@ -432,6 +433,7 @@ void fwd_bf16_kernel(Params p) {
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) o[db] *= corr;
       rs = exp_pack_sum(m_ref == -INFINITY ? 0.f : m_ref);
+      m_sub = m_ref == -INFINITY ? -1e30f : m_ref;
     }
     l += rs;
   };
