@@ -25,15 +25,19 @@
 // registers as the MFMA B operand and computes S^T = K Q^T, so a lane owns one
 // query row (column of S^T) and half of the tile's keys: row max and row sum
 // are in-lane plus one exchange with lane ^ 32. The P tile then feeds the
-// second MFMA (O^T = V^T P^T) straight from registers; V is transposed once
-// into LDS when it is staged. K/V tiles are double-buffered in LDS: the next
-// tile's global loads are in flight while the current tile is computed.
+// second MFMA (O^T = V^T P^T) straight from registers; V stays row-major in
+// LDS and the bf16 kernel reads it transposed (ds_read_b64_tr_b16), the fp32
+// kernel with its dims spread over the accumulator blocks. K/V tiles are
+// double-buffered in LDS: the next tile's copy is in flight while the current
+// tile is computed.
 //
 // Workgroup order: heaviest query tiles (latest rows under a causal mask)
 // first; when the number of (batch, head, split) units is a multiple of 8 the
 // blocks are remapped so that the query heads sharing one K/V head land on the
 // same XCD (MI355X dispatches workgroups round-robin over its 8 XCDs, each
-// with its own L2).
+// with its own L2). The fp32 kernel can also run persistently: a fixed number
+// of workgroups, each over a host-computed list of (query tile, key split)
+// items (Params::sched).
 #include "fa_kernels.h"
 
 #include <hip/hip_runtime.h>
