@@ -18,8 +18,8 @@ import math
 
 from ._lib import FA_BF16, FA_F32, FA_MAX_SPLITS, FaError, lib, library_path
 
-__all__ = ["fwd", "fwd_into", "plan_splits", "release", "FaError", "library_path",
-           "default_scale", "FA_F32", "FA_BF16", "FA_MAX_SPLITS"]
+__all__ = ["fwd", "fwd_into", "plan_splits", "schedule_table", "release", "FaError",
+           "library_path", "default_scale", "FA_F32", "FA_BF16", "FA_MAX_SPLITS"]
 
 
 def _dtype_code(t):
