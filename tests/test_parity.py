@@ -199,3 +199,19 @@ def test_benchmark_workload(idx):
     lh = host64(lse)
     assert np.all(np.isfinite(lh[:, :, cnt > 0]))
     assert torch.isfinite(o.float()).all().item()
+
+
+def test_fp32_causal_small_grid_runs_persistent_pieces():
+    # the fp32 causal MHA workload has 256 query tiles (fewer than two per CU):
+    # it runs as persistent workgroups over key-split pieces and a merge
+    import attention_forward_online_fa_amd as fa
+    wl = W.CONFIGS[1]
+    ns = fa.plan_splits(wl.B, wl.H, wl.HKV, wl.Sq, wl.Sk, wl.D, causal=bool(wl.causal),
+                        window=wl.window, dtype=wl.dtype)
+    assert ns > 1
+    # every piece list, and the result against the oracle on a smaller grid of
+    # the same kind (all rows), with two calls in a row using the cached list
+    small = wl_small("f32", 2, 4, 4, 640, 640, 64, 1, 0, seed=77)
+    assert fa.plan_splits(2, 4, 4, 640, 640, 64, causal=True, dtype="f32") > 1
+    check_full(small)
+    check_full(small)
