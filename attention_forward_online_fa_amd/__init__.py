@@ -7,7 +7,7 @@ checks and marshals arguments. torch provides device memory and streams.
     o, lse = fwd(q, k, v, causal=True, window=0)
 
 q: [B, H, Sq, D], k and v: [B, HKV, Sk, D], contiguous CUDA (HIP) tensors of
-dtype float32 or bfloat16; o has q's shape and dtype, lse is float32
+dtype float32, bfloat16 or float16; o has q's shape and dtype, lse is float32
 [B, H, Sq] in natural-log units. A row with no visible key gets o = 0 and
 lse = -inf.
 """
@@ -16,10 +16,10 @@ from __future__ import annotations
 import ctypes
 import math
 
-from ._lib import FA_BF16, FA_F32, FA_MAX_SPLITS, FaError, lib, library_path
+from ._lib import FA_BF16, FA_F16, FA_F32, FA_MAX_SPLITS, FaError, lib, library_path
 
 __all__ = ["fwd", "fwd_into", "plan_splits", "schedule_table", "release", "FaError",
-           "library_path", "default_scale", "FA_F32", "FA_BF16", "FA_MAX_SPLITS"]
+           "library_path", "default_scale", "FA_F32", "FA_BF16", "FA_F16", "FA_MAX_SPLITS"]
 
 
 def _dtype_code(t):
@@ -28,7 +28,20 @@ def _dtype_code(t):
         return FA_F32
     if t.dtype == torch.bfloat16:
         return FA_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+    if t.dtype == torch.float16:
+        return FA_F16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32, bfloat16 or float16")
+
+
+_DTYPE_NAMES = {"f32": FA_F32, "bf16": FA_BF16, "f16": FA_F16}
+
+
+def _dtype_name_code(dtype) -> int:
+    if dtype in _DTYPE_NAMES.values():
+        return int(dtype)
+    if dtype in _DTYPE_NAMES:
+        return _DTYPE_NAMES[dtype]
+    raise TypeError(f"unknown dtype {dtype!r}: use 'f32', 'bf16' or 'f16'")
 
 
 def default_scale(D: int) -> float:
@@ -87,7 +100,7 @@ def fwd(q, k, v, *, causal=False, window=0, scale=None, num_splits=0, stream=Non
 
 def plan_splits(B, H, HKV, Sq, Sk, D, *, causal=False, window=0, dtype="bf16") -> int:
     """Key-axis split count the library picks for this problem on the current device."""
-    code = FA_BF16 if dtype in ("bf16", FA_BF16) else FA_F32
+    code = _dtype_name_code(dtype)
     r = lib().fa_plan_splits(B, H, HKV, Sq, Sk, D, int(bool(causal)), int(window), code)
     if r < 0:
         raise FaError(-r)
@@ -97,7 +110,7 @@ def plan_splits(B, H, HKV, Sq, Sk, D, *, causal=False, window=0, dtype="bf16") -
 def schedule_table(B, H, HKV, Sq, Sk, D, nslot, *, causal=False, window=0, dtype="f32"):
     """Persistent-launch item lists for nslot workgroups (host only): returns
     (num_splits, offsets[nslot + 1], items)."""
-    code = FA_BF16 if dtype in ("bf16", FA_BF16) else FA_F32
+    code = _dtype_name_code(dtype)
     args = (B, H, HKV, Sq, Sk, D, int(bool(causal)), int(window), code, nslot)
     n = lib().fa_schedule_table(*args, None, 0, None)
     if n < 0:

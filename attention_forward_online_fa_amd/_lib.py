@@ -9,6 +9,7 @@ from . import build as _build
 
 FA_F32 = 0
 FA_BF16 = 1
+FA_F16 = 2
 FA_MAX_SPLITS = 64
 
 STATUS = {

@@ -83,11 +83,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_args(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int window,
                int dtype) {
   if (B < 1 || H < 1 || HKV < 1 || Sq < 1 || Sk < 1 || D < 1) return FA_ERR_SHAPE;
-  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_DTYPE;
   if (D != 64 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
   if (H % HKV != 0) return FA_ERR_GQA;
   if (window < 0 || (causal != 0 && causal != 1)) return FA_ERR_WINDOW;
-  const int esz = dtype == FA_BF16 ? 2 : 4;
+  const int esz = dtype == FA_F32 ? 4 : 2;
   // Element counts must stay far from 64-bit overflow in every address.
   const double q_bytes = (double)B * H * Sq * D * esz;
   const double kv_bytes = (double)B * HKV * Sk * D * esz;
@@ -332,8 +332,8 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   p.Sk = Sk;
   p.group = H / HKV;
   p.sl = (float)((double)scale * 1.4426950408889634);
-  if (dtype == FA_BF16) {
-    // The bf16 kernel needs a positive multiplier: q.k * scale = (-q).k * |scale|
+  if (dtype != FA_F32) {
+    // The 16-bit kernel needs a positive multiplier: q.k * scale = (-q).k * |scale|
     // exactly, and for scale = 0 a multiplier of 1e-30 leaves every exp2
     // argument within 1e-20 of 0, where exp2 rounds to exactly 1.
     p.neg_q = scale < 0.f ? 1 : 0;
@@ -432,7 +432,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_SHAPE: return "invalid shape: a dimension is < 1 or the problem is too large";
     case FA_ERR_GQA: return "H must be a multiple of HKV";
     case FA_ERR_HEAD_DIM: return "head dimension D must be 64, 128 or 256";
-    case FA_ERR_DTYPE: return "dtype must be FA_F32 (0) or FA_BF16 (1)";
+    case FA_ERR_DTYPE: return "dtype must be FA_F32 (0), FA_BF16 (1) or FA_F16 (2)";
     case FA_ERR_WINDOW: return "window must be >= 0 and causal 0 or 1";
     case FA_ERR_ALIGN: return "every buffer must be 16-byte aligned";
     case FA_ERR_HIP: return "HIP runtime error";

@@ -26,7 +26,7 @@
 // query row (column of S^T) and half of the tile's keys: row max and row sum
 // are in-lane plus one exchange with lane ^ 32. The P tile then feeds the
 // second MFMA (O^T = V^T P^T) straight from registers; V stays row-major in
-// LDS and the bf16 kernel reads it transposed (ds_read_b64_tr_b16), the fp32
+// LDS and the 16-bit kernel reads it transposed (ds_read_b64_tr_b16), the fp32
 // kernel with its dims spread over the accumulator blocks. K/V tiles are
 // double-buffered in LDS: the next tile's copy is in flight while the current
 // tile is computed.
@@ -45,11 +45,44 @@
 
 namespace fa {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// The two 16-bit input types of the MFMA kernel. P is rounded to the input
+// type for the PV product; its row-sum bound (the rescale trigger of the
+// softmax below) keeps every P inside that type's range.
+template <typename E>
+struct Elt;
+template <>
+struct Elt<__bf16> {
+  typedef __bf16 x8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 x4 __attribute__((ext_vector_type(4)));
+  typedef __bf16 x2 __attribute__((ext_vector_type(2)));
+  static constexpr float kRowSumLimit = 1.8446744e19f;   // 2^64
+  static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float dot2(x2 a, x2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+  }
+};
+template <>
+struct Elt<_Float16> {
+  typedef _Float16 x8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 x4 __attribute__((ext_vector_type(4)));
+  typedef _Float16 x2 __attribute__((ext_vector_type(2)));
+  // 2^15: a lane's row sum bounds each of its P values, so every P stays
+  // below the float16 maximum (65504) between rescales.
+  static constexpr float kRowSumLimit = 32768.f;
+  static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float dot2(x2 a, x2 b, float c) {
+    return __builtin_amdgcn_fdot2(a, b, c, false);
+  }
+};
 
 constexpr int kThreads = 256;   // 4 wavefronts of 64
 constexpr float kLn2 = 0.693147180559945309f;
@@ -143,8 +176,8 @@ __device__ __forceinline__ void finish_row(const Params& p, int b, int h, int sp
   }
 }
 
-// ====================================================================== bf16
-// S^T tile = K Q^T with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims from
+// ================================================= 16-bit inputs (bf16, fp16)
+// S^T tile = K Q^T with v_mfma_f32_32x32x16_bf16 (or _f16): A = 32 keys x 16 dims from
 // LDS, B = 16 dims x 32 query rows from registers. In the accumulator, lane
 // (q = lane % 32, g = lane / 32) holds rows 8(v/4) + 4g + v%4 of S^T. Loading
 // A row r from key pi(r) (bits 2 and 3 of r swapped) makes element v of that
@@ -197,12 +230,13 @@ struct Bf16Tile {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-__device__ __forceinline__ bf16x8 read_v_pair(const char* base, int off0, int off1) {
+template <typename X8>
+__device__ __forceinline__ X8 read_v_pair(const char* base, int off0, int off1) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_char*)(base + off0));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_char*)(base + off1));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
+  return __builtin_bit_cast(X8, v);
 }
 
 // One 16-byte-per-lane HBM -> LDS copy: lane l's 16 bytes at base + voff land
@@ -226,10 +260,14 @@ __device__ __forceinline__ float half_max(float x) {
 
 constexpr float kRowSumLimit = 1.8446744e19f;   // 2^64: row-sum bound that triggers a rescale
 
-template <int D, int BN>
+// E = __bf16 or _Float16 (inputs, O and the rounded P); fp32 accumulation,
+// softmax and LSE either way.
+template <typename E, int D, int BN>
 __global__ __launch_bounds__(kThreads, (D == 128 ? 3 : 2))
-void fwd_bf16_kernel(Params p) {
+void fwd_16b_kernel(Params p) {
   using T = Bf16Tile<D, BN>;
+  using X = Elt<E>;
+  typedef typename X::x8 e16x8;
   // K and V tiles double-buffered; four separate objects let the compiler see
   // that the copy filling one buffer never aliases the reads of another (it
   // would otherwise wait for the in-flight copy before reading).
@@ -246,9 +284,9 @@ void fwd_bf16_kernel(Params p) {
   const int qw = q0 + wave * 32;
   const int i = qw + l32;
 
-  const __bf16* Qp = (const __bf16*)p.Q + (size_t)(w.b * p.H + w.h) * p.Sq * D;
-  const __bf16* Kp = (const __bf16*)p.K + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
-  const __bf16* Vp = (const __bf16*)p.V + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
+  const E* Qp = (const E*)p.Q + (size_t)(w.b * p.H + w.h) * p.Sq * D;
+  const E* Kp = (const E*)p.K + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
+  const E* Vp = (const E*)p.V + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
 
   int lo, hi;
   key_range(p, q0, kBlockM, w.split, lo, hi);
@@ -262,8 +300,8 @@ void fwd_bf16_kernel(Params p) {
   auto issue = [&](int kt, char* kdst, char* vdst, bool full = false) {
     // a full tile needs no bound: BN rows are in range
     const unsigned bytes = full ? (unsigned)(BN * T::ROW) : (unsigned)min((long)(p.Sk - kt) * T::ROW, 0x7fffffffL);
-    const __bf16* kb = Kp + (size_t)kt * D;
-    const __bf16* vb = Vp + (size_t)kt * D;
+    const E* kb = Kp + (size_t)kt * D;
+    const E* vb = Vp + (size_t)kt * D;
 #pragma unroll
     for (int k = 0; k < T::NIW; ++k) {
       const int off = (wave * T::NIW + k) * 1024;
@@ -277,16 +315,16 @@ void fwd_bf16_kernel(Params p) {
   if (n_tiles > 0) issue(t0, kbuf0, vbuf0);
 
   // Query rows as the B operand: k-slot (g, e) of step t is dim 16t + 8g + e.
-  bf16x8 qf[T::DC];
+  e16x8 qf[T::DC];
 #pragma unroll
   for (int t = 0; t < T::DC; ++t) {
     if (i < p.Sq)
-      qf[t] = *(const bf16x8*)(Qp + (size_t)i * D + 16 * t + 8 * g);
+      qf[t] = *(const e16x8*)(Qp + (size_t)i * D + 16 * t + 8 * g);
     else
-      qf[t] = bf16x8{};
+      qf[t] = e16x8{};
     if (p.neg_q) {   // negative scale: use -Q and |scale| (exact sign flips)
       u32x4 bits = __builtin_bit_cast(u32x4, qf[t]) ^ 0x80008000u;
-      qf[t] = __builtin_bit_cast(bf16x8, bits);
+      qf[t] = __builtin_bit_cast(e16x8, bits);
     }
   }
 
@@ -321,7 +359,7 @@ void fwd_bf16_kernel(Params p) {
   float m_ref = -INFINITY, l = 0.f;
   const float sl = p.sl;
   f32x16 s[T::KB];
-  bf16x8 pf[T::KC];
+  e16x8 pf[T::KC];
 
   // ---- S^T = K Q^T for one tile
   auto qk = [&](const char* Ks) {
@@ -333,8 +371,8 @@ void fwd_bf16_kernel(Params p) {
     for (int t = 0; t < T::DC; ++t) {
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb) {
-        const bf16x8 a = *(const bf16x8*)(Ks + k_off(t) + kb * 32 * T::ROW);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb], 0, 0, 0);
+        const e16x8 a = *(const e16x8*)(Ks + k_off(t) + kb * 32 * T::ROW);
+        s[kb] = X::mfma(a, qf[t], s[kb]);
       }
     }
   };
@@ -364,12 +402,11 @@ void fwd_bf16_kernel(Params p) {
     }
   };
 
-  // ---- P = exp2(S - m_sub) packed to bf16; returns this lane's row sum of P.
-  // D <= 128 sums the fp32 values with VALU adds (v_dot2c_f32_bf16 issues to
-  // the matrix pipe, where it waits behind the other wavefronts' MFMAs);
-  // D = 256, at two wavefronts per SIMD and short of registers, sums the
-  // rounded bf16 values with dot2.
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  // ---- P = exp2(S - m_sub) packed to the input type; returns this lane's
+  // row sum of P. D <= 128 sums the fp32 values with VALU adds (the dot2
+  // instructions issue to the matrix pipe, where they wait behind the other
+  // wavefronts' MFMAs); D = 256, at two wavefronts per SIMD and short of
+  // registers, sums the rounded 16-bit values with dot2.
   auto exp_pack_sum = [&](float m_sub) {
     if constexpr (D == 256) {
 #pragma unroll
@@ -378,15 +415,15 @@ void fwd_bf16_kernel(Params p) {
         for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            pf[2 * kb + c2][e] = (__bf16)fast_exp2(fmaf(s[kb][8 * c2 + e], sl, -m_sub));
-      const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+            pf[2 * kb + c2][e] = (E)fast_exp2(fmaf(s[kb][8 * c2 + e], sl, -m_sub));
+      const typename X::x2 ones = {(E)1.f, (E)1.f};
       float rs = 0.f;
 #pragma unroll
       for (int c = 0; c < T::KC; ++c)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const bf16x2 two = {pf[c][e], pf[c][e + 1]};
-          rs = __builtin_amdgcn_fdot2_f32_bf16(two, ones, rs, false);
+          const typename X::x2 two = {pf[c][e], pf[c][e + 1]};
+          rs = X::dot2(two, ones, rs);
         }
       return rs;
     } else {
@@ -403,8 +440,8 @@ void fwd_bf16_kernel(Params p) {
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            pf[2 * kb + c2][e] = (__bf16)lo[e];
-            pf[2 * kb + c2][4 + e] = (__bf16)hi[e];
+            pf[2 * kb + c2][e] = (E)lo[e];
+            pf[2 * kb + c2][4 + e] = (E)hi[e];
           }
           ps += lo;
           ps += hi;
@@ -422,7 +459,7 @@ void fwd_bf16_kernel(Params p) {
   float m_sub = -1e30f;   // m_ref, or -1e30 while m_ref is -inf
   auto softmax = [&]() {
     float rs = exp_pack_sum(m_sub);
-    if (__any(!(rs <= kRowSumLimit))) {
+    if (__any(!(rs <= X::kRowSumLimit))) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb)
@@ -451,8 +488,8 @@ void fwd_bf16_kernel(Params p) {
       for (int db = 0; db < T::DB; ++db) {
         const int base = 16 * c * T::ROW;
         const int vo = v_off(db) + base;
-        const bf16x8 a = read_v_pair(Vs, vo, vo + 4 * T::ROW);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c], o[db], 0, 0, 0);
+        const e16x8 a = read_v_pair<e16x8>(Vs, vo, vo + 4 * T::ROW);
+        o[db] = X::mfma(a, pf[c], o[db]);
       }
     }
   };
@@ -532,15 +569,14 @@ void fwd_bf16_kernel(Params p) {
                      *(f32x4*)(dst + 32 * db + 8 * a + 4 * g) = v4;
                    }
                } else {
-                 __bf16* dst = (__bf16*)p.O + row * D;
+                 E* dst = (E*)p.O + row * D;
 #pragma unroll
                  for (int db = 0; db < T::DB; ++db)
 #pragma unroll
                    for (int a = 0; a < 4; ++a) {
-                     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                     bf16x4 v4 = {(__bf16)(o[db][4 * a] * inv), (__bf16)(o[db][4 * a + 1] * inv),
-                                  (__bf16)(o[db][4 * a + 2] * inv), (__bf16)(o[db][4 * a + 3] * inv)};
-                     *(bf16x4*)(dst + 32 * db + 8 * a + 4 * g) = v4;
+                     typename X::x4 v4 = {(E)(o[db][4 * a] * inv), (E)(o[db][4 * a + 1] * inv),
+                                          (E)(o[db][4 * a + 2] * inv), (E)(o[db][4 * a + 3] * inv)};
+                     *(typename X::x4*)(dst + 32 * db + 8 * a + 4 * g) = v4;
                    }
                }
              });
@@ -783,8 +819,8 @@ void merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpa
   }
   OutT* dst = O + (size_t)row * D + 4 * c;
   if constexpr (sizeof(OutT) == 2) {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    *(bf16x4*)dst = bf16x4{(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
+    typedef typename Elt<OutT>::x4 o4;
+    *(o4*)dst = o4{(OutT)acc[0], (OutT)acc[1], (OutT)acc[2], (OutT)acc[3]};
   } else {
     *(f32x4*)dst = acc;
   }
@@ -793,7 +829,7 @@ void merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpa
 
 // ================================================================ launch
 int key_tile(int dtype, int D) {
-  if (dtype == 1) return D >= 128 ? 32 : 64;
+  if (dtype != 0) return D >= 128 ? 32 : 64;   // 16-bit inputs
   return F32Tile<64>::BN;
 }
 
@@ -821,16 +857,21 @@ static hipError_t launch_merge(const Params& p, hipStream_t stream) {
 template <int D>
 static hipError_t launch_d(const Params& p, int dtype, hipStream_t stream) {
   const long blocks = (long)p.units * p.n_qblk;
-  if (dtype == 1) {   // (the bf16 kernel has no persistent form; sched is ignored)
-    constexpr int BN = D >= 128 ? 32 : 64;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BN>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  constexpr int BN = D >= 128 ? 32 : 64;
+  // (the 16-bit kernel has no persistent form; sched is ignored)
+  if (dtype == 1) {
+    hipLaunchKernelGGL((fwd_16b_kernel<__bf16, D, BN>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  } else if (dtype == 2) {
+    hipLaunchKernelGGL((fwd_16b_kernel<_Float16, D, BN>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   } else {
     const long grid = p.sched ? (long)p.nslot : blocks;
     hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  return dtype == 1 ? launch_merge<__bf16, D>(p, stream) : launch_merge<float, D>(p, stream);
+  if (dtype == 1) return launch_merge<__bf16, D>(p, stream);
+  if (dtype == 2) return launch_merge<_Float16, D>(p, stream);
+  return launch_merge<float, D>(p, stream);
 }
 
 hipError_t launch_forward(const Params& p, int dtype, int D, hipStream_t stream) {

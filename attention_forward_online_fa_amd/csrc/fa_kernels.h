@@ -18,8 +18,8 @@ struct Params {
   int B, H, HKV, Sq, Sk;
   int group;         // H / HKV
   float sl;          // scale * log2(e): scores are kept in base-2 units
-                     // (bf16 kernel: |scale| * log2(e) > 0, see neg_q)
-  int neg_q;         // bf16 kernel: 1 when scale < 0 (it then uses -Q and |scale|)
+                     // (16-bit kernel: |scale| * log2(e) > 0, see neg_q)
+  int neg_q;         // 16-bit kernel: 1 when scale < 0 (it then uses -Q and |scale|)
   int causal;
   int window;
   int nsplit;        // key-axis splits (1 = none)

@@ -31,7 +31,7 @@ import numpy as np  # noqa: E402
 
 import workloads as W  # noqa: E402
 
-PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (published)
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (published)
 KERNEL_SOURCES = [os.path.join(ROOT, "attention_forward_online_fa_amd", "csrc", f)
                   for f in ("fa_fwd.hip", "fa_api.cpp", "fa_kernels.h")]
 
@@ -49,7 +49,7 @@ def counted_flops(wl: W.Workload) -> float:
 
 
 def algorithmic_bytes(wl: W.Workload) -> int:
-    esz = 2 if wl.dtype == "bf16" else 4
+    esz = 4 if wl.dtype == "f32" else 2
     q = wl.B * wl.H * wl.Sq * wl.D * esz
     kv = 2 * wl.B * wl.HKV * wl.Sk * wl.D * esz
     return q + kv + q + wl.B * wl.H * wl.Sq * 4
@@ -77,8 +77,9 @@ def measured_traffic(wl: W.Workload):
 
 
 def device_inputs(inp, torch):
-    if inp.wl.dtype == "bf16":
-        conv = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    if inp.wl.dtype in ("bf16", "f16"):
+        tdt = torch.bfloat16 if inp.wl.dtype == "bf16" else torch.float16
+        conv = lambda b: torch.from_numpy(b.view(np.int16)).view(tdt).cuda()
         return conv(inp.q_bits), conv(inp.k_bits), conv(inp.v_bits)
     return tuple(torch.from_numpy(a).cuda() for a in (inp.q, inp.k, inp.v))
 

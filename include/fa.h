@@ -34,7 +34,10 @@ extern "C" {
 /* Element types of Q, K, V and O. LSE is always float32. */
 enum fa_dtype {
   FA_F32 = 0,   /* float32 in and out, float32 MFMA arithmetic            */
-  FA_BF16 = 1   /* bfloat16 in and out, float32 accumulate and softmax    */
+  FA_BF16 = 1,  /* bfloat16 in and out, float32 accumulate and softmax    */
+  FA_F16 = 2    /* float16 in and out, float32 accumulate and softmax     */
+                /* (mixed precision: the "Support mixed precision" TODO of
+                   the metal-flash-attention README)                      */
 };
 
 /* Status codes. Every argument error is detected on the host before any

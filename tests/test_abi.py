@@ -90,7 +90,7 @@ def test_null_pointer(which):
     (dict(B=0), 2), (dict(H=0), 2), (dict(HKV=0), 2), (dict(Sq=0), 2), (dict(Sk=-3), 2),
     (dict(H=6, HKV=4), 3), (dict(H=4, HKV=3), 3),
     (dict(D=96), 4), (dict(D=32), 4), (dict(D=512), 4),
-    (dict(dtype=2), 5), (dict(dtype=-1), 5),
+    (dict(dtype=3), 5), (dict(dtype=-1), 5),
     (dict(window=-1), 6), (dict(causal=2), 6),
     (dict(B=1 << 20, H=1 << 10, Sq=1 << 10), 2),
 ])

@@ -49,3 +49,31 @@ def test_sampled_rows_union_of_random_and_edges():
         assert (0, h, 0) in keys and (0, h, 511) in keys and (0, h, 7) in keys
     assert len(rows) <= 40 + wl.H * 16
     assert W.check_rows(W.make_inputs(W.CONFIGS[0])) is None
+
+
+def test_f16_round_to_nearest_even():
+    one = np.float32(1.0)
+    ulp = np.float32(2.0 ** -10)         # fp16 spacing at 1.0
+    x = np.array([1.0,
+                  one + ulp / 2,          # tie -> even (1.0)
+                  one + ulp + ulp / 2,    # tie -> even (1 + 2 ulp)
+                  one + ulp / 2 + np.float32(2.0 ** -20),   # just above tie -> up
+                  -2.5, 65504.0, 2.0 ** -24], dtype=np.float32)
+    bits = W.round_to_f16_bits(x)
+    assert bits[0] == 0x3C00
+    assert bits[1] == 0x3C00
+    assert bits[2] == 0x3C02
+    assert bits[3] == 0x3C01
+    assert bits[4] == 0xC100
+    assert bits[5] == 0x7BFF
+    assert bits[6] == 0x0001               # smallest subnormal
+    back = W.f16_bits_to_f32(bits)
+    assert np.all(np.abs(back - x) <= np.abs(x) * 2.0 ** -11)
+
+
+def test_f16_workload_inputs_are_rounded():
+    wl = W.small(W.CONFIGS[5], B=1, H=4, HKV=1, Sq=64, Sk=64)
+    assert wl.dtype == "f16"
+    a = W.make_inputs(wl)
+    np.testing.assert_array_equal(W.f16_bits_to_f32(a.q_bits), a.q)
+    np.testing.assert_array_equal(a.k.astype(np.float16).astype(np.float32), a.k)

@@ -8,7 +8,9 @@ sharing any code of the method.
 
 Workload shapes follow the five synthetic configurations of the benchmark
 (small reference case, fp32 causal MHA, bf16 causal GQA, fp32 sliding-window
-GQA, bf16 long non-square single head). Layout is [B, H, S, D] contiguous for
+GQA, bf16 long non-square single head), plus the causal GQA shape with fp16
+inputs (mixed precision, the "Support mixed precision" item of the
+metal-flash-attention README's TODO list). Layout is [B, H, S, D] contiguous for
 Q and O, [B, HKV, S, D] for K and V, as in the boostr ``flash.wgsl`` header
 comment and the rustytorch ``flash_attention_forward.metal`` buffer comments.
 
@@ -16,8 +18,9 @@ Recipe (stated once, used everywhere):
   * generator: ``numpy.random.default_rng`` on a ``SeedSequence(seed)`` spawned
     into four independent streams (Q, K, V, row sample);
   * seed = 20261202 + config index (0-based);
-  * values are drawn in float32; for bf16 workloads they are rounded to the
-    nearest bf16 (ties to even) and both sides read the rounded values.
+  * values are drawn in float32; for bf16 and fp16 workloads they are rounded
+    to the nearest bf16 / fp16 value (ties to even) and both sides read the
+    rounded values.
 """
 from __future__ import annotations
 
@@ -38,7 +41,7 @@ class Workload:
     Sq: int
     Sk: int
     D: int
-    dtype: str            # "f32" or "bf16"
+    dtype: str            # "f32", "bf16" or "f16"
     causal: int
     window: int
     q_dist: str = "normal"     # "normal" | "uniform"
@@ -76,6 +79,9 @@ CONFIGS = [
     Workload("long_bf16_sq8192_sk65536_d256", 1, 1, 1, 8192, 65536, 256, "bf16", 0, 0,
              v_dist="uniform", check="sampled", n_random_rows=256, edge_rows=0,
              seed_index=4),
+    Workload("gqa_causal_f16_b2h32kv8_s4096_d128", 2, 32, 8, 4096, 4096, 128, "f16", 1, 0,
+             amplitude=0.5, check="sampled", n_random_rows=4096, edge_rows=64,
+             seed_index=5),
 ]
 
 # The configuration the throughput metric is quoted on (bf16 causal GQA).
@@ -98,6 +104,24 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
+def round_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 array -> uint16 IEEE half bit patterns, round to nearest, ties to
+    even (numpy's float32 -> float16 conversion). Inputs must lie inside the
+    half range."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert np.all(np.abs(x) <= 65504.0), "fp16 rounding expects inputs inside the half range"
+    return x.astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return bits.view(np.float16).astype(np.float32)
+
+
+# 16-bit input types: (float32 -> bits, bits -> float32)
+ROUNDING = {"bf16": (round_to_bf16_bits, bf16_bits_to_f32),
+            "f16": (round_to_f16_bits, f16_bits_to_f32)}
+
+
 def _draw(rng: np.random.Generator, shape, dist: str) -> np.ndarray:
     if dist == "normal":
         return rng.standard_normal(shape, dtype=np.float32)
@@ -111,8 +135,8 @@ class Inputs:
     """Host copies of one workload's inputs.
 
     ``q``/``k``/``v`` are float32 arrays holding exactly the values the GPU
-    reads (for bf16 workloads they are the rounded values); ``*_bits`` are the
-    bf16 bit patterns (uint16) for bf16 workloads, else None."""
+    reads (for 16-bit workloads they are the rounded values); ``*_bits`` are
+    the bf16 / fp16 bit patterns (uint16) for 16-bit workloads, else None."""
     wl: Workload
     q: np.ndarray
     k: np.ndarray
@@ -133,13 +157,10 @@ def make_inputs(wl: Workload, seed: int | None = None) -> Inputs:
         a = np.float32(wl.amplitude)
         q, k, v = q * a, k * a, v * a
     out = Inputs(wl, q, k, v, rows_rng=np.random.default_rng(srow))
-    if wl.dtype == "bf16":
-        out.q_bits = round_to_bf16_bits(q)
-        out.k_bits = round_to_bf16_bits(k)
-        out.v_bits = round_to_bf16_bits(v)
-        out.q = bf16_bits_to_f32(out.q_bits)
-        out.k = bf16_bits_to_f32(out.k_bits)
-        out.v = bf16_bits_to_f32(out.v_bits)
+    if wl.dtype in ROUNDING:
+        to_bits, to_f32 = ROUNDING[wl.dtype]
+        out.q_bits, out.k_bits, out.v_bits = to_bits(q), to_bits(k), to_bits(v)
+        out.q, out.k, out.v = to_f32(out.q_bits), to_f32(out.k_bits), to_f32(out.v_bits)
     return out
 
 
