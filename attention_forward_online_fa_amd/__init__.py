@@ -6,10 +6,13 @@ checks and marshals arguments. torch provides device memory and streams.
 
     o, lse = fwd(q, k, v, causal=True, window=0)
 
-q: [B, H, Sq, D], k and v: [B, HKV, Sk, D], contiguous CUDA (HIP) tensors of
-dtype float32, bfloat16 or float16; o has q's shape and dtype, lse is float32
+q: [B, H, Sq, D], k and v: [B, HKV, Sk, D] CUDA (HIP) tensors of dtype
+float32, bfloat16 or float16; o has q's shape and dtype, lse is float32
 [B, H, Sq] in natural-log units. A row with no visible key gets o = 0 and
-lse = -inf.
+lse = -inf. Contiguous tensors go through fa_fwd_ex; any other strides with a
+contiguous last dimension (e.g. token-major [B, S, H, D] storage viewed as
+[B, H, S, D] with ``.transpose(1, 2)``, or slices of packed QKV) through
+fa_fwd_strided, which checks the stride rules of include/fa.h.
 """
 from __future__ import annotations
 
@@ -54,10 +57,10 @@ def _check(q, k, v):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
         if t.dim() != 4:
             raise ValueError(f"{name} must be 4-D [B, heads, S, D]")
+        if t.stride(3) != 1 and t.shape[3] > 1:
+            raise ValueError(f"{name}: the head dimension must be contiguous (stride 1)")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share one dtype")
     if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3]:
@@ -70,29 +73,41 @@ def fwd_into(q, k, v, o, lse, *, causal=False, window=0, scale=None, num_splits=
     _check(q, k, v)
     B, H, Sq, D = q.shape
     HKV, Sk = k.shape[1], k.shape[2]
-    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
-        raise ValueError("o must be contiguous with q's shape and dtype")
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_cuda:
+        raise ValueError("o must be a device tensor with q's shape and dtype")
+    if o.stride(3) != 1 and o.shape[3] > 1:
+        raise ValueError("o: the head dimension must be contiguous (stride 1)")
     if tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be contiguous float32 [B, H, Sq]")
     if scale is None:
         scale = default_scale(D)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    st = lib().fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                         B, H, HKV, Sq, Sk, D, float(scale), int(bool(causal)), int(window),
-                         _dtype_code(q), int(num_splits), stream.cuda_stream)
+    if all(t.is_contiguous() for t in (q, k, v, o)):
+        st = lib().fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), B, H, HKV, Sq, Sk, D, float(scale),
+                             int(bool(causal)), int(window), _dtype_code(q), int(num_splits),
+                             stream.cuda_stream)
+    else:
+        st3 = [(ctypes.c_longlong * 3)(*t.stride()[:3]) for t in (q, k, v, o)]
+        ptr = [ctypes.cast(a, ctypes.c_void_p) for a in st3]
+        st = lib().fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr(), B, H, HKV, Sq, Sk, D, *ptr, float(scale),
+                                  int(bool(causal)), int(window), _dtype_code(q),
+                                  int(num_splits), stream.cuda_stream)
     if st != 0:
         raise FaError(st)
     return o, lse
 
 
 def fwd(q, k, v, *, causal=False, window=0, scale=None, num_splits=0, stream=None):
-    """Forward pass; allocates o and lse with torch. Returns (o, lse)."""
+    """Forward pass; allocates o (with q's memory layout) and lse with torch.
+    Returns (o, lse)."""
     import torch
     _check(q, k, v)
     B, H, Sq, _ = q.shape
     with torch.cuda.device(q.device):
-        o = torch.empty_like(q)
+        o = torch.empty_like(q)       # keeps q's strides when q is dense
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     return fwd_into(q, k, v, o, lse, causal=causal, window=window, scale=scale,
                     num_splits=num_splits, stream=stream)

@@ -15,7 +15,7 @@ FA_MAX_SPLITS = 64
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULLPTR", 2: "FA_ERR_SHAPE", 3: "FA_ERR_GQA",
     4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_DTYPE", 6: "FA_ERR_WINDOW", 7: "FA_ERR_ALIGN",
-    8: "FA_ERR_HIP", 9: "FA_ERR_WORKSPACE", 10: "FA_ERR_SPLITS",
+    8: "FA_ERR_HIP", 9: "FA_ERR_WORKSPACE", 10: "FA_ERR_SPLITS", 11: "FA_ERR_STRIDE",
 }
 
 # Every symbol include/fa.h declares, with its ctypes signature.
@@ -23,6 +23,8 @@ _P, _I, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
 SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P]),
+    "fa_fwd_strided": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
+                            _F, _I, _I, _I, _I, _P]),
     "fa_plan_splits": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "fa_schedule_table": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),

@@ -30,7 +30,8 @@ using SchedKey = std::array<int, 12>;
 struct DeviceState {
   bool init = false;
   int num_cus = 0;
-  int f32_bpc[3] = {-1, -1, -1};   // fp32 workgroups per CU for D = 64, 128, 256
+  int f32_bpc[2][3] = {{-1, -1, -1}, {-1, -1, -1}};   // fp32 workgroups per CU
+                                                      // [contiguous, strided][D = 64, 128, 256]
   hipMemPool_t pool = nullptr;
   std::map<SchedKey, Sched> scheds;
 };
@@ -143,14 +144,15 @@ int item_tiles(int q0, int BM, int BN, int split, int split_len, int Sq, int Sk,
 // Slots of a persistent launch for this problem, or 0 when it runs one
 // workgroup per item.
 int persistent_slots(DeviceState& s, int B, int H, int Sq, int D, int causal, int window,
-                     int dtype) {
+                     int dtype, int strided) {
   if (dtype != FA_F32 || (!causal && window <= 0)) return 0;
   const int BM = fa::block_m(dtype, D);
   const long qtiles = (long)B * H * ((Sq + BM - 1) / BM);
   if (qtiles >= 2L * s.num_cus) return 0;
   const int di = D == 64 ? 0 : D == 128 ? 1 : 2;
-  if (s.f32_bpc[di] < 0) s.f32_bpc[di] = fa::f32_blocks_per_cu(D);
-  return s.f32_bpc[di] > 0 ? s.f32_bpc[di] * s.num_cus : 0;
+  int& bpc = s.f32_bpc[strided ? 1 : 0][di];
+  if (bpc < 0) bpc = fa::f32_blocks_per_cu(D, strided);
+  return bpc > 0 ? bpc * s.num_cus : 0;
 }
 
 // Key splits for a persistent launch: the longest query tile cut into pieces
@@ -269,10 +271,10 @@ void resolve_splits(int requested, int B, int H, int Sq, int Sk, int D, int caus
 
 // Splits, keys per split and persistent slots (0 = none) for one call.
 void plan(DeviceState& s, int requested, int B, int H, int Sq, int Sk, int D, int causal,
-          int window, int dtype, int* ns, int* split_len, int* nslot) {
+          int window, int dtype, int strided, int* ns, int* split_len, int* nslot) {
   {
     std::lock_guard<std::mutex> lk(g_mu);
-    *nslot = persistent_slots(s, B, H, Sq, D, causal, window, dtype);
+    *nslot = persistent_slots(s, B, H, Sq, D, causal, window, dtype, strided);
   }
   if (*nslot > 0 && requested == 0)
     requested = persistent_splits(B, H, Sq, Sk, D, causal, window, dtype, *nslot);
@@ -301,15 +303,63 @@ int schedule_for(DeviceState& s, int B, int H, int HKV, int Sq, int Sk, int D, i
   return FA_OK;
 }
 
+// Element strides (batch, head, row) of one tensor: the caller's, or those of a
+// contiguous [B, heads, S, D] tensor when `given` is NULL.
+void tensor_strides(const long long* given, int heads, int S, int D, long long out[3]) {
+  if (given) {
+    out[0] = given[0];
+    out[1] = given[1];
+    out[2] = given[2];
+  } else {
+    out[2] = D;
+    out[1] = (long long)S * D;
+    out[0] = (long long)heads * S * D;
+  }
+}
+
+// Stride rules: non-negative; every row start 16-byte aligned; rows of one
+// head do not overlap (row stride >= D); for K and V the row stride is a
+// multiple of D (the 16-bit kernel's swizzled LDS copies need it) and a key
+// tile spans less than 2^31 bytes; every element offset fits far inside int64.
+int check_strides(const long long st[3], int B, int heads, int S, int D, int esz, bool kv) {
+  for (int a = 0; a < 3; ++a)
+    if (st[a] < 0 || (st[a] * esz) % 16 != 0) return FA_ERR_STRIDE;
+  if (st[2] < D) return FA_ERR_STRIDE;
+  if (kv && (st[2] % D != 0 || (double)st[2] * esz * 64 >= 2147483647.0)) return FA_ERR_STRIDE;
+  const double last = (double)(B - 1) * st[0] + (double)(heads - 1) * st[1] +
+                      (double)(S - 1) * st[2] + D;
+  if (last * esz > 4.0e18) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
 int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
-            int HKV, int Sq, int Sk, int D, float scale, int causal, int window, int dtype,
-            int num_splits, void* stream_ptr) {
+            int HKV, int Sq, int Sk, int D, const long long* q_strides,
+            const long long* k_strides, const long long* v_strides, const long long* o_strides,
+            float scale, int causal, int window, int dtype, int num_splits, void* stream_ptr) {
   if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULLPTR;
   int st = check_args(B, H, HKV, Sq, Sk, D, causal, window, dtype);
   if (st != FA_OK) return st;
   if (num_splits < 0 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
     return FA_ERR_ALIGN;
+  const int esz = dtype == FA_F32 ? 4 : 2;
+  long long qs[3], ks[3], vs[3], os[3];
+  tensor_strides(q_strides, H, Sq, D, qs);
+  tensor_strides(k_strides, HKV, Sk, D, ks);
+  tensor_strides(v_strides, HKV, Sk, D, vs);
+  tensor_strides(o_strides, H, Sq, D, os);
+  if ((st = check_strides(qs, B, H, Sq, D, esz, false)) != FA_OK ||
+      (st = check_strides(ks, B, HKV, Sk, D, esz, true)) != FA_OK ||
+      (st = check_strides(vs, B, HKV, Sk, D, esz, true)) != FA_OK ||
+      (st = check_strides(os, B, H, Sq, D, esz, false)) != FA_OK)
+    return st;
+  // The kernels' contiguous form whenever the strides are those of contiguous tensors.
+  long long cq[3], ck[3];
+  tensor_strides(nullptr, H, Sq, D, cq);
+  tensor_strides(nullptr, HKV, Sk, D, ck);
+  const bool same_q = std::equal(qs, qs + 3, cq) && std::equal(os, os + 3, cq);
+  const bool same_kv = std::equal(ks, ks + 3, ck) && std::equal(vs, vs + 3, ck);
+  const int strided = (same_q && same_kv) ? 0 : 1;
 
   DeviceState* ds = nullptr;
   st = device_state(&ds);
@@ -317,7 +367,8 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
 
   const int BM = fa::block_m(dtype, D);
   int ns = 1, split_len = 0, nslot = 0;
-  plan(*ds, num_splits, B, H, Sq, Sk, D, causal, window, dtype, &ns, &split_len, &nslot);
+  plan(*ds, num_splits, B, H, Sq, Sk, D, causal, window, dtype, strided, &ns, &split_len,
+       &nslot);
 
   fa::Params p = {};
   p.Q = Q;
@@ -350,6 +401,10 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   if (blocks < 1 || blocks > 2147483647L) return FA_ERR_SHAPE;
   p.units = (int)units;
   p.xcd_remap = (p.units % 8 == 0) ? 1 : 0;
+  std::copy(qs, qs + 3, p.qs);
+  std::copy(ks, ks + 3, p.ks);
+  std::copy(vs, vs + 3, p.vs);
+  std::copy(os, os + 3, p.os);
   if (nslot > 0) {
     st = schedule_for(*ds, B, H, HKV, Sq, Sk, D, causal, window, dtype, ns, split_len, nslot,
                       &p.sched);
@@ -373,7 +428,7 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
     p.Opart = static_cast<float*>(ws);
     p.Lpart = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
   }
-  const hipError_t e = fa::launch_forward(p, dtype, D, stream);
+  const hipError_t e = fa::launch_forward(p, dtype, D, strided, stream);
   const hipError_t f = ws ? hipFreeAsync(ws, stream) : hipSuccess;
   return (e == hipSuccess && f == hipSuccess) ? FA_OK : FA_ERR_HIP;
 }
@@ -385,14 +440,24 @@ extern "C" {
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
            int HKV, int Sq, int Sk, int D, float scale, int causal, int window, int dtype,
            void* stream) {
-  return forward(Q, K, V, O, LSE, B, H, HKV, Sq, Sk, D, scale, causal, window, dtype, 0, stream);
+  return forward(Q, K, V, O, LSE, B, H, HKV, Sq, Sk, D, nullptr, nullptr, nullptr, nullptr, scale,
+                 causal, window, dtype, 0, stream);
 }
 
 int fa_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
               int HKV, int Sq, int Sk, int D, float scale, int causal, int window, int dtype,
               int num_splits, void* stream) {
-  return forward(Q, K, V, O, LSE, B, H, HKV, Sq, Sk, D, scale, causal, window, dtype,
-                 num_splits, stream);
+  return forward(Q, K, V, O, LSE, B, H, HKV, Sq, Sk, D, nullptr, nullptr, nullptr, nullptr, scale,
+                 causal, window, dtype, num_splits, stream);
+}
+
+int fa_fwd_strided(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                   int H, int HKV, int Sq, int Sk, int D, const long long* q_strides,
+                   const long long* k_strides, const long long* v_strides,
+                   const long long* o_strides, float scale, int causal, int window, int dtype,
+                   int num_splits, void* stream) {
+  return forward(Q, K, V, O, LSE, B, H, HKV, Sq, Sk, D, q_strides, k_strides, v_strides,
+                 o_strides, scale, causal, window, dtype, num_splits, stream);
 }
 
 int fa_plan_splits(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int window,
@@ -403,7 +468,7 @@ int fa_plan_splits(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int
   st = device_state(&ds);
   if (st != FA_OK) return -st;
   int ns = 1, split_len = 0, nslot = 0;
-  plan(*ds, 0, B, H, Sq, Sk, D, causal, window, dtype, &ns, &split_len, &nslot);
+  plan(*ds, 0, B, H, Sq, Sk, D, causal, window, dtype, 0, &ns, &split_len, &nslot);
   return ns;
 }
 
@@ -438,6 +503,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_HIP: return "HIP runtime error";
     case FA_ERR_WORKSPACE: return "could not allocate the split-K workspace";
     case FA_ERR_SPLITS: return "num_splits must be in [0, FA_MAX_SPLITS]";
+    case FA_ERR_STRIDE: return "invalid strides: negative, not 16-byte multiples, rows overlapping, or a K/V row stride that is not a multiple of D";
     default: return "unknown status";
   }
 }

@@ -217,14 +217,22 @@ struct Bf16Tile {
   static constexpr int swz_v(int key) { return CPR >= 16 ? 4 * (key & 3) : 4 * ((key >> 1) & 1); }
   // Tile byte offset that LDS chunk P of a copy reads: logical chunk
   // (P % CPR) ^ swz(row) of row P / CPR.
-  static constexpr int dma_off(int P, bool v) {
-    return (P / CPR) * ROW + (((P % CPR) ^ (v ? swz_v(P / CPR) : swz_k(P / CPR))) << 4);
+  static constexpr int chunk_off(int P, bool v) {
+    return ((P % CPR) ^ (v ? swz_v(P / CPR) : swz_k(P / CPR))) << 4;
   }
+  static constexpr int dma_off(int P, bool v) { return (P / CPR) * ROW + chunk_off(P, v); }
   // The offsets of copy instruction k (chunks 64k.. of a wavefront's share)
   // differ from those of instruction 0 by the same XOR in every lane: the row
   // step and the swizzle touch disjoint bits. One register per buffer then
   // holds a lane's offsets.
   static constexpr int dma_xor(int k, bool v) { return dma_off(64 * k, v) ^ dma_off(0, v); }
+  // Strided rows (a row stride R that is a multiple of ROW): the row part of
+  // an offset, row * R, no longer fits the XOR. It is additive instead
+  // (instruction k adds k * RPI * R, uniform) and stays in the vector offset,
+  // which the buffer range check covers; the chunk part keeps its
+  // per-instruction XOR.
+  static constexpr int RPI = 64 / CPR;                   // rows per copy instruction
+  static constexpr int chunk_xor(int k, bool v) { return dma_xor(k, v) & (ROW - 1); }
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -261,8 +269,9 @@ __device__ __forceinline__ float half_max(float x) {
 constexpr float kRowSumLimit = 1.8446744e19f;   // 2^64: row-sum bound that triggers a rescale
 
 // E = __bf16 or _Float16 (inputs, O and the rounded P); fp32 accumulation,
-// softmax and LSE either way.
-template <typename E, int D, int BN>
+// softmax and LSE either way. Strided: Q, K, V and O are addressed through
+// p.qs .. p.os (batch, head, row strides); otherwise they are contiguous.
+template <typename E, int D, int BN, bool Strided>
 __global__ __launch_bounds__(kThreads, (D == 128 ? 3 : 2))
 void fwd_16b_kernel(Params p) {
   using T = Bf16Tile<D, BN>;
@@ -284,9 +293,23 @@ void fwd_16b_kernel(Params p) {
   const int qw = q0 + wave * 32;
   const int i = qw + l32;
 
-  const E* Qp = (const E*)p.Q + (size_t)(w.b * p.H + w.h) * p.Sq * D;
-  const E* Kp = (const E*)p.K + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
-  const E* Vp = (const E*)p.V + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
+  const E* Qp;
+  const E* Kp;
+  const E* Vp;
+  long long qr = D;   // element row strides
+  int krb = T::ROW, vrb = T::ROW;   // K / V row strides in bytes (strided: multiples of ROW)
+  if constexpr (Strided) {
+    Qp = (const E*)p.Q + w.b * p.qs[0] + w.h * p.qs[1];
+    Kp = (const E*)p.K + w.b * p.ks[0] + w.hkv * p.ks[1];
+    Vp = (const E*)p.V + w.b * p.vs[0] + w.hkv * p.vs[1];
+    qr = p.qs[2];
+    krb = (int)(p.ks[2] * 2);
+    vrb = (int)(p.vs[2] * 2);
+  } else {
+    Qp = (const E*)p.Q + (size_t)(w.b * p.H + w.h) * p.Sq * D;
+    Kp = (const E*)p.K + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
+    Vp = (const E*)p.V + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
+  }
 
   int lo, hi;
   key_range(p, q0, kBlockM, w.split, lo, hi);
@@ -295,18 +318,35 @@ void fwd_16b_kernel(Params p) {
 
   // DMA: LDS chunk P = 64 (wave NIW + k) + lane of a tile holds logical chunk
   // (P % CPR) ^ swz(row) of row P / CPR.
-  const int voff_k = T::dma_off(64 * wave * T::NIW + lane, false);
-  const int voff_v = T::dma_off(64 * wave * T::NIW + lane, true);
+  const int P0 = 64 * wave * T::NIW + lane;
+  const int voff_k = Strided ? (P0 / T::CPR) * krb + T::chunk_off(P0, false) : T::dma_off(P0, false);
+  const int voff_v = Strided ? (P0 / T::CPR) * vrb + T::chunk_off(P0, true) : T::dma_off(P0, true);
   auto issue = [&](int kt, char* kdst, char* vdst, bool full = false) {
-    // a full tile needs no bound: BN rows are in range
-    const unsigned bytes = full ? (unsigned)(BN * T::ROW) : (unsigned)min((long)(p.Sk - kt) * T::ROW, 0x7fffffffL);
-    const E* kb = Kp + (size_t)kt * D;
-    const E* vb = Vp + (size_t)kt * D;
+    if constexpr (Strided) {
+      // valid bytes from the tile's first row: up to the end of row Sk - 1
+      const unsigned kbytes = full ? (unsigned)((BN - 1) * krb + T::ROW)
+                                   : (unsigned)min((long long)(p.Sk - kt - 1) * krb + T::ROW, 0x7fffffffLL);
+      const unsigned vbytes = full ? (unsigned)((BN - 1) * vrb + T::ROW)
+                                   : (unsigned)min((long long)(p.Sk - kt - 1) * vrb + T::ROW, 0x7fffffffLL);
+      const E* kb = Kp + (long long)kt * p.ks[2];
+      const E* vb = Vp + (long long)kt * p.vs[2];
 #pragma unroll
-    for (int k = 0; k < T::NIW; ++k) {
-      const int off = (wave * T::NIW + k) * 1024;
-      dma16(kb, bytes, voff_k ^ T::dma_xor(k, false), kdst + off);
-      dma16(vb, bytes, voff_v ^ T::dma_xor(k, true), vdst + off);
+      for (int k = 0; k < T::NIW; ++k) {
+        const int off = (wave * T::NIW + k) * 1024;
+        dma16(kb, kbytes, (voff_k ^ T::chunk_xor(k, false)) + k * T::RPI * krb, kdst + off);
+        dma16(vb, vbytes, (voff_v ^ T::chunk_xor(k, true)) + k * T::RPI * vrb, vdst + off);
+      }
+    } else {
+      // a full tile needs no bound: BN rows are in range
+      const unsigned bytes = full ? (unsigned)(BN * T::ROW) : (unsigned)min((long)(p.Sk - kt) * T::ROW, 0x7fffffffL);
+      const E* kb = Kp + (size_t)kt * D;
+      const E* vb = Vp + (size_t)kt * D;
+#pragma unroll
+      for (int k = 0; k < T::NIW; ++k) {
+        const int off = (wave * T::NIW + k) * 1024;
+        dma16(kb, bytes, voff_k ^ T::dma_xor(k, false), kdst + off);
+        dma16(vb, bytes, voff_v ^ T::dma_xor(k, true), vdst + off);
+      }
     }
   };
 
@@ -319,7 +359,7 @@ void fwd_16b_kernel(Params p) {
 #pragma unroll
   for (int t = 0; t < T::DC; ++t) {
     if (i < p.Sq)
-      qf[t] = *(const e16x8*)(Qp + (size_t)i * D + 16 * t + 8 * g);
+      qf[t] = *(const e16x8*)(Qp + (long long)i * qr + 16 * t + 8 * g);
     else
       qf[t] = e16x8{};
     if (p.neg_q) {   // negative scale: use -Q and |scale| (exact sign flips)
@@ -569,7 +609,8 @@ void fwd_16b_kernel(Params p) {
                      *(f32x4*)(dst + 32 * db + 8 * a + 4 * g) = v4;
                    }
                } else {
-                 E* dst = (E*)p.O + row * D;
+                 E* dst = Strided ? (E*)p.O + w.b * p.os[0] + w.h * p.os[1] + (long long)i * p.os[2]
+                                  : (E*)p.O + row * D;
 #pragma unroll
                  for (int db = 0; db < T::DB; ++db)
 #pragma unroll
@@ -602,7 +643,7 @@ struct F32Tile {
   static_assert(BN * C4 % kThreads == 0, "tile must split evenly over the workgroup");
 };
 
-template <int D>
+template <int D, bool Strided>
 __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1))
 void fwd_f32_kernel(Params p) {
   using T = F32Tile<D>;
@@ -619,9 +660,22 @@ void fwd_f32_kernel(Params p) {
   const int qw = q0 + wave * 32;
   const int i = qw + l32;
 
-  const float* Qp = (const float*)p.Q + (size_t)(w.b * p.H + w.h) * p.Sq * D;
-  const float* Kp = (const float*)p.K + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
-  const float* Vp = (const float*)p.V + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
+  const float* Qp;
+  const float* Kp;
+  const float* Vp;
+  long long qr = D, kr = D, vr = D;   // element row strides
+  if constexpr (Strided) {
+    Qp = (const float*)p.Q + w.b * p.qs[0] + w.h * p.qs[1];
+    Kp = (const float*)p.K + w.b * p.ks[0] + w.hkv * p.ks[1];
+    Vp = (const float*)p.V + w.b * p.vs[0] + w.hkv * p.vs[1];
+    qr = p.qs[2];
+    kr = p.ks[2];
+    vr = p.vs[2];
+  } else {
+    Qp = (const float*)p.Q + (size_t)(w.b * p.H + w.h) * p.Sq * D;
+    Kp = (const float*)p.K + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
+    Vp = (const float*)p.V + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
+  }
 
   int lo, hi;
   key_range(p, q0, kBlockM, w.split, lo, hi);
@@ -631,7 +685,7 @@ void fwd_f32_kernel(Params p) {
   float qf[T::DH];
 #pragma unroll
   for (int t4 = 0; t4 < T::DH / 4; ++t4) {
-    f32x4 v = i < p.Sq ? *(const f32x4*)(Qp + (size_t)i * D + T::DH * g + 4 * t4) : f32x4{};
+    f32x4 v = i < p.Sq ? *(const f32x4*)(Qp + (long long)i * qr + T::DH * g + 4 * t4) : f32x4{};
     qf[4 * t4 + 0] = v[0];
     qf[4 * t4 + 1] = v[1];
     qf[4 * t4 + 2] = v[2];
@@ -651,8 +705,8 @@ void fwd_f32_kernel(Params p) {
       const int row = c / T::C4, c4 = c % T::C4;
       const int key = kt + row;
       const bool ok = key < p.Sk;
-      kreg[it] = ok ? *(const f32x4*)(Kp + (size_t)key * D + 4 * c4) : f32x4{};
-      vreg[it] = ok ? *(const f32x4*)(Vp + (size_t)key * D + 4 * c4) : f32x4{};
+      kreg[it] = ok ? *(const f32x4*)(Kp + (long long)key * kr + 4 * c4) : f32x4{};
+      vreg[it] = ok ? *(const f32x4*)(Vp + (long long)key * vr + 4 * c4) : f32x4{};
     }
   };
   auto store_tile = [&](float* st) __attribute__((always_inline)) {
@@ -764,6 +818,8 @@ void fwd_f32_kernel(Params p) {
                if (partial) {
                  const size_t rows = (size_t)p.B * p.H * p.Sq;
                  dst = p.Opart + ((size_t)split * rows + row) * D;
+               } else if constexpr (Strided) {
+                 dst = (float*)p.O + w.b * p.os[0] + w.h * p.os[1] + (long long)i * p.os[2];
                } else {
                  dst = (float*)p.O + row * D;
                }
@@ -792,11 +848,13 @@ void fwd_f32_kernel(Params p) {
 // O = sum_s exp(LSE_s - LSE) O_s and LSE = log sum_s exp(LSE_s): the block
 // form of the online-softmax rescale. A split that saw no key has
 // LSE_s = -inf and weight 0; a row with no key in any split gets O = 0 and
-// LSE = -inf.
-template <typename OutT, int D>
+// LSE = -inf. Strided: O row (b, h, i) of the flat row index (b H + h) Sq + i
+// sits at O + b os[0] + h os[1] + i os[2].
+template <typename OutT, int D, bool Strided>
 __global__ __launch_bounds__(kThreads)
 void merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpart,
-                  OutT* __restrict__ O, float* __restrict__ LSE, long rows, int nsplit) {
+                  OutT* __restrict__ O, float* __restrict__ LSE, long rows, int nsplit,
+                  int H, int Sq, long long os0, long long os1, long long os2) {
   constexpr int TPR = D / 4;               // threads per row, 4 dims each
   constexpr int RPB = kThreads / TPR;
   const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
@@ -817,7 +875,13 @@ void merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpa
     }
     acc *= 1.f / den;
   }
-  OutT* dst = O + (size_t)row * D + 4 * c;
+  OutT* dst;
+  if constexpr (Strided) {
+    const long bh = row / Sq;
+    dst = O + (bh / H) * os0 + (bh % H) * os1 + (row % Sq) * os2 + 4 * c;
+  } else {
+    dst = O + (size_t)row * D + 4 * c;
+  }
   if constexpr (sizeof(OutT) == 2) {
     typedef typename Elt<OutT>::x4 o4;
     *(o4*)dst = o4{(OutT)acc[0], (OutT)acc[1], (OutT)acc[2], (OutT)acc[3]};
@@ -835,50 +899,63 @@ int key_tile(int dtype, int D) {
 
 int block_m(int dtype, int D) { return kBlockM; }
 
-int f32_blocks_per_cu(int D) {
+template <int D>
+static int f32_occupancy(bool strided) {
   int n = 0;
-  hipError_t e = hipErrorInvalidValue;
-  if (D == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<64>, kThreads, 0);
-  if (D == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<128>, kThreads, 0);
-  if (D == 256) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<256>, kThreads, 0);
+  const hipError_t e =
+      strided ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<D, true>, kThreads, 0)
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<D, false>, kThreads, 0);
   return e == hipSuccess ? n : 0;
 }
 
-template <typename OutT, int D>
+int f32_blocks_per_cu(int D, int strided) {
+  if (D == 64) return f32_occupancy<64>(strided != 0);
+  if (D == 128) return f32_occupancy<128>(strided != 0);
+  if (D == 256) return f32_occupancy<256>(strided != 0);
+  return 0;
+}
+
+template <typename OutT, int D, bool Strided>
 static hipError_t launch_merge(const Params& p, hipStream_t stream) {
   const long rows = (long)p.B * p.H * p.Sq;
   constexpr int RPB = kThreads / (D / 4);
   const long blocks = (rows + RPB - 1) / RPB;
-  hipLaunchKernelGGL((merge_kernel<OutT, D>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                     p.Opart, p.Lpart, (OutT*)p.O, p.LSE, rows, p.nsplit);
+  hipLaunchKernelGGL((merge_kernel<OutT, D, Strided>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                     stream, p.Opart, p.Lpart, (OutT*)p.O, p.LSE, rows, p.nsplit, p.H, p.Sq,
+                     p.os[0], p.os[1], p.os[2]);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool Strided>
 static hipError_t launch_d(const Params& p, int dtype, hipStream_t stream) {
   const long blocks = (long)p.units * p.n_qblk;
   constexpr int BN = D >= 128 ? 32 : 64;
   // (the 16-bit kernel has no persistent form; sched is ignored)
   if (dtype == 1) {
-    hipLaunchKernelGGL((fwd_16b_kernel<__bf16, D, BN>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_16b_kernel<__bf16, D, BN, Strided>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   } else if (dtype == 2) {
-    hipLaunchKernelGGL((fwd_16b_kernel<_Float16, D, BN>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_16b_kernel<_Float16, D, BN, Strided>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   } else {
     const long grid = p.sched ? (long)p.nslot : blocks;
-    hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, Strided>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  if (dtype == 1) return launch_merge<__bf16, D>(p, stream);
-  if (dtype == 2) return launch_merge<_Float16, D>(p, stream);
-  return launch_merge<float, D>(p, stream);
+  if (dtype == 1) return launch_merge<__bf16, D, Strided>(p, stream);
+  if (dtype == 2) return launch_merge<_Float16, D, Strided>(p, stream);
+  return launch_merge<float, D, Strided>(p, stream);
 }
 
-hipError_t launch_forward(const Params& p, int dtype, int D, hipStream_t stream) {
+template <int D>
+static hipError_t launch_layout(const Params& p, int dtype, int strided, hipStream_t stream) {
+  return strided ? launch_d<D, true>(p, dtype, stream) : launch_d<D, false>(p, dtype, stream);
+}
+
+hipError_t launch_forward(const Params& p, int dtype, int D, int strided, hipStream_t stream) {
   switch (D) {
-    case 64: return launch_d<64>(p, dtype, stream);
-    case 128: return launch_d<128>(p, dtype, stream);
-    case 256: return launch_d<256>(p, dtype, stream);
+    case 64: return launch_layout<64>(p, dtype, strided, stream);
+    case 128: return launch_layout<128>(p, dtype, strided, stream);
+    case 256: return launch_layout<256>(p, dtype, strided, stream);
     default: return hipErrorInvalidValue;
   }
 }

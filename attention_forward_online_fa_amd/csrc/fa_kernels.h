@@ -32,16 +32,23 @@ struct Params {
   // qblk * units + unit. Null: one workgroup per item in the default order.
   const int* sched;
   int nslot;
+  // Element strides (batch, head, row) of Q, K, V and O; the head dimension
+  // is contiguous. Contiguous [B, heads, S, D] tensors have (heads S D, S D, D);
+  // the kernels read them only in their strided form (Strided = true), where
+  // the row strides of K and V are multiples of D.
+  long long qs[3], ks[3], vs[3], os[3];
 };
 
 // Tile shape per (dtype, D): query rows per workgroup and keys per K/V tile.
 constexpr int kBlockM = 128;
 int key_tile(int dtype, int D);
 int block_m(int dtype, int D);
-// Workgroups of the fp32 kernel that fit on one CU at head dim D (0 on error).
-int f32_blocks_per_cu(int D);
+// Workgroups of the fp32 kernel (contiguous or strided form) that fit on one
+// CU at head dim D (0 on error).
+int f32_blocks_per_cu(int D, int strided);
 
 // Queue the forward kernel (and the merge kernel when p.nsplit > 1).
-hipError_t launch_forward(const Params& p, int dtype, int D, hipStream_t stream);
+// strided = 0: every tensor is contiguous and p.qs .. p.os are not read.
+hipError_t launch_forward(const Params& p, int dtype, int D, int strided, hipStream_t stream);
 
 }  // namespace fa

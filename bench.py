@@ -77,11 +77,7 @@ def measured_traffic(wl: W.Workload):
 
 
 def device_inputs(inp, torch):
-    if inp.wl.dtype in ("bf16", "f16"):
-        tdt = torch.bfloat16 if inp.wl.dtype == "bf16" else torch.float16
-        conv = lambda b: torch.from_numpy(b.view(np.int16)).view(tdt).cuda()
-        return conv(inp.q_bits), conv(inp.k_bits), conv(inp.v_bits)
-    return tuple(torch.from_numpy(a).cuda() for a in (inp.q, inp.k, inp.v))
+    return W.device_tensors(inp, torch, "cuda")
 
 
 def cpu_baseline(wl: W.Workload, inp, target_rows: int):
@@ -148,7 +144,7 @@ def main():
     wl = W.CONFIGS[args.config]
     inp = W.make_inputs(wl)
     q, k, v = device_inputs(inp, torch)
-    o = torch.empty_like(q)
+    o = torch.empty_like(q)          # q's layout (token-major workloads: token-major o)
     lse = torch.empty((wl.B, wl.H, wl.Sq), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream()
     scale = wl.scale()
@@ -200,6 +196,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "HKV": wl.HKV, "Sq": wl.Sq,
                    "Sk": wl.Sk, "D": wl.D, "causal": wl.causal, "window": wl.window,
+                   "layout": wl.layout,
                    "num_splits": splits, "counted_flops": flops,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,

@@ -53,7 +53,8 @@ enum fa_status {
   FA_ERR_ALIGN = 7,     /* a buffer is not 16-byte aligned                     */
   FA_ERR_HIP = 8,       /* the HIP runtime reported an error                   */
   FA_ERR_WORKSPACE = 9, /* split-K workspace could not be allocated            */
-  FA_ERR_SPLITS = 10    /* num_splits < 0 or above FA_MAX_SPLITS               */
+  FA_ERR_SPLITS = 10,   /* num_splits < 0 or above FA_MAX_SPLITS               */
+  FA_ERR_STRIDE = 11    /* fa_fwd_strided: a stride breaks the stride rules    */
 };
 
 #define FA_MAX_SPLITS 64
@@ -102,6 +103,35 @@ int fa_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE,
               int B, int H, int HKV, int Sq, int Sk, int D,
               float scale, int causal, int window, int dtype,
               int num_splits, void* stream);
+
+/*
+ * fa_fwd_strided - fa_fwd_ex on tensors with arbitrary batch, head and row
+ * strides, e.g. the token-major [B, S, heads, D] layout of the forge
+ * flash_attention.metal kernels (row stride heads * D, head stride D), or
+ * views into packed QKV / KV buffers.
+ *
+ *   q_strides, k_strides, v_strides, o_strides
+ *          host pointers to 3 element strides each: {batch, head, row}; the
+ *          head dimension D is contiguous (stride 1). NULL = the contiguous
+ *          [B, heads, S, D] strides of that tensor. Read during the call only.
+ *   Element (b, h, i, d) of Q lives at Q + b q_strides[0] + h q_strides[1] +
+ *   i q_strides[2] + d, and likewise for K and V (with the kv head) and O.
+ *   LSE stays contiguous [B, H, Sq] float32.
+ *
+ * Stride rules (else FA_ERR_STRIDE): every stride >= 0 and a multiple of 16
+ * bytes; every row stride >= D; the K and V row strides are multiples of D
+ * and below 2^31 / 64 bytes. Batch or head strides of 0 (broadcast inputs)
+ * are allowed for Q, K and V; O's rows must not overlap one another or the
+ * inputs (not checked). When all four tensors have contiguous strides the
+ * call runs exactly as fa_fwd_ex. Same arguments, ownership and other errors
+ * as fa_fwd_ex.
+ */
+int fa_fwd_strided(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                   int B, int H, int HKV, int Sq, int Sk, int D,
+                   const long long* q_strides, const long long* k_strides,
+                   const long long* v_strides, const long long* o_strides,
+                   float scale, int causal, int window, int dtype,
+                   int num_splits, void* stream);
 
 /*
  * fa_plan_splits - the number of key-axis splits fa_fwd would use for this

@@ -122,3 +122,36 @@ def test_python_binding_fails_loudly_on_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):
         fa.fwd(q, q, q)
+
+
+# ---------------------------------------------------------------- strided entry
+def call_strided(qs=None, ks=None, vs=None, os_=None, **over):
+    a = dict(GOOD, **over)
+    arr = lambda t: None if t is None else ctypes.cast((ctypes.c_longlong * 3)(*t), ctypes.c_void_p)
+    return _lib.lib().fa_fwd_strided(A, A, A, A, A, a["B"], a["H"], a["HKV"], a["Sq"], a["Sk"],
+                                     a["D"], arr(qs), arr(ks), arr(vs), arr(os_), a["scale"],
+                                     a["causal"], a["window"], a["dtype"], 0, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(qs=(0, 128, -128)),               # negative
+    dict(ks=(0, 128, 132)),                # K row stride not a multiple of D (and of 16 bytes)
+    dict(vs=(8192, 128, 384 - 8)),         # V row stride not a multiple of D
+    dict(qs=(8192, 128, 64)),              # row stride < D: rows overlap
+    dict(os_=(8192, 3, 512)),              # head stride not a multiple of 16 bytes (bf16)
+    dict(ks=(0, 128, 128 * (1 << 24))),    # key tile would span >= 2^31 bytes
+])
+def test_strided_rule_errors(kw):
+    assert call_strided(**kw) == 11
+
+
+def test_strided_other_errors_come_first():
+    assert call_strided(qs=(0, 128, -128), D=96) == 4
+    assert call_strided(qs=(0, 128, -128), dtype=7) == 5
+    ptr_a = _lib.lib().fa_fwd_strided(None, A, A, A, A, 1, 4, 2, 64, 64, 128, None, None, None,
+                                      None, 0.125, 1, 0, 1, 0, None)
+    assert ptr_a == 1
+
+
+def test_strided_offset_overflow_is_a_shape_error():
+    assert call_strided(ks=(1 << 61, 128, 128 * 4), B=4) == 2

@@ -36,12 +36,7 @@ def _say(msg):
 
 def to_device(inp):
     import attention_forward_online_fa_amd  # noqa: F401  (fails loudly if the library is missing)
-    if inp.wl.dtype in ("bf16", "f16"):
-        tdt = torch.bfloat16 if inp.wl.dtype == "bf16" else torch.float16
-        conv = lambda bits: torch.from_numpy(bits.view(np.int16)).view(tdt).cuda()
-        return conv(inp.q_bits), conv(inp.k_bits), conv(inp.v_bits)
-    return (torch.from_numpy(inp.q).cuda(), torch.from_numpy(inp.k).cuda(),
-            torch.from_numpy(inp.v).cuda())
+    return W.device_tensors(inp, torch, "cuda")
 
 
 def run_gpu(inp, num_splits=0, scale=None):

@@ -77,3 +77,18 @@ def test_f16_workload_inputs_are_rounded():
     a = W.make_inputs(wl)
     np.testing.assert_array_equal(W.f16_bits_to_f32(a.q_bits), a.q)
     np.testing.assert_array_equal(a.k.astype(np.float16).astype(np.float32), a.k)
+
+
+def test_device_tensors_token_major_view():
+    import torch
+    wl = W.small(W.CONFIGS[6], B=2, H=4, HKV=2, Sq=16, Sk=24)
+    assert wl.layout == "bshd"
+    inp = W.make_inputs(wl)
+    q, k, v = W.device_tensors(inp, torch, "cpu")
+    assert q.shape == (2, 4, 16, 128) and k.shape == (2, 2, 24, 128)
+    assert q.stride() == (16 * 4 * 128, 128, 4 * 128, 1)      # storage [B, S, H, D]
+    assert k.stride() == (24 * 2 * 128, 128, 2 * 128, 1)
+    np.testing.assert_array_equal(q.float().numpy(), inp.q)
+    np.testing.assert_array_equal(v.float().numpy(), inp.v)
+    c = W.device_tensors(W.make_inputs(W.small(wl, layout="bhsd")), torch, "cpu")
+    assert c[0].is_contiguous() and torch.equal(c[0], q)

@@ -10,7 +10,8 @@ Workload shapes follow the five synthetic configurations of the benchmark
 (small reference case, fp32 causal MHA, bf16 causal GQA, fp32 sliding-window
 GQA, bf16 long non-square single head), plus the causal GQA shape with fp16
 inputs (mixed precision, the "Support mixed precision" item of the
-metal-flash-attention README's TODO list). Layout is [B, H, S, D] contiguous for
+metal-flash-attention README's TODO list) and with token-major [B, S, H, D]
+storage (the layout of the forge flash_attention.metal kernels). Layout is [B, H, S, D] contiguous for
 Q and O, [B, HKV, S, D] for K and V, as in the boostr ``flash.wgsl`` header
 comment and the rustytorch ``flash_attention_forward.metal`` buffer comments.
 
@@ -52,6 +53,8 @@ class Workload:
     n_random_rows: int = 0      # for "sampled": distinct (b,h,i) drawn uniformly
     edge_rows: int = 0          # for "sampled": first/last rows of every (b,h)
     seed_index: int = 0
+    layout: str = "bhsd"        # device storage: "bhsd" contiguous [B, heads, S, D], or
+                                # "bshd" token-major [B, S, heads, D] (viewed as [B, heads, S, D])
 
     @property
     def group(self) -> int:
@@ -82,6 +85,9 @@ CONFIGS = [
     Workload("gqa_causal_f16_b2h32kv8_s4096_d128", 2, 32, 8, 4096, 4096, 128, "f16", 1, 0,
              amplitude=0.5, check="sampled", n_random_rows=4096, edge_rows=64,
              seed_index=5),
+    Workload("gqa_causal_bf16_bshd_b2h32kv8_s4096_d128", 2, 32, 8, 4096, 4096, 128, "bf16", 1,
+             0, amplitude=0.5, check="sampled", n_random_rows=4096, edge_rows=64,
+             seed_index=6, layout="bshd"),
 ]
 
 # The configuration the throughput metric is quoted on (bf16 causal GQA).
@@ -192,3 +198,26 @@ def check_rows(inp: Inputs) -> np.ndarray | None:
 def small(wl: Workload, **kw) -> Workload:
     """A copy of a workload with some fields replaced (for reduced-size tests)."""
     return replace(wl, **kw)
+
+
+def device_tensors(inp: Inputs, torch, device="cuda"):
+    """(q, k, v) as torch tensors on `device` holding exactly the workload's
+    values, shaped [B, heads, S, D]. "bshd" workloads are stored token-major
+    and handed over as the [B, heads, S, D] view of that storage."""
+    wl = inp.wl
+    if wl.dtype in ROUNDING:
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float16
+        arrs = [inp.q_bits.view(np.int16), inp.k_bits.view(np.int16), inp.v_bits.view(np.int16)]
+    else:
+        tdt = None
+        arrs = [inp.q, inp.k, inp.v]
+    out = []
+    for a in arrs:
+        if wl.layout == "bshd":
+            a = np.ascontiguousarray(a.transpose(0, 2, 1, 3))
+        t = torch.from_numpy(a)
+        if tdt is not None:
+            t = t.view(tdt)
+        t = t.to(device)
+        out.append(t.transpose(1, 2) if wl.layout == "bshd" else t)
+    return tuple(out)
