@@ -15,6 +15,11 @@ Sources (four web pages on fused attention; cited by page and section):
     the dot-then-scale score, the top-left causal test (key index greater
     than query index is skipped), and the per-row log-sum-exp output kept for
     the backward pass.
+  * philipturner/metal-flash-attention README, "Modifications to
+    FlashAttention": block sparsity with programmable block masks held in
+    memory, covering causal and arbitrary sparsity patterns. Here a block
+    mask has one byte per (query block, key block); a key is visible only if
+    its block's byte is nonzero (on top of the causal and window rules).
   * spb/forge ``src/kernels/flash_attention.metal``, header comment and the
     forward kernel ``flash_attn_fwd``: the online-softmax identity whose
     end result is the plain softmax, the GQA head map hkv = h / (H / HKV),
@@ -59,6 +64,30 @@ def visible_mask(i: np.ndarray, Sk: int, causal: bool, window: int) -> np.ndarra
     return vis
 
 
+# Block sizes of the block-mask format (query rows x keys per mask byte).
+MASK_BLOCK_Q = 128
+MASK_BLOCK_K = 64
+
+
+def block_visible(mask_bh: np.ndarray, i: np.ndarray, Sk: int, block_q: int = MASK_BLOCK_Q,
+                  block_k: int = MASK_BLOCK_K) -> np.ndarray:
+    """Boolean [len(i), Sk]: the mask byte of (i // block_q, j // block_k) is
+    nonzero. mask_bh is one (batch, head) slice [n_qblocks, n_kblocks]."""
+    i = np.asarray(i, dtype=np.int64)
+    j = np.arange(Sk, dtype=np.int64)
+    return mask_bh[(i // block_q)[:, None], (j // block_k)[None, :]] != 0
+
+
+def _mask_slice(block_mask, b: int, h: int, hk: int, H: int):
+    """The [n_qblocks, n_kblocks] slice a (b, h) row reads: the mask's batch
+    axis is 1 (shared) or B, its head axis 1 (shared), HKV (per kv head) or
+    H (per query head)."""
+    mb = 0 if block_mask.shape[0] == 1 else b
+    mh = block_mask.shape[1]
+    hh = h if mh == H else (hk if mh > 1 else 0)
+    return block_mask[mb, hh]
+
+
 def _softmax_rows(S: np.ndarray, vis: np.ndarray, Vh: np.ndarray):
     """Masked softmax of score rows S [n, Sk] (fp64) applied to Vh [Sk, D].
 
@@ -83,9 +112,12 @@ def _softmax_rows(S: np.ndarray, vis: np.ndarray, Vh: np.ndarray):
     return O, lse
 
 
-def attention(Q, K, V, scale: float, causal: bool = False, window: int = 0):
+def attention(Q, K, V, scale: float, causal: bool = False, window: int = 0,
+              block_mask=None, block_q: int = MASK_BLOCK_Q, block_k: int = MASK_BLOCK_K):
     """Full forward: returns (O [B,H,Sq,D] fp64, LSE [B,H,Sq] fp64).
 
+    block_mask: None, or [1 or B, 1 or HKV or H, ceil(Sq/block_q),
+    ceil(Sk/block_k)] of which nonzero entries mark visible blocks.
     Materialises the full Sq x Sk score matrix for one (b, h) at a time."""
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -103,12 +135,17 @@ def attention(Q, K, V, scale: float, causal: bool = False, window: int = 0):
         for h in range(H):
             hk = h // g                       # GQA head map
             S = scale * (Q[b, h] @ K[b, hk].T)
-            O[b, h], LSE[b, h] = _softmax_rows(S, vis, V[b, hk])
+            vbh = vis
+            if block_mask is not None:
+                mbh = _mask_slice(block_mask, b, h, hk, H)
+                vbh = vis & block_visible(mbh, rows, Sk, block_q, block_k)
+            O[b, h], LSE[b, h] = _softmax_rows(S, vbh, V[b, hk])
     return O, LSE
 
 
-def attention_rows(Q, K, V, scale: float, causal: bool, window: int, rows):
-    """Forward for selected query rows only.
+def attention_rows(Q, K, V, scale: float, causal: bool, window: int, rows, block_mask=None,
+                   block_q: int = MASK_BLOCK_Q, block_k: int = MASK_BLOCK_K):
+    """Forward for selected query rows only (block_mask as in ``attention``).
 
     rows: int array [n, 3] of (b, h, i). Returns (O [n, D], LSE [n]) in the
     order given. Materialises the score rows [n_bh, Sk] per (b, h)."""
@@ -130,7 +167,11 @@ def attention_rows(Q, K, V, scale: float, causal: bool, window: int, rows):
         Kh = np.asarray(K[b, hk], dtype=np.float64)
         Vh = np.asarray(V[b, hk], dtype=np.float64)
         S = scale * (q @ Kh.T)
-        O[sel], LSE[sel] = _softmax_rows(S, visible_mask(ii, Sk, causal, window), Vh)
+        vis = visible_mask(ii, Sk, causal, window)
+        if block_mask is not None:
+            vis = vis & block_visible(_mask_slice(block_mask, b, h, hk, H), ii, Sk, block_q,
+                                      block_k)
+        O[sel], LSE[sel] = _softmax_rows(S, vis, Vh)
     return O, LSE
 
 
