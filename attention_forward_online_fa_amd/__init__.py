@@ -12,17 +12,21 @@ float32, bfloat16 or float16; o has q's shape and dtype, lse is float32
 lse = -inf. Contiguous tensors go through fa_fwd_ex; any other strides with a
 contiguous last dimension (e.g. token-major [B, S, H, D] storage viewed as
 [B, H, S, D] with ``.transpose(1, 2)``, or slices of packed QKV) through
-fa_fwd_strided, which checks the stride rules of include/fa.h.
+fa_fwd_strided, which checks the stride rules of include/fa.h. A block mask
+(``block_mask=``, uint8 or bool [1 or B, 1 or HKV or H, ceil(Sq/128),
+ceil(Sk/64)] on the device) runs fa_fwd_block_sparse.
 """
 from __future__ import annotations
 
 import ctypes
 import math
 
-from ._lib import FA_BF16, FA_F16, FA_F32, FA_MAX_SPLITS, FaError, lib, library_path
+from ._lib import (FA_BF16, FA_F16, FA_F32, FA_MASK_BLOCK_K, FA_MASK_BLOCK_Q, FA_MAX_SPLITS,
+                   FaError, lib, library_path)
 
 __all__ = ["fwd", "fwd_into", "plan_splits", "schedule_table", "release", "FaError",
-           "library_path", "default_scale", "FA_F32", "FA_BF16", "FA_F16", "FA_MAX_SPLITS"]
+           "library_path", "default_scale", "FA_F32", "FA_BF16", "FA_F16", "FA_MAX_SPLITS",
+           "FA_MASK_BLOCK_Q", "FA_MASK_BLOCK_K"]
 
 
 def _dtype_code(t):
@@ -67,7 +71,21 @@ def _check(q, k, v):
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
 
 
-def fwd_into(q, k, v, o, lse, *, causal=False, window=0, scale=None, num_splits=0, stream=None):
+def _check_mask(block_mask, B, H, HKV, Sq, Sk, q):
+    import torch
+    if not block_mask.is_cuda or block_mask.device != q.device:
+        raise ValueError("block_mask must be on q's device")
+    if block_mask.dtype not in (torch.uint8, torch.bool) or not block_mask.is_contiguous():
+        raise ValueError("block_mask must be a contiguous uint8 or bool tensor")
+    nqb = -(-Sq // FA_MASK_BLOCK_Q)
+    nkb = -(-Sk // FA_MASK_BLOCK_K)
+    if block_mask.dim() != 4 or tuple(block_mask.shape[2:]) != (nqb, nkb):
+        raise ValueError(f"block_mask must be [1 or B, 1 or HKV or H, {nqb}, {nkb}], "
+                         f"got {tuple(block_mask.shape)}")
+
+
+def fwd_into(q, k, v, o, lse, *, causal=False, window=0, scale=None, num_splits=0, stream=None,
+             block_mask=None):
     """Run the forward pass into caller-provided o and lse. Returns (o, lse)."""
     import torch
     _check(q, k, v)
@@ -83,7 +101,17 @@ def fwd_into(q, k, v, o, lse, *, causal=False, window=0, scale=None, num_splits=
         scale = default_scale(D)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    if all(t.is_contiguous() for t in (q, k, v, o)):
+    if block_mask is not None:
+        if not all(t.is_contiguous() for t in (q, k, v, o)):
+            raise ValueError("a block mask needs contiguous q, k, v and o")
+        _check_mask(block_mask, B, H, HKV, Sq, Sk, q)
+        st = lib().fa_fwd_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       lse.data_ptr(), B, H, HKV, Sq, Sk, D,
+                                       block_mask.data_ptr(), block_mask.shape[0],
+                                       block_mask.shape[1], float(scale), int(bool(causal)),
+                                       int(window), _dtype_code(q), int(num_splits),
+                                       stream.cuda_stream)
+    elif all(t.is_contiguous() for t in (q, k, v, o)):
         st = lib().fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                              lse.data_ptr(), B, H, HKV, Sq, Sk, D, float(scale),
                              int(bool(causal)), int(window), _dtype_code(q), int(num_splits),
@@ -100,7 +128,8 @@ def fwd_into(q, k, v, o, lse, *, causal=False, window=0, scale=None, num_splits=
     return o, lse
 
 
-def fwd(q, k, v, *, causal=False, window=0, scale=None, num_splits=0, stream=None):
+def fwd(q, k, v, *, causal=False, window=0, scale=None, num_splits=0, stream=None,
+        block_mask=None):
     """Forward pass; allocates o (with q's memory layout) and lse with torch.
     Returns (o, lse)."""
     import torch
@@ -110,7 +139,7 @@ def fwd(q, k, v, *, causal=False, window=0, scale=None, num_splits=0, stream=Non
         o = torch.empty_like(q)       # keeps q's strides when q is dense
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     return fwd_into(q, k, v, o, lse, causal=causal, window=window, scale=scale,
-                    num_splits=num_splits, stream=stream)
+                    num_splits=num_splits, stream=stream, block_mask=block_mask)
 
 
 def plan_splits(B, H, HKV, Sq, Sk, D, *, causal=False, window=0, dtype="bf16") -> int:

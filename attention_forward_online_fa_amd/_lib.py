@@ -8,6 +8,8 @@ import threading
 from . import build as _build
 
 FA_F32 = 0
+FA_MASK_BLOCK_Q = 128
+FA_MASK_BLOCK_K = 64
 FA_BF16 = 1
 FA_F16 = 2
 FA_MAX_SPLITS = 64
@@ -16,6 +18,7 @@ STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULLPTR", 2: "FA_ERR_SHAPE", 3: "FA_ERR_GQA",
     4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_DTYPE", 6: "FA_ERR_WINDOW", 7: "FA_ERR_ALIGN",
     8: "FA_ERR_HIP", 9: "FA_ERR_WORKSPACE", 10: "FA_ERR_SPLITS", 11: "FA_ERR_STRIDE",
+    12: "FA_ERR_MASK",
 }
 
 # Every symbol include/fa.h declares, with its ctypes signature.
@@ -25,6 +28,8 @@ SIGNATURES = {
     "fa_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P]),
     "fa_fwd_strided": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
                             _F, _I, _I, _I, _I, _P]),
+    "fa_fwd_block_sparse": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _I,
+                                 _F, _I, _I, _I, _I, _P]),
     "fa_plan_splits": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "fa_schedule_table": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),

@@ -30,8 +30,8 @@ using SchedKey = std::array<int, 12>;
 struct DeviceState {
   bool init = false;
   int num_cus = 0;
-  int f32_bpc[2][3] = {{-1, -1, -1}, {-1, -1, -1}};   // fp32 workgroups per CU
-                                                      // [contiguous, strided][D = 64, 128, 256]
+  int f32_bpc[3][3] = {{-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}};   // fp32 workgroups per CU
+                                                                    // [form][D = 64, 128, 256]
   hipMemPool_t pool = nullptr;
   std::map<SchedKey, Sched> scheds;
 };
@@ -144,14 +144,14 @@ int item_tiles(int q0, int BM, int BN, int split, int split_len, int Sq, int Sk,
 // Slots of a persistent launch for this problem, or 0 when it runs one
 // workgroup per item.
 int persistent_slots(DeviceState& s, int B, int H, int Sq, int D, int causal, int window,
-                     int dtype, int strided) {
+                     int dtype, int form) {
   if (dtype != FA_F32 || (!causal && window <= 0)) return 0;
   const int BM = fa::block_m(dtype, D);
   const long qtiles = (long)B * H * ((Sq + BM - 1) / BM);
   if (qtiles >= 2L * s.num_cus) return 0;
   const int di = D == 64 ? 0 : D == 128 ? 1 : 2;
-  int& bpc = s.f32_bpc[strided ? 1 : 0][di];
-  if (bpc < 0) bpc = fa::f32_blocks_per_cu(D, strided);
+  int& bpc = s.f32_bpc[form][di];
+  if (bpc < 0) bpc = fa::f32_blocks_per_cu(D, form);
   return bpc > 0 ? bpc * s.num_cus : 0;
 }
 
@@ -271,14 +271,22 @@ void resolve_splits(int requested, int B, int H, int Sq, int Sk, int D, int caus
 
 // Splits, keys per split and persistent slots (0 = none) for one call.
 void plan(DeviceState& s, int requested, int B, int H, int Sq, int Sk, int D, int causal,
-          int window, int dtype, int strided, int* ns, int* split_len, int* nslot) {
+          int window, int dtype, int form, int* ns, int* split_len, int* nslot) {
   {
     std::lock_guard<std::mutex> lk(g_mu);
-    *nslot = persistent_slots(s, B, H, Sq, D, causal, window, dtype, strided);
+    *nslot = persistent_slots(s, B, H, Sq, D, causal, window, dtype, form);
   }
   if (*nslot > 0 && requested == 0)
     requested = persistent_splits(B, H, Sq, Sk, D, causal, window, dtype, *nslot);
   resolve_splits(requested, B, H, Sq, Sk, D, causal, window, dtype, s.num_cus, ns, split_len);
+  if (form == fa::kFormBlockSparse && *split_len / fa::key_tile(dtype, D) > fa::kMaxListTiles) {
+    // a workgroup's visible-tile list holds at most kMaxListTiles tiles: split
+    // the key axis at least that finely
+    const int sk_tiles = (Sk + fa::key_tile(dtype, D) - 1) / fa::key_tile(dtype, D);
+    const int need = (sk_tiles + fa::kMaxListTiles - 1) / fa::kMaxListTiles;
+    resolve_splits(std::min(std::max(need, *ns), FA_MAX_SPLITS), B, H, Sq, Sk, D, causal, window,
+                   dtype, s.num_cus, ns, split_len);
+  }
 }
 
 // The device copy of a persistent schedule, built and uploaded on first use
@@ -332,13 +340,23 @@ int check_strides(const long long st[3], int B, int heads, int S, int D, int esz
   return FA_OK;
 }
 
+// Block mask of fa_fwd_block_sparse (NULL for the dense entry points).
+struct MaskArg {
+  const unsigned char* mask;
+  int batch, heads;
+};
+
 int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
             int HKV, int Sq, int Sk, int D, const long long* q_strides,
             const long long* k_strides, const long long* v_strides, const long long* o_strides,
-            float scale, int causal, int window, int dtype, int num_splits, void* stream_ptr) {
-  if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULLPTR;
+            float scale, int causal, int window, int dtype, int num_splits, void* stream_ptr,
+            const MaskArg* bm = nullptr) {
+  if (!Q || !K || !V || !O || !LSE || (bm && !bm->mask)) return FA_ERR_NULLPTR;
   int st = check_args(B, H, HKV, Sq, Sk, D, causal, window, dtype);
   if (st != FA_OK) return st;
+  if (bm && ((bm->batch != 1 && bm->batch != B) ||
+             (bm->heads != 1 && bm->heads != HKV && bm->heads != H)))
+    return FA_ERR_MASK;
   if (num_splits < 0 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
     return FA_ERR_ALIGN;
@@ -359,7 +377,8 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   tensor_strides(nullptr, HKV, Sk, D, ck);
   const bool same_q = std::equal(qs, qs + 3, cq) && std::equal(os, os + 3, cq);
   const bool same_kv = std::equal(ks, ks + 3, ck) && std::equal(vs, vs + 3, ck);
-  const int strided = (same_q && same_kv) ? 0 : 1;
+  const int form = bm ? fa::kFormBlockSparse
+                     : (same_q && same_kv) ? fa::kFormContiguous : fa::kFormStrided;
 
   DeviceState* ds = nullptr;
   st = device_state(&ds);
@@ -367,8 +386,9 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
 
   const int BM = fa::block_m(dtype, D);
   int ns = 1, split_len = 0, nslot = 0;
-  plan(*ds, num_splits, B, H, Sq, Sk, D, causal, window, dtype, strided, &ns, &split_len,
-       &nslot);
+  plan(*ds, num_splits, B, H, Sq, Sk, D, causal, window, dtype, form, &ns, &split_len, &nslot);
+  if (split_len / fa::key_tile(dtype, D) > fa::kMaxListTiles && form == fa::kFormBlockSparse)
+    return FA_ERR_SHAPE;   // more key tiles than FA_MAX_SPLITS lists can hold
 
   fa::Params p = {};
   p.Q = Q;
@@ -405,6 +425,14 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   std::copy(ks, ks + 3, p.ks);
   std::copy(vs, vs + 3, p.vs);
   std::copy(os, os + 3, p.os);
+  if (bm) {
+    const long long nqb = p.n_qblk, nkb = (Sk + fa::kMaskBlockK - 1) / fa::kMaskBlockK;
+    p.bmask = bm->mask;
+    p.bm_nkb = (int)nkb;
+    p.bm_sh = bm->heads == 1 ? 0 : nqb * nkb;
+    p.bm_sb = bm->batch == 1 ? 0 : (long long)bm->heads * nqb * nkb;
+    p.bm_by_kv = (bm->heads == HKV && HKV != H) ? 1 : 0;
+  }
   if (nslot > 0) {
     st = schedule_for(*ds, B, H, HKV, Sq, Sk, D, causal, window, dtype, ns, split_len, nslot,
                       &p.sched);
@@ -428,7 +456,7 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
     p.Opart = static_cast<float*>(ws);
     p.Lpart = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
   }
-  const hipError_t e = fa::launch_forward(p, dtype, D, strided, stream);
+  const hipError_t e = fa::launch_forward(p, dtype, D, form, stream);
   const hipError_t f = ws ? hipFreeAsync(ws, stream) : hipSuccess;
   return (e == hipSuccess && f == hipSuccess) ? FA_OK : FA_ERR_HIP;
 }
@@ -458,6 +486,15 @@ int fa_fwd_strided(const void* Q, const void* K, const void* V, void* O, float* 
                    int num_splits, void* stream) {
   return forward(Q, K, V, O, LSE, B, H, HKV, Sq, Sk, D, q_strides, k_strides, v_strides,
                  o_strides, scale, causal, window, dtype, num_splits, stream);
+}
+
+int fa_fwd_block_sparse(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                        int H, int HKV, int Sq, int Sk, int D, const unsigned char* block_mask,
+                        int mask_batch, int mask_heads, float scale, int causal, int window,
+                        int dtype, int num_splits, void* stream) {
+  const MaskArg bm = {block_mask, mask_batch, mask_heads};
+  return forward(Q, K, V, O, LSE, B, H, HKV, Sq, Sk, D, nullptr, nullptr, nullptr, nullptr, scale,
+                 causal, window, dtype, num_splits, stream, &bm);
 }
 
 int fa_plan_splits(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int window,
@@ -503,6 +540,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_HIP: return "HIP runtime error";
     case FA_ERR_WORKSPACE: return "could not allocate the split-K workspace";
     case FA_ERR_SPLITS: return "num_splits must be in [0, FA_MAX_SPLITS]";
+    case FA_ERR_MASK: return "block mask: batch axis must be 1 or B, head axis 1, HKV or H";
     case FA_ERR_STRIDE: return "invalid strides: negative, not 16-byte multiples, rows overlapping, or a K/V row stride that is not a multiple of D";
     default: return "unknown status";
   }

@@ -176,6 +176,35 @@ __device__ __forceinline__ void finish_row(const Params& p, int b, int h, int sp
   }
 }
 
+// ============================================================ block masks
+// Block-sparse form: the key tiles t in [0, n) of a workgroup's range (tile t
+// holds keys t0 + t bn ..) whose mask byte is nonzero, in order, go to
+// list[]; returns how many (uniform). Wave 0 compacts 64 candidate tiles per
+// round with a ballot; the others wait at the barrier. The workgroup then
+// visits only these tiles: their copies and their compute.
+__device__ __forceinline__ int build_tile_list(const unsigned char* mrow, int t0, int n, int bn,
+                                               unsigned short* list, int* count, int wave,
+                                               int lane) {
+  if (wave == 0) {
+    int cnt = 0;
+    for (int base = 0; base < n; base += 64) {
+      const int t = base + lane;
+      const bool vis = t < n && mrow[(t0 + t * bn) / kMaskBlockK] != 0;
+      const unsigned long long bal = __ballot(vis);
+      if (vis) list[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (unsigned short)t;
+      cnt += __popcll(bal);
+    }
+    if (lane == 0) *count = cnt;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*count);
+}
+
+__device__ __forceinline__ const unsigned char* mask_row(const Params& p, int b, int h, int hkv,
+                                                         int qblk) {
+  return p.bmask + b * p.bm_sb + (p.bm_by_kv ? hkv : h) * p.bm_sh + (long long)qblk * p.bm_nkb;
+}
+
 // ================================================= 16-bit inputs (bf16, fp16)
 // S^T tile = K Q^T with v_mfma_f32_32x32x16_bf16 (or _f16): A = 32 keys x 16 dims from
 // LDS, B = 16 dims x 32 query rows from registers. In the accumulator, lane
@@ -269,11 +298,15 @@ __device__ __forceinline__ float half_max(float x) {
 constexpr float kRowSumLimit = 1.8446744e19f;   // 2^64: row-sum bound that triggers a rescale
 
 // E = __bf16 or _Float16 (inputs, O and the rounded P); fp32 accumulation,
-// softmax and LSE either way. Strided: Q, K, V and O are addressed through
-// p.qs .. p.os (batch, head, row strides); otherwise they are contiguous.
-template <typename E, int D, int BN, bool Strided>
+// softmax and LSE either way. Form kFormStrided: Q, K, V and O are addressed
+// through p.qs .. p.os (batch, head, row strides); otherwise they are
+// contiguous. Form kFormBlockSparse: only the key tiles whose block-mask
+// byte is nonzero are copied and computed.
+template <typename E, int D, int BN, int Form>
 __global__ __launch_bounds__(kThreads, (D == 128 ? 3 : 2))
 void fwd_16b_kernel(Params p) {
+  constexpr bool Strided = Form == kFormStrided, Sparse = Form == kFormBlockSparse;
+  static_assert(kMaskBlockK % BN == 0, "a key tile lies inside one mask block");
   using T = Bf16Tile<D, BN>;
   using X = Elt<E>;
   typedef typename X::x8 e16x8;
@@ -314,7 +347,19 @@ void fwd_16b_kernel(Params p) {
   int lo, hi;
   key_range(p, q0, kBlockM, w.split, lo, hi);
   const int t0 = (lo / BN) * BN;
-  const int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
+  int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
+  __shared__ unsigned short tlist[Sparse ? kMaxListTiles : 1];
+  __shared__ int tcount;
+  if constexpr (Sparse)
+    n_tiles = build_tile_list(mask_row(p, w.b, w.h, w.hkv, w.qblk), t0, n_tiles, BN, tlist,
+                              &tcount, wave, lane);
+  // first key of the t-th tile visited
+  auto tile_kt = [&](int t) {
+    if constexpr (Sparse)
+      return t0 + BN * __builtin_amdgcn_readfirstlane((int)tlist[t]);
+    else
+      return t0 + t * BN;
+  };
 
   // DMA: LDS chunk P = 64 (wave NIW + k) + lane of a tile holds logical chunk
   // (P % CPR) ^ swz(row) of row P / CPR.
@@ -352,7 +397,7 @@ void fwd_16b_kernel(Params p) {
 
   // The first K/V copy goes out before the query rows are loaded, so the two
   // latencies overlap.
-  if (n_tiles > 0) issue(t0, kbuf0, vbuf0);
+  if (n_tiles > 0) issue(tile_kt(0), kbuf0, vbuf0);
 
   // Query rows as the B operand: k-slot (g, e) of step t is dim 16t + 8g + e.
   e16x8 qf[T::DC];
@@ -541,9 +586,9 @@ void fwd_16b_kernel(Params p) {
 
   // One tile: K(t), V(t) in (Kc, Vc); the copy of tile t+1 goes to (Kn, Vn).
   auto step = [&](int t, const char* Kc, const char* Vc, char* Kn, char* Vn) __attribute__((always_inline)) {
-    const int kt = t0 + t * BN;
+    const int kt = tile_kt(t);
     wait_dma_and_sync();
-    if (t + 1 < n_tiles) issue(kt + BN, Kn, Vn);
+    if (t + 1 < n_tiles) issue(tile_kt(t + 1), Kn, Vn);
     if (wave_skips(kt)) return;
     qk(Kc);
     mask(kt);
@@ -566,7 +611,7 @@ void fwd_16b_kernel(Params p) {
   // are also fully visible to every row of the block.
   const int full_hi = min(n_tiles, (p.Sk - t0) / BN);
   int u_lo = 0, u_hi = 0;
-  if (q0 + kBlockM <= p.Sq) {
+  if (!Sparse && q0 + kBlockM <= p.Sq) {   // (block-sparse: tiles are not consecutive)
     u_hi = full_hi;
     if (p.causal) u_hi = min(u_hi, max(0, (q0 - t0 + 1) / BN));
     if (p.window > 0) {
@@ -643,9 +688,10 @@ struct F32Tile {
   static_assert(BN * C4 % kThreads == 0, "tile must split evenly over the workgroup");
 };
 
-template <int D, bool Strided>
+template <int D, int Form>
 __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1))
 void fwd_f32_kernel(Params p) {
+  constexpr bool Strided = Form == kFormStrided, Sparse = Form == kFormBlockSparse;
   using T = F32Tile<D>;
   constexpr int BN = T::BN;
   __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE_F];
@@ -680,7 +726,18 @@ void fwd_f32_kernel(Params p) {
   int lo, hi;
   key_range(p, q0, kBlockM, w.split, lo, hi);
   const int t0 = (lo / BN) * BN;
-  const int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
+  int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
+  __shared__ unsigned short tlist[Sparse ? kMaxListTiles : 1];
+  __shared__ int tcount;
+  if constexpr (Sparse)
+    n_tiles = build_tile_list(mask_row(p, w.b, w.h, w.hkv, w.qblk), t0, n_tiles, BN, tlist,
+                              &tcount, wave, lane);
+  auto tile_kt = [&](int t) {
+    if constexpr (Sparse)
+      return t0 + BN * __builtin_amdgcn_readfirstlane((int)tlist[t]);
+    else
+      return t0 + t * BN;
+  };
 
   float qf[T::DH];
 #pragma unroll
@@ -720,16 +777,16 @@ void fwd_f32_kernel(Params p) {
   };
 
   if (n_tiles > 0) {
-    load_tile(t0);
+    load_tile(tile_kt(0));
     store_tile(smem);
   }
   __syncthreads();
 
   for (int it = 0; it < n_tiles; ++it) {
-    const int kt = t0 + it * BN;
+    const int kt = tile_kt(it);
     const float* Ks = smem + (it & 1) * T::STAGE_F;
     const float* Vs = Ks + T::TILE_F;
-    if (it + 1 < n_tiles) load_tile(kt + BN);
+    if (it + 1 < n_tiles) load_tile(tile_kt(it + 1));
 
     const bool skip = qw >= p.Sq || (p.causal && kt > qw + 31) ||
                       (p.window > 0 && kt + BN - 1 < qw - p.window + 1);
@@ -900,18 +957,22 @@ int key_tile(int dtype, int D) {
 int block_m(int dtype, int D) { return kBlockM; }
 
 template <int D>
-static int f32_occupancy(bool strided) {
+static int f32_occupancy(int form) {
   int n = 0;
-  const hipError_t e =
-      strided ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<D, true>, kThreads, 0)
-              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<D, false>, kThreads, 0);
+  hipError_t e = hipErrorInvalidValue;
+  if (form == kFormContiguous)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<D, kFormContiguous>, kThreads, 0);
+  if (form == kFormStrided)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<D, kFormStrided>, kThreads, 0);
+  if (form == kFormBlockSparse)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<D, kFormBlockSparse>, kThreads, 0);
   return e == hipSuccess ? n : 0;
 }
 
-int f32_blocks_per_cu(int D, int strided) {
-  if (D == 64) return f32_occupancy<64>(strided != 0);
-  if (D == 128) return f32_occupancy<128>(strided != 0);
-  if (D == 256) return f32_occupancy<256>(strided != 0);
+int f32_blocks_per_cu(int D, int form) {
+  if (D == 64) return f32_occupancy<64>(form);
+  if (D == 128) return f32_occupancy<128>(form);
+  if (D == 256) return f32_occupancy<256>(form);
   return 0;
 }
 
@@ -926,18 +987,19 @@ static hipError_t launch_merge(const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool Strided>
+template <int D, int Form>
 static hipError_t launch_d(const Params& p, int dtype, hipStream_t stream) {
+  constexpr bool Strided = Form == kFormStrided;
   const long blocks = (long)p.units * p.n_qblk;
   constexpr int BN = D >= 128 ? 32 : 64;
   // (the 16-bit kernel has no persistent form; sched is ignored)
   if (dtype == 1) {
-    hipLaunchKernelGGL((fwd_16b_kernel<__bf16, D, BN, Strided>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_16b_kernel<__bf16, D, BN, Form>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   } else if (dtype == 2) {
-    hipLaunchKernelGGL((fwd_16b_kernel<_Float16, D, BN, Strided>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_16b_kernel<_Float16, D, BN, Form>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   } else {
     const long grid = p.sched ? (long)p.nslot : blocks;
-    hipLaunchKernelGGL((fwd_f32_kernel<D, Strided>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, Form>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
@@ -947,15 +1009,17 @@ static hipError_t launch_d(const Params& p, int dtype, hipStream_t stream) {
 }
 
 template <int D>
-static hipError_t launch_layout(const Params& p, int dtype, int strided, hipStream_t stream) {
-  return strided ? launch_d<D, true>(p, dtype, stream) : launch_d<D, false>(p, dtype, stream);
+static hipError_t launch_form(const Params& p, int dtype, int form, hipStream_t stream) {
+  if (form == kFormStrided) return launch_d<D, kFormStrided>(p, dtype, stream);
+  if (form == kFormBlockSparse) return launch_d<D, kFormBlockSparse>(p, dtype, stream);
+  return launch_d<D, kFormContiguous>(p, dtype, stream);
 }
 
-hipError_t launch_forward(const Params& p, int dtype, int D, int strided, hipStream_t stream) {
+hipError_t launch_forward(const Params& p, int dtype, int D, int form, hipStream_t stream) {
   switch (D) {
-    case 64: return launch_layout<64>(p, dtype, strided, stream);
-    case 128: return launch_layout<128>(p, dtype, strided, stream);
-    case 256: return launch_layout<256>(p, dtype, strided, stream);
+    case 64: return launch_form<64>(p, dtype, form, stream);
+    case 128: return launch_form<128>(p, dtype, form, stream);
+    case 256: return launch_form<256>(p, dtype, form, stream);
     default: return hipErrorInvalidValue;
   }
 }

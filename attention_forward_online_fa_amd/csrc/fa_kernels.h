@@ -37,18 +37,36 @@ struct Params {
   // the kernels read them only in their strided form (Strided = true), where
   // the row strides of K and V are multiples of D.
   long long qs[3], ks[3], vs[3], os[3];
+  // Block mask (kFormBlockSparse): bytes [mask batch][mask heads][n_qblk][bm_nkb];
+  // a nonzero byte makes its kBlockM-row x kMaskBlockK-key block visible.
+  // Row (b, h, qblk) of the mask starts at bmask + b bm_sb + hm bm_sh + qblk bm_nkb
+  // with hm = kv head if bm_by_kv, else query head (strides 0 = shared axis).
+  const unsigned char* bmask;
+  long long bm_sb, bm_sh;
+  int bm_nkb;
+  int bm_by_kv;
 };
+
+// Kernel forms: contiguous tensors, strided tensors (p.qs .. p.os), and
+// contiguous tensors under a block mask.
+constexpr int kFormContiguous = 0;
+constexpr int kFormStrided = 1;
+constexpr int kFormBlockSparse = 2;
+// Keys per block-mask byte, and the most key tiles one workgroup's range may
+// hold under a block mask (its visible-tile list lives in LDS).
+constexpr int kMaskBlockK = 64;
+constexpr int kMaxListTiles = 2048;
 
 // Tile shape per (dtype, D): query rows per workgroup and keys per K/V tile.
 constexpr int kBlockM = 128;
 int key_tile(int dtype, int D);
 int block_m(int dtype, int D);
-// Workgroups of the fp32 kernel (contiguous or strided form) that fit on one
-// CU at head dim D (0 on error).
-int f32_blocks_per_cu(int D, int strided);
+// Workgroups of the fp32 kernel (in the given form) that fit on one CU at
+// head dim D (0 on error).
+int f32_blocks_per_cu(int D, int form);
 
-// Queue the forward kernel (and the merge kernel when p.nsplit > 1).
-// strided = 0: every tensor is contiguous and p.qs .. p.os are not read.
-hipError_t launch_forward(const Params& p, int dtype, int D, int strided, hipStream_t stream);
+// Queue the forward kernel (and the merge kernel when p.nsplit > 1) in the
+// given form (kFormContiguous: p.qs .. p.os and the mask are not read).
+hipError_t launch_forward(const Params& p, int dtype, int D, int form, hipStream_t stream);
 
 }  // namespace fa

@@ -36,16 +36,33 @@ KERNEL_SOURCES = [os.path.join(ROOT, "attention_forward_online_fa_amd", "csrc", 
                   for f in ("fa_fwd.hip", "fa_api.cpp", "fa_kernels.h")]
 
 
-def visible_pairs(wl: W.Workload) -> int:
-    """sum_i |visible(i)| for one (b, h), in closed form per row."""
+def row_counts(wl: W.Workload, i: np.ndarray, mask_bh=None) -> np.ndarray:
+    """|visible(i)| for query rows i of one (b, h): the causal / window key
+    range [lo, hi), intersected with the visible blocks of a block mask."""
+    i = np.asarray(i, dtype=np.int64)
+    hi = np.minimum(i + 1, wl.Sk) if wl.causal else np.full(len(i), wl.Sk, np.int64)
+    lo = np.maximum(i - wl.window + 1, 0) if wl.window > 0 else np.zeros(len(i), np.int64)
+    if mask_bh is None:
+        return np.maximum(hi - lo, 0)
+    c0 = np.arange(mask_bh.shape[1], dtype=np.int64) * W.MASK_BLOCK_K       # block key ranges
+    c1 = np.minimum(c0 + W.MASK_BLOCK_K, wl.Sk)
+    inter = np.maximum(np.minimum(c1[None, :], hi[:, None]) - np.maximum(c0[None, :], lo[:, None]), 0)
+    return (inter * (mask_bh[i // W.MASK_BLOCK_Q] != 0)).sum(axis=1)
+
+
+def counted_flops(wl: W.Workload, block_mask=None) -> float:
+    """4 D flop per visible (query, key) pair over every (b, h)."""
     i = np.arange(wl.Sq, dtype=np.int64)
-    hi = np.minimum(i + 1, wl.Sk) if wl.causal else np.full(wl.Sq, wl.Sk, np.int64)
-    lo = np.maximum(i - wl.window + 1, 0) if wl.window > 0 else np.zeros(wl.Sq, np.int64)
-    return int(np.maximum(hi - lo, 0).sum())
-
-
-def counted_flops(wl: W.Workload) -> float:
-    return 4.0 * wl.B * wl.H * wl.D * visible_pairs(wl)
+    if block_mask is None:
+        return 4.0 * wl.B * wl.H * wl.D * float(row_counts(wl, i).sum())
+    total = 0.0
+    g = wl.H // wl.HKV
+    for b in range(wl.B):
+        for h in range(wl.H):
+            mb = 0 if block_mask.shape[0] == 1 else b
+            mh = h if block_mask.shape[1] == wl.H else (h // g if block_mask.shape[1] > 1 else 0)
+            total += float(row_counts(wl, i, block_mask[mb, mh]).sum())
+    return 4.0 * wl.D * total
 
 
 def algorithmic_bytes(wl: W.Workload) -> int:
@@ -92,12 +109,21 @@ def cpu_baseline(wl: W.Workload, inp, target_rows: int):
     total = wl.B * wl.H * wl.Sq
     flat = np.sort(rng.choice(total, size=min(target_rows, total), replace=False))
     rows = np.stack([flat // (wl.H * wl.Sq), (flat // wl.Sq) % wl.H, flat % wl.Sq], axis=1)
-    i = rows[:, 2]
-    hi = np.minimum(i + 1, wl.Sk) if wl.causal else np.full(len(i), wl.Sk)
-    lo = np.maximum(i - wl.window + 1, 0) if wl.window > 0 else np.zeros(len(i), np.int64)
-    flops = 4.0 * wl.D * float(np.maximum(hi - lo, 0).sum())
+    bm = inp.block_mask
+    if bm is None:
+        flops = 4.0 * wl.D * float(row_counts(wl, rows[:, 2]).sum())
+    else:
+        g = wl.H // wl.HKV
+        flops = 0.0
+        bh = rows[:, 0] * wl.H + rows[:, 1]
+        for key in np.unique(bh):
+            b, h = int(key // wl.H), int(key % wl.H)
+            mb = 0 if bm.shape[0] == 1 else b
+            mh = h if bm.shape[1] == wl.H else (h // g if bm.shape[1] > 1 else 0)
+            flops += 4.0 * wl.D * float(row_counts(wl, rows[bh == key, 2], bm[mb, mh]).sum())
     t0 = time.perf_counter()
-    attention_rows(inp.q, inp.k, inp.v, wl.scale(), bool(wl.causal), wl.window, rows)
+    attention_rows(inp.q, inp.k, inp.v, wl.scale(), bool(wl.causal), wl.window, rows,
+                   block_mask=bm)
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
@@ -144,6 +170,7 @@ def main():
     wl = W.CONFIGS[args.config]
     inp = W.make_inputs(wl)
     q, k, v = device_inputs(inp, torch)
+    bmask = W.device_mask(inp, torch, "cuda")
     o = torch.empty_like(q)          # q's layout (token-major workloads: token-major o)
     lse = torch.empty((wl.B, wl.H, wl.Sq), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream()
@@ -153,7 +180,7 @@ def main():
 
     def step():
         fa.fwd_into(q, k, v, o, lse, causal=bool(wl.causal), window=wl.window, scale=scale,
-                    num_splits=args.num_splits, stream=stream)
+                    num_splits=args.num_splits, stream=stream, block_mask=bmask)
 
     for _ in range(args.warmup):
         step()
@@ -175,7 +202,7 @@ def main():
     ev_ms = ev0.elapsed_time(ev1) / args.steps          # HIP events on the launch stream
     ms_per_step = wall * 1e3 / args.steps
 
-    flops = counted_flops(wl)
+    flops = counted_flops(wl, inp.block_mask)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (ev_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
@@ -196,7 +223,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "HKV": wl.HKV, "Sq": wl.Sq,
                    "Sk": wl.Sk, "D": wl.D, "causal": wl.causal, "window": wl.window,
-                   "layout": wl.layout,
+                   "layout": wl.layout, "block_mask": wl.mask or None,
                    "num_splits": splits, "counted_flops": flops,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,

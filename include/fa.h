@@ -54,7 +54,8 @@ enum fa_status {
   FA_ERR_HIP = 8,       /* the HIP runtime reported an error                   */
   FA_ERR_WORKSPACE = 9, /* split-K workspace could not be allocated            */
   FA_ERR_SPLITS = 10,   /* num_splits < 0 or above FA_MAX_SPLITS               */
-  FA_ERR_STRIDE = 11    /* fa_fwd_strided: a stride breaks the stride rules    */
+  FA_ERR_STRIDE = 11,   /* fa_fwd_strided: a stride breaks the stride rules    */
+  FA_ERR_MASK = 12      /* fa_fwd_block_sparse: mask axes are not 1 / B, 1 / HKV / H */
 };
 
 #define FA_MAX_SPLITS 64
@@ -132,6 +133,38 @@ int fa_fwd_strided(const void* Q, const void* K, const void* V, void* O, float* 
                    const long long* v_strides, const long long* o_strides,
                    float scale, int causal, int window, int dtype,
                    int num_splits, void* stream);
+
+/* Block-mask granularity of fa_fwd_block_sparse: query rows x keys per byte. */
+#define FA_MASK_BLOCK_Q 128
+#define FA_MASK_BLOCK_K 64
+
+/*
+ * fa_fwd_block_sparse - fa_fwd_ex under a programmable block mask: the block
+ * sparsity of the metal-flash-attention README ("Modifications to
+ * FlashAttention": block masks held in memory, covering causal and arbitrary
+ * sparsity patterns).
+ *
+ *   block_mask  device pointer, unsigned bytes, contiguous
+ *               [mask_batch][mask_heads][ceil(Sq / FA_MASK_BLOCK_Q)][ceil(Sk / FA_MASK_BLOCK_K)]
+ *   mask_batch  1 (one mask for every batch entry) or B
+ *   mask_heads  1 (shared), HKV (per kv head) or H (per query head)
+ *
+ * Key j is visible to query row i of (b, h) when the causal and window rules
+ * allow it AND the mask byte of block (i / FA_MASK_BLOCK_Q, j / FA_MASK_BLOCK_K)
+ * for (b, h) is nonzero. Rows left with no visible key get O = 0 and
+ * LSE = -inf. Key blocks whose byte is 0 are neither read nor computed.
+ * Q, K, V, O contiguous as for fa_fwd. The mask is read by the kernels on
+ * `stream` (it must stay valid until they complete) and is not modified.
+ * Errors as fa_fwd_ex, plus FA_ERR_NULLPTR for a NULL mask and FA_ERR_MASK
+ * for other mask axis sizes. Key ranges of more than 2048 key tiles per
+ * workgroup are split along the key axis automatically (FA_ERR_SHAPE if
+ * FA_MAX_SPLITS splits are not enough).
+ */
+int fa_fwd_block_sparse(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                        int B, int H, int HKV, int Sq, int Sk, int D,
+                        const unsigned char* block_mask, int mask_batch, int mask_heads,
+                        float scale, int causal, int window, int dtype,
+                        int num_splits, void* stream);
 
 /*
  * fa_plan_splits - the number of key-axis splits fa_fwd would use for this

@@ -155,3 +155,32 @@ def test_strided_other_errors_come_first():
 
 def test_strided_offset_overflow_is_a_shape_error():
     assert call_strided(ks=(1 << 61, 128, 128 * 4), B=4) == 2
+
+
+# ------------------------------------------------------------ block-sparse entry
+def call_sparse(mask=A, mb=1, mh=1, **over):
+    a = dict(GOOD, **over)
+    return _lib.lib().fa_fwd_block_sparse(A, A, A, A, A, a["B"], a["H"], a["HKV"], a["Sq"],
+                                          a["Sk"], a["D"], mask, mb, mh, a["scale"],
+                                          a["causal"], a["window"], a["dtype"], 0, None)
+
+
+def test_block_sparse_null_mask():
+    assert call_sparse(mask=None) == 1
+
+
+@pytest.mark.parametrize("mb,mh", [(2, 1), (0, 1), (1, 3), (1, 0), (1, 8)])
+def test_block_sparse_bad_mask_axes(mb, mh):
+    # GOOD: B = 1, H = 4, HKV = 2
+    assert call_sparse(mb=mb, mh=mh) == 12
+
+
+def test_block_sparse_shape_errors_come_first():
+    assert call_sparse(D=96) == 4
+    assert call_sparse(H=4, HKV=3) == 3
+
+
+def test_mask_block_constants_match_header():
+    src = open(os.path.join(ROOT, "include", "fa.h")).read()
+    assert re.search(r"#define FA_MASK_BLOCK_Q (\d+)", src).group(1) == str(_lib.FA_MASK_BLOCK_Q)
+    assert re.search(r"#define FA_MASK_BLOCK_K (\d+)", src).group(1) == str(_lib.FA_MASK_BLOCK_K)

@@ -44,7 +44,8 @@ def run_gpu(inp, num_splits=0, scale=None):
     wl = inp.wl
     q, k, v = to_device(inp)
     o, lse = fa.fwd(q, k, v, causal=bool(wl.causal), window=wl.window,
-                    scale=wl.scale() if scale is None else scale, num_splits=num_splits)
+                    scale=wl.scale() if scale is None else scale, num_splits=num_splits,
+                    block_mask=W.device_mask(inp, torch, "cuda"))
     torch.cuda.synchronize()
     return o, lse
 
@@ -70,7 +71,8 @@ def check_full(wl, num_splits=0, scale=None, inp=None):
     _say(f"[parity] {wl} splits={num_splits}")
     s = wl.scale() if scale is None else scale
     o, lse = run_gpu(inp, num_splits, s)
-    O, L = attention(inp.q, inp.k, inp.v, s, bool(wl.causal), wl.window)
+    O, L = attention(inp.q, inp.k, inp.v, s, bool(wl.causal), wl.window,
+                     block_mask=inp.block_mask)
     compare(host64(o), host64(lse), O, L, TOL[wl.dtype], wl.name)
     return o, lse
 
@@ -228,19 +230,24 @@ def test_benchmark_workload(idx):
     rows = W.check_rows(inp)
     s = wl.scale()
     if rows is None:
-        O, L = attention(inp.q, inp.k, inp.v, s, bool(wl.causal), wl.window)
+        O, L = attention(inp.q, inp.k, inp.v, s, bool(wl.causal), wl.window,
+                         block_mask=inp.block_mask)
         compare(host64(o), host64(lse), O, L, TOL[wl.dtype], wl.name)
         return
     idx_t = torch.from_numpy(rows).cuda()
     og = o[idx_t[:, 0], idx_t[:, 1], idx_t[:, 2]]
     lg = lse[idx_t[:, 0], idx_t[:, 1], idx_t[:, 2]]
-    O, L = attention_rows(inp.q, inp.k, inp.v, s, bool(wl.causal), wl.window, rows)
+    O, L = attention_rows(inp.q, inp.k, inp.v, s, bool(wl.causal), wl.window, rows,
+                          block_mask=inp.block_mask)
     compare(host64(og), host64(lg), O, L, TOL[wl.dtype], f"{wl.name} ({len(rows)} rows)")
     # properties over every row: finite outputs, LSE >= max score lower bound
     # (LSE >= log of one term) is not cheap here; check finiteness everywhere.
-    cnt = visible_count(wl.Sq, wl.Sk, bool(wl.causal), wl.window)
     lh = host64(lse)
-    assert np.all(np.isfinite(lh[:, :, cnt > 0]))
+    if inp.block_mask is None:
+        cnt = visible_count(wl.Sq, wl.Sk, bool(wl.causal), wl.window)
+        assert np.all(np.isfinite(lh[:, :, cnt > 0]))
+    else:   # every row of these masks sees its own diagonal block and key block 0
+        assert np.all(np.isfinite(lh))
     assert torch.isfinite(o.float()).all().item()
 
 

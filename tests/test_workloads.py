@@ -92,3 +92,46 @@ def test_device_tensors_token_major_view():
     np.testing.assert_array_equal(v.float().numpy(), inp.v)
     c = W.device_tensors(W.make_inputs(W.small(wl, layout="bhsd")), torch, "cpu")
     assert c[0].is_contiguous() and torch.equal(c[0], q)
+
+
+def test_block_mask_recipe():
+    wl = W.CONFIGS[7]
+    assert wl.mask == "band_random" and not wl.causal
+    small = W.small(wl, B=1, H=4, HKV=2, Sq=1000, Sk=1300)
+    a, b = W.make_inputs(small), W.make_inputs(small)
+    np.testing.assert_array_equal(a.block_mask, b.block_mask)
+    m = a.block_mask
+    assert m.shape == (1, 2, 8, 21) and m.dtype == np.uint8
+    for r in range(8):
+        assert np.all(m[0, :, r, 0] == 1)                           # global block
+        for c in range(max(0, 2 * r - 2), min(21, 2 * r + 2)):
+            assert np.all(m[0, :, r, c] == 1)                       # local band
+    assert 0.1 < float(m.mean()) < 0.6
+    # the full-size mask: density near band + global + 15 % random
+    full = W.make_inputs(W.small(wl, B=1, H=8, HKV=8, Sq=4096, Sk=4096)).block_mask
+    assert 0.15 < float(full.mean()) < 0.3
+
+
+def test_bench_counted_flops_match_oracle_masks():
+    # bench.py's closed-form per-row counts against the oracle's own masks
+    import importlib.util
+    import os
+    from oracle import block_visible, visible_mask
+    spec = importlib.util.spec_from_file_location(
+        "bench", os.path.join(os.path.dirname(os.path.dirname(__file__)), "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    for causal, window in [(0, 0), (1, 0), (1, 150), (0, 300)]:
+        wl = W.small(W.CONFIGS[7], B=2, H=4, HKV=2, Sq=700, Sk=900, causal=causal,
+                     window=window)
+        inp = W.make_inputs(wl)
+        i = np.arange(wl.Sq)
+        want = 0
+        for b in range(wl.B):
+            for h in range(wl.H):
+                vis = visible_mask(i, wl.Sk, bool(causal), window)
+                vis &= block_visible(inp.block_mask[0, h // 2], i, wl.Sk)
+                want += int(vis.sum())
+        assert bench.counted_flops(wl, inp.block_mask) == 4.0 * wl.D * want
+        plain = int(visible_mask(i, wl.Sk, bool(causal), window).sum()) * wl.B * wl.H
+        assert bench.counted_flops(wl) == 4.0 * wl.D * plain

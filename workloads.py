@@ -10,8 +10,10 @@ Workload shapes follow the five synthetic configurations of the benchmark
 (small reference case, fp32 causal MHA, bf16 causal GQA, fp32 sliding-window
 GQA, bf16 long non-square single head), plus the causal GQA shape with fp16
 inputs (mixed precision, the "Support mixed precision" item of the
-metal-flash-attention README's TODO list) and with token-major [B, S, H, D]
-storage (the layout of the forge flash_attention.metal kernels). Layout is [B, H, S, D] contiguous for
+metal-flash-attention README's TODO list), with token-major [B, S, H, D]
+storage (the layout of the forge flash_attention.metal kernels), and
+non-causal under a block mask (the block sparsity of the metal-flash-attention
+README's "Modifications to FlashAttention"; recipe in make_block_mask). Layout is [B, H, S, D] contiguous for
 Q and O, [B, HKV, S, D] for K and V, as in the boostr ``flash.wgsl`` header
 comment and the rustytorch ``flash_attention_forward.metal`` buffer comments.
 
@@ -55,6 +57,8 @@ class Workload:
     seed_index: int = 0
     layout: str = "bhsd"        # device storage: "bhsd" contiguous [B, heads, S, D], or
                                 # "bshd" token-major [B, S, heads, D] (viewed as [B, heads, S, D])
+    mask: str = ""              # "" (none) or "band_random": a block mask, see make_block_mask
+    mask_p: float = 0.0         # "band_random": probability of each extra random block
 
     @property
     def group(self) -> int:
@@ -88,7 +92,14 @@ CONFIGS = [
     Workload("gqa_causal_bf16_bshd_b2h32kv8_s4096_d128", 2, 32, 8, 4096, 4096, 128, "bf16", 1,
              0, amplitude=0.5, check="sampled", n_random_rows=4096, edge_rows=64,
              seed_index=6, layout="bshd"),
+    Workload("blocksparse_bf16_b2h32kv8_s4096_d128", 2, 32, 8, 4096, 4096, 128, "bf16", 0, 0,
+             amplitude=0.5, check="sampled", n_random_rows=4096, edge_rows=64,
+             seed_index=7, mask="band_random", mask_p=0.15),
 ]
+
+# Block-mask granularity (query rows x keys per mask byte).
+MASK_BLOCK_Q = 128
+MASK_BLOCK_K = 64
 
 # The configuration the throughput metric is quoted on (bf16 causal GQA).
 HEADLINE = 2
@@ -151,6 +162,7 @@ class Inputs:
     k_bits: np.ndarray | None = None
     v_bits: np.ndarray | None = None
     rows_rng: np.random.Generator | None = field(default=None, repr=False)
+    block_mask: np.ndarray | None = None     # uint8 [1, HKV, nqb, nkb] for masked workloads
 
 
 def make_inputs(wl: Workload, seed: int | None = None) -> Inputs:
@@ -163,11 +175,39 @@ def make_inputs(wl: Workload, seed: int | None = None) -> Inputs:
         a = np.float32(wl.amplitude)
         q, k, v = q * a, k * a, v * a
     out = Inputs(wl, q, k, v, rows_rng=np.random.default_rng(srow))
+    if wl.mask:
+        out.block_mask = make_block_mask(wl, np.random.default_rng(
+            np.random.SeedSequence(seed).spawn(5)[4]))
     if wl.dtype in ROUNDING:
         to_bits, to_f32 = ROUNDING[wl.dtype]
         out.q_bits, out.k_bits, out.v_bits = to_bits(q), to_bits(k), to_bits(v)
         out.q, out.k, out.v = to_f32(out.q_bits), to_f32(out.k_bits), to_f32(out.v_bits)
     return out
+
+
+def make_block_mask(wl: Workload, rng: np.random.Generator) -> np.ndarray:
+    """Seeded block mask [1, HKV, nqb, nkb] (uint8), one per kv head, shared
+    over the batch. "band_random": query block r (rows 128 r ..) sees the key
+    blocks of its own rows and the two before them (c in [2r - 2, 2r + 1], a
+    local band), key block 0 (a global prefix), and each other block with
+    probability mask_p."""
+    assert wl.mask == "band_random", wl.mask
+    nqb = -(-wl.Sq // MASK_BLOCK_Q)
+    nkb = -(-wl.Sk // MASK_BLOCK_K)
+    r = np.arange(nqb)[:, None]
+    c = np.arange(nkb)[None, :]
+    per = MASK_BLOCK_Q // MASK_BLOCK_K
+    band = (c >= per * r - 2) & (c <= per * r + per - 1)
+    base = band | (c == 0)
+    extra = rng.random((1, wl.HKV, nqb, nkb)) < wl.mask_p
+    return (base[None, None] | extra).astype(np.uint8)
+
+
+def device_mask(inp: Inputs, torch, device="cuda"):
+    """The workload's block mask on `device`, or None."""
+    if inp.block_mask is None:
+        return None
+    return torch.from_numpy(inp.block_mask).to(device)
 
 
 def check_rows(inp: Inputs) -> np.ndarray | None:
