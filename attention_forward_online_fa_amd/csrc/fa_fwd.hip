@@ -512,7 +512,8 @@ void fwd_16b_kernel(Params p) {
         }
       return rs;
     } else {
-      f32x4 ps = {0.f, 0.f, 0.f, 0.f};   // four partial sums
+      f32x4 ps;   // four partial sums (the first chunk initialises them: adding to
+                  // a zero vector would cost four adds, as 0 + x is not x for x = -0)
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
@@ -528,8 +529,12 @@ void fwd_16b_kernel(Params p) {
             pf[2 * kb + c2][e] = (E)lo[e];
             pf[2 * kb + c2][4 + e] = (E)hi[e];
           }
-          ps += lo;
-          ps += hi;
+          if (kb == 0 && c2 == 0) {
+            ps = lo + hi;
+          } else {
+            ps += lo;
+            ps += hi;
+          }
         }
       return (ps[0] + ps[1]) + (ps[2] + ps[3]);
     }
@@ -569,12 +574,26 @@ void fwd_16b_kernel(Params p) {
     if constexpr (VR == 1) asm volatile("" : "+v"(voff[0]));
 #pragma unroll
     for (int c = 0; c < T::KC; ++c) {
+      if constexpr (D <= 128) {
+        // all V operands of this 16-key chunk first, then its MFMAs
+        e16x8 a[T::DB];
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-        const int base = 16 * c * T::ROW;
-        const int vo = v_off(db) + base;
-        const e16x8 a = read_v_pair<e16x8>(Vs, vo, vo + 4 * T::ROW);
-        o[db] = X::mfma(a, pf[c], o[db]);
+        for (int db = 0; db < T::DB; ++db) {
+          const int vo = v_off(db) + 16 * c * T::ROW;
+          a[db] = read_v_pair<e16x8>(Vs, vo, vo + 4 * T::ROW);
+        }
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) o[db] = X::mfma(a[db], pf[c], o[db]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::DB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, T::DB, 0);
+      } else {
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) {
+          const int base = 16 * c * T::ROW;
+          const int vo = v_off(db) + base;
+          const e16x8 a = read_v_pair<e16x8>(Vs, vo, vo + 4 * T::ROW);
+          o[db] = X::mfma(a, pf[c], o[db]);
+        }
       }
     }
   };
@@ -817,11 +836,11 @@ void fwd_f32_kernel(Params p) {
       // recomputed. O and l always share the reference: the same softmax.
       f32x16 e;
       auto exps = [&](float m_sub) __attribute__((always_inline)) {
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        float part[4];   // the first four exponentials initialise the partial sums
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           e[v] = fast_exp2(s[v] - m_sub);
-          part[v & 3] += e[v];
+          part[v & 3] = v < 4 ? e[v] : part[v & 3] + e[v];
         }
         return (part[0] + part[1]) + (part[2] + part[3]);
       };
