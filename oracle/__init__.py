@@ -3,8 +3,8 @@
 Only tests, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg may
 import this package. The product path never does.
 """
-from .attention import (MASK_BLOCK_K, MASK_BLOCK_Q, attention, attention_rows, block_visible,
-                        visible_count, visible_mask)
+from .attention import (MASK_BLOCK_K, MASK_BLOCK_Q, attention, attention_backward,
+                        attention_rows, block_visible, visible_count, visible_mask)
 
-__all__ = ["attention", "attention_rows", "visible_count", "visible_mask", "block_visible",
+__all__ = ["attention", "attention_backward", "attention_rows", "visible_count", "visible_mask", "block_visible",
            "MASK_BLOCK_Q", "MASK_BLOCK_K"]

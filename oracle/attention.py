@@ -20,8 +20,9 @@ Sources (four web pages on fused attention; cited by page and section):
     memory, covering causal and arbitrary sparsity patterns. Here a block
     mask has one byte per (query block, key block); a key is visible only if
     its block's byte is nonzero (on top of the causal and window rules).
-  * spb/forge ``src/kernels/flash_attention.metal``, header comment and the
-    forward kernel ``flash_attn_fwd``: the online-softmax identity whose
+  * spb/forge ``src/kernels/flash_attention.metal``, header comment, the
+    forward kernel ``flash_attn_fwd`` and the backward kernels
+    ``flash_attn_bwd_dq`` / ``_dk`` / ``_dv`` (the gradients below): the online-softmax identity whose
     end result is the plain softmax, the GQA head map hkv = h / (H / HKV),
     the sliding window (keys j >= i - window + 1, self included, 0 = full
     attention), and the stored L = m + log(l).
@@ -181,3 +182,51 @@ def visible_count(Sq: int, Sk: int, causal: bool, window: int) -> np.ndarray:
     hi = np.minimum(i + 1, Sk) if causal else np.full(Sq, Sk, dtype=np.int64)
     lo = np.maximum(i - window + 1, 0) if window > 0 else np.zeros(Sq, dtype=np.int64)
     return np.maximum(hi - lo, 0)
+
+
+def attention_backward(Q, K, V, dO, scale: float, causal: bool = False, window: int = 0):
+    """Gradients (dQ, dK, dV) of L = sum(O * dO), all fp64, for O = attention(...).
+
+    From the definition (forge ``flash_attention.metal`` backward section): with
+    P the masked softmax of scale * Q K^T (P_ij = exp(s_ij - LSE_i) on the
+    visible keys, 0 elsewhere),
+        dV_j  = sum_i P_ij dO_i
+        dP_ij = dO_i . V_j
+        D_i   = dO_i . O_i               (= sum_j P_ij dP_ij)
+        dS_ij = P_ij (dP_ij - D_i)
+        dQ_i  = scale sum_j dS_ij K_j
+        dK_j  = scale sum_i dS_ij Q_i
+    with dK and dV summed over the query heads that share a kv head (GQA).
+    Rows with no visible key have P = 0: they contribute nothing and get dQ = 0.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    B, H, Sq, D = Q.shape
+    HKV, Sk = K.shape[1], K.shape[2]
+    assert H % HKV == 0, "H must be a multiple of HKV"
+    g = H // HKV
+    scale = float(np.float64(scale))
+    vis = visible_mask(np.arange(Sq), Sk, causal, window)
+    nonempty = vis.any(axis=1)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for b in range(B):
+        for h in range(H):
+            hk = h // g
+            S = np.where(vis, scale * (Q[b, h] @ K[b, hk].T), -np.inf)
+            m = np.where(nonempty, S.max(axis=1, initial=-np.inf), 0.0)
+            E = np.exp(S - m[:, None])
+            l = E.sum(axis=1)
+            P = np.zeros_like(E)
+            P[nonempty] = E[nonempty] / l[nonempty, None]
+            O = P @ V[b, hk]
+            dP = dO[b, h] @ V[b, hk].T
+            Drow = (dO[b, h] * O).sum(axis=1)
+            dS = P * (dP - Drow[:, None])
+            dQ[b, h] = scale * (dS @ K[b, hk])
+            dK[b, hk] += scale * (dS.T @ Q[b, h])
+            dV[b, hk] += P.T @ dO[b, h]
+    return dQ, dK, dV
