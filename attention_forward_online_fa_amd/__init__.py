@@ -24,7 +24,7 @@ import math
 from ._lib import (FA_BF16, FA_F16, FA_F32, FA_MASK_BLOCK_K, FA_MASK_BLOCK_Q, FA_MAX_SPLITS,
                    FaError, lib, library_path)
 
-__all__ = ["fwd", "fwd_into", "plan_splits", "schedule_table", "release", "FaError",
+__all__ = ["fwd", "fwd_into", "bwd", "plan_splits", "schedule_table", "release", "FaError",
            "library_path", "default_scale", "FA_F32", "FA_BF16", "FA_F16", "FA_MAX_SPLITS",
            "FA_MASK_BLOCK_Q", "FA_MASK_BLOCK_K"]
 
@@ -140,6 +140,38 @@ def fwd(q, k, v, *, causal=False, window=0, scale=None, num_splits=0, stream=Non
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     return fwd_into(q, k, v, o, lse, causal=causal, window=window, scale=scale,
                     num_splits=num_splits, stream=stream, block_mask=block_mask)
+
+
+def bwd(q, k, v, o, lse, do, *, causal=False, window=0, scale=None, stream=None):
+    """Backward pass (fa_bwd): float32 (dq, dk, dv), the gradients of
+    sum(o * do) for o, lse = fwd(q, k, v, ...) with the same arguments.
+    Contiguous tensors; o and do have q's shape and dtype."""
+    import torch
+    _check(q, k, v)
+    B, H, Sq, D = q.shape
+    HKV, Sk = k.shape[1], k.shape[2]
+    for name, t in (("o", o), ("do", do)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor with q's shape and dtype")
+    if tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, Sq]")
+    if not all(t.is_contiguous() for t in (q, k, v, o, do, lse)):
+        raise ValueError("the backward pass takes contiguous tensors")
+    if scale is None:
+        scale = default_scale(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+        dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    st = lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, HKV, Sq,
+                      Sk, D, float(scale), int(bool(causal)), int(window), _dtype_code(q),
+                      stream.cuda_stream)
+    if st != 0:
+        raise FaError(st)
+    return dq, dk, dv
 
 
 def plan_splits(B, H, HKV, Sq, Sk, D, *, causal=False, window=0, dtype="bf16") -> int:

@@ -189,6 +189,33 @@ int fa_schedule_table(int B, int H, int HKV, int Sq, int Sk, int D,
                       int causal, int window, int dtype, int nslot,
                       int* table, int capacity, int* num_splits);
 
+/*
+ * fa_bwd - backward pass: the gradients of sum(O * dO) with respect to Q, K
+ * and V, for O and LSE from fa_fwd with the same arguments. It follows the
+ * backward kernels of the forge flash_attention.metal page: probabilities
+ * recomputed from the saved LSE, D_i = dO_i . O_i, dS = P (dO V^T - D),
+ * dQ = scale dS K, dK = scale dS^T Q and dV = P^T dO, with dK and dV summed
+ * over the query heads of each kv head; per-row accumulation, no atomics
+ * (deterministic).
+ *
+ *   Q, K, V, O, dO  device pointers, contiguous, element type `dtype`
+ *                   (Q, O, dO [B, H, Sq, D]; K, V [B, HKV, Sk, D])
+ *   LSE             device pointer, [B, H, Sq] float32 (the forward's output)
+ *   dQ              device pointer, [B, H, Sq, D]   float32 (written)
+ *   dK, dV          device pointers, [B, HKV, Sk, D] float32 (written; keys no
+ *                   query sees get 0)
+ *   scale, causal, window, dtype: as for fa_fwd; rows with LSE = -inf (no
+ *   visible key) get dQ = 0 and contribute nothing.
+ *
+ * Contiguous tensors only; no block mask. All buffers 16-byte aligned. A
+ * [B, H, Sq] float32 workspace comes from the device's default memory pool,
+ * stream-ordered. Asynchronous on `stream`. Errors as fa_fwd.
+ */
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+           const float* LSE, float* dQ, float* dK, float* dV,
+           int B, int H, int HKV, int Sq, int Sk, int D,
+           float scale, int causal, int window, int dtype, void* stream);
+
 /* fa_status_string - static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 

@@ -184,3 +184,27 @@ def test_mask_block_constants_match_header():
     src = open(os.path.join(ROOT, "include", "fa.h")).read()
     assert re.search(r"#define FA_MASK_BLOCK_Q (\d+)", src).group(1) == str(_lib.FA_MASK_BLOCK_Q)
     assert re.search(r"#define FA_MASK_BLOCK_K (\d+)", src).group(1) == str(_lib.FA_MASK_BLOCK_K)
+
+
+# ---------------------------------------------------------------- backward entry
+def call_bwd(ptrs=(A,) * 9, **over):
+    a = dict(GOOD, **over)
+    return _lib.lib().fa_bwd(*ptrs, a["B"], a["H"], a["HKV"], a["Sq"], a["Sk"], a["D"],
+                             a["scale"], a["causal"], a["window"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("which", range(9))
+def test_bwd_null_and_misaligned(which):
+    ptrs = [A] * 9
+    ptrs[which] = None
+    assert call_bwd(tuple(ptrs)) == 1
+    ptrs[which] = A + 4
+    assert call_bwd(tuple(ptrs)) == 7
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(B=0), 2), (dict(H=6, HKV=4), 3), (dict(D=96), 4), (dict(dtype=3), 5),
+    (dict(window=-1), 6), (dict(causal=2), 6),
+])
+def test_bwd_argument_errors(over, code):
+    assert call_bwd(**over) == code

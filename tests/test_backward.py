@@ -1,0 +1,100 @@
+"""GPU parity of the backward pass (fa_bwd) against the fp64 oracle's
+gradients, on the same seeded inputs; O and LSE come from the library's own
+forward pass, as a caller would use them.
+
+Tolerance (absolute, scaled by the largest reference magnitude r = max(1,
+max|ref|) of each gradient): fp32 inputs 1e-4 r; bf16 3e-2 r and fp16 1e-2 r.
+The 16-bit bounds come from the forward output: the backward reads O rounded
+to the input type, so D_i = dO_i . O_i carries a relative error up to 2^-9
+(bf16) or 2^-11 (fp16) of sum|dO||O|, and every dS_ij = P_ij (dP_ij - D_i)
+inherits it; the inputs themselves are exact on both sides."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention_backward
+from test_parity import host64, to_device, wl_small
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 3e-2, "f16": 1e-2}
+
+
+def grads(wl, seed=0):
+    import attention_forward_online_fa_amd as fa
+    inp = W.make_inputs(wl)
+    q, k, v = to_device(inp)
+    rng = np.random.default_rng(wl.seed + 1000 + seed)
+    dO = rng.standard_normal(q.shape).astype(np.float32)
+    if wl.dtype in W.ROUNDING:
+        to_bits, to_f32 = W.ROUNDING[wl.dtype]
+        bits = to_bits(dO)
+        dO = to_f32(bits)
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float16
+        do = torch.from_numpy(bits.view(np.int16)).view(tdt).cuda()
+    else:
+        do = torch.from_numpy(dO).cuda()
+    print(f"[backward] {wl}", flush=True)
+    o, lse = fa.fwd(q, k, v, causal=bool(wl.causal), window=wl.window, scale=wl.scale())
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=bool(wl.causal), window=wl.window,
+                        scale=wl.scale())
+    torch.cuda.synchronize()
+    ref = attention_backward(inp.q, inp.k, inp.v, dO, wl.scale(), bool(wl.causal), wl.window)
+    return (host64(dq), host64(dk), host64(dv)), ref
+
+
+CASES = [
+    # dtype, B, H, HKV, Sq, Sk, D, causal, window
+    ("f32", 1, 1, 1, 64, 64, 64, 0, 0),
+    ("f32", 2, 4, 2, 150, 150, 64, 1, 0),
+    ("f32", 1, 4, 1, 130, 90, 128, 1, 0),        # Sq > Sk
+    ("f32", 1, 2, 2, 100, 170, 128, 0, 40),      # window without causal
+    ("f32", 1, 2, 1, 90, 120, 256, 1, 30),
+    ("bf16", 2, 4, 2, 150, 150, 64, 1, 0),
+    ("bf16", 1, 4, 1, 200, 230, 128, 0, 0),
+    ("bf16", 1, 2, 1, 90, 120, 256, 1, 30),
+    ("f16", 1, 4, 2, 160, 160, 128, 1, 50),
+    ("f16", 1, 2, 1, 70, 100, 256, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["-".join(map(str, c)) for c in CASES])
+def test_backward_matches_oracle(case):
+    wl = wl_small(*case, seed=sum(case[1:]) + 3)
+    got, ref = grads(wl)
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        scale_r = max(1.0, float(np.abs(r).max()))
+        err = float(np.abs(g - r).max())
+        print(f"  {name}: max|d|={err:.3e} (tol {TOL[wl.dtype] * scale_r:.3e})", flush=True)
+        assert np.all(np.isfinite(g)), name
+        assert err <= TOL[wl.dtype] * scale_r, f"{name}: {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_empty_rows_and_unseen_keys(dtype):
+    # Sq=8, Sk=40, causal, window 1: rows 0..7 see only their own key; keys
+    # 8..39 are seen by no row (dK = dV = 0 there); no row is empty.
+    # Sq=40, Sk=8, causal, window 1: rows >= 8 see nothing (dQ = 0 there).
+    for shape in [(1, 2, 1, 8, 40, 64, 1, 1), (1, 2, 1, 40, 8, 64, 1, 1)]:
+        wl = wl_small(dtype, *shape, seed=sum(shape))
+        (dq, dk, dv), ref = grads(wl)
+        Sq, Sk = shape[3], shape[4]
+        if Sk > Sq:
+            assert np.all(dk[:, :, Sq:] == 0) and np.all(dv[:, :, Sq:] == 0)
+        else:
+            assert np.all(dq[:, :, Sk:] == 0)
+        for g, r in zip((dq, dk, dv), ref):
+            assert float(np.abs(g - r).max()) <= TOL[dtype] * max(1.0, float(np.abs(r).max()))
+
+
+def test_backward_deterministic():
+    import attention_forward_online_fa_amd as fa
+    wl = wl_small("bf16", 1, 4, 1, 300, 300, 128, 1, 0, seed=5)
+    q, k, v = to_device(W.make_inputs(wl))
+    do = torch.randn_like(q)
+    o, lse = fa.fwd(q, k, v, causal=True)
+    a = fa.bwd(q, k, v, o, lse, do, causal=True)
+    b = fa.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
