@@ -16,7 +16,7 @@
 // Work decomposition: a group of 16 lanes owns one row (a query row in the
 // dQ kernel, a key row in the dK/dV kernel) and holds D/16 consecutive
 // elements of each row vector per lane; dot products reduce over the 16 lanes
-// with four xor shuffles. A wavefront serves four rows, a workgroup 16. This
+// with four DPP row rotations. A wavefront serves four rows, a workgroup 16. This
 // is the pages' thread-per-row design mapped to wavefronts, on the VALU (no
 // MFMA): a baseline that is exact to fp32 rounding, not a tuned kernel.
 #include <hip/hip_runtime.h>
@@ -33,12 +33,20 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <typename E>
 __device__ __forceinline__ float to_f32(E x) { return (float)x; }
 
-// Sum over the 16 lanes of one row group.
+// Value of lane (l + n) mod 16 of the same 16-lane row (DPP row_ror:n).
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), 0x120 + N, 0xf, 0xf, false));
+}
+
+// Sum over the 16 lanes of one row group (every lane gets the total):
+// register-to-register rotations within the row, no LDS round trips.
 __device__ __forceinline__ float group_sum(float x) {
-  x += __shfl_xor(x, 8);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 1);
+  x += row_ror<8>(x);
+  x += row_ror<4>(x);
+  x += row_ror<2>(x);
+  x += row_ror<1>(x);
   return x;
 }
 
@@ -97,10 +105,23 @@ void bwd_dq_kernel(BwdParams p) {
   int lo, hi;
   row_keys(p, i, lo, hi);
   if (L2 == -INFINITY) hi = lo;            // empty row: P = 0 everywhere
+  // key j + 1's rows are loaded while key j is computed
+  float kn[NE], vn[NE];
+  if (lo < hi) {
+    load_part<E, NE>(Kh + (long)lo * D, kn);
+    load_part<E, NE>(Vh + (long)lo * D, vn);
+  }
   for (int j = lo; j < hi; ++j) {
     float k[NE], v[NE];
-    load_part<E, NE>(Kh + (long)j * D, k);
-    load_part<E, NE>(Vh + (long)j * D, v);
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      k[e] = kn[e];
+      v[e] = vn[e];
+    }
+    if (j + 1 < hi) {
+      load_part<E, NE>(Kh + (long)(j + 1) * D, kn);
+      load_part<E, NE>(Vh + (long)(j + 1) * D, vn);
+    }
     float s = 0.f, dp = 0.f;
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
@@ -146,11 +167,29 @@ void bwd_dkdv_kernel(BwdParams p) {
   key_rows(p, j, lo, hi);
   for (int h = hk * g; h < hk * g + g; ++h) {
     const long base = ((long)b * p.H + h) * p.Sq;
+    // query row i + 1 is loaded while row i is computed
+    float qn[NE], gn[NE], ln = 0.f, dn = 0.f;
+    if (lo < hi) {
+      load_part<E, NE>((const E*)p.Q + (base + lo) * D + l16 * NE, qn);
+      load_part<E, NE>((const E*)p.dO + (base + lo) * D + l16 * NE, gn);
+      ln = p.LSE[base + lo];
+      dn = p.Dws[base + lo];
+    }
     for (int i = lo; i < hi; ++i) {
       const long row = base + i;
       float q[NE], go[NE];
-      load_part<E, NE>((const E*)p.Q + row * D + l16 * NE, q);
-      load_part<E, NE>((const E*)p.dO + row * D + l16 * NE, go);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        q[e] = qn[e];
+        go[e] = gn[e];
+      }
+      const float Li = ln, Di = dn;
+      if (i + 1 < hi) {
+        load_part<E, NE>((const E*)p.Q + (row + 1) * D + l16 * NE, qn);
+        load_part<E, NE>((const E*)p.dO + (row + 1) * D + l16 * NE, gn);
+        ln = p.LSE[row + 1];
+        dn = p.Dws[row + 1];
+      }
       float s = 0.f, dp = 0.f;
 #pragma unroll
       for (int e = 0; e < NE; ++e) {
@@ -160,8 +199,8 @@ void bwd_dkdv_kernel(BwdParams p) {
       s = group_sum(s);
       dp = group_sum(dp);
       // row i sees key j, so it is not empty and its LSE is finite
-      const float pr = __builtin_amdgcn_exp2f(fmaf(s, sl, -p.LSE[row] * kLog2e));
-      const float ds = pr * (dp - p.Dws[row]);
+      const float pr = __builtin_amdgcn_exp2f(fmaf(s, sl, -Li * kLog2e));
+      const float ds = pr * (dp - Di);
 #pragma unroll
       for (int e = 0; e < NE; ++e) {
         dv[e] = fmaf(pr, go[e], dv[e]);

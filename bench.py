@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the fused attention forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config IDX]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config IDX] [--pass fwd|bwd]
 
 A step is one fa_fwd call (every kernel of the forward pass, including the
 key-split merge when the library splits) over one batch of synthetic inputs
@@ -13,7 +13,9 @@ headline metric is quoted on. Prints one JSON line.
 
 Metric: TFLOP/s counting 4*B*H*D*sum_i |visible keys of row i| (masked
 pairs are not counted), i.e. the two matrix products of attention restricted
-to the mask.
+to the mask. With --pass bwd a step is one backward pass (fa_bwd, on O and
+LSE from one forward pass made before timing) and the count is 10*D per
+visible pair (the five products of the backward pass).
 """
 from __future__ import annotations
 
@@ -32,6 +34,9 @@ import numpy as np  # noqa: E402
 import workloads as W  # noqa: E402
 
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (published)
+# Published fp32 vector peak: 256 flop per clock per CU x 256 CUs x 2.4 GHz = 157.3 TFLOP/s.
+# It counts packed fp32 FMAs; code built without them (as this library is) tops out at half.
+PEAK_VALU_F32 = 157.3
 KERNEL_SOURCES = [os.path.join(ROOT, "attention_forward_online_fa_amd", "csrc", f)
                   for f in ("fa_fwd.hip", "fa_api.cpp", "fa_kernels.h")]
 
@@ -97,6 +102,75 @@ def device_inputs(inp, torch):
     return W.device_tensors(inp, torch, "cuda")
 
 
+def bench_backward(args, wl, inp, q, k, v, torch, fa):
+    """Time the backward pass; prints one JSON line."""
+    if inp.block_mask is not None or wl.layout != "bhsd":
+        print("the backward pass takes contiguous tensors without a block mask", file=sys.stderr)
+        sys.exit(2)
+    stream = torch.cuda.current_stream()
+    scale = wl.scale()
+    o, lse = fa.fwd(q, k, v, causal=bool(wl.causal), window=wl.window, scale=scale)
+    g, bits = W.make_grad_output(inp)
+    if bits is not None:
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float16
+        do = torch.from_numpy(bits.view(np.int16)).view(tdt).cuda()
+    else:
+        do = torch.from_numpy(g).cuda()
+
+    def step():
+        fa.bwd(q, k, v, o, lse, do, causal=bool(wl.causal), window=wl.window, scale=scale,
+               stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_warm = time.perf_counter() + args.warmup_seconds
+    while time.perf_counter() < t_warm:
+        step()
+        torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    flops = 2.5 * counted_flops(wl)          # 10 D per visible pair
+    rec = {
+        "metric": "attention bwd TFLOP/s (unmasked FLOPs, 10*D per visible pair), 1xMI355X",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "pass": "bwd", "B": wl.B, "H": wl.H, "HKV": wl.HKV,
+                   "Sq": wl.Sq, "Sk": wl.Sk, "D": wl.D, "causal": wl.causal,
+                   "window": wl.window, "counted_flops": flops, "parallelism": "single GPU"},
+        "roofline": {"bound": "alu", "achieved": round(flops / (ev_ms * 1e-3) / 1e12, 3),
+                     "peak": PEAK_VALU_F32, "unit": "TFLOP/s",
+                     "frac": round(flops / (ev_ms * 1e-3) / 1e12 / PEAK_VALU_F32, 4),
+                     "traffic": None, "kernel_ms": round(ev_ms, 5)},
+    }
+    if args.cpu_rows > 0:
+        # the oracle's backward on one (batch, kv-head group) slice of the workload
+        from oracle import attention_backward
+        gsz = wl.H // wl.HKV
+        sl = W.small(wl, B=1, H=gsz, HKV=1)
+        t1 = time.perf_counter()
+        attention_backward(inp.q[:1, :gsz], inp.k[:1, :1], inp.v[:1, :1], g[:1, :gsz],
+                           scale, bool(wl.causal), wl.window)
+        dt = time.perf_counter() - t1
+        rec["cpu_baseline"] = {"value": round(2.5 * counted_flops(sl) / dt / 1e12, 6),
+                               "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)),
+                               "kind": "oracle",
+                               "sample": f"batch 0, kv head 0 and its {gsz} query heads, fp64 "
+                                         f"numpy, {dt:.2f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def cpu_baseline(wl: W.Workload, inp, target_rows: int):
     """The fp64 oracle on a bounded row sample of the same workload."""
     from oracle import attention_rows
@@ -143,6 +217,8 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's choice")
     ap.add_argument("--cpu-rows", type=int, default=262144,
                     help="rows of the CPU-oracle sample (0 = skip the CPU leg)")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
+                    help="fwd: the forward pass (default); bwd: the backward pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run a plain device-to-device copy of MIB "
                          "MiB (reference for scaling HBM byte counters)")
@@ -171,6 +247,9 @@ def main():
     inp = W.make_inputs(wl)
     q, k, v = device_inputs(inp, torch)
     bmask = W.device_mask(inp, torch, "cuda")
+    if args.which == "bwd":
+        bench_backward(args, wl, inp, q, k, v, torch, fa)
+        return
     o = torch.empty_like(q)          # q's layout (token-major workloads: token-major o)
     lse = torch.empty((wl.B, wl.H, wl.Sq), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream()

@@ -203,6 +203,21 @@ def make_block_mask(wl: Workload, rng: np.random.Generator) -> np.ndarray:
     return (base[None, None] | extra).astype(np.uint8)
 
 
+def make_grad_output(inp: Inputs):
+    """Seeded gradient of the loss with respect to O (same shape as Q), for
+    the backward pass: N(0, 1) drawn in float32 from a sixth stream of the
+    workload's seed, rounded like the inputs for 16-bit workloads. Returns
+    (values as float32, bits or None)."""
+    wl = inp.wl
+    rng = np.random.default_rng(np.random.SeedSequence(wl.seed).spawn(6)[5])
+    g = rng.standard_normal((wl.B, wl.H, wl.Sq, wl.D), dtype=np.float32)
+    if wl.dtype in ROUNDING:
+        to_bits, to_f32 = ROUNDING[wl.dtype]
+        bits = to_bits(g)
+        return to_f32(bits), bits
+    return g, None
+
+
 def device_mask(inp: Inputs, torch, device="cuda"):
     """The workload's block mask on `device`, or None."""
     if inp.block_mask is None:
