@@ -346,6 +346,23 @@ struct MaskArg {
   int batch, heads;
 };
 
+// O's rows must be disjoint: with its (batch, head, row) axes sorted by stride
+// (axes of extent 1 left out), every stride must reach past the extent the
+// smaller axes span (a row spans D elements).
+bool output_rows_disjoint(const long long st[3], int B, int H, int Sq, int D) {
+  std::array<std::pair<long long, long long>, 3> ax = {
+      std::make_pair(st[2], (long long)Sq), std::make_pair(st[1], (long long)H),
+      std::make_pair(st[0], (long long)B)};
+  std::sort(ax.begin(), ax.end());
+  long long span = D;   // elements covered by the axes already placed
+  for (const auto& a : ax) {
+    if (a.second == 1) continue;
+    if (a.first < span) return false;
+    span = a.first * (a.second - 1) + span;
+  }
+  return true;
+}
+
 int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
             int HKV, int Sq, int Sk, int D, const long long* q_strides,
             const long long* k_strides, const long long* v_strides, const long long* o_strides,
@@ -371,6 +388,7 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
       (st = check_strides(vs, B, HKV, Sk, D, esz, true)) != FA_OK ||
       (st = check_strides(os, B, H, Sq, D, esz, false)) != FA_OK)
     return st;
+  if (!output_rows_disjoint(os, B, H, Sq, D)) return FA_ERR_STRIDE;
   // The kernels' contiguous form whenever the strides are those of contiguous tensors.
   long long cq[3], ck[3];
   tensor_strides(nullptr, H, Sq, D, cq);

@@ -121,9 +121,10 @@ int fa_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE,
  *
  * Stride rules (else FA_ERR_STRIDE): every stride >= 0 and a multiple of 16
  * bytes; every row stride >= D; the K and V row strides are multiples of D
- * and below 2^31 / 64 bytes. Batch or head strides of 0 (broadcast inputs)
- * are allowed for Q, K and V; O's rows must not overlap one another or the
- * inputs (not checked). When all four tensors have contiguous strides the
+ * and below 2^31 / 64 bytes; O's rows are pairwise disjoint (checked: its
+ * axes sorted by stride, each stride reaches past the extent of the smaller
+ * ones). Batch or head strides of 0 (broadcast inputs) are allowed for Q, K
+ * and V. O must not overlap the inputs (not checked). When all four tensors have contiguous strides the
  * call runs exactly as fa_fwd_ex. Same arguments, ownership and other errors
  * as fa_fwd_ex.
  */

@@ -140,6 +140,9 @@ def call_strided(qs=None, ks=None, vs=None, os_=None, **over):
     dict(qs=(8192, 128, 64)),              # row stride < D: rows overlap
     dict(os_=(8192, 3, 512)),              # head stride not a multiple of 16 bytes (bf16)
     dict(ks=(0, 128, 128 * (1 << 24))),    # key tile would span >= 2^31 bytes
+    dict(os_=(8192, 0, 128)),              # O heads alias one another
+    dict(os_=(0, 8192, 128), B=2),         # O batch entries alias
+    dict(os_=(64 * 128, 128, 256)),        # O heads interleave with rows (head 1 row 0 = head 0 row 0.5)
 ])
 def test_strided_rule_errors(kw):
     assert call_strided(**kw) == 11
@@ -208,3 +211,17 @@ def test_bwd_null_and_misaligned(which):
 ])
 def test_bwd_argument_errors(over, code):
     assert call_bwd(**over) == code
+
+
+@pytest.mark.parametrize("os_", [
+    (4 * 64 * 128, 64 * 128, 128),         # contiguous [B, H, S, D]
+    (64 * 4 * 128, 128, 4 * 128),          # token-major [B, S, H, D]
+    (0, 64 * 128, 128),                    # B = 1: a zero batch stride is harmless
+    (8 * 64 * 128, 2 * 64 * 128, 128),     # padded head stride
+])
+@pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                    reason="valid arguments would reach a kernel launch on fake pointers")
+def test_disjoint_output_strides_pass_the_stride_checks(os_):
+    # valid O strides get past every stride rule; with no GPU present the call
+    # then stops at the device query (FA_ERR_HIP), never FA_ERR_STRIDE
+    assert call_strided(os_=os_, Sq=64, Sk=64) == 8
