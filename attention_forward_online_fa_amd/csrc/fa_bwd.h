@@ -19,6 +19,12 @@ struct BwdParams {
   int B, H, HKV, Sq, Sk;
   float scale;
   int causal, window;
+  // MFMA dQ kernel (16-bit inputs): |scale| log2(e) (at least 1e-30, so a
+  // masked score of -inf stays -inf) with Q negated when scale < 0, and the
+  // number of 128-row query tiles
+  float sl_abs;
+  int neg_q;
+  int n_qblk;
 };
 
 // Queue the dQ kernel (which also writes Dws) and then the dK/dV kernel.

@@ -23,6 +23,7 @@
 #include <stdint.h>
 
 #include "fa_bwd.h"
+#include "fa_tile.h"
 
 namespace fa {
 
@@ -217,11 +218,187 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------------ MFMA dQ
+// dQ for 16-bit inputs at D <= 128 on MFMA, in the forward kernel's layout:
+// a workgroup is 4 wavefronts x 32 query rows, K and V tiles of 32 keys are
+// double-buffered in LDS by the buffer unit, and a lane owns one query row.
+//   S^T  = K Q^T          (A: K rows from LDS, B: Q rows in registers)
+//   dP^T = V dO^T         (A: V rows from LDS, B: dO rows in registers)
+//   P = exp2(S^T |scale| log2 e - LSE log2 e),  dS^T = P (dP^T - D_i)
+//   dQ^T += K^T dS^T      (A: K^T by transposed reads of the K tile, B: dS^T
+//                          packed to the input type as the forward packs P)
+// Both tiles use the K swizzle (their rows are read as MFMA A operands); the
+// K^T reads then take each lane's two key rows with their own swizzle.
+// D_i = dO_i . O_i is formed here and written for the dK/dV kernel.
+template <typename E, int D>
+__global__ __launch_bounds__(kBwdThreads, 2)
+void bwd_dq_mfma_kernel(BwdParams p) {
+  constexpr int BN = 32;
+  using T = Bf16Tile<D, BN>;
+  using X = Elt<E>;
+  typedef typename X::x8 e16x8;
+  static_assert(D <= 128, "one offset register per K operand step");
+  __shared__ __attribute__((aligned(1024))) char kbuf0[T::TILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[T::TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[T::TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[T::TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int units = p.B * p.H;
+  const int qblk = p.n_qblk - 1 - (int)(blockIdx.x / units);   // heaviest query tiles first
+  const int u = blockIdx.x % units;
+  const int h = u % p.H, b = u / p.H;
+  const int hkv = h / (p.H / p.HKV);
+  const int q0 = qblk * 128, qw = q0 + wave * 32, i = qw + l32;
+  const bool row_ok = i < p.Sq;
+  const long row = ((long)b * p.H + h) * p.Sq + i;
+
+  const E* Qh = (const E*)p.Q + ((long)b * p.H + h) * p.Sq * D;
+  const E* Oh = (const E*)p.O + ((long)b * p.H + h) * p.Sq * D;
+  const E* dOh = (const E*)p.dO + ((long)b * p.H + h) * p.Sq * D;
+  const E* Kp = (const E*)p.K + ((long)b * p.HKV + hkv) * p.Sk * D;
+  const E* Vp = (const E*)p.V + ((long)b * p.HKV + hkv) * p.Sk * D;
+
+  // key range of the block
+  int lo = 0, hi = p.Sk;
+  if (p.causal) hi = min(hi, min(q0 + 128, p.Sq));
+  if (p.window > 0) lo = max(0, q0 - p.window + 1);
+  const int t0 = (lo / BN) * BN;
+  const int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
+
+  const int voff = T::dma_off(64 * wave * T::NIW + lane, false);
+  auto issue = [&](int kt, char* kd, char* vd) {
+    const unsigned bytes = (unsigned)min((long)(p.Sk - kt) * T::ROW, 0x7fffffffL);
+    const E* kb = Kp + (size_t)kt * D;
+    const E* vb = Vp + (size_t)kt * D;
+#pragma unroll
+    for (int k = 0; k < T::NIW; ++k) {
+      const int off = (wave * T::NIW + k) * 1024;
+      dma16(kb, bytes, voff ^ T::dma_xor(k, false), kd + off);
+      dma16(vb, bytes, voff ^ T::dma_xor(k, false), vd + off);
+    }
+  };
+  if (n_tiles > 0) issue(t0, kbuf0, vbuf0);
+
+  // Q and dO rows as B operands (k-slot (g, e) of step t is dim 16t + 8g + e);
+  // D_i from the same dims of O, summed over the two lane halves.
+  e16x8 qf[T::DC], dof[T::DC];
+  float dd = 0.f;
+#pragma unroll
+  for (int t = 0; t < T::DC; ++t) {
+    if (row_ok) {
+      qf[t] = *(const e16x8*)(Qh + (size_t)i * D + 16 * t + 8 * g);
+      dof[t] = *(const e16x8*)(dOh + (size_t)i * D + 16 * t + 8 * g);
+      const e16x8 ov = *(const e16x8*)(Oh + (size_t)i * D + 16 * t + 8 * g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dd = fmaf((float)dof[t][e], (float)ov[e], dd);
+    } else {
+      qf[t] = e16x8{};
+      dof[t] = e16x8{};
+    }
+    if (p.neg_q) {   // negative scale: -Q and |scale| (exact sign flips)
+      u32x4 bits = __builtin_bit_cast(u32x4, qf[t]) ^ 0x80008000u;
+      qf[t] = __builtin_bit_cast(e16x8, bits);
+    }
+  }
+  const float Di = dd + __shfl_xor(dd, 32);
+  // base-2 LSE; +inf for rows past Sq or with no visible key, so that P = 0
+  float L2 = row_ok ? p.LSE[row] * 1.4426950408889634f : INFINITY;
+  if (L2 == -INFINITY) L2 = INFINITY;
+  const float sl = p.sl_abs;
+
+  // operand offsets (tile-relative): K/V rows for S^T and dP^T, K^T for dQ^T
+  const int krow = perm_row(l32);
+  int koff[T::DC];
+#pragma unroll
+  for (int t = 0; t < T::DC; ++t) koff[t] = krow * T::ROW + (((2 * t + g) ^ T::swz_k(krow)) << 4);
+  const int blk = lane >> 4, li = lane & 15;
+  const int vrow = 8 * g + (li >> 2);
+  int kt0[T::DB], kt1[T::DB];
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db) {
+    const int chunk = 4 * db + 2 * (blk & 1) + ((li & 3) >> 1);
+    kt0[db] = vrow * T::ROW + ((chunk ^ T::swz_k(vrow)) << 4) + 8 * (li & 1);
+    kt1[db] = (vrow + 4) * T::ROW + ((chunk ^ T::swz_k(vrow + 4)) << 4) + 8 * (li & 1);
+  }
+
+  f32x16 dq[T::DB];
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db) dq[db] = f32x16{};
+
+  auto step = [&](int t, const char* Kc, const char* Vc, char* Kn, char* Vn) __attribute__((always_inline)) {
+    const int kt = t0 + t * BN;
+    wait_dma_and_sync();
+    if (t + 1 < n_tiles) issue(kt + BN, Kn, Vn);
+    if (qw >= p.Sq || (p.causal && kt > qw + 31) ||
+        (p.window > 0 && kt + BN - 1 < qw - p.window + 1))
+      return;
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int t2 = 0; t2 < T::DC; ++t2) {
+      const e16x8 ak = *(const e16x8*)(Kc + koff[t2]);
+      const e16x8 av = *(const e16x8*)(Vc + koff[t2]);
+      s = X::mfma(ak, qf[t2], s);
+      dp = X::mfma(av, dof[t2], dp);
+    }
+    // element v holds key kt + 8g + c, c = 16 (v / 8) + v % 8
+    const bool edge = (kt + BN > p.Sk) || (p.causal && kt + BN - 1 > qw) ||
+                      (p.window > 0 && kt < qw + 31 - p.window + 1);
+    typename X::x8 dsf[2];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float x = fmaf(s[v], sl, -L2);
+      if (edge) {
+        const int j = kt + 8 * g + 16 * (v >> 3) + (v & 7);
+        const bool vis = j < p.Sk && (!p.causal || j <= i) && (p.window <= 0 || j > i - p.window);
+        x = vis ? x : -INFINITY;
+      }
+      const float pr = __builtin_amdgcn_exp2f(x);
+      dsf[v >> 3][v & 7] = (E)(pr * (dp[v] - Di));
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      e16x8 a[T::DB];
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db)
+        a[db] = read_v_pair<e16x8>(Kc, kt0[db] + 16 * c * T::ROW, kt1[db] + 16 * c * T::ROW);
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) dq[db] = X::mfma(a[db], dsf[c], dq[db]);
+    }
+  };
+
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, kbuf0, vbuf0, kbuf1, vbuf1);
+    if (t + 1 < n_tiles) step(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
+  }
+
+  // lane holds dims 32 db + 8 a + 4 g + (0..3) of row i
+  if (row_ok) {
+    float* dst = p.dQ + row * D;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 v4 = {dq[db][4 * a] * p.scale, dq[db][4 * a + 1] * p.scale,
+                          dq[db][4 * a + 2] * p.scale, dq[db][4 * a + 3] * p.scale};
+        *(f32x4*)(dst + 32 * db + 8 * a + 4 * g) = v4;
+      }
+    if (g == 0) p.Dws[row] = Di;
+  }
+}
+
 template <typename E, int D>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const long rows = (long)p.B * p.H * p.Sq, krows = (long)p.B * p.HKV * p.Sk;
-  hipLaunchKernelGGL((bwd_dq_kernel<E, D>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
-                     dim3(kBwdThreads), 0, stream, p);
+  if constexpr (sizeof(E) == 2 && D <= 128) {
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D>), dim3((unsigned)((long)p.B * p.H * p.n_qblk)),
+                       dim3(kBwdThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+                       dim3(kBwdThreads), 0, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>), dim3((unsigned)((krows + kRowsPerBlock - 1) / kRowsPerBlock)),

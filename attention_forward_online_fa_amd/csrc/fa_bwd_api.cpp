@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 
 #include "fa_bwd.h"
@@ -59,6 +60,11 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
   p.scale = scale;
   p.causal = causal;
   p.window = window;
+  p.neg_q = scale < 0.f ? 1 : 0;
+  const double mag = std::fabs((double)scale) * 1.4426950408889634;
+  p.sl_abs = mag > 1e-30 ? (float)mag : 1e-30f;
+  p.n_qblk = (Sq + 127) / 128;
+  if ((double)B * H * p.n_qblk > 2147483647.0) return FA_ERR_SHAPE;
   // D_i workspace, stream-ordered from the device's default memory pool
   void* ws = nullptr;
   if (hipMallocAsync(&ws, (size_t)B * H * Sq * sizeof(float), stream) != hipSuccess)
