@@ -389,6 +389,195 @@ void bwd_dq_mfma_kernel(BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------- MFMA dK, dV
+// dK and dV for 16-bit inputs at D <= 128 on MFMA, the mirror of the dQ
+// kernel: a workgroup owns 128 keys (4 wavefronts x 32, a lane owns one key)
+// with K and V rows in registers, and walks 32-row tiles of Q and dO (and the
+// tile rows' base-2 LSE and D_i) through LDS, over every query head of the kv
+// head, double-buffered by the buffer unit.
+//   S  = Q K^T, dP = dO V^T      (A: Q / dO rows from LDS, B: K / V rows)
+//   P  = exp2(S |scale| log2 e - LSE log2 e),  dS = P (dP - D)
+//   dV^T += dO^T P,  dK^T += Q^T dS   (A: transposed reads of the dO / Q
+//                                      tiles, B: P / dS packed to the input type)
+template <typename E, int D>
+__global__ __launch_bounds__(kBwdThreads, 1)
+void bwd_dkdv_mfma_kernel(BwdParams p) {
+  constexpr int BM = 32;   // query rows per tile
+  using T = Bf16Tile<D, BM>;
+  using X = Elt<E>;
+  typedef typename X::x8 e16x8;
+  static_assert(D <= 128, "one offset register per operand step");
+  __shared__ __attribute__((aligned(1024))) char qbuf0[T::TILE];
+  __shared__ __attribute__((aligned(1024))) char qbuf1[T::TILE];
+  __shared__ __attribute__((aligned(1024))) char obuf0[T::TILE];
+  __shared__ __attribute__((aligned(1024))) char obuf1[T::TILE];
+  __shared__ __attribute__((aligned(16))) float lbuf0[2 * BM];   // [0, 32): base-2 LSE, [32, 64): D
+  __shared__ __attribute__((aligned(16))) float lbuf1[2 * BM];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int units = p.B * p.HKV;
+  const int kblk = blockIdx.x / units;   // ascending: under a causal mask the first keys see most rows
+  const int u = blockIdx.x % units;
+  const int hkv = u % p.HKV, b = u / p.HKV;
+  const int gh = p.H / p.HKV;
+  const int k0 = kblk * 128, kw = k0 + wave * 32, j = kw + l32;
+  const bool key_ok = j < p.Sk;
+  const long krow = ((long)b * p.HKV + hkv) * p.Sk + j;
+
+  // query rows [r_lo, r_hi) that see some key of the block
+  int r_lo = 0, r_hi = p.Sq;
+  if (p.causal) r_lo = min(k0, p.Sq);
+  if (p.window > 0) r_hi = min(p.Sq, k0 + 128 + p.window - 1);
+  const int rt0 = (r_lo / BM) * BM;
+  const int n_rt = r_hi > r_lo ? (r_hi - rt0 + BM - 1) / BM : 0;
+  const int n_tiles = n_rt * gh;   // (query head, row tile) pairs
+
+  const int voff = T::dma_off(64 * wave * T::NIW + lane, false);
+  auto issue = [&](int t, char* qd, char* od, float* ld) {
+    const int h = hkv * gh + t / n_rt, r0 = rt0 + (t % n_rt) * BM;
+    const long base = ((long)b * p.H + h) * p.Sq;
+    // the tile rows' LSE (lanes 0..31) and D (lanes 32..63), loaded first
+    float x = 0.f;
+    if (wave == 0) {
+      const int r = r0 + l32;
+      if (g == 0) {
+        x = r < p.Sq ? p.LSE[base + r] * 1.4426950408889634f : INFINITY;
+        if (x == -INFINITY) x = INFINITY;   // a row with no visible key: P = 0
+      } else {
+        x = r < p.Sq ? p.Dws[base + r] : 0.f;
+      }
+    }
+    const unsigned bytes = (unsigned)min((long)(p.Sq - r0) * T::ROW, 0x7fffffffL);
+    const E* qb = (const E*)p.Q + (base + r0) * D;
+    const E* ob = (const E*)p.dO + (base + r0) * D;
+#pragma unroll
+    for (int k = 0; k < T::NIW; ++k) {
+      const int off = (wave * T::NIW + k) * 1024;
+      dma16(qb, bytes, voff ^ T::dma_xor(k, false), qd + off);
+      dma16(ob, bytes, voff ^ T::dma_xor(k, false), od + off);
+    }
+    if (wave == 0) ld[lane] = x;
+  };
+  if (n_tiles > 0) issue(0, qbuf0, obuf0, lbuf0);
+
+  // K and V rows as B operands (k-slot (g, e) of step t is dim 16t + 8g + e)
+  e16x8 kf[T::DC], vf[T::DC];
+#pragma unroll
+  for (int t = 0; t < T::DC; ++t) {
+    if (key_ok) {
+      kf[t] = *(const e16x8*)((const E*)p.K + krow * D + 16 * t + 8 * g);
+      vf[t] = *(const e16x8*)((const E*)p.V + krow * D + 16 * t + 8 * g);
+    } else {
+      kf[t] = e16x8{};
+      vf[t] = e16x8{};
+    }
+    if (p.neg_q) {   // negative scale: -K and |scale| (exact sign flips)
+      u32x4 bits = __builtin_bit_cast(u32x4, kf[t]) ^ 0x80008000u;
+      kf[t] = __builtin_bit_cast(e16x8, bits);
+    }
+  }
+  const float sl = p.sl_abs;
+
+  // operand offsets (tile-relative): Q / dO rows for S and dP, their
+  // transposes for dK^T and dV^T
+  const int qrow = perm_row(l32);
+  int roff[T::DC];
+#pragma unroll
+  for (int t = 0; t < T::DC; ++t) roff[t] = qrow * T::ROW + (((2 * t + g) ^ T::swz_k(qrow)) << 4);
+  const int blk = lane >> 4, li = lane & 15;
+  const int vrow = 8 * g + (li >> 2);
+  int tr0[T::DB], tr1[T::DB];
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db) {
+    const int chunk = 4 * db + 2 * (blk & 1) + ((li & 3) >> 1);
+    tr0[db] = vrow * T::ROW + ((chunk ^ T::swz_k(vrow)) << 4) + 8 * (li & 1);
+    tr1[db] = (vrow + 4) * T::ROW + ((chunk ^ T::swz_k(vrow + 4)) << 4) + 8 * (li & 1);
+  }
+
+  f32x16 dk[T::DB], dv[T::DB];
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db) dk[db] = dv[db] = f32x16{};
+
+  auto step = [&](int t, const char* Qc, const char* Oc, const float* Lc, char* Qn, char* On,
+                  float* Ln) __attribute__((always_inline)) {
+    const int r0 = rt0 + (t % n_rt) * BM;
+    wait_dma_and_sync();
+    if (t + 1 < n_tiles) issue(t + 1, Qn, On, Ln);
+    if (kw >= p.Sk || (p.causal && r0 + BM - 1 < kw) ||
+        (p.window > 0 && r0 > kw + 31 + p.window - 1))
+      return;
+    f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int t2 = 0; t2 < T::DC; ++t2) {
+      const e16x8 aq = *(const e16x8*)(Qc + roff[t2]);
+      const e16x8 ao = *(const e16x8*)(Oc + roff[t2]);
+      sc = X::mfma(aq, kf[t2], sc);
+      dp = X::mfma(ao, vf[t2], dp);
+    }
+    // element v holds query row r0 + 8g + c, c = 16 (v / 8) + v % 8
+    f32x4 lq[4], dq4[4];
+#pragma unroll
+    for (int h4 = 0; h4 < 4; ++h4) {
+      const int rr = 16 * (h4 >> 1) + 8 * g + 4 * (h4 & 1);
+      lq[h4] = *(const f32x4*)(Lc + rr);
+      dq4[h4] = *(const f32x4*)(Lc + BM + rr);
+    }
+    const bool edge = (kw + 31 >= p.Sk) || (p.causal && r0 < kw + 31) ||
+                      (p.window > 0 && r0 + BM - 1 > kw + p.window - 1);
+    typename X::x8 pp[2], ds[2];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float l2 = lq[v >> 2][v & 3], dd = dq4[v >> 2][v & 3];
+      float x = fmaf(sc[v], sl, -l2);
+      if (edge) {
+        const int r = r0 + 8 * g + 16 * (v >> 3) + (v & 7);
+        const bool vis = j < p.Sk && (!p.causal || j <= r) && (p.window <= 0 || j > r - p.window);
+        x = vis ? x : -INFINITY;
+      }
+      const float pr = __builtin_amdgcn_exp2f(x);
+      pp[v >> 3][v & 7] = (E)pr;
+      ds[v >> 3][v & 7] = (E)(pr * (dp[v] - dd));
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      e16x8 ao[T::DB], aq[T::DB];
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        ao[db] = read_v_pair<e16x8>(Oc, tr0[db] + 16 * c * T::ROW, tr1[db] + 16 * c * T::ROW);
+        aq[db] = read_v_pair<e16x8>(Qc, tr0[db] + 16 * c * T::ROW, tr1[db] + 16 * c * T::ROW);
+      }
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        dv[db] = X::mfma(ao[db], pp[c], dv[db]);
+        dk[db] = X::mfma(aq[db], ds[c], dk[db]);
+      }
+    }
+  };
+
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, qbuf0, obuf0, lbuf0, qbuf1, obuf1, lbuf1);
+    if (t + 1 < n_tiles) step(t + 1, qbuf1, obuf1, lbuf1, qbuf0, obuf0, lbuf0);
+  }
+
+  // lane holds dims 32 db + 8 a + 4 g + (0..3) of key j
+  if (key_ok) {
+    float* odk = p.dK + krow * D;
+    float* odv = p.dV + krow * D;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 k4 = {dk[db][4 * a] * p.scale, dk[db][4 * a + 1] * p.scale,
+                          dk[db][4 * a + 2] * p.scale, dk[db][4 * a + 3] * p.scale};
+        const f32x4 v4 = {dv[db][4 * a], dv[db][4 * a + 1], dv[db][4 * a + 2], dv[db][4 * a + 3]};
+        *(f32x4*)(odk + 32 * db + 8 * a + 4 * g) = k4;
+        *(f32x4*)(odv + 32 * db + 8 * a + 4 * g) = v4;
+      }
+  }
+}
+
 template <typename E, int D>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const long rows = (long)p.B * p.H * p.Sq, krows = (long)p.B * p.HKV * p.Sk;
@@ -401,8 +590,14 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>), dim3((unsigned)((krows + kRowsPerBlock - 1) / kRowsPerBlock)),
-                     dim3(kBwdThreads), 0, stream, p);
+  if constexpr (sizeof(E) == 2 && D <= 128) {
+    const long kblocks = (long)p.B * p.HKV * ((p.Sk + 127) / 128);
+    hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D>), dim3((unsigned)kblocks), dim3(kBwdThreads), 0,
+                       stream, p);
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>), dim3((unsigned)((krows + kRowsPerBlock - 1) / kRowsPerBlock)),
+                       dim3(kBwdThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

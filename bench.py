@@ -140,6 +140,12 @@ def bench_backward(args, wl, inp, q, k, v, torch, fa):
     ev_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     flops = 2.5 * counted_flops(wl)          # 10 D per visible pair
+    # 16-bit inputs at D <= 128 run the MFMA backward kernels; the rest the
+    # per-row VALU kernels
+    if wl.dtype != "f32" and wl.D <= 128:
+        bound, peak = "mfma", PEAK_TFLOPS[wl.dtype]
+    else:
+        bound, peak = "alu", PEAK_VALU_F32
     rec = {
         "metric": "attention bwd TFLOP/s (unmasked FLOPs, 10*D per visible pair), 1xMI355X",
         "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
@@ -149,9 +155,9 @@ def bench_backward(args, wl, inp, q, k, v, torch, fa):
         "config": {"workload": wl.name, "pass": "bwd", "B": wl.B, "H": wl.H, "HKV": wl.HKV,
                    "Sq": wl.Sq, "Sk": wl.Sk, "D": wl.D, "causal": wl.causal,
                    "window": wl.window, "counted_flops": flops, "parallelism": "single GPU"},
-        "roofline": {"bound": "alu", "achieved": round(flops / (ev_ms * 1e-3) / 1e12, 3),
-                     "peak": PEAK_VALU_F32, "unit": "TFLOP/s",
-                     "frac": round(flops / (ev_ms * 1e-3) / 1e12 / PEAK_VALU_F32, 4),
+        "roofline": {"bound": bound, "achieved": round(flops / (ev_ms * 1e-3) / 1e12, 3),
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(flops / (ev_ms * 1e-3) / 1e12 / peak, 4),
                      "traffic": None, "kernel_ms": round(ev_ms, 5)},
     }
     if args.cpu_rows > 0:
