@@ -4,10 +4,11 @@ forward pass, as a caller would use them.
 
 Tolerance (absolute, scaled by the largest reference magnitude r = max(1,
 max|ref|) of each gradient): fp32 inputs 1e-4 r; bf16 3e-2 r and fp16 1e-2 r.
-The 16-bit bounds come from the forward output: the backward reads O rounded
-to the input type, so D_i = dO_i . O_i carries a relative error up to 2^-9
-(bf16) or 2^-11 (fp16) of sum|dO||O|, and every dS_ij = P_ij (dP_ij - D_i)
-inherits it; the inputs themselves are exact on both sides."""
+The 16-bit bounds come from the forward output and the MFMA operands: the
+backward reads O rounded to the input type, so D_i = dO_i . O_i carries a
+relative error up to 2^-9 (bf16) or 2^-11 (fp16) of sum|dO||O|, every dS_ij =
+P_ij (dP_ij - D_i) inherits it, and P and dS are rounded once more to the
+input type as MFMA operands; the inputs themselves are exact on both sides."""
 import numpy as np
 import pytest
 
@@ -59,6 +60,15 @@ CASES = [
 ]
 
 
+# several query tiles and key blocks for the MFMA kernels (16-bit, D <= 128)
+CASES += [
+    ("bf16", 1, 8, 2, 1024, 1024, 128, 1, 0),
+    ("bf16", 1, 4, 4, 700, 1100, 64, 0, 0),
+    ("f16", 1, 4, 1, 1000, 1000, 128, 1, 300),
+    ("bf16", 2, 2, 1, 900, 600, 128, 0, 250),
+]
+
+
 @pytest.mark.parametrize("case", CASES, ids=["-".join(map(str, c)) for c in CASES])
 def test_backward_matches_oracle(case):
     wl = wl_small(*case, seed=sum(case[1:]) + 3)
@@ -71,7 +81,7 @@ def test_backward_matches_oracle(case):
         assert err <= TOL[wl.dtype] * scale_r, f"{name}: {err:.3e}"
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_backward_empty_rows_and_unseen_keys(dtype):
     # Sq=8, Sk=40, causal, window 1: rows 0..7 see only their own key; keys
     # 8..39 are seen by no row (dK = dV = 0 there); no row is empty.
