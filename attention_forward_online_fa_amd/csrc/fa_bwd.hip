@@ -227,8 +227,10 @@ void bwd_dkdv_kernel(BwdParams p) {
 //   P = exp2(S^T |scale| log2 e - LSE log2 e),  dS^T = P (dP^T - D_i)
 //   dQ^T += K^T dS^T      (A: K^T by transposed reads of the K tile, B: dS^T
 //                          packed to the input type as the forward packs P)
-// Both tiles use the K swizzle (their rows are read as MFMA A operands); the
-// K^T reads then take each lane's two key rows with their own swizzle.
+// Row reads and transposed reads of one tile want different LDS swizzles
+// (with either one alone, half the LDS cycles of these kernels went to bank
+// conflicts), so the K tile is copied twice: with the K swizzle for S^T and
+// with the V swizzle for K^T; V is read by rows only.
 // D_i = dO_i . O_i is formed here and written for the dK/dV kernel.
 template <typename E, int D>
 __global__ __launch_bounds__(kBwdThreads, 2)
@@ -240,6 +242,8 @@ void bwd_dq_mfma_kernel(BwdParams p) {
   static_assert(D <= 128, "one offset register per K operand step");
   __shared__ __attribute__((aligned(1024))) char kbuf0[T::TILE];
   __shared__ __attribute__((aligned(1024))) char kbuf1[T::TILE];
+  __shared__ __attribute__((aligned(1024))) char ktbuf0[T::TILE];   // K again, V swizzle
+  __shared__ __attribute__((aligned(1024))) char ktbuf1[T::TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf0[T::TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf1[T::TILE];
 
@@ -269,7 +273,8 @@ void bwd_dq_mfma_kernel(BwdParams p) {
   const int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
 
   const int voff = T::dma_off(64 * wave * T::NIW + lane, false);
-  auto issue = [&](int kt, char* kd, char* vd) {
+  const int voff_t = T::dma_off(64 * wave * T::NIW + lane, true);
+  auto issue = [&](int kt, char* kd, char* ktd, char* vd) {
     const unsigned bytes = (unsigned)min((long)(p.Sk - kt) * T::ROW, 0x7fffffffL);
     const E* kb = Kp + (size_t)kt * D;
     const E* vb = Vp + (size_t)kt * D;
@@ -277,10 +282,11 @@ void bwd_dq_mfma_kernel(BwdParams p) {
     for (int k = 0; k < T::NIW; ++k) {
       const int off = (wave * T::NIW + k) * 1024;
       dma16(kb, bytes, voff ^ T::dma_xor(k, false), kd + off);
+      dma16(kb, bytes, voff_t ^ T::dma_xor(k, true), ktd + off);
       dma16(vb, bytes, voff ^ T::dma_xor(k, false), vd + off);
     }
   };
-  if (n_tiles > 0) issue(t0, kbuf0, vbuf0);
+  if (n_tiles > 0) issue(t0, kbuf0, ktbuf0, vbuf0);
 
   // Q and dO rows as B operands (k-slot (g, e) of step t is dim 16t + 8g + e);
   // D_i from the same dims of O, summed over the two lane halves.
@@ -314,24 +320,26 @@ void bwd_dq_mfma_kernel(BwdParams p) {
   int koff[T::DC];
 #pragma unroll
   for (int t = 0; t < T::DC; ++t) koff[t] = krow * T::ROW + (((2 * t + g) ^ T::swz_k(krow)) << 4);
+  // transposed reads, as the forward reads V^T (rows vrow and vrow + 4 share
+  // one V swizzle)
   const int blk = lane >> 4, li = lane & 15;
   const int vrow = 8 * g + (li >> 2);
-  int kt0[T::DB], kt1[T::DB];
+  int ktoff[T::DB];
 #pragma unroll
   for (int db = 0; db < T::DB; ++db) {
     const int chunk = 4 * db + 2 * (blk & 1) + ((li & 3) >> 1);
-    kt0[db] = vrow * T::ROW + ((chunk ^ T::swz_k(vrow)) << 4) + 8 * (li & 1);
-    kt1[db] = (vrow + 4) * T::ROW + ((chunk ^ T::swz_k(vrow + 4)) << 4) + 8 * (li & 1);
+    ktoff[db] = vrow * T::ROW + ((chunk ^ T::swz_v(vrow)) << 4) + 8 * (li & 1);
   }
 
   f32x16 dq[T::DB];
 #pragma unroll
   for (int db = 0; db < T::DB; ++db) dq[db] = f32x16{};
 
-  auto step = [&](int t, const char* Kc, const char* Vc, char* Kn, char* Vn) __attribute__((always_inline)) {
+  auto step = [&](int t, const char* Kc, const char* KTc, const char* Vc, char* Kn, char* KTn,
+                  char* Vn) __attribute__((always_inline)) {
     const int kt = t0 + t * BN;
     wait_dma_and_sync();
-    if (t + 1 < n_tiles) issue(kt + BN, Kn, Vn);
+    if (t + 1 < n_tiles) issue(kt + BN, Kn, KTn, Vn);
     if (qw >= p.Sq || (p.causal && kt > qw + 31) ||
         (p.window > 0 && kt + BN - 1 < qw - p.window + 1))
       return;
@@ -362,16 +370,18 @@ void bwd_dq_mfma_kernel(BwdParams p) {
     for (int c = 0; c < 2; ++c) {
       e16x8 a[T::DB];
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db)
-        a[db] = read_v_pair<e16x8>(Kc, kt0[db] + 16 * c * T::ROW, kt1[db] + 16 * c * T::ROW);
+      for (int db = 0; db < T::DB; ++db) {
+        const int o = ktoff[db] + 16 * c * T::ROW;
+        a[db] = read_v_pair<e16x8>(KTc, o, o + 4 * T::ROW);
+      }
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) dq[db] = X::mfma(a[db], dsf[c], dq[db]);
     }
   };
 
   for (int t = 0; t < n_tiles; t += 2) {
-    step(t, kbuf0, vbuf0, kbuf1, vbuf1);
-    if (t + 1 < n_tiles) step(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
+    step(t, kbuf0, ktbuf0, vbuf0, kbuf1, ktbuf1, vbuf1);
+    if (t + 1 < n_tiles) step(t + 1, kbuf1, ktbuf1, vbuf1, kbuf0, ktbuf0, vbuf0);
   }
 
   // lane holds dims 32 db + 8 a + 4 g + (0..3) of row i
@@ -407,10 +417,16 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   using X = Elt<E>;
   typedef typename X::x8 e16x8;
   static_assert(D <= 128, "one offset register per operand step");
+  // Q and dO tiles twice each: K swizzle for the row reads, V swizzle for the
+  // transposed reads (see the dQ kernel)
   __shared__ __attribute__((aligned(1024))) char qbuf0[T::TILE];
   __shared__ __attribute__((aligned(1024))) char qbuf1[T::TILE];
+  __shared__ __attribute__((aligned(1024))) char qtbuf0[T::TILE];
+  __shared__ __attribute__((aligned(1024))) char qtbuf1[T::TILE];
   __shared__ __attribute__((aligned(1024))) char obuf0[T::TILE];
   __shared__ __attribute__((aligned(1024))) char obuf1[T::TILE];
+  __shared__ __attribute__((aligned(1024))) char otbuf0[T::TILE];
+  __shared__ __attribute__((aligned(1024))) char otbuf1[T::TILE];
   __shared__ __attribute__((aligned(16))) float lbuf0[2 * BM];   // [0, 32): base-2 LSE, [32, 64): D
   __shared__ __attribute__((aligned(16))) float lbuf1[2 * BM];
 
@@ -435,7 +451,8 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   const int n_tiles = n_rt * gh;   // (query head, row tile) pairs
 
   const int voff = T::dma_off(64 * wave * T::NIW + lane, false);
-  auto issue = [&](int t, char* qd, char* od, float* ld) {
+  const int voff_t = T::dma_off(64 * wave * T::NIW + lane, true);
+  auto issue = [&](int t, char* qd, char* qtd, char* od, char* otd, float* ld) {
     const int h = hkv * gh + t / n_rt, r0 = rt0 + (t % n_rt) * BM;
     const long base = ((long)b * p.H + h) * p.Sq;
     // the tile rows' LSE (lanes 0..31) and D (lanes 32..63), loaded first
@@ -456,11 +473,13 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
     for (int k = 0; k < T::NIW; ++k) {
       const int off = (wave * T::NIW + k) * 1024;
       dma16(qb, bytes, voff ^ T::dma_xor(k, false), qd + off);
+      dma16(qb, bytes, voff_t ^ T::dma_xor(k, true), qtd + off);
       dma16(ob, bytes, voff ^ T::dma_xor(k, false), od + off);
+      dma16(ob, bytes, voff_t ^ T::dma_xor(k, true), otd + off);
     }
     if (wave == 0) ld[lane] = x;
   };
-  if (n_tiles > 0) issue(0, qbuf0, obuf0, lbuf0);
+  if (n_tiles > 0) issue(0, qbuf0, qtbuf0, obuf0, otbuf0, lbuf0);
 
   // K and V rows as B operands (k-slot (g, e) of step t is dim 16t + 8g + e)
   e16x8 kf[T::DC], vf[T::DC];
@@ -488,23 +507,23 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   for (int t = 0; t < T::DC; ++t) roff[t] = qrow * T::ROW + (((2 * t + g) ^ T::swz_k(qrow)) << 4);
   const int blk = lane >> 4, li = lane & 15;
   const int vrow = 8 * g + (li >> 2);
-  int tr0[T::DB], tr1[T::DB];
+  int troff[T::DB];
 #pragma unroll
   for (int db = 0; db < T::DB; ++db) {
     const int chunk = 4 * db + 2 * (blk & 1) + ((li & 3) >> 1);
-    tr0[db] = vrow * T::ROW + ((chunk ^ T::swz_k(vrow)) << 4) + 8 * (li & 1);
-    tr1[db] = (vrow + 4) * T::ROW + ((chunk ^ T::swz_k(vrow + 4)) << 4) + 8 * (li & 1);
+    troff[db] = vrow * T::ROW + ((chunk ^ T::swz_v(vrow)) << 4) + 8 * (li & 1);
   }
 
   f32x16 dk[T::DB], dv[T::DB];
 #pragma unroll
   for (int db = 0; db < T::DB; ++db) dk[db] = dv[db] = f32x16{};
 
-  auto step = [&](int t, const char* Qc, const char* Oc, const float* Lc, char* Qn, char* On,
+  auto step = [&](int t, const char* Qc, const char* QTc, const char* Oc, const char* OTc,
+                  const float* Lc, char* Qn, char* QTn, char* On, char* OTn,
                   float* Ln) __attribute__((always_inline)) {
     const int r0 = rt0 + (t % n_rt) * BM;
     wait_dma_and_sync();
-    if (t + 1 < n_tiles) issue(t + 1, Qn, On, Ln);
+    if (t + 1 < n_tiles) issue(t + 1, Qn, QTn, On, OTn, Ln);
     if (kw >= p.Sk || (p.causal && r0 + BM - 1 < kw) ||
         (p.window > 0 && r0 > kw + 31 + p.window - 1))
       return;
@@ -545,8 +564,9 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
       e16x8 ao[T::DB], aq[T::DB];
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) {
-        ao[db] = read_v_pair<e16x8>(Oc, tr0[db] + 16 * c * T::ROW, tr1[db] + 16 * c * T::ROW);
-        aq[db] = read_v_pair<e16x8>(Qc, tr0[db] + 16 * c * T::ROW, tr1[db] + 16 * c * T::ROW);
+        const int o = troff[db] + 16 * c * T::ROW;
+        ao[db] = read_v_pair<e16x8>(OTc, o, o + 4 * T::ROW);
+        aq[db] = read_v_pair<e16x8>(QTc, o, o + 4 * T::ROW);
       }
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) {
@@ -557,8 +577,9 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   };
 
   for (int t = 0; t < n_tiles; t += 2) {
-    step(t, qbuf0, obuf0, lbuf0, qbuf1, obuf1, lbuf1);
-    if (t + 1 < n_tiles) step(t + 1, qbuf1, obuf1, lbuf1, qbuf0, obuf0, lbuf0);
+    step(t, qbuf0, qtbuf0, obuf0, otbuf0, lbuf0, qbuf1, qtbuf1, obuf1, otbuf1, lbuf1);
+    if (t + 1 < n_tiles)
+      step(t + 1, qbuf1, qtbuf1, obuf1, otbuf1, lbuf1, qbuf0, qtbuf0, obuf0, otbuf0, lbuf0);
   }
 
   // lane holds dims 32 db + 8 a + 4 g + (0..3) of key j
