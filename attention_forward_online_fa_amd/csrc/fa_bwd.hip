@@ -412,7 +412,10 @@ void bwd_dq_mfma_kernel(BwdParams p) {
 template <typename E, int D>
 __global__ __launch_bounds__(kBwdThreads, 1)
 void bwd_dkdv_mfma_kernel(BwdParams p) {
-  constexpr int BM = 32;   // query rows per tile
+  // 64 query rows per copied tile, worked as two independent 32-row halves
+  // between barriers, so one half's MFMAs can issue under the other's
+  // exponentials (one wavefront per SIMD leaves no other wavefront to do it)
+  constexpr int BM = 64, HM = 32;
   using T = Bf16Tile<D, BM>;
   using X = Elt<E>;
   typedef typename X::x8 e16x8;
@@ -427,7 +430,7 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char obuf1[T::TILE];
   __shared__ __attribute__((aligned(1024))) char otbuf0[T::TILE];
   __shared__ __attribute__((aligned(1024))) char otbuf1[T::TILE];
-  __shared__ __attribute__((aligned(16))) float lbuf0[2 * BM];   // [0, 32): base-2 LSE, [32, 64): D
+  __shared__ __attribute__((aligned(16))) float lbuf0[2 * BM];   // [0, 64): base-2 LSE, [64, 128): D
   __shared__ __attribute__((aligned(16))) float lbuf1[2 * BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -455,16 +458,14 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   auto issue = [&](int t, char* qd, char* qtd, char* od, char* otd, float* ld) {
     const int h = hkv * gh + t / n_rt, r0 = rt0 + (t % n_rt) * BM;
     const long base = ((long)b * p.H + h) * p.Sq;
-    // the tile rows' LSE (lanes 0..31) and D (lanes 32..63), loaded first
+    // the tile rows' base-2 LSE (wave 0) and D (wave 1), loaded first
+    const int r = r0 + lane;
     float x = 0.f;
     if (wave == 0) {
-      const int r = r0 + l32;
-      if (g == 0) {
-        x = r < p.Sq ? p.LSE[base + r] * 1.4426950408889634f : INFINITY;
-        if (x == -INFINITY) x = INFINITY;   // a row with no visible key: P = 0
-      } else {
-        x = r < p.Sq ? p.Dws[base + r] : 0.f;
-      }
+      x = r < p.Sq ? p.LSE[base + r] * 1.4426950408889634f : INFINITY;
+      if (x == -INFINITY) x = INFINITY;   // a row with no visible key: P = 0
+    } else if (wave == 1) {
+      x = r < p.Sq ? p.Dws[base + r] : 0.f;
     }
     const unsigned bytes = (unsigned)min((long)(p.Sq - r0) * T::ROW, 0x7fffffffL);
     const E* qb = (const E*)p.Q + (base + r0) * D;
@@ -477,7 +478,7 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
       dma16(ob, bytes, voff ^ T::dma_xor(k, false), od + off);
       dma16(ob, bytes, voff_t ^ T::dma_xor(k, true), otd + off);
     }
-    if (wave == 0) ld[lane] = x;
+    if (wave < 2) ld[wave * BM + lane] = x;
   };
   if (n_tiles > 0) issue(0, qbuf0, qtbuf0, obuf0, otbuf0, lbuf0);
 
@@ -485,13 +486,8 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   e16x8 kf[T::DC], vf[T::DC];
 #pragma unroll
   for (int t = 0; t < T::DC; ++t) {
-    if (key_ok) {
-      kf[t] = *(const e16x8*)((const E*)p.K + krow * D + 16 * t + 8 * g);
-      vf[t] = *(const e16x8*)((const E*)p.V + krow * D + 16 * t + 8 * g);
-    } else {
-      kf[t] = e16x8{};
-      vf[t] = e16x8{};
-    }
+    kf[t] = key_ok ? *(const e16x8*)((const E*)p.K + krow * D + 16 * t + 8 * g) : e16x8{};
+    vf[t] = key_ok ? *(const e16x8*)((const E*)p.V + krow * D + 16 * t + 8 * g) : e16x8{};
     if (p.neg_q) {   // negative scale: -K and |scale| (exact sign flips)
       u32x4 bits = __builtin_bit_cast(u32x4, kf[t]) ^ 0x80008000u;
       kf[t] = __builtin_bit_cast(e16x8, bits);
@@ -499,8 +495,8 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   }
   const float sl = p.sl_abs;
 
-  // operand offsets (tile-relative): Q / dO rows for S and dP, their
-  // transposes for dK^T and dV^T
+  // operand offsets (tile-relative, first half; the second half is 32 rows on,
+  // where both swizzles repeat): Q / dO rows, and their transposes
   const int qrow = perm_row(l32);
   int roff[T::DC];
 #pragma unroll
@@ -527,53 +523,62 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
     if (kw >= p.Sk || (p.causal && r0 + BM - 1 < kw) ||
         (p.window > 0 && r0 > kw + 31 + p.window - 1))
       return;
-    f32x16 sc = f32x16{}, dp = f32x16{};
+    f32x16 sc[2], dp[2];
 #pragma unroll
-    for (int t2 = 0; t2 < T::DC; ++t2) {
-      const e16x8 aq = *(const e16x8*)(Qc + roff[t2]);
-      const e16x8 ao = *(const e16x8*)(Oc + roff[t2]);
-      sc = X::mfma(aq, kf[t2], sc);
-      dp = X::mfma(ao, vf[t2], dp);
-    }
-    // element v holds query row r0 + 8g + c, c = 16 (v / 8) + v % 8
-    f32x4 lq[4], dq4[4];
+    for (int hh = 0; hh < 2; ++hh) {
+      sc[hh] = f32x16{};
+      dp[hh] = f32x16{};
 #pragma unroll
-    for (int h4 = 0; h4 < 4; ++h4) {
-      const int rr = 16 * (h4 >> 1) + 8 * g + 4 * (h4 & 1);
-      lq[h4] = *(const f32x4*)(Lc + rr);
-      dq4[h4] = *(const f32x4*)(Lc + BM + rr);
+      for (int t2 = 0; t2 < T::DC; ++t2) {
+        const e16x8 aq = *(const e16x8*)(Qc + roff[t2] + hh * HM * T::ROW);
+        const e16x8 ao = *(const e16x8*)(Oc + roff[t2] + hh * HM * T::ROW);
+        sc[hh] = X::mfma(aq, kf[t2], sc[hh]);
+        dp[hh] = X::mfma(ao, vf[t2], dp[hh]);
+      }
     }
     const bool edge = (kw + 31 >= p.Sk) || (p.causal && r0 < kw + 31) ||
                       (p.window > 0 && r0 + BM - 1 > kw + p.window - 1);
-    typename X::x8 pp[2], ds[2];
+    typename X::x8 pp[2][2], ds[2][2];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float l2 = lq[v >> 2][v & 3], dd = dq4[v >> 2][v & 3];
-      float x = fmaf(sc[v], sl, -l2);
-      if (edge) {
-        const int r = r0 + 8 * g + 16 * (v >> 3) + (v & 7);
-        const bool vis = j < p.Sk && (!p.causal || j <= r) && (p.window <= 0 || j > r - p.window);
-        x = vis ? x : -INFINITY;
-      }
-      const float pr = __builtin_amdgcn_exp2f(x);
-      pp[v >> 3][v & 7] = (E)pr;
-      ds[v >> 3][v & 7] = (E)(pr * (dp[v] - dd));
-    }
+    for (int hh = 0; hh < 2; ++hh) {
+      // element v holds query row r0 + 32 hh + 8g + c, c = 16 (v / 8) + v % 8
+      f32x4 lq[4], dq4[4];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      e16x8 ao[T::DB], aq[T::DB];
-#pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-        const int o = troff[db] + 16 * c * T::ROW;
-        ao[db] = read_v_pair<e16x8>(OTc, o, o + 4 * T::ROW);
-        aq[db] = read_v_pair<e16x8>(QTc, o, o + 4 * T::ROW);
+      for (int h4 = 0; h4 < 4; ++h4) {
+        const int rr = HM * hh + 16 * (h4 >> 1) + 8 * g + 4 * (h4 & 1);
+        lq[h4] = *(const f32x4*)(Lc + rr);
+        dq4[h4] = *(const f32x4*)(Lc + BM + rr);
       }
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-        dv[db] = X::mfma(ao[db], pp[c], dv[db]);
-        dk[db] = X::mfma(aq[db], ds[c], dk[db]);
+      for (int v = 0; v < 16; ++v) {
+        float x = fmaf(sc[hh][v], sl, -lq[v >> 2][v & 3]);
+        if (edge) {
+          const int r = r0 + HM * hh + 8 * g + 16 * (v >> 3) + (v & 7);
+          const bool vis = j < p.Sk && (!p.causal || j <= r) && (p.window <= 0 || j > r - p.window);
+          x = vis ? x : -INFINITY;
+        }
+        const float pr = __builtin_amdgcn_exp2f(x);
+        pp[hh][v >> 3][v & 7] = (E)pr;
+        ds[hh][v >> 3][v & 7] = (E)(pr * (dp[hh][v] - dq4[v >> 2][v & 3]));
       }
     }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        e16x8 ao[T::DB], aq[T::DB];
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) {
+          const int o = troff[db] + (HM * hh + 16 * c) * T::ROW;
+          ao[db] = read_v_pair<e16x8>(OTc, o, o + 4 * T::ROW);
+          aq[db] = read_v_pair<e16x8>(QTc, o, o + 4 * T::ROW);
+        }
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) {
+          dv[db] = X::mfma(ao[db], pp[hh][c], dv[db]);
+          dk[db] = X::mfma(aq[db], ds[hh][c], dk[db]);
+        }
+      }
   };
 
   for (int t = 0; t < n_tiles; t += 2) {
