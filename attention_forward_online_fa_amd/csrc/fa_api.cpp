@@ -30,7 +30,7 @@ using SchedKey = std::array<int, 12>;
 struct DeviceState {
   bool init = false;
   int num_cus = 0;
-  int f32_bpc[3][3] = {{-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}};   // fp32 workgroups per CU
+  int f32_bpc[fa::kForms][3] = {{-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}};   // fp32 workgroups per CU
                                                                     // [form][D = 64, 128, 256]
   hipMemPool_t pool = nullptr;
   std::map<SchedKey, Sched> scheds;
@@ -85,7 +85,7 @@ int check_args(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int win
                int dtype) {
   if (B < 1 || H < 1 || HKV < 1 || Sq < 1 || Sk < 1 || D < 1) return FA_ERR_SHAPE;
   if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_DTYPE;
-  if (D != 64 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
+  if (fa::tile_dim(D) == 0) return FA_ERR_HEAD_DIM;
   if (H % HKV != 0) return FA_ERR_GQA;
   if (window < 0 || (causal != 0 && causal != 1)) return FA_ERR_WINDOW;
   const int esz = dtype == FA_F32 ? 4 : 2;
@@ -326,14 +326,18 @@ void tensor_strides(const long long* given, int heads, int S, int D, long long o
 }
 
 // Stride rules: non-negative; every row start 16-byte aligned; rows of one
-// head do not overlap (row stride >= D); for K and V the row stride is a
-// multiple of D (the 16-bit kernel's swizzled LDS copies need it) and a key
-// tile spans less than 2^31 bytes; every element offset fits far inside int64.
+// head do not overlap (row stride >= D); for K and V a key tile spans less
+// than 2^31 bytes and, at D = 64, 128 and 256, the row stride is a multiple
+// of D (the strided form's swizzled LDS copies need it; the padded form of
+// the other head dims addresses each copied chunk in full); every element
+// offset fits far inside int64.
 int check_strides(const long long st[3], int B, int heads, int S, int D, int esz, bool kv) {
   for (int a = 0; a < 3; ++a)
     if (st[a] < 0 || (st[a] * esz) % 16 != 0) return FA_ERR_STRIDE;
   if (st[2] < D) return FA_ERR_STRIDE;
-  if (kv && (st[2] % D != 0 || (double)st[2] * esz * 64 >= 2147483647.0)) return FA_ERR_STRIDE;
+  if (kv && ((fa::tile_dim(D) == D && st[2] % D != 0) ||
+             (double)st[2] * esz * 64 >= 2147483647.0))
+    return FA_ERR_STRIDE;
   const double last = (double)(B - 1) * st[0] + (double)(heads - 1) * st[1] +
                       (double)(S - 1) * st[2] + D;
   if (last * esz > 4.0e18) return FA_ERR_SHAPE;
@@ -395,8 +399,13 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   tensor_strides(nullptr, HKV, Sk, D, ck);
   const bool same_q = std::equal(qs, qs + 3, cq) && std::equal(os, os + 3, cq);
   const bool same_kv = std::equal(ks, ks + 3, ck) && std::equal(vs, vs + 3, ck);
-  const int form = bm ? fa::kFormBlockSparse
-                     : (same_q && same_kv) ? fa::kFormContiguous : fa::kFormStrided;
+  // Head dims 16 .. 96 other than 64 run the padded form on the 64 or 128
+  // tile (any strides; no block mask).
+  const int DT = fa::tile_dim(D);
+  if (DT != D && bm) return FA_ERR_HEAD_DIM;
+  const int form = DT != D ? fa::kFormPadded
+                   : bm    ? fa::kFormBlockSparse
+                   : (same_q && same_kv) ? fa::kFormContiguous : fa::kFormStrided;
 
   DeviceState* ds = nullptr;
   st = device_state(&ds);
@@ -404,8 +413,8 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
 
   const int BM = fa::block_m(dtype, D);
   int ns = 1, split_len = 0, nslot = 0;
-  plan(*ds, num_splits, B, H, Sq, Sk, D, causal, window, dtype, form, &ns, &split_len, &nslot);
-  if (split_len / fa::key_tile(dtype, D) > fa::kMaxListTiles && form == fa::kFormBlockSparse)
+  plan(*ds, num_splits, B, H, Sq, Sk, DT, causal, window, dtype, form, &ns, &split_len, &nslot);
+  if (split_len / fa::key_tile(dtype, DT) > fa::kMaxListTiles && form == fa::kFormBlockSparse)
     return FA_ERR_SHAPE;   // more key tiles than FA_MAX_SPLITS lists can hold
 
   fa::Params p = {};
@@ -419,6 +428,7 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   p.HKV = HKV;
   p.Sq = Sq;
   p.Sk = Sk;
+  p.dv = D;
   p.group = H / HKV;
   p.sl = (float)((double)scale * 1.4426950408889634);
   if (dtype != FA_F32) {
@@ -452,7 +462,7 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
     p.bm_by_kv = (bm->heads == HKV && HKV != H) ? 1 : 0;
   }
   if (nslot > 0) {
-    st = schedule_for(*ds, B, H, HKV, Sq, Sk, D, causal, window, dtype, ns, split_len, nslot,
+    st = schedule_for(*ds, B, H, HKV, Sq, Sk, DT, causal, window, dtype, ns, split_len, nslot,
                       &p.sched);
     if (st != FA_OK) return st;
     p.nslot = nslot;
@@ -467,14 +477,14 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
     st = workspace_pool(dev, *ds, &pool);
     if (st != FA_OK) return st;
     const size_t rows = (size_t)B * H * Sq;
-    const size_t o_bytes = (size_t)ns * rows * D * sizeof(float);
+    const size_t o_bytes = (size_t)ns * rows * DT * sizeof(float);
     const size_t l_bytes = (size_t)ns * rows * sizeof(float);
     if (hipMallocFromPoolAsync(&ws, o_bytes + l_bytes, pool, stream) != hipSuccess)
       return FA_ERR_WORKSPACE;
     p.Opart = static_cast<float*>(ws);
     p.Lpart = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
   }
-  const hipError_t e = fa::launch_forward(p, dtype, D, form, stream);
+  const hipError_t e = fa::launch_forward(p, dtype, DT, form, stream);
   const hipError_t f = ws ? hipFreeAsync(ws, stream) : hipSuccess;
   return (e == hipSuccess && f == hipSuccess) ? FA_OK : FA_ERR_HIP;
 }
@@ -523,7 +533,9 @@ int fa_plan_splits(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int
   st = device_state(&ds);
   if (st != FA_OK) return -st;
   int ns = 1, split_len = 0, nslot = 0;
-  plan(*ds, 0, B, H, Sq, Sk, D, causal, window, dtype, 0, &ns, &split_len, &nslot);
+  const int DT = fa::tile_dim(D);
+  plan(*ds, 0, B, H, Sq, Sk, DT, causal, window, dtype,
+       DT != D ? fa::kFormPadded : fa::kFormContiguous, &ns, &split_len, &nslot);
   return ns;
 }
 
@@ -536,10 +548,11 @@ int fa_schedule_table(int B, int H, int HKV, int Sq, int Sk, int D, int causal, 
   const long items = (long)B * H * FA_MAX_SPLITS * ((Sq + BM - 1) / BM);
   if (items + nslot + 1 > 2147483647L) return -FA_ERR_SHAPE;
   int ns = 1, split_len = 0;
-  resolve_splits(persistent_splits(B, H, Sq, Sk, D, causal, window, dtype, nslot), B, H, Sq, Sk,
-                 D, causal, window, dtype, 1, &ns, &split_len);
+  const int DT = fa::tile_dim(D);
+  resolve_splits(persistent_splits(B, H, Sq, Sk, DT, causal, window, dtype, nslot), B, H, Sq, Sk,
+                 DT, causal, window, dtype, 1, &ns, &split_len);
   const std::vector<int> t =
-      build_schedule(B, H, HKV, Sq, Sk, D, causal, window, dtype, ns, split_len, nslot);
+      build_schedule(B, H, HKV, Sq, Sk, DT, causal, window, dtype, ns, split_len, nslot);
   if (num_splits) *num_splits = ns;
   for (int i = 0; i < (int)t.size() && i < capacity; ++i) table[i] = t[i];
   return (int)t.size();
@@ -551,7 +564,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_NULLPTR: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape: a dimension is < 1 or the problem is too large";
     case FA_ERR_GQA: return "H must be a multiple of HKV";
-    case FA_ERR_HEAD_DIM: return "head dimension D must be 64, 128 or 256";
+    case FA_ERR_HEAD_DIM: return "head dimension D must be 16, 32, 48, 64, 80, 96, 128 or 256 (block masks: 64, 128 or 256)";
     case FA_ERR_DTYPE: return "dtype must be FA_F32 (0), FA_BF16 (1) or FA_F16 (2)";
     case FA_ERR_WINDOW: return "window must be >= 0 and causal 0 or 1";
     case FA_ERR_ALIGN: return "every buffer must be 16-byte aligned";

@@ -607,7 +607,7 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
 template <typename E, int D>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const long rows = (long)p.B * p.H * p.Sq, krows = (long)p.B * p.HKV * p.Sk;
-  if constexpr (sizeof(E) == 2 && D <= 128) {
+  if constexpr (sizeof(E) == 2 && (D == 64 || D == 128)) {
     hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D>), dim3((unsigned)((long)p.B * p.H * p.n_qblk)),
                        dim3(kBwdThreads), 0, stream, p);
   } else {
@@ -616,7 +616,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (sizeof(E) == 2 && D <= 128) {
+  if constexpr (sizeof(E) == 2 && (D == 64 || D == 128)) {
     const long kblocks = (long)p.B * p.HKV * ((p.Sk + 127) / 128);
     hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D>), dim3((unsigned)kblocks), dim3(kBwdThreads), 0,
                        stream, p);
@@ -630,7 +630,12 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
 template <typename E>
 static hipError_t launch_bwd_e(const BwdParams& p, int D, hipStream_t stream) {
   switch (D) {
+    case 16: return launch_bwd_t<E, 16>(p, stream);
+    case 32: return launch_bwd_t<E, 32>(p, stream);
+    case 48: return launch_bwd_t<E, 48>(p, stream);
     case 64: return launch_bwd_t<E, 64>(p, stream);
+    case 80: return launch_bwd_t<E, 80>(p, stream);
+    case 96: return launch_bwd_t<E, 96>(p, stream);
     case 128: return launch_bwd_t<E, 128>(p, stream);
     case 256: return launch_bwd_t<E, 256>(p, stream);
     default: return hipErrorInvalidValue;

@@ -16,7 +16,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_bwd(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int window, int dtype) {
   if (B < 1 || H < 1 || HKV < 1 || Sq < 1 || Sk < 1 || D < 1) return FA_ERR_SHAPE;
   if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_DTYPE;
-  if (D != 64 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
+  if (D != 16 && D != 32 && D != 48 && D != 64 && D != 80 && D != 96 && D != 128 && D != 256)
+    return FA_ERR_HEAD_DIM;
   if (H % HKV != 0) return FA_ERR_GQA;
   if (window < 0 || (causal != 0 && causal != 1)) return FA_ERR_WINDOW;
   // every row index (b H + h) Sq + i and element offset is formed in 64 bits;

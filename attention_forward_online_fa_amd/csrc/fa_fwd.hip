@@ -180,11 +180,15 @@ constexpr float kRowSumLimit = 1.8446744e19f;   // 2^64: row-sum bound that trig
 // softmax and LSE either way. Form kFormStrided: Q, K, V and O are addressed
 // through p.qs .. p.os (batch, head, row strides); otherwise they are
 // contiguous. Form kFormBlockSparse: only the key tiles whose block-mask
-// byte is nonzero are copied and computed.
+// byte is nonzero are copied and computed. Form kFormPadded: strided tensors
+// with rows of p.dv < D elements; the tile's dims from p.dv on are zeros
+// (Q in registers, and K/V chunks whose copy offsets are sent out of the
+// buffer's range), so S is exact and O's padded dims, never stored, are 0.
 template <typename E, int D, int BN, int Form>
 __global__ __launch_bounds__(kThreads, (D == 128 ? 3 : 2))
 void fwd_16b_kernel(Params p) {
-  constexpr bool Strided = Form == kFormStrided, Sparse = Form == kFormBlockSparse;
+  constexpr bool Pad = Form == kFormPadded;
+  constexpr bool Strided = Form == kFormStrided || Pad, Sparse = Form == kFormBlockSparse;
   static_assert(kMaskBlockK % BN == 0, "a key tile lies inside one mask block");
   using T = Bf16Tile<D, BN>;
   using X = Elt<E>;
@@ -245,8 +249,37 @@ void fwd_16b_kernel(Params p) {
   const int P0 = 64 * wave * T::NIW + lane;
   const int voff_k = Strided ? (P0 / T::CPR) * krb + T::chunk_off(P0, false) : T::dma_off(P0, false);
   const int voff_v = Strided ? (P0 / T::CPR) * vrb + T::chunk_off(P0, true) : T::dma_off(P0, true);
+  // Padded rows: each copy instruction's lane offset in full (a row stride
+  // need not be a multiple of the tile row), or one past the buffer's range
+  // for a chunk at or beyond dim p.dv, which then lands in LDS as zeros.
+  constexpr int kOutOfRange = 0x7ffffff0;
+  int pk_off[Pad ? T::NIW : 1], pv_off[Pad ? T::NIW : 1];
+  if constexpr (Pad) {
+#pragma unroll
+    for (int k = 0; k < T::NIW; ++k) {
+      const int P = P0 + 64 * k, row = P / T::CPR;
+      const int ck = (P % T::CPR) ^ T::swz_k(row), cv = (P % T::CPR) ^ T::swz_v(row);
+      pk_off[k] = 8 * ck < p.dv ? row * krb + 16 * ck : kOutOfRange;
+      pv_off[k] = 8 * cv < p.dv ? row * vrb + 16 * cv : kOutOfRange;
+    }
+  }
   auto issue = [&](int kt, char* kdst, char* vdst, bool full = false) {
-    if constexpr (Strided) {
+    if constexpr (Pad) {
+      // valid bytes from the tile's first row: up to the end of row Sk - 1
+      const int rb = 2 * p.dv;
+      const unsigned kbytes = full ? (unsigned)((BN - 1) * krb + rb)
+                                   : (unsigned)min((long long)(p.Sk - kt - 1) * krb + rb, 0x7fffffffLL);
+      const unsigned vbytes = full ? (unsigned)((BN - 1) * vrb + rb)
+                                   : (unsigned)min((long long)(p.Sk - kt - 1) * vrb + rb, 0x7fffffffLL);
+      const E* kb = Kp + (long long)kt * p.ks[2];
+      const E* vb = Vp + (long long)kt * p.vs[2];
+#pragma unroll
+      for (int k = 0; k < T::NIW; ++k) {
+        const int off = (wave * T::NIW + k) * 1024;
+        dma16(kb, kbytes, pk_off[k], kdst + off);
+        dma16(vb, vbytes, pv_off[k], vdst + off);
+      }
+    } else if constexpr (Strided) {
       // valid bytes from the tile's first row: up to the end of row Sk - 1
       const unsigned kbytes = full ? (unsigned)((BN - 1) * krb + T::ROW)
                                    : (unsigned)min((long long)(p.Sk - kt - 1) * krb + T::ROW, 0x7fffffffLL);
@@ -282,7 +315,7 @@ void fwd_16b_kernel(Params p) {
   e16x8 qf[T::DC];
 #pragma unroll
   for (int t = 0; t < T::DC; ++t) {
-    if (i < p.Sq)
+    if (i < p.Sq && (!Pad || 16 * t < p.dv))
       qf[t] = *(const e16x8*)(Qp + (long long)i * qr + 16 * t + 8 * g);
     else
       qf[t] = e16x8{};
@@ -547,6 +580,7 @@ void fwd_16b_kernel(Params p) {
                  for (int db = 0; db < T::DB; ++db)
 #pragma unroll
                    for (int a = 0; a < 4; ++a) {
+                     if (Pad && 32 * db + 8 * a >= p.dv) continue;   // (dv: a multiple of 16)
                      f32x4 v4 = {o[db][4 * a] * inv, o[db][4 * a + 1] * inv,
                                  o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv};
                      *(f32x4*)(dst + 32 * db + 8 * a + 4 * g) = v4;
@@ -558,6 +592,7 @@ void fwd_16b_kernel(Params p) {
                  for (int db = 0; db < T::DB; ++db)
 #pragma unroll
                    for (int a = 0; a < 4; ++a) {
+                     if (Pad && 32 * db + 8 * a >= p.dv) continue;
                      typename X::x4 v4 = {(E)(o[db][4 * a] * inv), (E)(o[db][4 * a + 1] * inv),
                                           (E)(o[db][4 * a + 2] * inv), (E)(o[db][4 * a + 3] * inv)};
                      *(typename X::x4*)(dst + 32 * db + 8 * a + 4 * g) = v4;
@@ -586,10 +621,13 @@ struct F32Tile {
   static_assert(BN * C4 % kThreads == 0, "tile must split evenly over the workgroup");
 };
 
+// Forms as for the 16-bit kernel; kFormPadded loads zeros for Q, K and V
+// dims from p.dv on and stores O's first p.dv dims.
 template <int D, int Form>
 __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1))
 void fwd_f32_kernel(Params p) {
-  constexpr bool Strided = Form == kFormStrided, Sparse = Form == kFormBlockSparse;
+  constexpr bool Pad = Form == kFormPadded;
+  constexpr bool Strided = Form == kFormStrided || Pad, Sparse = Form == kFormBlockSparse;
   using T = F32Tile<D>;
   constexpr int BN = T::BN;
   __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE_F];
@@ -640,7 +678,8 @@ void fwd_f32_kernel(Params p) {
   float qf[T::DH];
 #pragma unroll
   for (int t4 = 0; t4 < T::DH / 4; ++t4) {
-    f32x4 v = i < p.Sq ? *(const f32x4*)(Qp + (long long)i * qr + T::DH * g + 4 * t4) : f32x4{};
+    const bool ok = i < p.Sq && (!Pad || T::DH * g + 4 * t4 < p.dv);
+    f32x4 v = ok ? *(const f32x4*)(Qp + (long long)i * qr + T::DH * g + 4 * t4) : f32x4{};
     qf[4 * t4 + 0] = v[0];
     qf[4 * t4 + 1] = v[1];
     qf[4 * t4 + 2] = v[2];
@@ -659,7 +698,7 @@ void fwd_f32_kernel(Params p) {
       const int c = tid + it * kThreads;
       const int row = c / T::C4, c4 = c % T::C4;
       const int key = kt + row;
-      const bool ok = key < p.Sk;
+      const bool ok = key < p.Sk && (!Pad || 4 * c4 < p.dv);
       kreg[it] = ok ? *(const f32x4*)(Kp + (long long)key * kr + 4 * c4) : f32x4{};
       vreg[it] = ok ? *(const f32x4*)(Vp + (long long)key * vr + 4 * c4) : f32x4{};
     }
@@ -785,13 +824,15 @@ void fwd_f32_kernel(Params p) {
                  if (T::DB % 4 == 0) {
 #pragma unroll
                    for (int c4 = 0; c4 < T::DB / 4; ++c4) {
+                     if (Pad && T::DB * mrow + 4 * c4 >= p.dv) continue;
                      f32x4 x = {o[4 * c4][v] * inv, o[4 * c4 + 1][v] * inv,
                                 o[4 * c4 + 2][v] * inv, o[4 * c4 + 3][v] * inv};
                      *(f32x4*)(d0 + 4 * c4) = x;
                    }
                  } else {
 #pragma unroll
-                   for (int db = 0; db < T::DB; ++db) d0[db] = o[db][v] * inv;
+                   for (int db = 0; db < T::DB; ++db)
+                     if (!Pad || T::DB * mrow + db < p.dv) d0[db] = o[db][v] * inv;
                  }
                }
              });
@@ -804,17 +845,19 @@ void fwd_f32_kernel(Params p) {
 // form of the online-softmax rescale. A split that saw no key has
 // LSE_s = -inf and weight 0; a row with no key in any split gets O = 0 and
 // LSE = -inf. Strided: O row (b, h, i) of the flat row index (b H + h) Sq + i
-// sits at O + b os[0] + h os[1] + i os[2].
+// sits at O + b os[0] + h os[1] + i os[2]. Partial rows hold D floats of
+// which the first dv (a multiple of 4) are O's dims.
 template <typename OutT, int D, bool Strided>
 __global__ __launch_bounds__(kThreads)
 void merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpart,
                   OutT* __restrict__ O, float* __restrict__ LSE, long rows, int nsplit,
-                  int H, int Sq, long long os0, long long os1, long long os2) {
+                  int H, int Sq, long long os0, long long os1, long long os2, int dv) {
   constexpr int TPR = D / 4;               // threads per row, 4 dims each
   constexpr int RPB = kThreads / TPR;
   const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
   const int c = threadIdx.x % TPR;
   if (row >= rows) return;
+  const bool on = 4 * c < dv;
   float M = -INFINITY;
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, Lpart[(size_t)s * rows + row]);
   f32x4 acc = f32x4{};
@@ -825,8 +868,7 @@ void merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpa
       if (ls == -INFINITY) continue;   // no key in this split (its O part is not written)
       const float wgt = __expf(ls - M);
       den += wgt;
-      const f32x4 x = *(const f32x4*)(Opart + ((size_t)s * rows + row) * D + 4 * c);
-      acc += wgt * x;
+      if (on) acc += wgt * *(const f32x4*)(Opart + ((size_t)s * rows + row) * D + 4 * c);
     }
     acc *= 1.f / den;
   }
@@ -837,7 +879,8 @@ void merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpa
   } else {
     dst = O + (size_t)row * D + 4 * c;
   }
-  if constexpr (sizeof(OutT) == 2) {
+  if (!on) {
+  } else if constexpr (sizeof(OutT) == 2) {
     typedef typename Elt<OutT>::x4 o4;
     *(o4*)dst = o4{(OutT)acc[0], (OutT)acc[1], (OutT)acc[2], (OutT)acc[3]};
   } else {
@@ -864,6 +907,9 @@ static int f32_occupancy(int form) {
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<D, kFormStrided>, kThreads, 0);
   if (form == kFormBlockSparse)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<D, kFormBlockSparse>, kThreads, 0);
+  if constexpr (D <= 128)
+    if (form == kFormPadded)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<D, kFormPadded>, kThreads, 0);
   return e == hipSuccess ? n : 0;
 }
 
@@ -881,13 +927,13 @@ static hipError_t launch_merge(const Params& p, hipStream_t stream) {
   const long blocks = (rows + RPB - 1) / RPB;
   hipLaunchKernelGGL((merge_kernel<OutT, D, Strided>), dim3((unsigned)blocks), dim3(kThreads), 0,
                      stream, p.Opart, p.Lpart, (OutT*)p.O, p.LSE, rows, p.nsplit, p.H, p.Sq,
-                     p.os[0], p.os[1], p.os[2]);
+                     p.os[0], p.os[1], p.os[2], p.dv);
   return hipGetLastError();
 }
 
 template <int D, int Form>
 static hipError_t launch_d(const Params& p, int dtype, hipStream_t stream) {
-  constexpr bool Strided = Form == kFormStrided;
+  constexpr bool Strided = Form == kFormStrided || Form == kFormPadded;
   const long blocks = (long)p.units * p.n_qblk;
   constexpr int BN = D >= 128 ? 32 : 64;
   // (the 16-bit kernel has no persistent form; sched is ignored)
@@ -910,6 +956,10 @@ template <int D>
 static hipError_t launch_form(const Params& p, int dtype, int form, hipStream_t stream) {
   if (form == kFormStrided) return launch_d<D, kFormStrided>(p, dtype, stream);
   if (form == kFormBlockSparse) return launch_d<D, kFormBlockSparse>(p, dtype, stream);
+  if (form == kFormPadded) {
+    if constexpr (D <= 128) return launch_d<D, kFormPadded>(p, dtype, stream);
+    return hipErrorInvalidValue;   // padded head dims run on the 64 and 128 tiles
+  }
   return launch_d<D, kFormContiguous>(p, dtype, stream);
 }
 

@@ -13,9 +13,10 @@ struct Params {
   const void* V;
   void* O;
   float* LSE;
-  float* Opart;      // [nsplit][B*H*Sq][D] fp32 partial outputs (nsplit > 1)
+  float* Opart;      // [nsplit][B*H*Sq][DT] fp32 partial outputs (nsplit > 1; DT = tile dim)
   float* Lpart;      // [nsplit][B*H*Sq]    partial log-sum-exp    (nsplit > 1)
   int B, H, HKV, Sq, Sk;
+  int dv;            // head dim of the tensors (kFormPadded: below the kernel's tile dim)
   int group;         // H / HKV
   float sl;          // scale * log2(e): scores are kept in base-2 units
                      // (16-bit kernel: |scale| * log2(e) > 0, see neg_q)
@@ -34,8 +35,9 @@ struct Params {
   int nslot;
   // Element strides (batch, head, row) of Q, K, V and O; the head dimension
   // is contiguous. Contiguous [B, heads, S, D] tensors have (heads S D, S D, D);
-  // the kernels read them only in their strided form (Strided = true), where
-  // the row strides of K and V are multiples of D.
+  // the kernels read them only in their strided and padded forms. In the
+  // strided form the row strides of K and V are multiples of D; the padded
+  // form takes any row stride that keeps rows 16-byte aligned.
   long long qs[3], ks[3], vs[3], os[3];
   // Block mask (kFormBlockSparse): bytes [mask batch][mask heads][n_qblk][bm_nkb];
   // a nonzero byte makes its kBlockM-row x kMaskBlockK-key block visible.
@@ -47,11 +49,15 @@ struct Params {
   int bm_by_kv;
 };
 
-// Kernel forms: contiguous tensors, strided tensors (p.qs .. p.os), and
-// contiguous tensors under a block mask.
+// Kernel forms: contiguous tensors, strided tensors (p.qs .. p.os),
+// contiguous tensors under a block mask, and padded: strided tensors whose
+// head dim p.dv (a multiple of 16) is below the kernel's tile dim, the
+// remaining dims of every Q row and K/V tile row held as zeros on chip.
 constexpr int kFormContiguous = 0;
 constexpr int kFormStrided = 1;
 constexpr int kFormBlockSparse = 2;
+constexpr int kFormPadded = 3;
+constexpr int kForms = 4;
 // Keys per block-mask byte, and the most key tiles one workgroup's range may
 // hold under a block mask (its visible-tile list lives in LDS).
 constexpr int kMaskBlockK = 64;
@@ -62,11 +68,20 @@ constexpr int kBlockM = 128;
 int key_tile(int dtype, int D);
 int block_m(int dtype, int D);
 // Workgroups of the fp32 kernel (in the given form) that fit on one CU at
-// head dim D (0 on error).
+// tile dim D (0 on error).
 int f32_blocks_per_cu(int D, int form);
 
+// Tile dim of the kernel that serves head dim dv: dv itself for 64, 128 and
+// 256; 64 or 128 for the padded dims 16, 32, 48 and 80, 96 (0: unsupported).
+constexpr int tile_dim(int dv) {
+  return (dv == 64 || dv == 128 || dv == 256) ? dv
+         : (dv == 16 || dv == 32 || dv == 48) ? 64
+         : (dv == 80 || dv == 96) ? 128 : 0;
+}
+
 // Queue the forward kernel (and the merge kernel when p.nsplit > 1) in the
-// given form (kFormContiguous: p.qs .. p.os and the mask are not read).
+// given form at tile dim D (kFormContiguous: p.qs .. p.os and the mask are
+// not read; kFormPadded: D = tile_dim(p.dv), D = 64 or 128).
 hipError_t launch_forward(const Params& p, int dtype, int D, int form, hipStream_t stream);
 
 }  // namespace fa

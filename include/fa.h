@@ -47,7 +47,8 @@ enum fa_status {
   FA_ERR_NULLPTR = 1,   /* a required pointer is NULL                          */
   FA_ERR_SHAPE = 2,     /* a dimension < 1, or a tensor larger than 2^62 bytes */
   FA_ERR_GQA = 3,       /* H is not a multiple of HKV                          */
-  FA_ERR_HEAD_DIM = 4,  /* D not in {64, 128, 256}                             */
+  FA_ERR_HEAD_DIM = 4,  /* D not in {16, 32, 48, 64, 80, 96, 128, 256}; block
+                           masks: D not in {64, 128, 256}                       */
   FA_ERR_DTYPE = 5,     /* dtype not an fa_dtype value                         */
   FA_ERR_WINDOW = 6,    /* window < 0 or causal not 0/1                        */
   FA_ERR_ALIGN = 7,     /* a buffer is not 16-byte aligned                     */
@@ -68,6 +69,10 @@ enum fa_status {
  *   V    device pointer, [B, HKV, Sk, D] contiguous, element type `dtype`
  *   O    device pointer, [B, H,   Sq, D] contiguous, element type `dtype` (written)
  *   LSE  device pointer, [B, H,   Sq]    contiguous, float32, natural log (written)
+ *   D      head dim: 16, 32, 48, 64, 80, 96, 128 or 256 (the head dims the
+ *          forge flash_attention.metal page instantiates, and 256). 16 .. 96
+ *          other than 64 run on the 64- or 128-dim kernels with the missing
+ *          dims held as zeros on chip (no padded copy in memory).
  *   scale  multiplies q.k after the dot product (callers usually pass 1/sqrt(D))
  *   causal 0 or 1; window >= 0 (0 = none)
  *   stream hipStream_t to queue the work on, NULL = the null stream
@@ -120,8 +125,8 @@ int fa_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE,
  *   LSE stays contiguous [B, H, Sq] float32.
  *
  * Stride rules (else FA_ERR_STRIDE): every stride >= 0 and a multiple of 16
- * bytes; every row stride >= D; the K and V row strides are multiples of D
- * and below 2^31 / 64 bytes; O's rows are pairwise disjoint (checked: its
+ * bytes; every row stride >= D; the K and V row strides are below 2^31 / 64
+ * bytes and, for D = 64, 128 and 256, multiples of D; O's rows are pairwise disjoint (checked: its
  * axes sorted by stride, each stride reaches past the extent of the smaller
  * ones). Batch or head strides of 0 (broadcast inputs) are allowed for Q, K
  * and V. O must not overlap the inputs (not checked). When all four tensors have contiguous strides the
@@ -154,7 +159,7 @@ int fa_fwd_strided(const void* Q, const void* K, const void* V, void* O, float* 
  * allow it AND the mask byte of block (i / FA_MASK_BLOCK_Q, j / FA_MASK_BLOCK_K)
  * for (b, h) is nonzero. Rows left with no visible key get O = 0 and
  * LSE = -inf. Key blocks whose byte is 0 are neither read nor computed.
- * Q, K, V, O contiguous as for fa_fwd. The mask is read by the kernels on
+ * Q, K, V, O contiguous as for fa_fwd; D = 64, 128 or 256. The mask is read by the kernels on
  * `stream` (it must stay valid until they complete) and is not modified.
  * Errors as fa_fwd_ex, plus FA_ERR_NULLPTR for a NULL mask and FA_ERR_MASK
  * for other mask axis sizes. Key ranges of more than 2048 key tiles per
@@ -205,7 +210,7 @@ int fa_schedule_table(int B, int H, int HKV, int Sq, int Sk, int D,
  *   dQ              device pointer, [B, H, Sq, D]   float32 (written)
  *   dK, dV          device pointers, [B, HKV, Sk, D] float32 (written; keys no
  *                   query sees get 0)
- *   scale, causal, window, dtype: as for fa_fwd; rows with LSE = -inf (no
+ *   D, scale, causal, window, dtype: as for fa_fwd; rows with LSE = -inf (no
  *   visible key) get dQ = 0 and contribute nothing.
  *
  * Contiguous tensors only; no block mask. All buffers 16-byte aligned. A

@@ -89,7 +89,7 @@ def test_null_pointer(which):
 @pytest.mark.parametrize("over,code", [
     (dict(B=0), 2), (dict(H=0), 2), (dict(HKV=0), 2), (dict(Sq=0), 2), (dict(Sk=-3), 2),
     (dict(H=6, HKV=4), 3), (dict(H=4, HKV=3), 3),
-    (dict(D=96), 4), (dict(D=32), 4), (dict(D=512), 4),
+    (dict(D=40), 4), (dict(D=8), 4), (dict(D=112), 4), (dict(D=192), 4), (dict(D=512), 4),
     (dict(dtype=3), 5), (dict(dtype=-1), 5),
     (dict(window=-1), 6), (dict(causal=2), 6),
     (dict(B=1 << 20, H=1 << 10, Sq=1 << 10), 2),
@@ -113,7 +113,7 @@ def test_misaligned_buffer(which):
 def test_plan_splits_rejects_bad_args_without_device():
     lib = _lib.lib()
     assert lib.fa_plan_splits(1, 4, 3, 64, 64, 128, 0, 0, 1) == -3
-    assert lib.fa_plan_splits(1, 4, 4, 64, 64, 80, 0, 0, 1) == -4
+    assert lib.fa_plan_splits(1, 4, 4, 64, 64, 40, 0, 0, 1) == -4
 
 
 def test_python_binding_fails_loudly_on_cpu_tensors():
@@ -149,7 +149,7 @@ def test_strided_rule_errors(kw):
 
 
 def test_strided_other_errors_come_first():
-    assert call_strided(qs=(0, 128, -128), D=96) == 4
+    assert call_strided(qs=(0, 128, -128), D=40) == 4
     assert call_strided(qs=(0, 128, -128), dtype=7) == 5
     ptr_a = _lib.lib().fa_fwd_strided(None, A, A, A, A, 1, 4, 2, 64, 64, 128, None, None, None,
                                       None, 0.125, 1, 0, 1, 0, None)
@@ -179,7 +179,8 @@ def test_block_sparse_bad_mask_axes(mb, mh):
 
 
 def test_block_sparse_shape_errors_come_first():
-    assert call_sparse(D=96) == 4
+    assert call_sparse(D=40) == 4
+    assert call_sparse(D=96) == 4       # padded head dims take no block mask
     assert call_sparse(H=4, HKV=3) == 3
 
 
@@ -206,7 +207,7 @@ def test_bwd_null_and_misaligned(which):
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(B=0), 2), (dict(H=6, HKV=4), 3), (dict(D=96), 4), (dict(dtype=3), 5),
+    (dict(B=0), 2), (dict(H=6, HKV=4), 3), (dict(D=40), 4), (dict(D=512), 4), (dict(dtype=3), 5),
     (dict(window=-1), 6), (dict(causal=2), 6),
 ])
 def test_bwd_argument_errors(over, code):
@@ -225,3 +226,20 @@ def test_disjoint_output_strides_pass_the_stride_checks(os_):
     # valid O strides get past every stride rule; with no GPU present the call
     # then stops at the device query (FA_ERR_HIP), never FA_ERR_STRIDE
     assert call_strided(os_=os_, Sq=64, Sk=64) == 8
+
+
+@pytest.mark.parametrize("D,ks", [
+    (96, (0, 64 * 112, 112)),              # K row stride 112: not a multiple of 96
+    (48, (0, 64 * 48, 48)),                # contiguous rows of 48
+    (80, None),
+    (16, (0, 64 * 16, 16)),
+])
+@pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                    reason="valid arguments would reach a kernel launch on fake pointers")
+def test_padded_head_dims_pass_the_checks(D, ks):
+    # head dims 16 .. 96 take any 16-byte row stride for K and V (the padded
+    # form addresses every copied chunk in full): past every check, the call
+    # stops at the device query
+    assert call_strided(ks=ks, D=D, Sq=64, Sk=64) == 8
+    assert call(D=D) == 8
+    assert call_bwd(D=D) == 9           # the backward stops at its workspace allocation

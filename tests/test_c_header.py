@@ -23,7 +23,7 @@ int main(void) {
   char* a = (char*)0x10000;
   int bad = 0;
   if (fa_fwd(a, a, a, a, (float*)a, 1, 4, 3, 64, 64, 128, 0.125f, 1, 0, FA_BF16, NULL) != FA_ERR_GQA) bad |= 1;
-  if (fa_fwd_ex(a, a, a, a, (float*)a, 1, 4, 2, 64, 64, 96, 0.125f, 1, 0, FA_F16, 0, NULL) != FA_ERR_HEAD_DIM) bad |= 2;
+  if (fa_fwd_ex(a, a, a, a, (float*)a, 1, 4, 2, 64, 64, 40, 0.125f, 1, 0, FA_F16, 0, NULL) != FA_ERR_HEAD_DIM) bad |= 2;
   if (fa_fwd_strided(a, a, a, a, (float*)a, 1, 4, 2, 64, 64, 128, st, NULL, NULL, NULL,
                      0.125f, 1, 0, FA_BF16, 0, NULL) != FA_ERR_STRIDE) bad |= 4;
   if (fa_fwd_block_sparse(a, a, a, a, (float*)a, 1, 4, 2, 64, 64, 128, (const unsigned char*)a,
