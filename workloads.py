@@ -95,6 +95,13 @@ CONFIGS = [
     Workload("blocksparse_bf16_b2h32kv8_s4096_d128", 2, 32, 8, 4096, 4096, 128, "bf16", 0, 0,
              amplitude=0.5, check="sampled", n_random_rows=4096, edge_rows=64,
              seed_index=7, mask="band_random", mask_p=0.15),
+    # head dims below the kernel tiles (the padded form): the bf16 headline
+    # shape at D = 96 and the fp32 causal MHA shape at D = 32
+    Workload("gqa_causal_bf16_b2h32kv8_s4096_d96", 2, 32, 8, 4096, 4096, 96, "bf16", 1, 0,
+             amplitude=0.5, check="sampled", n_random_rows=4096, edge_rows=64,
+             seed_index=8),
+    Workload("mha_causal_f32_b4h8_s1024_d32", 4, 8, 8, 1024, 1024, 32, "f32", 1, 0,
+             check="all", seed_index=9),
 ]
 
 # Block-mask granularity (query rows x keys per mask byte).
