@@ -181,13 +181,17 @@ constexpr float kRowSumLimit = 1.8446744e19f;   // 2^64: row-sum bound that trig
 // through p.qs .. p.os (batch, head, row strides); otherwise they are
 // contiguous. Form kFormBlockSparse: only the key tiles whose block-mask
 // byte is nonzero are copied and computed. Form kFormPadded: strided tensors
-// with rows of p.dv < D elements; the tile's dims from p.dv on are zeros
-// (Q in registers, and K/V chunks whose copy offsets are sent out of the
-// buffer's range), so S is exact and O's padded dims, never stored, are 0.
-template <typename E, int D, int BN, int Form>
+// with rows of DV < D elements (DV = p.dv, a multiple of 16). The K/V tiles
+// keep the D-dim layout with zeros from dim DV on (chunks whose copy offsets
+// are sent out of the buffer's range); Q^T takes only the DV / 16 k-steps of
+// real dims and O^T only the ceil(DV / 32) dim blocks that hold real dims.
+template <typename E, int D, int BN, int Form, int DV = D>
 __global__ __launch_bounds__(kThreads, (D == 128 ? 3 : 2))
 void fwd_16b_kernel(Params p) {
   constexpr bool Pad = Form == kFormPadded;
+  static_assert(Pad ? (DV % 16 == 0 && DV < D) : DV == D, "padded head dims only");
+  constexpr int DC = DV / 16;             // k-steps of the S MFMA over real dims
+  constexpr int DB = (DV + 31) / 32;      // O^T dim blocks holding real dims
   constexpr bool Strided = Form == kFormStrided || Pad, Sparse = Form == kFormBlockSparse;
   static_assert(kMaskBlockK % BN == 0, "a key tile lies inside one mask block");
   using T = Bf16Tile<D, BN>;
@@ -251,7 +255,7 @@ void fwd_16b_kernel(Params p) {
   const int voff_v = Strided ? (P0 / T::CPR) * vrb + T::chunk_off(P0, true) : T::dma_off(P0, true);
   // Padded rows: each copy instruction's lane offset in full (a row stride
   // need not be a multiple of the tile row), or one past the buffer's range
-  // for a chunk at or beyond dim p.dv, which then lands in LDS as zeros.
+  // for a chunk at or beyond dim DV, which then lands in LDS as zeros.
   constexpr int kOutOfRange = 0x7ffffff0;
   int pk_off[Pad ? T::NIW : 1], pv_off[Pad ? T::NIW : 1];
   if constexpr (Pad) {
@@ -259,14 +263,14 @@ void fwd_16b_kernel(Params p) {
     for (int k = 0; k < T::NIW; ++k) {
       const int P = P0 + 64 * k, row = P / T::CPR;
       const int ck = (P % T::CPR) ^ T::swz_k(row), cv = (P % T::CPR) ^ T::swz_v(row);
-      pk_off[k] = 8 * ck < p.dv ? row * krb + 16 * ck : kOutOfRange;
-      pv_off[k] = 8 * cv < p.dv ? row * vrb + 16 * cv : kOutOfRange;
+      pk_off[k] = 8 * ck < DV ? row * krb + 16 * ck : kOutOfRange;
+      pv_off[k] = 8 * cv < DV ? row * vrb + 16 * cv : kOutOfRange;
     }
   }
   auto issue = [&](int kt, char* kdst, char* vdst, bool full = false) {
     if constexpr (Pad) {
       // valid bytes from the tile's first row: up to the end of row Sk - 1
-      const int rb = 2 * p.dv;
+      constexpr int rb = 2 * DV;
       const unsigned kbytes = full ? (unsigned)((BN - 1) * krb + rb)
                                    : (unsigned)min((long long)(p.Sk - kt - 1) * krb + rb, 0x7fffffffLL);
       const unsigned vbytes = full ? (unsigned)((BN - 1) * vrb + rb)
@@ -312,10 +316,10 @@ void fwd_16b_kernel(Params p) {
   if (n_tiles > 0) issue(tile_kt(0), kbuf0, vbuf0);
 
   // Query rows as the B operand: k-slot (g, e) of step t is dim 16t + 8g + e.
-  e16x8 qf[T::DC];
+  e16x8 qf[DC];
 #pragma unroll
-  for (int t = 0; t < T::DC; ++t) {
-    if (i < p.Sq && (!Pad || 16 * t < p.dv))
+  for (int t = 0; t < DC; ++t) {
+    if (i < p.Sq)
       qf[t] = *(const e16x8*)(Qp + (long long)i * qr + 16 * t + 8 * g);
     else
       qf[t] = e16x8{};
@@ -332,7 +336,7 @@ void fwd_16b_kernel(Params p) {
   // lane. D <= 128 keeps them in registers; D = 256, short of registers at two
   // wavefronts per SIMD, forms them with one XOR each.
   const int krow = perm_row(l32);
-  constexpr int KO = T::DC < 8 ? T::DC : 8;
+  constexpr int KO = DC < 8 ? DC : 8;
   constexpr int KR = D == 256 ? 1 : KO;
   int koff[KR];
 #pragma unroll
@@ -340,7 +344,7 @@ void fwd_16b_kernel(Params p) {
   auto k_off = [&](int t) { return (KR == 1 ? koff[0] ^ (32 * (t % KO)) : koff[t % KO]) + (t / KO) * 256; };
   const int blk = lane >> 4, li = lane & 15;
   const int vrow = 8 * g + (li >> 2);                       // + 16 C + 4 h
-  constexpr int VO = T::DB < 4 ? T::DB : 4;
+  constexpr int VO = DB < 4 ? DB : 4;
   constexpr int VR = D == 256 ? 1 : VO;
   int voff[VR];
 #pragma unroll
@@ -350,9 +354,9 @@ void fwd_16b_kernel(Params p) {
   }
   auto v_off = [&](int db) { return (VR == 1 ? voff[0] ^ (64 * (db % VO)) : voff[db % VO]) + (db / VO) * 256; };
 
-  f32x16 o[T::DB];
+  f32x16 o[DB];
 #pragma unroll
-  for (int db = 0; db < T::DB; ++db) o[db] = f32x16{};
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m_ref = -INFINITY, l = 0.f;
   const float sl = p.sl;
   f32x16 s[T::KB];
@@ -365,7 +369,7 @@ void fwd_16b_kernel(Params p) {
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-    for (int t = 0; t < T::DC; ++t) {
+    for (int t = 0; t < DC; ++t) {
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb) {
         const e16x8 a = *(const e16x8*)(Ks + k_off(t) + kb * 32 * T::ROW);
@@ -474,7 +478,7 @@ void fwd_16b_kernel(Params p) {
       m_ref = m_new;
       l *= corr;
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db) o[db] *= corr;
+      for (int db = 0; db < DB; ++db) o[db] *= corr;
       rs = exp_pack_sum(m_ref == -INFINITY ? 0.f : m_ref);
       m_sub = m_ref == -INFINITY ? -1e30f : m_ref;
     }
@@ -488,19 +492,19 @@ void fwd_16b_kernel(Params p) {
     for (int c = 0; c < T::KC; ++c) {
       if constexpr (D <= 128) {
         // all V operands of this 16-key chunk first, then its MFMAs
-        e16x8 a[T::DB];
+        e16x8 a[DB];
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db) {
+        for (int db = 0; db < DB; ++db) {
           const int vo = v_off(db) + 16 * c * T::ROW;
           a[db] = read_v_pair<e16x8>(Vs, vo, vo + 4 * T::ROW);
         }
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db) o[db] = X::mfma(a[db], pf[c], o[db]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::DB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, T::DB, 0);
+        for (int db = 0; db < DB; ++db) o[db] = X::mfma(a[db], pf[c], o[db]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, DB, 0);
       } else {
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db) {
+        for (int db = 0; db < DB; ++db) {
           const int base = 16 * c * T::ROW;
           const int vo = v_off(db) + base;
           const e16x8 a = read_v_pair<e16x8>(Vs, vo, vo + 4 * T::ROW);
@@ -577,10 +581,10 @@ void fwd_16b_kernel(Params p) {
                  const size_t rows = (size_t)p.B * p.H * p.Sq;
                  float* dst = p.Opart + ((size_t)split * rows + row) * D;
 #pragma unroll
-                 for (int db = 0; db < T::DB; ++db)
+                 for (int db = 0; db < DB; ++db)
 #pragma unroll
                    for (int a = 0; a < 4; ++a) {
-                     if (Pad && 32 * db + 8 * a >= p.dv) continue;   // (dv: a multiple of 16)
+                     if (32 * db + 8 * a >= DV) continue;   // (DV: a multiple of 16)
                      f32x4 v4 = {o[db][4 * a] * inv, o[db][4 * a + 1] * inv,
                                  o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv};
                      *(f32x4*)(dst + 32 * db + 8 * a + 4 * g) = v4;
@@ -589,10 +593,10 @@ void fwd_16b_kernel(Params p) {
                  E* dst = Strided ? (E*)p.O + w.b * p.os[0] + w.h * p.os[1] + (long long)i * p.os[2]
                                   : (E*)p.O + row * D;
 #pragma unroll
-                 for (int db = 0; db < T::DB; ++db)
+                 for (int db = 0; db < DB; ++db)
 #pragma unroll
                    for (int a = 0; a < 4; ++a) {
-                     if (Pad && 32 * db + 8 * a >= p.dv) continue;
+                     if (32 * db + 8 * a >= DV) continue;
                      typename X::x4 v4 = {(E)(o[db][4 * a] * inv), (E)(o[db][4 * a + 1] * inv),
                                           (E)(o[db][4 * a + 2] * inv), (E)(o[db][4 * a + 3] * inv)};
                      *(typename X::x4*)(dst + 32 * db + 8 * a + 4 * g) = v4;
@@ -931,16 +935,46 @@ static hipError_t launch_merge(const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename E, int D, int BN, int Form, int DV = D>
+static hipError_t launch_16b_e(const Params& p, long blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((fwd_16b_kernel<E, D, BN, Form, DV>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  return hipSuccess;
+}
+
+// The 16-bit kernel at tile dim D; the padded form is instantiated per head dim.
+template <int D, int BN, int Form>
+static hipError_t launch_16b(const Params& p, bool bf16, long blocks, hipStream_t stream) {
+  if constexpr (Form == kFormPadded) {
+    switch (p.dv) {
+#define FA_PADDED_DV(X)                                                                   \
+      case X:                                                                             \
+        if constexpr (tile_dim(X) == D)                                                   \
+          return bf16 ? launch_16b_e<__bf16, D, BN, Form, X>(p, blocks, stream)            \
+                      : launch_16b_e<_Float16, D, BN, Form, X>(p, blocks, stream);        \
+        return hipErrorInvalidValue;
+      FA_PADDED_DV(16)
+      FA_PADDED_DV(32)
+      FA_PADDED_DV(48)
+      FA_PADDED_DV(80)
+      FA_PADDED_DV(96)
+#undef FA_PADDED_DV
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    return bf16 ? launch_16b_e<__bf16, D, BN, Form>(p, blocks, stream)
+                : launch_16b_e<_Float16, D, BN, Form>(p, blocks, stream);
+  }
+}
+
 template <int D, int Form>
 static hipError_t launch_d(const Params& p, int dtype, hipStream_t stream) {
   constexpr bool Strided = Form == kFormStrided || Form == kFormPadded;
   const long blocks = (long)p.units * p.n_qblk;
   constexpr int BN = D >= 128 ? 32 : 64;
   // (the 16-bit kernel has no persistent form; sched is ignored)
-  if (dtype == 1) {
-    hipLaunchKernelGGL((fwd_16b_kernel<__bf16, D, BN, Form>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
-  } else if (dtype == 2) {
-    hipLaunchKernelGGL((fwd_16b_kernel<_Float16, D, BN, Form>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  if (dtype == 1 || dtype == 2) {
+    const hipError_t e = launch_16b<D, BN, Form>(p, dtype == 1, blocks, stream);
+    if (e != hipSuccess) return e;
   } else {
     const long grid = p.sched ? (long)p.nslot : blocks;
     hipLaunchKernelGGL((fwd_f32_kernel<D, Form>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
