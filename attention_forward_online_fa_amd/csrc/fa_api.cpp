@@ -13,6 +13,7 @@
 #include <queue>
 #include <vector>
 
+#include "fa_bwd.h"
 #include "fa_kernels.h"
 
 namespace {
@@ -490,6 +491,22 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
 }
 
 }  // namespace
+
+namespace fa {
+// Stream-ordered workspace from this library's pool on the current device
+// (the pool of the split workspace; freed blocks stay cached until fa_release).
+int library_workspace(size_t bytes, hipStream_t stream, void** out) {
+  DeviceState* ds = nullptr;
+  int st = device_state(&ds);
+  if (st != FA_OK) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  hipMemPool_t pool = nullptr;
+  st = workspace_pool(dev, *ds, &pool);
+  if (st != FA_OK) return st;
+  return hipMallocFromPoolAsync(out, bytes, pool, stream) == hipSuccess ? FA_OK : FA_ERR_WORKSPACE;
+}
+}  // namespace fa
 
 extern "C" {
 

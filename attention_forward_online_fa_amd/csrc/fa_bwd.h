@@ -3,6 +3,8 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
+
 namespace fa {
 
 struct BwdParams {
@@ -29,5 +31,19 @@ struct BwdParams {
 
 // Queue the dQ kernel (which also writes Dws) and then the dK/dV kernel.
 hipError_t launch_backward(const BwdParams& p, int dtype, int D, hipStream_t stream);
+
+// Row copies for the 16-bit backward at head dims 16 .. 96 (other than 64),
+// which runs the MFMA kernels of the 64 or 128 tile on zero-padded copies:
+// rows of src_bytes -> rows of dst_bytes with zeros after src_bytes (both
+// multiples of 16), and back for the fp32 gradients (dt -> dv floats per row,
+// both multiples of 4).
+hipError_t launch_pad_rows(const void* src, void* dst, long rows, int src_bytes, int dst_bytes,
+                           hipStream_t stream);
+hipError_t launch_unpad_rows(const float* src, float* dst, long rows, int dt, int dv,
+                             hipStream_t stream);
+
+// Stream-ordered workspace of `bytes` from the library's memory pool on the
+// current device (fa_api.cpp); release with hipFreeAsync. Returns an fa_status.
+int library_workspace(size_t bytes, hipStream_t stream, void** out);
 
 }  // namespace fa

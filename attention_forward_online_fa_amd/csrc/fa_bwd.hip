@@ -642,6 +642,44 @@ static hipError_t launch_bwd_e(const BwdParams& p, int D, hipStream_t stream) {
   }
 }
 
+// One 16-byte chunk per thread: chunk c of destination row r is chunk c of
+// source row r, or zeros past the source row.
+__global__ __launch_bounds__(256) void pad_rows_kernel(const uint4* __restrict__ src,
+                                                       uint4* __restrict__ dst, long rows, int cs,
+                                                       int ct) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * ct) return;
+  const long r = idx / ct;
+  const int c = (int)(idx - r * ct);
+  dst[idx] = c < cs ? src[r * cs + c] : make_uint4(0u, 0u, 0u, 0u);
+}
+
+// One float4 per thread: the first cs float4 of each ct-float4 row.
+__global__ __launch_bounds__(256) void unpad_rows_kernel(const float4* __restrict__ src,
+                                                         float4* __restrict__ dst, long rows,
+                                                         int ct, int cs) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * cs) return;
+  const long r = idx / cs;
+  dst[idx] = src[r * ct + (idx - r * cs)];
+}
+
+hipError_t launch_pad_rows(const void* src, void* dst, long rows, int src_bytes, int dst_bytes,
+                           hipStream_t stream) {
+  const long n = rows * (dst_bytes / 16);
+  hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     (const uint4*)src, (uint4*)dst, rows, src_bytes / 16, dst_bytes / 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpad_rows(const float* src, float* dst, long rows, int dt, int dv,
+                             hipStream_t stream) {
+  const long n = rows * (dv / 4);
+  hipLaunchKernelGGL(unpad_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     (const float4*)src, (float4*)dst, rows, dt / 4, dv / 4);
+  return hipGetLastError();
+}
+
 hipError_t launch_backward(const BwdParams& p, int dtype, int D, hipStream_t stream) {
   if (dtype == 0) return launch_bwd_e<float>(p, D, stream);
   if (dtype == 1) return launch_bwd_e<__bf16>(p, D, stream);

@@ -66,12 +66,53 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
   p.sl_abs = mag > 1e-30 ? (float)mag : 1e-30f;
   p.n_qblk = (Sq + 127) / 128;
   if ((double)B * H * p.n_qblk > 2147483647.0) return FA_ERR_SHAPE;
-  // D_i workspace, stream-ordered from the device's default memory pool
+  // 16-bit inputs at head dims 16 .. 96 other than 64 run the MFMA kernels of
+  // the 64 or 128 tile on copies whose rows are zero-padded to the tile dim:
+  // the zero dims add exact zeros to every dot product, and the gradients'
+  // padded dims (zero) are dropped when they are copied back.
+  const bool padded = dtype != FA_F32 && D != 64 && D != 128 && D != 256;
+  const int DT = padded ? (D < 64 ? 64 : 128) : D;
+  const size_t nq = (size_t)B * H * Sq, nk = (size_t)B * HKV * Sk;
+  auto up = [](size_t bytes) { return (bytes + 255) / 256 * 256; };
+  // workspace, stream-ordered from the library's memory pool: D_i, and when
+  // padded Q, O, dO, K, V (input type) and dQ, dK, dV (fp32) at DT
+  const size_t b_d = up(nq * sizeof(float));
+  const size_t b_q = padded ? up(nq * DT * 2) : 0, b_k = padded ? up(nk * DT * 2) : 0;
+  const size_t b_gq = padded ? up(nq * DT * 4) : 0, b_gk = padded ? up(nk * DT * 4) : 0;
   void* ws = nullptr;
-  if (hipMallocAsync(&ws, (size_t)B * H * Sq * sizeof(float), stream) != hipSuccess)
-    return FA_ERR_WORKSPACE;
-  p.Dws = static_cast<float*>(ws);
-  const hipError_t e = fa::launch_backward(p, dtype, D, stream);
+  const int wst = fa::library_workspace(b_d + 3 * b_q + 2 * b_k + b_gq + 2 * b_gk, stream, &ws);
+  if (wst != FA_OK) return wst;
+  char* w = static_cast<char*>(ws);
+  p.Dws = reinterpret_cast<float*>(w);
+  hipError_t e = hipSuccess;
+  if (padded) {
+    char* q = w + b_d;
+    char* o = q + b_q;
+    char* go = o + b_q;
+    char* k = go + b_q;
+    char* v = k + b_k;
+    float* gq = reinterpret_cast<float*>(v + b_k);
+    float* gk = reinterpret_cast<float*>(reinterpret_cast<char*>(gq) + b_gq);
+    float* gv = reinterpret_cast<float*>(reinterpret_cast<char*>(gk) + b_gk);
+    const struct { const void* src; void* dst; size_t rows; } pads[5] = {
+        {Q, q, nq}, {O, o, nq}, {dO, go, nq}, {K, k, nk}, {V, v, nk}};
+    for (const auto& t : pads)
+      if (e == hipSuccess) e = fa::launch_pad_rows(t.src, t.dst, (long)t.rows, 2 * D, 2 * DT, stream);
+    p.Q = q;
+    p.O = o;
+    p.dO = go;
+    p.K = k;
+    p.V = v;
+    p.dQ = gq;
+    p.dK = gk;
+    p.dV = gv;
+    if (e == hipSuccess) e = fa::launch_backward(p, dtype, DT, stream);
+    if (e == hipSuccess) e = fa::launch_unpad_rows(gq, dQ, (long)nq, DT, D, stream);
+    if (e == hipSuccess) e = fa::launch_unpad_rows(gk, dK, (long)nk, DT, D, stream);
+    if (e == hipSuccess) e = fa::launch_unpad_rows(gv, dV, (long)nk, DT, D, stream);
+  } else {
+    e = fa::launch_backward(p, dtype, D, stream);
+  }
   const hipError_t f = hipFreeAsync(ws, stream);
   return (e == hipSuccess && f == hipSuccess) ? FA_OK : FA_ERR_HIP;
 }

@@ -140,9 +140,9 @@ def bench_backward(args, wl, inp, q, k, v, torch, fa):
     ev_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     flops = 2.5 * counted_flops(wl)          # 10 D per visible pair
-    # 16-bit inputs at D = 64 and 128 run the MFMA backward kernels; the rest
-    # the per-row VALU kernels
-    if wl.dtype != "f32" and wl.D in (64, 128):
+    # 16-bit inputs at D <= 128 run the MFMA backward kernels (head dims other
+    # than 64 and 128 on zero-padded copies); the rest the per-row VALU kernels
+    if wl.dtype != "f32" and wl.D <= 128:
         bound, peak = "mfma", PEAK_TFLOPS[wl.dtype]
     else:
         bound, peak = "alu", PEAK_VALU_F32

@@ -214,8 +214,11 @@ int fa_schedule_table(int B, int H, int HKV, int Sq, int Sk, int D,
  *   visible key) get dQ = 0 and contribute nothing.
  *
  * Contiguous tensors only; no block mask. All buffers 16-byte aligned. A
- * [B, H, Sq] float32 workspace comes from the device's default memory pool,
- * stream-ordered. Asynchronous on `stream`. Errors as fa_fwd.
+ * [B, H, Sq] float32 workspace comes from the library's stream-ordered memory
+ * pool (the one fa_release trims). For bf16/fp16 inputs at D = 16, 32, 48,
+ * 80 or 96 the work runs on copies of Q, K, V, O, dO (and of the fp32
+ * gradients) zero-padded to D = 64 or 128, also from that pool.
+ * Asynchronous on `stream`. Errors as fa_fwd.
  */
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
            const float* LSE, float* dQ, float* dK, float* dV,
