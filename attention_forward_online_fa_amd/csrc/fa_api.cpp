@@ -31,8 +31,11 @@ using SchedKey = std::array<int, 12>;
 struct DeviceState {
   bool init = false;
   int num_cus = 0;
-  int f32_bpc[fa::kForms][3] = {{-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}};   // fp32 workgroups per CU
-                                                                    // [form][D = 64, 128, 256]
+  int f32_bpc[fa::kForms][5];   // fp32 workgroups per CU [form][D = 32, 64, 96, 128, 256]; -1 = not queried
+  DeviceState() {
+    for (auto& f : f32_bpc)
+      for (int& x : f) x = -1;
+  }
   hipMemPool_t pool = nullptr;
   std::map<SchedKey, Sched> scheds;
 };
@@ -86,7 +89,7 @@ int check_args(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int win
                int dtype) {
   if (B < 1 || H < 1 || HKV < 1 || Sq < 1 || Sk < 1 || D < 1) return FA_ERR_SHAPE;
   if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_DTYPE;
-  if (fa::tile_dim(D) == 0) return FA_ERR_HEAD_DIM;
+  if (fa::tile_dim(D, dtype) == 0) return FA_ERR_HEAD_DIM;
   if (H % HKV != 0) return FA_ERR_GQA;
   if (window < 0 || (causal != 0 && causal != 1)) return FA_ERR_WINDOW;
   const int esz = dtype == FA_F32 ? 4 : 2;
@@ -150,7 +153,7 @@ int persistent_slots(DeviceState& s, int B, int H, int Sq, int D, int causal, in
   const int BM = fa::block_m(dtype, D);
   const long qtiles = (long)B * H * ((Sq + BM - 1) / BM);
   if (qtiles >= 2L * s.num_cus) return 0;
-  const int di = D == 64 ? 0 : D == 128 ? 1 : 2;
+  const int di = D == 32 ? 0 : D == 64 ? 1 : D == 96 ? 2 : D == 128 ? 3 : 4;
   int& bpc = s.f32_bpc[form][di];
   if (bpc < 0) bpc = fa::f32_blocks_per_cu(D, form);
   return bpc > 0 ? bpc * s.num_cus : 0;
@@ -333,10 +336,11 @@ void tensor_strides(const long long* given, int heads, int S, int D, long long o
 // the other head dims addresses each copied chunk in full); every element
 // offset fits far inside int64.
 int check_strides(const long long st[3], int B, int heads, int S, int D, int esz, bool kv) {
+  const int dtype = esz == 4 ? FA_F32 : FA_BF16;   // (the 16-bit types share their tiles)
   for (int a = 0; a < 3; ++a)
     if (st[a] < 0 || (st[a] * esz) % 16 != 0) return FA_ERR_STRIDE;
   if (st[2] < D) return FA_ERR_STRIDE;
-  if (kv && ((fa::tile_dim(D) == D && st[2] % D != 0) ||
+  if (kv && ((fa::tile_dim(D, dtype) == D && st[2] % D != 0) ||
              (double)st[2] * esz * 64 >= 2147483647.0))
     return FA_ERR_STRIDE;
   const double last = (double)(B - 1) * st[0] + (double)(heads - 1) * st[1] +
@@ -400,10 +404,10 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   tensor_strides(nullptr, HKV, Sk, D, ck);
   const bool same_q = std::equal(qs, qs + 3, cq) && std::equal(os, os + 3, cq);
   const bool same_kv = std::equal(ks, ks + 3, ck) && std::equal(vs, vs + 3, ck);
-  // Head dims 16 .. 96 other than 64 run the padded form on the 64 or 128
-  // tile (any strides; no block mask).
-  const int DT = fa::tile_dim(D);
-  if (DT != D && bm) return FA_ERR_HEAD_DIM;
+  // Head dims below their kernel's tile dim run the padded form (any
+  // strides); block masks take D = 64, 128 or 256.
+  const int DT = fa::tile_dim(D, dtype);
+  if (bm && D != 64 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
   const int form = DT != D ? fa::kFormPadded
                    : bm    ? fa::kFormBlockSparse
                    : (same_q && same_kv) ? fa::kFormContiguous : fa::kFormStrided;
@@ -550,7 +554,7 @@ int fa_plan_splits(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int
   st = device_state(&ds);
   if (st != FA_OK) return -st;
   int ns = 1, split_len = 0, nslot = 0;
-  const int DT = fa::tile_dim(D);
+  const int DT = fa::tile_dim(D, dtype);
   plan(*ds, 0, B, H, Sq, Sk, DT, causal, window, dtype,
        DT != D ? fa::kFormPadded : fa::kFormContiguous, &ns, &split_len, &nslot);
   return ns;
@@ -565,7 +569,7 @@ int fa_schedule_table(int B, int H, int HKV, int Sq, int Sk, int D, int causal, 
   const long items = (long)B * H * FA_MAX_SPLITS * ((Sq + BM - 1) / BM);
   if (items + nslot + 1 > 2147483647L) return -FA_ERR_SHAPE;
   int ns = 1, split_len = 0;
-  const int DT = fa::tile_dim(D);
+  const int DT = fa::tile_dim(D, dtype);
   resolve_splits(persistent_splits(B, H, Sq, Sk, DT, causal, window, dtype, nslot), B, H, Sq, Sk,
                  DT, causal, window, dtype, 1, &ns, &split_len);
   const std::vector<int> t =

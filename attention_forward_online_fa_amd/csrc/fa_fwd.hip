@@ -858,6 +858,7 @@ void merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpa
                   int H, int Sq, long long os0, long long os1, long long os2, int dv) {
   constexpr int TPR = D / 4;               // threads per row, 4 dims each
   constexpr int RPB = kThreads / TPR;
+  if (threadIdx.x >= RPB * TPR) return;    // (D = 96: 16 threads left over)
   const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
   const int c = threadIdx.x % TPR;
   if (row >= rows) return;
@@ -918,7 +919,9 @@ static int f32_occupancy(int form) {
 }
 
 int f32_blocks_per_cu(int D, int form) {
+  if (D == 32) return f32_occupancy<32>(form);
   if (D == 64) return f32_occupancy<64>(form);
+  if (D == 96) return f32_occupancy<96>(form);
   if (D == 128) return f32_occupancy<128>(form);
   if (D == 256) return f32_occupancy<256>(form);
   return 0;
@@ -948,7 +951,7 @@ static hipError_t launch_16b(const Params& p, bool bf16, long blocks, hipStream_
     switch (p.dv) {
 #define FA_PADDED_DV(X)                                                                   \
       case X:                                                                             \
-        if constexpr (tile_dim(X) == D)                                                   \
+        if constexpr (tile_dim(X, 1) == D)                                                \
           return bf16 ? launch_16b_e<__bf16, D, BN, Form, X>(p, blocks, stream)            \
                       : launch_16b_e<_Float16, D, BN, Form, X>(p, blocks, stream);        \
         return hipErrorInvalidValue;
@@ -973,16 +976,21 @@ static hipError_t launch_d(const Params& p, int dtype, hipStream_t stream) {
   constexpr int BN = D >= 128 ? 32 : 64;
   // (the 16-bit kernel has no persistent form; sched is ignored)
   if (dtype == 1 || dtype == 2) {
-    const hipError_t e = launch_16b<D, BN, Form>(p, dtype == 1, blocks, stream);
-    if (e != hipSuccess) return e;
+    if constexpr (D == 32 || D == 96) return hipErrorInvalidValue;   // fp32-only tile dims
+    else {
+      const hipError_t e = launch_16b<D, BN, Form>(p, dtype == 1, blocks, stream);
+      if (e != hipSuccess) return e;
+    }
   } else {
     const long grid = p.sched ? (long)p.nslot : blocks;
     hipLaunchKernelGGL((fwd_f32_kernel<D, Form>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  if (dtype == 1) return launch_merge<__bf16, D, Strided>(p, stream);
-  if (dtype == 2) return launch_merge<_Float16, D, Strided>(p, stream);
+  if constexpr (D != 32 && D != 96) {
+    if (dtype == 1) return launch_merge<__bf16, D, Strided>(p, stream);
+    if (dtype == 2) return launch_merge<_Float16, D, Strided>(p, stream);
+  }
   return launch_merge<float, D, Strided>(p, stream);
 }
 
@@ -999,7 +1007,9 @@ static hipError_t launch_form(const Params& p, int dtype, int form, hipStream_t 
 
 hipError_t launch_forward(const Params& p, int dtype, int D, int form, hipStream_t stream) {
   switch (D) {
+    case 32: return launch_form<32>(p, dtype, form, stream);
     case 64: return launch_form<64>(p, dtype, form, stream);
+    case 96: return launch_form<96>(p, dtype, form, stream);
     case 128: return launch_form<128>(p, dtype, form, stream);
     case 256: return launch_form<256>(p, dtype, form, stream);
     default: return hipErrorInvalidValue;

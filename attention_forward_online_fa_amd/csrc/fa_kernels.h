@@ -71,17 +71,21 @@ int block_m(int dtype, int D);
 // tile dim D (0 on error).
 int f32_blocks_per_cu(int D, int form);
 
-// Tile dim of the kernel that serves head dim dv: dv itself for 64, 128 and
-// 256; 64 or 128 for the padded dims 16, 32, 48 and 80, 96 (0: unsupported).
-constexpr int tile_dim(int dv) {
-  return (dv == 64 || dv == 128 || dv == 256) ? dv
-         : (dv == 16 || dv == 32 || dv == 48) ? 64
-         : (dv == 80 || dv == 96) ? 128 : 0;
+// Tile dim of the kernel that serves head dim dv for the input type (0:
+// unsupported). 16-bit kernels: 64, 128, 256 natively; 16, 32, 48 padded to
+// 64 and 80, 96 to 128. fp32 kernel: 32, 64, 96, 128, 256 natively; 16
+// padded to 32, 48 to 64 and 80 to 96.
+constexpr int tile_dim(int dv, int dtype) {
+  if (dv == 64 || dv == 128 || dv == 256) return dv;
+  if (dtype == 0) {
+    return dv == 32 || dv == 96 ? dv : dv == 16 ? 32 : dv == 48 ? 64 : dv == 80 ? 96 : 0;
+  }
+  return (dv == 16 || dv == 32 || dv == 48) ? 64 : (dv == 80 || dv == 96) ? 128 : 0;
 }
 
 // Queue the forward kernel (and the merge kernel when p.nsplit > 1) in the
 // given form at tile dim D (kFormContiguous: p.qs .. p.os and the mask are
-// not read; kFormPadded: D = tile_dim(p.dv), D = 64 or 128).
+// not read; kFormPadded: D = tile_dim(p.dv, dtype) > p.dv).
 hipError_t launch_forward(const Params& p, int dtype, int D, int form, hipStream_t stream);
 
 }  // namespace fa

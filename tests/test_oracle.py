@@ -253,6 +253,8 @@ def test_shift_stability_large_scores():
     (1, 8, 2, 37, 53, 16, 1, 0),     # Sq != Sk, top-left causal
     (2, 2, 1, 50, 50, 8, 1, 7),      # sliding window
     (1, 2, 2, 30, 45, 8, 0, 9),      # window without causal
+    (1, 4, 2, 24, 30, 48, 1, 0),     # head dims of the padded kernel form
+    (1, 2, 1, 20, 20, 96, 0, 6),
 ])
 def test_against_torch_sdpa_float64(shape):
     B, H, HKV, Sq, Sk, D, causal, window = shape
