@@ -70,9 +70,10 @@ enum fa_status {
  *   O    device pointer, [B, H,   Sq, D] contiguous, element type `dtype` (written)
  *   LSE  device pointer, [B, H,   Sq]    contiguous, float32, natural log (written)
  *   D      head dim: 16, 32, 48, 64, 80, 96, 128 or 256 (the head dims the
- *          forge flash_attention.metal page instantiates, and 256). 16 .. 96
- *          other than 64 run on the 64- or 128-dim kernels with the missing
- *          dims held as zeros on chip (no padded copy in memory).
+ *          forge flash_attention.metal page instantiates, and 256). Dims
+ *          without a kernel of their own (bf16/fp16: 16, 32, 48, 80, 96;
+ *          float32: 16, 48, 80) run on the next larger kernel with the
+ *          missing dims held as zeros on chip (no padded copy in memory).
  *   scale  multiplies q.k after the dot product (callers usually pass 1/sqrt(D))
  *   causal 0 or 1; window >= 0 (0 = none)
  *   stream hipStream_t to queue the work on, NULL = the null stream
