@@ -69,43 +69,59 @@ __device__ __forceinline__ void key_rows(const BwdParams& p, int j, int& lo, int
   hi = p.window > 0 ? min(p.Sq, j + p.window) : p.Sq;
 }
 
-// One 16-lane group per query row (b, h, i): D_i, then dQ_i.
+// Rows per 16-lane group in the per-row kernels: two rows of one head share
+// every K/V (dQ) or Q/dO (dK/dV) load and give the group two independent
+// dot-product chains; one at D = 256, where registers run short.
+template <int D>
+constexpr int rows_per_group() { return D <= 128 ? 2 : 1; }
+
+// D_i, then dQ_i, for R consecutive query rows (b, h, i0 ..) per 16-lane group.
 template <typename E, int D>
 __global__ __launch_bounds__(kBwdThreads)
 void bwd_dq_kernel(BwdParams p) {
-  constexpr int NE = D / 16;
+  constexpr int NE = D / 16, R = rows_per_group<D>();
   const int lane = threadIdx.x & 63, l16 = lane & 15;
-  const long row = (long)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
-  const long rows = (long)p.B * p.H * p.Sq;
-  if (row >= rows) return;   // whole 16-lane groups leave together
-  const int i = (int)(row % p.Sq);
-  const long bh = row / p.Sq;
+  const long grp = (long)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
+  const long per_head = (p.Sq + R - 1) / R;
+  if (grp >= (long)p.B * p.H * per_head) return;   // whole 16-lane groups leave together
+  const long bh = grp / per_head;
+  const int i0 = (int)(grp - bh * per_head) * R;
   const int h = (int)(bh % p.H), b = (int)(bh / p.H);
   const int hk = h / (p.H / p.HKV);
-
-  const E* Qr = (const E*)p.Q + row * D + l16 * NE;
-  const E* Or = (const E*)p.O + row * D + l16 * NE;
-  const E* dOr = (const E*)p.dO + row * D + l16 * NE;
   const E* Kh = (const E*)p.K + ((long)b * p.HKV + hk) * p.Sk * D + l16 * NE;
   const E* Vh = (const E*)p.V + ((long)b * p.HKV + hk) * p.Sk * D + l16 * NE;
-
-  float q[NE], o[NE], go[NE], dq[NE];
-  load_part<E, NE>(Qr, q);
-  load_part<E, NE>(Or, o);
-  load_part<E, NE>(dOr, go);
-  float dd = 0.f;
-#pragma unroll
-  for (int e = 0; e < NE; ++e) {
-    dd = fmaf(go[e], o[e], dd);
-    dq[e] = 0.f;
-  }
-  const float Di = group_sum(dd);
-  const float L2 = p.LSE[row] * kLog2e;   // base-2 log-sum-exp (-inf: no visible key)
   const float sl = p.scale * kLog2e;
 
-  int lo, hi;
-  row_keys(p, i, lo, hi);
-  if (L2 == -INFINITY) hi = lo;            // empty row: P = 0 everywhere
+  float q[R][NE], go[R][NE], dq[R][NE], Di[R], L2[R];
+  int rlo[R], rhi[R];
+  int lo = p.Sk, hi = 0;   // union of the rows' visible keys
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = i0 + r;
+    rlo[r] = 0;
+    rhi[r] = 0;
+    float dd = 0.f;
+    L2[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) q[r][e] = go[r][e] = dq[r][e] = 0.f;
+    if (i < p.Sq) {
+      const long row = bh * p.Sq + i;
+      float o[NE];
+      load_part<E, NE>((const E*)p.Q + row * D + l16 * NE, q[r]);
+      load_part<E, NE>((const E*)p.O + row * D + l16 * NE, o);
+      load_part<E, NE>((const E*)p.dO + row * D + l16 * NE, go[r]);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) dd = fmaf(go[r][e], o[e], dd);
+      L2[r] = p.LSE[row] * kLog2e;         // base-2 log-sum-exp (-inf: no visible key)
+      row_keys(p, i, rlo[r], rhi[r]);
+      if (L2[r] == -INFINITY) rhi[r] = rlo[r];   // empty row: P = 0 everywhere
+      if (rlo[r] < rhi[r]) {
+        lo = min(lo, rlo[r]);
+        hi = max(hi, rhi[r]);
+      }
+    }
+    Di[r] = group_sum(dd);
+  }
   // key j + 1's rows are loaded while key j is computed
   float kn[NE], vn[NE];
   if (lo < hi) {
@@ -123,49 +139,78 @@ void bwd_dq_kernel(BwdParams p) {
       load_part<E, NE>(Kh + (long)(j + 1) * D, kn);
       load_part<E, NE>(Vh + (long)(j + 1) * D, vn);
     }
-    float s = 0.f, dp = 0.f;
+    float s[R], dp[R];
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      s = fmaf(q[e], k[e], s);
-      dp = fmaf(go[e], v[e], dp);
+    for (int r = 0; r < R; ++r) {
+      s[r] = dp[r] = 0.f;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        s[r] = fmaf(q[r][e], k[e], s[r]);
+        dp[r] = fmaf(go[r][e], v[e], dp[r]);
+      }
     }
-    s = group_sum(s);
-    dp = group_sum(dp);
-    const float pr = __builtin_amdgcn_exp2f(fmaf(s, sl, -L2));
-    const float ds = pr * (dp - Di);
 #pragma unroll
-    for (int e = 0; e < NE; ++e) dq[e] = fmaf(ds, k[e], dq[e]);
+    for (int r = 0; r < R; ++r) {
+      s[r] = group_sum(s[r]);
+      dp[r] = group_sum(dp[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const bool in = j >= rlo[r] && j < rhi[r];
+      const float pr = in ? __builtin_amdgcn_exp2f(fmaf(s[r], sl, -L2[r])) : 0.f;
+      const float ds = pr * (dp[r] - Di[r]);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) dq[r][e] = fmaf(ds, k[e], dq[r][e]);
+    }
   }
-  float* out = p.dQ + row * D + l16 * NE;
 #pragma unroll
-  for (int e = 0; e < NE; ++e) out[e] = p.scale * dq[e];
-  if (l16 == 0) p.Dws[row] = Di;
+  for (int r = 0; r < R; ++r) {
+    if (i0 + r >= p.Sq) continue;
+    const long row = bh * p.Sq + i0 + r;
+    float* out = p.dQ + row * D + l16 * NE;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) out[e] = p.scale * dq[r][e];
+    if (l16 == 0) p.Dws[row] = Di[r];
+  }
 }
 
-// One 16-lane group per key row (b, hk, j): dK_j and dV_j over the query
-// heads of kv head hk and the query rows that see key j.
+// dK_j and dV_j for R consecutive key rows (b, hk, j0 ..) per 16-lane group,
+// over the query heads of kv head hk and the query rows that see each key.
 template <typename E, int D>
 __global__ __launch_bounds__(kBwdThreads)
 void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NE = D / 16;
+  constexpr int NE = D / 16, R = rows_per_group<D>();
   const int lane = threadIdx.x & 63, l16 = lane & 15;
-  const long krow = (long)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
-  const long krows = (long)p.B * p.HKV * p.Sk;
-  if (krow >= krows) return;
-  const int j = (int)(krow % p.Sk);
-  const long bhk = krow / p.Sk;
+  const long grp = (long)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
+  const long per_head = (p.Sk + R - 1) / R;
+  if (grp >= (long)p.B * p.HKV * per_head) return;
+  const long bhk = grp / per_head;
+  const int j0 = (int)(grp - bhk * per_head) * R;
   const int hk = (int)(bhk % p.HKV), b = (int)(bhk / p.HKV);
   const int g = p.H / p.HKV;
-
-  float k[NE], v[NE], dk[NE], dv[NE];
-  load_part<E, NE>((const E*)p.K + krow * D + l16 * NE, k);
-  load_part<E, NE>((const E*)p.V + krow * D + l16 * NE, v);
-#pragma unroll
-  for (int e = 0; e < NE; ++e) dk[e] = dv[e] = 0.f;
   const float sl = p.scale * kLog2e;
 
-  int lo, hi;
-  key_rows(p, j, lo, hi);
+  float k[R][NE], v[R][NE], dk[R][NE], dv[R][NE];
+  int rlo[R], rhi[R];
+  int lo = p.Sq, hi = 0;   // union of the query rows that see the keys
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int j = j0 + r;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) k[r][e] = v[r][e] = dk[r][e] = dv[r][e] = 0.f;
+    rlo[r] = rhi[r] = 0;
+    if (j < p.Sk) {
+      const long krow = bhk * p.Sk + j;
+      load_part<E, NE>((const E*)p.K + krow * D + l16 * NE, k[r]);
+      load_part<E, NE>((const E*)p.V + krow * D + l16 * NE, v[r]);
+      key_rows(p, j, rlo[r], rhi[r]);
+      if (rlo[r] < rhi[r]) {
+        lo = min(lo, rlo[r]);
+        hi = max(hi, rhi[r]);
+      }
+    }
+  }
+
   for (int h = hk * g; h < hk * g + g; ++h) {
     const long base = ((long)b * p.H + h) * p.Sq;
     // query row i + 1 is loaded while row i is computed
@@ -191,30 +236,46 @@ void bwd_dkdv_kernel(BwdParams p) {
         ln = p.LSE[row + 1];
         dn = p.Dws[row + 1];
       }
-      float s = 0.f, dp = 0.f;
+      float s[R], dp[R];
 #pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        s = fmaf(q[e], k[e], s);
-        dp = fmaf(go[e], v[e], dp);
+      for (int r = 0; r < R; ++r) {
+        s[r] = dp[r] = 0.f;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+          s[r] = fmaf(q[e], k[r][e], s[r]);
+          dp[r] = fmaf(go[e], v[r][e], dp[r]);
+        }
       }
-      s = group_sum(s);
-      dp = group_sum(dp);
-      // row i sees key j, so it is not empty and its LSE is finite
-      const float pr = __builtin_amdgcn_exp2f(fmaf(s, sl, -Li * kLog2e));
-      const float ds = pr * (dp - Di);
 #pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        dv[e] = fmaf(pr, go[e], dv[e]);
-        dk[e] = fmaf(ds, q[e], dk[e]);
+      for (int r = 0; r < R; ++r) {
+        s[r] = group_sum(s[r]);
+        dp[r] = group_sum(dp[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        // a row that sees key j is not empty, so its LSE is finite
+        const bool in = i >= rlo[r] && i < rhi[r];
+        const float pr = in ? __builtin_amdgcn_exp2f(fmaf(s[r], sl, -Li * kLog2e)) : 0.f;
+        const float ds = pr * (dp[r] - Di);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+          dv[r][e] = fmaf(pr, go[e], dv[r][e]);
+          dk[r][e] = fmaf(ds, q[e], dk[r][e]);
+        }
       }
     }
   }
-  float* odk = p.dK + krow * D + l16 * NE;
-  float* odv = p.dV + krow * D + l16 * NE;
 #pragma unroll
-  for (int e = 0; e < NE; ++e) {
-    odk[e] = p.scale * dk[e];
-    odv[e] = dv[e];
+  for (int r = 0; r < R; ++r) {
+    if (j0 + r >= p.Sk) continue;
+    const long krow = bhk * p.Sk + j0 + r;
+    float* odk = p.dK + krow * D + l16 * NE;
+    float* odv = p.dV + krow * D + l16 * NE;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      odk[e] = p.scale * dk[r][e];
+      odv[e] = dv[r][e];
+    }
   }
 }
 
@@ -606,12 +667,13 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
 
 template <typename E, int D>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
-  const long rows = (long)p.B * p.H * p.Sq, krows = (long)p.B * p.HKV * p.Sk;
   if constexpr (sizeof(E) == 2 && (D == 64 || D == 128)) {
     hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D>), dim3((unsigned)((long)p.B * p.H * p.n_qblk)),
                        dim3(kBwdThreads), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+    constexpr int R = rows_per_group<D>();
+    const long groups = (long)p.B * p.H * ((p.Sq + R - 1) / R);
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D>), dim3((unsigned)((groups + kRowsPerBlock - 1) / kRowsPerBlock)),
                        dim3(kBwdThreads), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
@@ -621,7 +683,9 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D>), dim3((unsigned)kblocks), dim3(kBwdThreads), 0,
                        stream, p);
   } else {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>), dim3((unsigned)((krows + kRowsPerBlock - 1) / kRowsPerBlock)),
+    constexpr int R = rows_per_group<D>();
+    const long groups = (long)p.B * p.HKV * ((p.Sk + R - 1) / R);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>), dim3((unsigned)((groups + kRowsPerBlock - 1) / kRowsPerBlock)),
                        dim3(kBwdThreads), 0, stream, p);
   }
   return hipGetLastError();
