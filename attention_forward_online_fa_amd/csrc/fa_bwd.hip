@@ -13,12 +13,14 @@
 // D_i is computed once per query row by the dQ kernel and handed to the dK/dV
 // kernel through a workspace.
 //
-// Work decomposition: a group of 16 lanes owns one row (a query row in the
-// dQ kernel, a key row in the dK/dV kernel) and holds D/16 consecutive
-// elements of each row vector per lane; dot products reduce over the 16 lanes
-// with four DPP row rotations. A wavefront serves four rows, a workgroup 16. This
-// is the pages' thread-per-row design mapped to wavefronts, on the VALU (no
-// MFMA): a baseline that is exact to fp32 rounding, not a tuned kernel.
+// Work decomposition: a group of 16 lanes owns two consecutive rows of one
+// head (one row at D = 256): query rows in the dQ kernel, key rows in the
+// dK/dV kernel. A lane holds D/16 consecutive elements of each row vector;
+// dot products reduce over the 16 lanes with four DPP row rotations. A
+// wavefront holds four groups, a workgroup 16. This is the pages'
+// thread-per-row design mapped to wavefronts, on the VALU (no MFMA): exact to
+// fp32 rounding, used for fp32 inputs and D = 256; the MFMA kernels below
+// serve 16-bit inputs at D = 64 and 128.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
