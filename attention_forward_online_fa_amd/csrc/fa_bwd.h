@@ -27,6 +27,15 @@ struct BwdParams {
   float sl_abs;
   int neg_q;
   int n_qblk;
+  // Per-row kernels (fp32 inputs, D = 256) on small grids: each row group's
+  // range is cut into nch chunks of chunk_q keys (dQ kernel) or chunk_k query
+  // rows (dK/dV kernel), one per blockIdx.y; chunk c writes unscaled partial
+  // sums to part_q [nch][B H Sq][D] and part_k, part_v [nch][B HKV Sk][D],
+  // which are then added up in chunk order. nch = 1: gradients written directly.
+  int nch, chunk_q, chunk_k;
+  float* part_q;
+  float* part_k;
+  float* part_v;
 };
 
 // Queue the dQ kernel (which also writes Dws) and then the dK/dV kernel.

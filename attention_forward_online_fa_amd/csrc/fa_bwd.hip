@@ -124,6 +124,11 @@ void bwd_dq_kernel(BwdParams p) {
     }
     Di[r] = group_sum(dd);
   }
+  if (p.nch > 1) {   // this launch's chunk of the union (empty past its end)
+    const int c0 = lo + (int)blockIdx.y * p.chunk_q;
+    hi = min(hi, c0 + p.chunk_q);
+    lo = c0;
+  }
   // key j + 1's rows are loaded while key j is computed
   float kn[NE], vn[NE];
   if (lo < hi) {
@@ -169,10 +174,16 @@ void bwd_dq_kernel(BwdParams p) {
   for (int r = 0; r < R; ++r) {
     if (i0 + r >= p.Sq) continue;
     const long row = bh * p.Sq + i0 + r;
-    float* out = p.dQ + row * D + l16 * NE;
+    if (p.nch > 1) {
+      float* out = p.part_q + ((long)blockIdx.y * p.B * p.H * p.Sq + row) * D + l16 * NE;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) out[e] = p.scale * dq[r][e];
-    if (l16 == 0) p.Dws[row] = Di[r];
+      for (int e = 0; e < NE; ++e) out[e] = dq[r][e];
+    } else {
+      float* out = p.dQ + row * D + l16 * NE;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) out[e] = p.scale * dq[r][e];
+    }
+    if (l16 == 0 && blockIdx.y == 0) p.Dws[row] = Di[r];
   }
 }
 
@@ -211,6 +222,11 @@ void bwd_dkdv_kernel(BwdParams p) {
         hi = max(hi, rhi[r]);
       }
     }
+  }
+  if (p.nch > 1) {   // this launch's chunk of the union, in every query head
+    const int c0 = lo + (int)blockIdx.y * p.chunk_k;
+    hi = min(hi, c0 + p.chunk_k);
+    lo = c0;
   }
 
   for (int h = hk * g; h < hk * g + g; ++h) {
@@ -271,11 +287,14 @@ void bwd_dkdv_kernel(BwdParams p) {
   for (int r = 0; r < R; ++r) {
     if (j0 + r >= p.Sk) continue;
     const long krow = bhk * p.Sk + j0 + r;
-    float* odk = p.dK + krow * D + l16 * NE;
-    float* odv = p.dV + krow * D + l16 * NE;
+    const bool part = p.nch > 1;
+    const long prow = (long)blockIdx.y * p.B * p.HKV * p.Sk + krow;
+    float* odk = (part ? p.part_k + prow * D : p.dK + krow * D) + l16 * NE;
+    float* odv = (part ? p.part_v + prow * D : p.dV + krow * D) + l16 * NE;
+    const float ks = part ? 1.f : p.scale;
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
-      odk[e] = p.scale * dk[r][e];
+      odk[e] = ks * dk[r][e];
       odv[e] = dv[r][e];
     }
   }
@@ -667,6 +686,31 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   }
 }
 
+// out = scale * sum over c < nch of part[c] (n4 float4 per part), in chunk order.
+__global__ __launch_bounds__(256) void sum_parts_kernel(const float4* __restrict__ part,
+                                                        float4* __restrict__ out, long n4, int nch,
+                                                        float scale) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n4) return;
+  float4 acc = part[idx];
+  for (int c = 1; c < nch; ++c) {
+    const float4 x = part[c * n4 + idx];
+    acc.x += x.x;
+    acc.y += x.y;
+    acc.z += x.z;
+    acc.w += x.w;
+  }
+  out[idx] = make_float4(acc.x * scale, acc.y * scale, acc.z * scale, acc.w * scale);
+}
+
+static hipError_t sum_parts(const float* part, float* out, long n, int nch, float scale,
+                            hipStream_t stream) {
+  const long n4 = n / 4;
+  hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                     (const float4*)part, (float4*)out, n4, nch, scale);
+  return hipGetLastError();
+}
+
 template <typename E, int D>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   if constexpr (sizeof(E) == 2 && (D == 64 || D == 128)) {
@@ -675,11 +719,16 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   } else {
     constexpr int R = rows_per_group<D>();
     const long groups = (long)p.B * p.H * ((p.Sq + R - 1) / R);
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D>), dim3((unsigned)((groups + kRowsPerBlock - 1) / kRowsPerBlock)),
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D>),
+                       dim3((unsigned)((groups + kRowsPerBlock - 1) / kRowsPerBlock), (unsigned)p.nch),
                        dim3(kBwdThreads), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.nch > 1) {
+    e = sum_parts(p.part_q, p.dQ, (long)p.B * p.H * p.Sq * D, p.nch, p.scale, stream);
+    if (e != hipSuccess) return e;
+  }
   if constexpr (sizeof(E) == 2 && (D == 64 || D == 128)) {
     const long kblocks = (long)p.B * p.HKV * ((p.Sk + 127) / 128);
     hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D>), dim3((unsigned)kblocks), dim3(kBwdThreads), 0,
@@ -687,10 +736,16 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   } else {
     constexpr int R = rows_per_group<D>();
     const long groups = (long)p.B * p.HKV * ((p.Sk + R - 1) / R);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>), dim3((unsigned)((groups + kRowsPerBlock - 1) / kRowsPerBlock)),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>),
+                       dim3((unsigned)((groups + kRowsPerBlock - 1) / kRowsPerBlock), (unsigned)p.nch),
                        dim3(kBwdThreads), 0, stream, p);
   }
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess || p.nch == 1) return e;
+  const long nk = (long)p.B * p.HKV * p.Sk * D;
+  e = sum_parts(p.part_k, p.dK, nk, p.nch, p.scale, stream);
+  if (e != hipSuccess) return e;
+  return sum_parts(p.part_v, p.dV, nk, p.nch, 1.f, stream);
 }
 
 template <typename E>

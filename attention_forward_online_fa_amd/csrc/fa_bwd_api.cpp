@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -79,11 +80,44 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
   const size_t b_d = up(nq * sizeof(float));
   const size_t b_q = padded ? up(nq * DT * 2) : 0, b_k = padded ? up(nk * DT * 2) : 0;
   const size_t b_gq = padded ? up(nq * DT * 4) : 0, b_gk = padded ? up(nk * DT * 4) : 0;
+  // The per-row kernels (fp32 inputs, D = 256) on grids too small to fill the
+  // GPU: each row group's range is cut into nch chunks that run side by side
+  // (a causal grid is otherwise bound by its longest rows), their partial
+  // sums added up afterwards in chunk order (deterministic). A group's range
+  // spans at most `span` + 1 keys (query rows): two adjacent rows' ranges.
+  p.nch = 1;
+  if (dtype == FA_F32 || D == 256) {
+    const int R = D <= 128 ? 2 : 1;
+    const long groups = (long)B * H * ((Sq + R - 1) / R);
+    const long target = 1L << 18;   // row groups that fill the GPU several times over
+    // keys per query row and query rows per key: at most `window` only under
+    // causal + window (a window alone bounds one side)
+    const bool band = causal && window > 0;
+    const long span_q = (band ? std::min(Sk, window) : Sk) + R - 1;
+    const long span_k = (band ? std::min(Sq, window) : Sq) + R - 1;
+    if (groups < target) {
+      long n = std::min({(target + groups - 1) / groups, (std::max(span_q, span_k) + 127) / 128, 8L});
+      const double per_chunk = (double)(nq + 2 * nk) * D * 4;
+      while (n > 1 && n * per_chunk > 512.0 * (1 << 20)) --n;   // workspace at most 512 MiB
+      p.nch = (int)std::max(1L, n);
+    }
+    p.chunk_q = (int)((span_q + p.nch - 1) / p.nch);
+    p.chunk_k = (int)((span_k + p.nch - 1) / p.nch);
+  }
+  const size_t b_pq = p.nch > 1 ? up((size_t)p.nch * nq * D * 4) : 0;
+  const size_t b_pk = p.nch > 1 ? up((size_t)p.nch * nk * D * 4) : 0;
   void* ws = nullptr;
-  const int wst = fa::library_workspace(b_d + 3 * b_q + 2 * b_k + b_gq + 2 * b_gk, stream, &ws);
+  const int wst = fa::library_workspace(b_d + 3 * b_q + 2 * b_k + b_gq + 2 * b_gk + b_pq + 2 * b_pk,
+                                        stream, &ws);
   if (wst != FA_OK) return wst;
   char* w = static_cast<char*>(ws);
   p.Dws = reinterpret_cast<float*>(w);
+  if (p.nch > 1) {
+    char* pp = w + b_d + 3 * b_q + 2 * b_k + b_gq + 2 * b_gk;
+    p.part_q = reinterpret_cast<float*>(pp);
+    p.part_k = reinterpret_cast<float*>(pp + b_pq);
+    p.part_v = reinterpret_cast<float*>(pp + b_pq + b_pk);
+  }
   hipError_t e = hipSuccess;
   if (padded) {
     char* q = w + b_d;

@@ -68,6 +68,15 @@ CASES += [
     ("bf16", 2, 2, 1, 900, 600, 128, 0, 250),
 ]
 
+# small grids on the per-row kernels (fp32, D = 256): the rows' ranges run in
+# up to eight chunks whose partial sums are added afterwards
+CASES += [
+    ("f32", 1, 2, 1, 1024, 1024, 64, 1, 0),      # eight chunks, causal
+    ("f32", 1, 2, 2, 600, 900, 32, 0, 100),      # a window alone: ranges up to Sk / Sq
+    ("f32", 1, 4, 1, 800, 800, 96, 1, 300),      # causal band of 300
+    ("bf16", 1, 2, 1, 600, 700, 256, 0, 0),      # one row per group
+]
+
 
 @pytest.mark.parametrize("case", CASES, ids=["-".join(map(str, c)) for c in CASES])
 def test_backward_matches_oracle(case):
@@ -96,6 +105,19 @@ def test_backward_empty_rows_and_unseen_keys(dtype):
             assert np.all(dq[:, :, Sk:] == 0)
         for g, r in zip((dq, dk, dv), ref):
             assert float(np.abs(g - r).max()) <= TOL[dtype] * max(1.0, float(np.abs(r).max()))
+
+
+def test_backward_deterministic_fp32_chunked():
+    # fp32 on a small grid: chunked ranges, partial sums added in a fixed order
+    import attention_forward_online_fa_amd as fa
+    wl = wl_small("f32", 1, 2, 1, 900, 900, 64, 1, 0, seed=6)
+    q, k, v = to_device(W.make_inputs(wl))
+    do = torch.randn_like(q)
+    o, lse = fa.fwd(q, k, v, causal=True)
+    a = fa.bwd(q, k, v, o, lse, do, causal=True)
+    b = fa.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
 
 
 def test_backward_deterministic():
