@@ -20,7 +20,9 @@
 // wavefront holds four groups, a workgroup 16. This is the pages'
 // thread-per-row design mapped to wavefronts, on the VALU (no MFMA): exact to
 // fp32 rounding, used for fp32 inputs and D = 256; the MFMA kernels below
-// serve 16-bit inputs at D = 64 and 128.
+// serve 16-bit inputs at D = 64 and 128. On small grids the per-row kernels
+// run each group's range in chunks (blockIdx.y) whose partial sums
+// sum_parts_kernel adds in chunk order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

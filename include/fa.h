@@ -218,7 +218,9 @@ int fa_schedule_table(int B, int H, int HKV, int Sq, int Sk, int D,
  * [B, H, Sq] float32 workspace comes from the library's stream-ordered memory
  * pool (the one fa_release trims). For bf16/fp16 inputs at D = 16, 32, 48,
  * 80 or 96 the work runs on copies of Q, K, V, O, dO (and of the fp32
- * gradients) zero-padded to D = 64 or 128, also from that pool.
+ * gradients) zero-padded to D = 64 or 128, also from that pool. float32
+ * inputs (and D = 256) on small grids take up to 512 MiB more there for
+ * partial sums, added up in a fixed order (results stay deterministic).
  * Asynchronous on `stream`. Errors as fa_fwd.
  */
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
