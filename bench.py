@@ -7,7 +7,10 @@ A step is one fa_fwd call (every kernel of the forward pass, including the
 key-split merge when the library splits) over one batch of synthetic inputs
 that are resident in HBM before timing starts. W untimed warm-up steps run
 first, then more untimed steps for --warmup-seconds (clock ramp-up), then
-exactly K timed steps. The default workload is the
+exactly K timed steps (HIP events on the launch stream bracket them; their
+mean is roofline.kernel_ms), then 100 more steps (20 backward) each
+bracketed by its own events, whose median and minimum are
+roofline.per_step_events. The default workload is the
 bf16 causal GQA configuration (B=2, H=32, HKV=8, S=4096, D=128), the one the
 headline metric is quoted on. Prints one JSON line.
 
@@ -77,6 +80,21 @@ def algorithmic_bytes(wl: W.Workload) -> int:
     return q + kv + q + wl.B * wl.H * wl.Sq * 4
 
 
+def per_step_events(step, stream, n: int) -> dict:
+    """Median and minimum of n steps each bracketed by its own pair of HIP
+    events on the launch stream (after the timed region; not part of it)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return {"n": n, "median_ms": round(float(np.median(ms)), 5), "min_ms": round(ms[0], 5)}
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -139,6 +157,7 @@ def bench_backward(args, wl, inp, q, k, v, torch, fa):
     wall = time.perf_counter() - t0
     ev_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
+    per_step = per_step_events(step, stream, 20)
     flops = 2.5 * counted_flops(wl)          # 10 D per visible pair
     # 16-bit inputs at D <= 128 run the MFMA backward kernels (head dims other
     # than 64 and 128 on zero-padded copies); the rest the per-row VALU kernels
@@ -158,6 +177,7 @@ def bench_backward(args, wl, inp, q, k, v, torch, fa):
         "roofline": {"bound": bound, "achieved": round(flops / (ev_ms * 1e-3) / 1e12, 3),
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": round(flops / (ev_ms * 1e-3) / 1e12 / peak, 4),
+                     "per_step_events": per_step,
                      "traffic": None, "kernel_ms": round(ev_ms, 5)},
     }
     if args.cpu_rows > 0:
@@ -286,6 +306,7 @@ def main():
     wall = time.perf_counter() - t0
     ev_ms = ev0.elapsed_time(ev1) / args.steps          # HIP events on the launch stream
     ms_per_step = wall * 1e3 / args.steps
+    per_step = per_step_events(step, stream, 100)
 
     flops = counted_flops(wl, inp.block_mask)
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -315,6 +336,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic,
                      "kernel_ms": round(ev_ms, 5),
+                     "per_step_events": per_step,
                      "algorithmic_bytes": algorithmic_bytes(wl)},
     }
     if args.cpu_rows > 0:
