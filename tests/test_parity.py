@@ -265,3 +265,23 @@ def test_fp32_causal_small_grid_runs_persistent_pieces():
     assert fa.plan_splits(2, 4, 4, 640, 640, 64, causal=True, dtype="f32") > 1
     check_full(small)
     check_full(small)
+
+
+# ------------------------------------------------------- very long key axis
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("splits", [0, 64])
+def test_very_long_key_axis(dtype, splits):
+    # one query tile over a million keys (ragged): the key axis is split into
+    # up to FA_MAX_SPLITS pieces of ~16k keys each and merged; every row checked
+    import attention_forward_online_fa_amd as fa
+    wl = wl_small(dtype, 1, 1, 1, 64, 1_000_003, 64, 0, 0, name="longkeys", seed=77)
+    inp = W.make_inputs(wl)
+    _say(f"[parity] {wl} splits={splits}")
+    q, k, v = to_device(inp)
+    o, lse = fa.fwd(q, k, v, scale=wl.scale(), num_splits=splits)
+    torch.cuda.synchronize()
+    if splits == 0:
+        assert fa.plan_splits(1, 1, 1, 64, wl.Sk, 64, dtype=dtype) == 64
+    rows = np.array([(0, 0, i) for i in range(wl.Sq)])
+    O, L = attention_rows(inp.q, inp.k, inp.v, wl.scale(), False, 0, rows)
+    compare(host64(o)[0, 0], host64(lse)[0, 0], O, L, TOL[wl.dtype], wl.name)
