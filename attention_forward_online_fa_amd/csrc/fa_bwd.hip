@@ -13,11 +13,11 @@
 // D_i is computed once per query row by the dQ kernel and handed to the dK/dV
 // kernel through a workspace.
 //
-// Work decomposition: a group of 16 lanes owns two consecutive rows of one
-// head (one row at D = 256): query rows in the dQ kernel, key rows in the
-// dK/dV kernel. A lane holds D/16 consecutive elements of each row vector;
-// dot products reduce over the 16 lanes with four DPP row rotations. A
-// wavefront holds four groups, a workgroup 16. This is the pages'
+// Work decomposition: a group of G = 4, 8 or 16 lanes (the fewest that keep
+// D / G <= 8) owns two consecutive rows of one head (one row at D = 256):
+// query rows in the dQ kernel, key rows in the dK/dV kernel. A lane holds
+// D / G consecutive elements of each row vector; dot products reduce over
+// the group with two to four DPP steps. This is the pages'
 // thread-per-row design mapped to wavefronts, on the VALU (no MFMA): exact to
 // fp32 rounding, used for fp32 inputs and D = 256; the MFMA kernels below
 // serve 16-bit inputs at D = 64 and 128. On small grids the per-row kernels
@@ -32,7 +32,7 @@
 namespace fa {
 
 constexpr int kBwdThreads = 256;   // 4 wavefronts x 4 rows
-constexpr int kRowsPerBlock = 16;
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <typename E>
@@ -47,11 +47,26 @@ __device__ __forceinline__ float row_ror(float x) {
 
 // Sum over the 16 lanes of one row group (every lane gets the total):
 // register-to-register rotations within the row, no LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the G lanes of one group (G = 4, 8 or 16, aligned): quad_perm
+// swaps within each 4 lanes, then row_half_mirror (8) or row rotations (16).
+template <int G>
 __device__ __forceinline__ float group_sum(float x) {
-  x += row_ror<8>(x);
-  x += row_ror<4>(x);
-  x += row_ror<2>(x);
-  x += row_ror<1>(x);
+  if constexpr (G == 16) {
+    x += row_ror<8>(x);
+    x += row_ror<4>(x);
+    x += row_ror<2>(x);
+    x += row_ror<1>(x);
+  } else {
+    x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+    x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+    if constexpr (G == 8) x += dpp<0x141>(x);   // row_half_mirror: the other quad of 8
+  }
   return x;
 }
 
@@ -77,23 +92,23 @@ __device__ __forceinline__ void key_rows(const BwdParams& p, int j, int& lo, int
 // every K/V (dQ) or Q/dO (dK/dV) load and give the group two independent
 // dot-product chains; one at D = 256, where registers run short.
 template <int D>
-constexpr int rows_per_group() { return D <= 128 ? 2 : 1; }
+constexpr int rows_per_group() { return bwd_rows_per_group(D); }
 
 // D_i, then dQ_i, for R consecutive query rows (b, h, i0 ..) per 16-lane group.
 template <typename E, int D>
 __global__ __launch_bounds__(kBwdThreads)
 void bwd_dq_kernel(BwdParams p) {
-  constexpr int NE = D / 16, R = rows_per_group<D>();
-  const int lane = threadIdx.x & 63, l16 = lane & 15;
-  const long grp = (long)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
+  constexpr int G = bwd_lanes_per_row(D), NE = D / G, R = rows_per_group<D>();
+  const int lg = threadIdx.x & (G - 1);    // lane within the group
+  const long grp = (long)blockIdx.x * (kBwdThreads / G) + threadIdx.x / G;
   const long per_head = (p.Sq + R - 1) / R;
   if (grp >= (long)p.B * p.H * per_head) return;   // whole 16-lane groups leave together
   const long bh = grp / per_head;
   const int i0 = (int)(grp - bh * per_head) * R;
   const int h = (int)(bh % p.H), b = (int)(bh / p.H);
   const int hk = h / (p.H / p.HKV);
-  const E* Kh = (const E*)p.K + ((long)b * p.HKV + hk) * p.Sk * D + l16 * NE;
-  const E* Vh = (const E*)p.V + ((long)b * p.HKV + hk) * p.Sk * D + l16 * NE;
+  const E* Kh = (const E*)p.K + ((long)b * p.HKV + hk) * p.Sk * D + lg * NE;
+  const E* Vh = (const E*)p.V + ((long)b * p.HKV + hk) * p.Sk * D + lg * NE;
   const float sl = p.scale * kLog2e;
 
   float q[R][NE], go[R][NE], dq[R][NE], Di[R], L2[R];
@@ -111,9 +126,9 @@ void bwd_dq_kernel(BwdParams p) {
     if (i < p.Sq) {
       const long row = bh * p.Sq + i;
       float o[NE];
-      load_part<E, NE>((const E*)p.Q + row * D + l16 * NE, q[r]);
-      load_part<E, NE>((const E*)p.O + row * D + l16 * NE, o);
-      load_part<E, NE>((const E*)p.dO + row * D + l16 * NE, go[r]);
+      load_part<E, NE>((const E*)p.Q + row * D + lg * NE, q[r]);
+      load_part<E, NE>((const E*)p.O + row * D + lg * NE, o);
+      load_part<E, NE>((const E*)p.dO + row * D + lg * NE, go[r]);
 #pragma unroll
       for (int e = 0; e < NE; ++e) dd = fmaf(go[r][e], o[e], dd);
       L2[r] = p.LSE[row] * kLog2e;         // base-2 log-sum-exp (-inf: no visible key)
@@ -124,7 +139,7 @@ void bwd_dq_kernel(BwdParams p) {
         hi = max(hi, rhi[r]);
       }
     }
-    Di[r] = group_sum(dd);
+    Di[r] = group_sum<G>(dd);
   }
   if (p.nch > 1) {   // this launch's chunk of the union (empty past its end)
     const int c0 = lo + (int)blockIdx.y * p.chunk_q;
@@ -160,8 +175,8 @@ void bwd_dq_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      s[r] = group_sum(s[r]);
-      dp[r] = group_sum(dp[r]);
+      s[r] = group_sum<G>(s[r]);
+      dp[r] = group_sum<G>(dp[r]);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -177,15 +192,15 @@ void bwd_dq_kernel(BwdParams p) {
     if (i0 + r >= p.Sq) continue;
     const long row = bh * p.Sq + i0 + r;
     if (p.nch > 1) {
-      float* out = p.part_q + ((long)blockIdx.y * p.B * p.H * p.Sq + row) * D + l16 * NE;
+      float* out = p.part_q + ((long)blockIdx.y * p.B * p.H * p.Sq + row) * D + lg * NE;
 #pragma unroll
       for (int e = 0; e < NE; ++e) out[e] = dq[r][e];
     } else {
-      float* out = p.dQ + row * D + l16 * NE;
+      float* out = p.dQ + row * D + lg * NE;
 #pragma unroll
       for (int e = 0; e < NE; ++e) out[e] = p.scale * dq[r][e];
     }
-    if (l16 == 0 && blockIdx.y == 0) p.Dws[row] = Di[r];
+    if (lg == 0 && blockIdx.y == 0) p.Dws[row] = Di[r];
   }
 }
 
@@ -194,9 +209,9 @@ void bwd_dq_kernel(BwdParams p) {
 template <typename E, int D>
 __global__ __launch_bounds__(kBwdThreads)
 void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NE = D / 16, R = rows_per_group<D>();
-  const int lane = threadIdx.x & 63, l16 = lane & 15;
-  const long grp = (long)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
+  constexpr int G = bwd_lanes_per_row(D), NE = D / G, R = rows_per_group<D>();
+  const int lg = threadIdx.x & (G - 1);    // lane within the group
+  const long grp = (long)blockIdx.x * (kBwdThreads / G) + threadIdx.x / G;
   const long per_head = (p.Sk + R - 1) / R;
   if (grp >= (long)p.B * p.HKV * per_head) return;
   const long bhk = grp / per_head;
@@ -216,8 +231,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     rlo[r] = rhi[r] = 0;
     if (j < p.Sk) {
       const long krow = bhk * p.Sk + j;
-      load_part<E, NE>((const E*)p.K + krow * D + l16 * NE, k[r]);
-      load_part<E, NE>((const E*)p.V + krow * D + l16 * NE, v[r]);
+      load_part<E, NE>((const E*)p.K + krow * D + lg * NE, k[r]);
+      load_part<E, NE>((const E*)p.V + krow * D + lg * NE, v[r]);
       key_rows(p, j, rlo[r], rhi[r]);
       if (rlo[r] < rhi[r]) {
         lo = min(lo, rlo[r]);
@@ -236,8 +251,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     // query row i + 1 is loaded while row i is computed
     float qn[NE], gn[NE], ln = 0.f, dn = 0.f;
     if (lo < hi) {
-      load_part<E, NE>((const E*)p.Q + (base + lo) * D + l16 * NE, qn);
-      load_part<E, NE>((const E*)p.dO + (base + lo) * D + l16 * NE, gn);
+      load_part<E, NE>((const E*)p.Q + (base + lo) * D + lg * NE, qn);
+      load_part<E, NE>((const E*)p.dO + (base + lo) * D + lg * NE, gn);
       ln = p.LSE[base + lo];
       dn = p.Dws[base + lo];
     }
@@ -251,8 +266,8 @@ void bwd_dkdv_kernel(BwdParams p) {
       }
       const float Li = ln, Di = dn;
       if (i + 1 < hi) {
-        load_part<E, NE>((const E*)p.Q + (row + 1) * D + l16 * NE, qn);
-        load_part<E, NE>((const E*)p.dO + (row + 1) * D + l16 * NE, gn);
+        load_part<E, NE>((const E*)p.Q + (row + 1) * D + lg * NE, qn);
+        load_part<E, NE>((const E*)p.dO + (row + 1) * D + lg * NE, gn);
         ln = p.LSE[row + 1];
         dn = p.Dws[row + 1];
       }
@@ -268,8 +283,8 @@ void bwd_dkdv_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        s[r] = group_sum(s[r]);
-        dp[r] = group_sum(dp[r]);
+        s[r] = group_sum<G>(s[r]);
+        dp[r] = group_sum<G>(dp[r]);
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -291,8 +306,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     const long krow = bhk * p.Sk + j0 + r;
     const bool part = p.nch > 1;
     const long prow = (long)blockIdx.y * p.B * p.HKV * p.Sk + krow;
-    float* odk = (part ? p.part_k + prow * D : p.dK + krow * D) + l16 * NE;
-    float* odv = (part ? p.part_v + prow * D : p.dV + krow * D) + l16 * NE;
+    float* odk = (part ? p.part_k + prow * D : p.dK + krow * D) + lg * NE;
+    float* odv = (part ? p.part_v + prow * D : p.dV + krow * D) + lg * NE;
     const float ks = part ? 1.f : p.scale;
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
@@ -719,10 +734,10 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D>), dim3((unsigned)((long)p.B * p.H * p.n_qblk)),
                        dim3(kBwdThreads), 0, stream, p);
   } else {
-    constexpr int R = rows_per_group<D>();
+    constexpr int R = rows_per_group<D>(), GPB = kBwdThreads / bwd_lanes_per_row(D);
     const long groups = (long)p.B * p.H * ((p.Sq + R - 1) / R);
     hipLaunchKernelGGL((bwd_dq_kernel<E, D>),
-                       dim3((unsigned)((groups + kRowsPerBlock - 1) / kRowsPerBlock), (unsigned)p.nch),
+                       dim3((unsigned)((groups + GPB - 1) / GPB), (unsigned)p.nch),
                        dim3(kBwdThreads), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
@@ -736,10 +751,10 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D>), dim3((unsigned)kblocks), dim3(kBwdThreads), 0,
                        stream, p);
   } else {
-    constexpr int R = rows_per_group<D>();
+    constexpr int R = rows_per_group<D>(), GPB = kBwdThreads / bwd_lanes_per_row(D);
     const long groups = (long)p.B * p.HKV * ((p.Sk + R - 1) / R);
     hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>),
-                       dim3((unsigned)((groups + kRowsPerBlock - 1) / kRowsPerBlock), (unsigned)p.nch),
+                       dim3((unsigned)((groups + GPB - 1) / GPB), (unsigned)p.nch),
                        dim3(kBwdThreads), 0, stream, p);
   }
   e = hipGetLastError();

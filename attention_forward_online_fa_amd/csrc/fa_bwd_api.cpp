@@ -87,7 +87,7 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
   // spans at most `span` + 1 keys (query rows): two adjacent rows' ranges.
   p.nch = 1;
   if (dtype == FA_F32 || D == 256) {
-    const int R = D <= 128 ? 2 : 1;
+    const int R = fa::bwd_rows_per_group(D);
     const long groups = (long)B * H * ((Sq + R - 1) / R);
     const long target = 1L << 18;   // row groups that fill the GPU several times over
     // keys per query row and query rows per key: at most `window` only under
