@@ -14,7 +14,8 @@
 // kernel through a workspace.
 //
 // Work decomposition: a group of G = 4, 8 or 16 lanes (the fewest that keep
-// D / G <= 8) owns two consecutive rows of one head (one row at D = 256):
+// D / G <= 8) owns R consecutive rows of one head (bwd_rows_per_group: 2, 4
+// with 16 lanes, 1 at D = 256):
 // query rows in the dQ kernel, key rows in the dK/dV kernel. A lane holds
 // D / G consecutive elements of each row vector; dot products reduce over
 // the group with two to four DPP steps. This is the pages'
