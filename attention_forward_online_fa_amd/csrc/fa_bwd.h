@@ -40,12 +40,10 @@ struct BwdParams {
 
 // Group shape of the per-row kernels (fp32 inputs, D = 256): lanes per row
 // (a group holds D / lanes elements of each row vector per lane: the fewest
-// lanes, 4, 8 or 16, that keep it at most 8) and rows of one head per group
-// (4 with 16 lanes, 2 with 4 or 8, 1 at D = 256; each measured best).
-constexpr int bwd_lanes_per_row(int D) { return D <= 32 ? 4 : D <= 64 ? 8 : 16; }
-constexpr int bwd_rows_per_group(int D) {
-  return D / bwd_lanes_per_row(D) > 8 ? 1 : bwd_lanes_per_row(D) == 16 ? 4 : 2;
-}
+// lanes, 4, 8, 16 or 32, that keep it at most 8) and rows of one head per
+// group (4 with 16 lanes, 2 otherwise; each measured best).
+constexpr int bwd_lanes_per_row(int D) { return D <= 32 ? 4 : D <= 64 ? 8 : D <= 128 ? 16 : 32; }
+constexpr int bwd_rows_per_group(int D) { return bwd_lanes_per_row(D) == 16 ? 4 : 2; }
 
 // Queue the dQ kernel (which also writes Dws) and then the dK/dV kernel.
 hipError_t launch_backward(const BwdParams& p, int dtype, int D, hipStream_t stream);

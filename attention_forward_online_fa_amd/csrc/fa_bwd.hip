@@ -13,12 +13,12 @@
 // D_i is computed once per query row by the dQ kernel and handed to the dK/dV
 // kernel through a workspace.
 //
-// Work decomposition: a group of G = 4, 8 or 16 lanes (the fewest that keep
-// D / G <= 8) owns R consecutive rows of one head (bwd_rows_per_group: 2, 4
-// with 16 lanes, 1 at D = 256):
+// Work decomposition: a group of G = 4, 8, 16 or 32 lanes (the fewest that
+// keep D / G <= 8) owns R consecutive rows of one head (bwd_rows_per_group:
+// 4 with 16 lanes, else 2):
 // query rows in the dQ kernel, key rows in the dK/dV kernel. A lane holds
 // D / G consecutive elements of each row vector; dot products reduce over
-// the group with two to four DPP steps. This is the pages'
+// the group with two to four DPP steps (and one lane permute at G = 32). This is the pages'
 // thread-per-row design mapped to wavefronts, on the VALU (no MFMA): exact to
 // fp32 rounding, used for fp32 inputs and D = 256; the MFMA kernels below
 // serve 16-bit inputs at D = 64 and 128. On small grids the per-row kernels
@@ -54,15 +54,17 @@ __device__ __forceinline__ float dpp(float x) {
       0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
 }
 
-// Sum over the G lanes of one group (G = 4, 8 or 16, aligned): quad_perm
-// swaps within each 4 lanes, then row_half_mirror (8) or row rotations (16).
+// Sum over the G lanes of one group (G = 4, 8, 16 or 32, aligned): quad_perm
+// swaps within each 4 lanes, then row_half_mirror (8); row rotations (16),
+// plus the other 16-lane row through a lane permute (32).
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
-  if constexpr (G == 16) {
+  if constexpr (G >= 16) {
     x += row_ror<8>(x);
     x += row_ror<4>(x);
     x += row_ror<2>(x);
     x += row_ror<1>(x);
+    if constexpr (G == 32) x += __shfl_xor(x, 16);
   } else {
     x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
     x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
