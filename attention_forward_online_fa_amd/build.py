@@ -5,6 +5,7 @@ source tree; nothing is JIT-compiled at run time.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -15,6 +16,8 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+# Hash of the sources and flags a library was built from, written beside it.
+HASH_PATH = LIB_PATH + ".srchash"
 SOURCES = [os.path.join(CSRC, "fa_fwd.hip"), os.path.join(CSRC, "fa_api.cpp"),
            os.path.join(CSRC, "fa_bwd.hip"), os.path.join(CSRC, "fa_bwd_api.cpp")]
 
@@ -25,6 +28,32 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+
+
+def source_files() -> list:
+    """Every file the library is compiled from: the sources, the internal
+    headers under csrc/ and the public header."""
+    hdrs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h"))
+    return [*SOURCES, *hdrs, os.path.join(INCLUDE, "fa.h")]
+
+
+def source_hash() -> str:
+    """sha256 over the compiler flags and every file of source_files()."""
+    h = hashlib.sha256(" ".join(HIP_FLAGS).encode())
+    for path in source_files():
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def built_hash():
+    """The source hash recorded when the library on disk was built, or None."""
+    try:
+        with open(HASH_PATH) as fh:
+            return fh.read().strip()
+    except OSError:
+        return None
 
 
 def hipcc() -> str:
@@ -63,9 +92,11 @@ def parse_resource_usage(remarks: str) -> dict:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source into libfa.so (always recompiles). Returns the path.
+    """Compile every source into libfa.so (always recompiles) and record the
+    source hash beside it. Returns the path.
 
     Fails if a kernel outside SCRATCH_ALLOWED uses scratch memory."""
+    digest = source_hash()
     tmp = LIB_PATH + f".tmp{os.getpid()}"
     cmd = [hipcc(), *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-I", INCLUDE,
            "-I", CSRC, *SOURCES, "-o", tmp]
@@ -85,13 +116,24 @@ def build(verbose: bool = False) -> str:
         os.remove(tmp)
         raise RuntimeError(f"kernels use scratch memory: {bad}")
     os.replace(tmp, LIB_PATH)
+    with open(HASH_PATH + ".tmp", "w") as fh:
+        fh.write(digest + "\n")
+    os.replace(HASH_PATH + ".tmp", HASH_PATH)
     return LIB_PATH
 
 
 def ensure_built() -> str:
-    """Build only if no library exists yet."""
+    """Build if no library exists yet; otherwise check that the library on
+    disk was built from the current sources and raise if it was not (a stale
+    library is never loaded silently)."""
     if not os.path.exists(LIB_PATH):
         build()
+        return LIB_PATH
+    have, want = built_hash(), source_hash()
+    if have != want:
+        raise RuntimeError(
+            f"{LIB_PATH} does not match the sources (recorded source hash {have}, current "
+            f"{want}): rebuild it with `python -m attention_forward_online_fa_amd.build`")
     return LIB_PATH
 
 

@@ -8,10 +8,12 @@
 //   dQ_i  = scale sum_j dS_ij k_j                 (kernel bwd_dq_kernel)
 //   dV_j  = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i
 //                                                 (kernel bwd_dkdv_kernel)
-// with dK and dV summed over the query heads of a kv head. As in forge, dK
-// and dV accumulate privately per key row (no atomics, deterministic), and
-// D_i is computed once per query row by the dQ kernel and handed to the dK/dV
-// kernel through a workspace.
+// with dK and dV summed over the query heads of a kv head. Every dK/dV row
+// has a single owner that sums its contributions in a fixed order, so no
+// atomics are needed and the result is deterministic (the approach of the
+// forge flash_attention.metal backward kernels). D_i is computed once per
+// query row by the dQ kernel and handed to the dK/dV kernel through a
+// workspace.
 //
 // Work decomposition: a group of G = 4, 8, 16 or 32 lanes (the fewest that
 // keep D / G <= 8) owns R consecutive rows of one head (bwd_rows_per_group:
@@ -91,9 +93,9 @@ __device__ __forceinline__ void key_rows(const BwdParams& p, int j, int& lo, int
   hi = p.window > 0 ? min(p.Sq, j + p.window) : p.Sq;
 }
 
-// Rows per 16-lane group in the per-row kernels: two rows of one head share
-// every K/V (dQ) or Q/dO (dK/dV) load and give the group two independent
-// dot-product chains; one at D = 256, where registers run short.
+// Rows per lane group in the per-row kernels: R rows of one head share every
+// K/V (dQ) or Q/dO (dK/dV) load and give the group R independent
+// dot-product chains; four with 16-lane groups, two with 4, 8 or 32 lanes.
 template <int D>
 constexpr int rows_per_group() { return bwd_rows_per_group(D); }
 

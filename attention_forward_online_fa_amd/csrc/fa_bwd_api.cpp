@@ -84,7 +84,8 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
   // GPU: each row group's range is cut into nch chunks that run side by side
   // (a causal grid is otherwise bound by its longest rows), their partial
   // sums added up afterwards in chunk order (deterministic). A group's range
-  // spans at most `span` + 1 keys (query rows): two adjacent rows' ranges.
+  // spans at most `span` + R - 1 keys (query rows): the ranges of its R
+  // adjacent rows.
   p.nch = 1;
   if (dtype == FA_F32 || D == 256) {
     const int R = fa::bwd_rows_per_group(D);

@@ -43,6 +43,16 @@ def test_library_exports_every_declared_symbol():
         assert re.search(rf"\bT {name}\b", out), f"{name} not a defined text symbol"
 
 
+def test_library_was_built_from_the_current_sources():
+    # build() records a hash of every source file and the compiler flags
+    # beside libfa.so; the loader refuses a library whose hash differs
+    from attention_forward_online_fa_amd import build as B
+    _lib.lib()
+    assert B.built_hash() == B.source_hash()
+    assert set(B.SOURCES) <= set(B.source_files())
+    assert HEADER in B.source_files()
+
+
 def test_library_has_no_undefined_symbols_of_its_own():
     # A kernel whose host-side launch stub was not emitted shows up as an
     # undefined fa:: symbol; the library would then fail to load on any box.

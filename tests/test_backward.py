@@ -74,7 +74,10 @@ CASES += [
     ("f32", 1, 2, 1, 1024, 1024, 64, 1, 0),      # eight chunks, causal
     ("f32", 1, 2, 2, 600, 900, 32, 0, 100),      # a window alone: ranges up to Sk / Sq
     ("f32", 1, 4, 1, 800, 800, 96, 1, 300),      # causal band of 300
-    ("bf16", 1, 2, 1, 600, 700, 256, 0, 0),      # one row per group
+    ("bf16", 1, 2, 1, 600, 700, 256, 0, 0),      # D = 256: two rows per 32-lane group
+    # odd Sq and Sk at D = 256: the last group of each kernel holds one row
+    ("bf16", 1, 2, 1, 91, 121, 256, 1, 30),
+    ("f32", 1, 2, 2, 77, 133, 256, 0, 0),
 ]
 
 

@@ -79,27 +79,22 @@ CONFIGS = [
     Workload("mha_causal_f32_b4h8_s1024_d64", 4, 8, 8, 1024, 1024, 64, "f32", 1, 0,
              check="all", seed_index=1),
     Workload("gqa_causal_bf16_b2h32kv8_s4096_d128", 2, 32, 8, 4096, 4096, 128, "bf16", 1, 0,
-             amplitude=0.5, check="sampled", n_random_rows=4096, edge_rows=64,
-             seed_index=2),
+             amplitude=0.5, check="all", seed_index=2),
     Workload("swa_gqa_f32_b1h16kv4_s16384_d128_w4096", 1, 16, 4, 16384, 16384, 128, "f32", 1, 4096,
              check="sampled", n_random_rows=512, edge_rows=64, seed_index=3),
     Workload("long_bf16_sq8192_sk65536_d256", 1, 1, 1, 8192, 65536, 256, "bf16", 0, 0,
              v_dist="uniform", check="sampled", n_random_rows=256, edge_rows=0,
              seed_index=4),
     Workload("gqa_causal_f16_b2h32kv8_s4096_d128", 2, 32, 8, 4096, 4096, 128, "f16", 1, 0,
-             amplitude=0.5, check="sampled", n_random_rows=4096, edge_rows=64,
-             seed_index=5),
+             amplitude=0.5, check="all", seed_index=5),
     Workload("gqa_causal_bf16_bshd_b2h32kv8_s4096_d128", 2, 32, 8, 4096, 4096, 128, "bf16", 1,
-             0, amplitude=0.5, check="sampled", n_random_rows=4096, edge_rows=64,
-             seed_index=6, layout="bshd"),
+             0, amplitude=0.5, check="all", seed_index=6, layout="bshd"),
     Workload("blocksparse_bf16_b2h32kv8_s4096_d128", 2, 32, 8, 4096, 4096, 128, "bf16", 0, 0,
-             amplitude=0.5, check="sampled", n_random_rows=4096, edge_rows=64,
-             seed_index=7, mask="band_random", mask_p=0.15),
+             amplitude=0.5, check="all", seed_index=7, mask="band_random", mask_p=0.15),
     # head dims below the kernel tiles (the padded form): the bf16 headline
     # shape at D = 96 and the fp32 causal MHA shape at D = 32
     Workload("gqa_causal_bf16_b2h32kv8_s4096_d96", 2, 32, 8, 4096, 4096, 96, "bf16", 1, 0,
-             amplitude=0.5, check="sampled", n_random_rows=4096, edge_rows=64,
-             seed_index=8),
+             amplitude=0.5, check="all", seed_index=8),
     Workload("mha_causal_f32_b4h8_s1024_d32", 4, 8, 8, 1024, 1024, 32, "f32", 1, 0,
              check="all", seed_index=9),
 ]
