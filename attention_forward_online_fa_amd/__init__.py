@@ -24,7 +24,8 @@ import math
 from ._lib import (FA_BF16, FA_F16, FA_F32, FA_MASK_BLOCK_K, FA_MASK_BLOCK_Q, FA_MAX_SPLITS,
                    FaError, lib, library_path)
 
-__all__ = ["fwd", "fwd_into", "bwd", "plan_splits", "schedule_table", "release", "FaError",
+__all__ = ["fwd", "fwd_into", "fwd_noalloc_into", "bwd", "plan_splits", "schedule_table",
+           "release", "FaError",
            "library_path", "default_scale", "FA_F32", "FA_BF16", "FA_F16", "FA_MAX_SPLITS",
            "FA_MASK_BLOCK_Q", "FA_MASK_BLOCK_K"]
 
@@ -123,6 +124,34 @@ def fwd_into(q, k, v, o, lse, *, causal=False, window=0, scale=None, num_splits=
                                   lse.data_ptr(), B, H, HKV, Sq, Sk, D, *ptr, float(scale),
                                   int(bool(causal)), int(window), _dtype_code(q),
                                   int(num_splits), stream.cuda_stream)
+    if st != 0:
+        raise FaError(st)
+    return o, lse
+
+
+def fwd_noalloc_into(q, k, v, o, lse, *, causal=False, window=0, scale=None, num_splits=0,
+                     stream=None):
+    """fwd_into through fa_fwd_noalloc: the library allocates no device memory
+    (its key-split partials live in a static per-GPU array). Contiguous
+    tensors only. Returns (o, lse)."""
+    import torch
+    _check(q, k, v)
+    B, H, Sq, D = q.shape
+    HKV, Sk = k.shape[1], k.shape[2]
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_cuda:
+        raise ValueError("o must be a device tensor with q's shape and dtype")
+    if tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, Sq]")
+    if not all(t.is_contiguous() for t in (q, k, v, o, lse)):
+        raise ValueError("fwd_noalloc_into takes contiguous tensors")
+    if scale is None:
+        scale = default_scale(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = lib().fa_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), B, H, HKV, Sq, Sk, D, float(scale),
+                              int(bool(causal)), int(window), _dtype_code(q), int(num_splits),
+                              stream.cuda_stream)
     if st != 0:
         raise FaError(st)
     return o, lse

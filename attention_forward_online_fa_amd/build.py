@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 # Hash of the sources and flags a library was built from, written beside it.
 HASH_PATH = LIB_PATH + ".srchash"
 SOURCES = [os.path.join(CSRC, "fa_fwd.hip"), os.path.join(CSRC, "fa_api.cpp"),
-           os.path.join(CSRC, "fa_bwd.hip"), os.path.join(CSRC, "fa_bwd_api.cpp")]
+           os.path.join(CSRC, "fa_bwd.hip"), os.path.join(CSRC, "fa_bwd_api.cpp"),
+           os.path.join(CSRC, "fa_noalloc.hip")]
 
 ARCH = "gfx950"
 HIP_FLAGS = [

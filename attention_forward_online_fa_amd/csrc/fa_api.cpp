@@ -274,9 +274,12 @@ void resolve_splits(int requested, int B, int H, int Sq, int Sk, int D, int caus
 }
 
 // Splits, keys per split and persistent slots (0 = none) for one call.
+// (persistent = false: one workgroup per item, whatever the shape)
 void plan(DeviceState& s, int requested, int B, int H, int Sq, int Sk, int D, int causal,
-          int window, int dtype, int form, int* ns, int* split_len, int* nslot) {
-  {
+          int window, int dtype, int form, int* ns, int* split_len, int* nslot,
+          bool persistent = true) {
+  *nslot = 0;
+  if (persistent) {
     std::lock_guard<std::mutex> lk(g_mu);
     *nslot = persistent_slots(s, B, H, Sq, D, causal, window, dtype, form);
   }
@@ -355,6 +358,13 @@ struct MaskArg {
   int batch, heads;
 };
 
+// Split workspace bytes: fp32 partial rows of the tile dim, then the partial
+// log-sum-exps.
+size_t split_workspace_bytes(int ns, int B, int H, int Sq, int DT) {
+  const size_t rows = (size_t)B * H * Sq;
+  return (size_t)ns * rows * DT * sizeof(float) + (size_t)ns * rows * sizeof(float);
+}
+
 // O's rows must be disjoint: with its (batch, head, row) axes sorted by stride
 // (axes of extent 1 left out), every stride must reach past the extent the
 // smaller axes span (a row spans D elements).
@@ -376,7 +386,7 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
             int HKV, int Sq, int Sk, int D, const long long* q_strides,
             const long long* k_strides, const long long* v_strides, const long long* o_strides,
             float scale, int causal, int window, int dtype, int num_splits, void* stream_ptr,
-            const MaskArg* bm = nullptr) {
+            const MaskArg* bm = nullptr, const fa::FixedWorkspace* fixed = nullptr) {
   if (!Q || !K || !V || !O || !LSE || (bm && !bm->mask)) return FA_ERR_NULLPTR;
   int st = check_args(B, H, HKV, Sq, Sk, D, causal, window, dtype);
   if (st != FA_OK) return st;
@@ -415,10 +425,25 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   DeviceState* ds = nullptr;
   st = device_state(&ds);
   if (st != FA_OK) return st;
+  void* fixed_ptr = nullptr;
+  if (fixed && (st = fixed->address(&fixed_ptr)) != FA_OK) return st;
 
   const int BM = fa::block_m(dtype, D);
   int ns = 1, split_len = 0, nslot = 0;
-  plan(*ds, num_splits, B, H, Sq, Sk, DT, causal, window, dtype, form, &ns, &split_len, &nslot);
+  // A fixed workspace: no persistent schedule (its device table would be
+  // allocated), and the split count must fit the workspace.
+  plan(*ds, num_splits, B, H, Sq, Sk, DT, causal, window, dtype, form, &ns, &split_len, &nslot,
+       fixed == nullptr);
+  if (fixed && ns > 1 && split_workspace_bytes(ns, B, H, Sq, DT) > fixed->bytes) {
+    if (num_splits != 0) return FA_ERR_WORKSPACE;   // the caller's count does not fit
+    // automatic count: the largest that fits (1 needs no workspace)
+    int want = ns - 1;
+    while (want > 1 && split_workspace_bytes(want, B, H, Sq, DT) > fixed->bytes) --want;
+    for (;; --want) {
+      resolve_splits(want, B, H, Sq, Sk, DT, causal, window, dtype, ds->num_cus, &ns, &split_len);
+      if (ns == 1 || split_workspace_bytes(ns, B, H, Sq, DT) <= fixed->bytes) break;
+    }
+  }
   if (split_len / fa::key_tile(dtype, DT) > fa::kMaxListTiles && form == fa::kFormBlockSparse)
     return FA_ERR_SHAPE;   // more key tiles than FA_MAX_SPLITS lists can hold
 
@@ -475,7 +500,11 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
   void* ws = nullptr;
-  if (ns > 1) {
+  if (ns > 1 && fixed) {
+    const size_t o_bytes = (size_t)ns * B * H * Sq * DT * sizeof(float);
+    p.Opart = static_cast<float*>(fixed_ptr);
+    p.Lpart = reinterpret_cast<float*>(static_cast<char*>(fixed_ptr) + o_bytes);
+  } else if (ns > 1) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
     hipMemPool_t pool = nullptr;
@@ -483,8 +512,8 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
     if (st != FA_OK) return st;
     const size_t rows = (size_t)B * H * Sq;
     const size_t o_bytes = (size_t)ns * rows * DT * sizeof(float);
-    const size_t l_bytes = (size_t)ns * rows * sizeof(float);
-    if (hipMallocFromPoolAsync(&ws, o_bytes + l_bytes, pool, stream) != hipSuccess)
+    if (hipMallocFromPoolAsync(&ws, split_workspace_bytes(ns, B, H, Sq, DT), pool, stream) !=
+        hipSuccess)
       return FA_ERR_WORKSPACE;
     p.Opart = static_cast<float*>(ws);
     p.Lpart = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
@@ -497,6 +526,14 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
 }  // namespace
 
 namespace fa {
+int forward_fixed_workspace(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            int B, int H, int HKV, int Sq, int Sk, int D, float scale,
+                            int causal, int window, int dtype, int num_splits, void* stream,
+                            const FixedWorkspace& ws) {
+  return forward(Q, K, V, O, LSE, B, H, HKV, Sq, Sk, D, nullptr, nullptr, nullptr, nullptr, scale,
+                 causal, window, dtype, num_splits, stream, nullptr, &ws);
+}
+
 // Stream-ordered workspace from this library's pool on the current device
 // (the pool of the split workspace; freed blocks stay cached until fa_release).
 int library_workspace(size_t bytes, hipStream_t stream, void** out) {

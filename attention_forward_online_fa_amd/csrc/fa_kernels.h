@@ -83,6 +83,23 @@ constexpr int tile_dim(int dv, int dtype) {
   return (dv == 16 || dv == 32 || dv == 48) ? 64 : (dv == 80 || dv == 96) ? 128 : 0;
 }
 
+// A fixed workspace for the split partials: `address` stores the current
+// device's address of `bytes` bytes of device memory (256-byte aligned) and
+// returns an fa_status; the forward calls it once, after the argument checks,
+// and then allocates nothing.
+struct FixedWorkspace {
+  int (*address)(void** out);
+  size_t bytes;
+};
+
+// fa_fwd_ex into a fixed workspace (fa_api.cpp): no persistent schedule, and
+// an automatic split count lowered until the partials fit; an explicit count
+// that does not fit returns FA_ERR_WORKSPACE.
+int forward_fixed_workspace(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            int B, int H, int HKV, int Sq, int Sk, int D, float scale,
+                            int causal, int window, int dtype, int num_splits, void* stream,
+                            const FixedWorkspace& ws);
+
 // Queue the forward kernel (and the merge kernel when p.nsplit > 1) in the
 // given form at tile dim D (kFormContiguous: p.qs .. p.os and the mask are
 // not read; kFormPadded: D = tile_dim(p.dv, dtype) > p.dv).

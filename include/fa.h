@@ -141,6 +141,36 @@ int fa_fwd_strided(const void* Q, const void* K, const void* V, void* O, float* 
                    float scale, int causal, int window, int dtype,
                    int num_splits, void* stream);
 
+/* Size of the static per-GPU workspace of fa_fwd_noalloc (68 MiB). */
+#define FA_NOALLOC_SCRATCH_BYTES (68u * 1024u * 1024u)
+
+/*
+ * fa_fwd_noalloc - fa_fwd_ex for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It calls no hipMalloc, hipFree or memory-pool routine.
+ *
+ * Same arguments as fa_fwd_ex; the caller still passes all five buffers.
+ * The key-split partials live in a static device array of
+ * FA_NOALLOC_SCRATCH_BYTES on each GPU the library runs on, held until the
+ * process ends; its address is looked up on the first call on each device.
+ * Differences from fa_fwd_ex:
+ *   - float32 causal / windowed problems with few query tiles run one
+ *     workgroup per item instead of the persistent schedule (whose device
+ *     table fa_fwd_ex allocates);
+ *   - num_splits = 0 takes fa_fwd_ex's automatic count, lowered until the
+ *     partials (num_splits * B * H * Sq * (D + 1) float32 values, D rounded
+ *     up to its kernel's tile dim) fit the array;
+ *   - an explicit num_splits whose partials do not fit returns
+ *     FA_ERR_WORKSPACE before any device work.
+ * All calls on one GPU share its array: calls that overlap on one GPU (on
+ * different streams or threads) race; calls queued in order on one stream
+ * do not. Asynchronous on `stream`. Other errors as fa_fwd_ex.
+ */
+int fa_fwd_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                   int B, int H, int HKV, int Sq, int Sk, int D,
+                   float scale, int causal, int window, int dtype,
+                   int num_splits, void* stream);
+
 /* Block-mask granularity of fa_fwd_block_sparse: query rows x keys per byte. */
 #define FA_MASK_BLOCK_Q 128
 #define FA_MASK_BLOCK_K 64
