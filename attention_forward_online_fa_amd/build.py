@@ -10,6 +10,8 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
@@ -24,11 +26,13 @@ SOURCES = [os.path.join(CSRC, "fa_fwd.hip"), os.path.join(CSRC, "fa_api.cpp"),
 
 ARCH = "gfx950"
 HIP_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # Keep the compiler from forming packed fp32 VALU instructions.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# Per-source compiler flags on top of HIP_FLAGS (by file name).
+FILE_FLAGS: dict = {}
 
 
 def source_files() -> list:
@@ -40,7 +44,7 @@ def source_files() -> list:
 
 def source_hash() -> str:
     """sha256 over the compiler flags and every file of source_files()."""
-    h = hashlib.sha256(" ".join(HIP_FLAGS).encode())
+    h = hashlib.sha256(" ".join(HIP_FLAGS).encode() + repr(sorted(FILE_FLAGS.items())).encode())
     for path in source_files():
         h.update(os.path.basename(path).encode() + b"\0")
         with open(path, "rb") as fh:
@@ -99,15 +103,36 @@ def build(verbose: bool = False) -> str:
     Fails if a kernel outside SCRATCH_ALLOWED uses scratch memory."""
     digest = source_hash()
     tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-I", INCLUDE,
-           "-I", CSRC, *SOURCES, "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        if os.path.exists(tmp):
-            os.remove(tmp)
-        raise RuntimeError(f"hipcc failed with status {res.returncode}: {' '.join(cmd)}")
-    usage = parse_resource_usage(res.stderr)
+    cc = hipcc()
+    objdir = tempfile.mkdtemp(prefix="fa_build_")
+    try:
+        def compile_one(src):
+            obj = os.path.join(objdir, os.path.basename(src) + ".o")
+            cmd = [cc, *HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []),
+                   "-Rpass-analysis=kernel-resource-usage", "-I", INCLUDE, "-I", CSRC, "-c", src,
+                   "-o", obj]
+            return cmd, obj, subprocess.run(cmd, capture_output=True, text=True)
+
+        jobs = max(1, min(len(SOURCES), os.cpu_count() or 1, 8))
+        with ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(compile_one, SOURCES))
+        remarks = ""
+        for cmd, _, res in results:
+            if res.returncode != 0:
+                sys.stderr.write(res.stdout + res.stderr)
+                raise RuntimeError(f"hipcc failed with status {res.returncode}: {' '.join(cmd)}")
+            remarks += res.stderr
+        link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for _, o, _ in results],
+                "-o", tmp]
+        res = subprocess.run(link, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            if os.path.exists(tmp):
+                os.remove(tmp)
+            raise RuntimeError(f"link failed with status {res.returncode}: {' '.join(link)}")
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
+    usage = parse_resource_usage(remarks)
     bad = [k for k, u in usage.items()
            if u.get("scratch", 0) > 0 and not any(a in k for a in SCRATCH_ALLOWED)]
     if verbose:

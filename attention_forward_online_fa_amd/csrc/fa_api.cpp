@@ -473,8 +473,20 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   p.window = window;
   p.nsplit = ns;
   p.split_len = split_len;
-  p.n_qblk = (Sq + BM - 1) / BM;
-  const long units = (long)B * H * ns;
+  // 16-bit kernel: the query heads sharing a kv head go into one workgroup
+  // (four, or two), each wavefront taking 32 rows of one head, so every
+  // wavefront of a workgroup sees the same key range (causal diagonal and
+  // window edges fall on fewer key tiles). Block masks keep one head and
+  // 128 rows per workgroup (the mask's row blocks).
+  const int group = H / HKV;
+  p.hp = (dtype == FA_F32 || form == fa::kFormBlockSparse) ? 1
+         : group % 4 == 0                                 ? 4
+         : group % 2 == 0                                 ? 2
+                                                          : 1;
+  p.packs = group / p.hp;
+  p.bm = BM / p.hp;
+  p.n_qblk = (Sq + p.bm - 1) / p.bm;
+  const long units = (long)B * HKV * p.packs * ns;
   const long blocks = units * p.n_qblk;
   if (blocks < 1 || blocks > 2147483647L) return FA_ERR_SHAPE;
   p.units = (int)units;

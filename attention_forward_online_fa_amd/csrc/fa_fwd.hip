@@ -20,8 +20,12 @@
 // axis) pay the per-element test, as the forge forward kernel does with its
 // kb_lim / jb_begin bounds.
 //
-// Work decomposition (gfx950): a workgroup is 4 wavefronts x 32 query rows =
-// 128 rows of one (batch, head). Each wavefront keeps its 32 query rows in
+// Work decomposition (gfx950): a workgroup is 4 wavefronts x 32 query rows.
+// The 16-bit kernel packs the query heads that share one K/V head into a
+// workgroup (hp = 4 or 2 heads, each with 128 / hp rows; one head and 128 rows
+// when the group size is odd, and under a block mask), so all of its
+// wavefronts see the same key range; the fp32 kernel takes 128 rows of one
+// (batch, head). Each wavefront keeps its 32 query rows in
 // registers as the MFMA B operand and computes S^T = K Q^T, so a lane owns one
 // query row (column of S^T) and half of the tile's keys: row max and row sum
 // are in-lane plus one exchange with lane ^ 32. The P tile then feeds the
@@ -38,6 +42,7 @@
 // with its own L2). The fp32 kernel can also run persistently: a fixed number
 // of workgroups, each over a host-computed list of (query tile, key split)
 // items (Params::sched).
+#include "fa_fwd_common.h"
 #include "fa_kernels.h"
 #include "fa_tile.h"
 
@@ -45,97 +50,6 @@
 #include <stdint.h>
 
 namespace fa {
-
-constexpr int kThreads = 256;   // 4 wavefronts of 64
-constexpr float kLn2 = 0.693147180559945309f;
-
-
-// ------------------------------------------------------------ work mapping
-struct Tile {
-  int b, h, hkv, qblk, split;
-};
-
-__device__ __forceinline__ Tile map_tile(const Params& p) {
-  const int i = blockIdx.x;
-  int t, u;
-  if (p.xcd_remap) {
-    // Block i runs on XCD i % 8 as that XCD's (i / 8)-th block. Give XCD x
-    // the contiguous unit range [x U/8, (x+1) U/8).
-    // Within an XCD: query tile major (heaviest first), then unit; the units
-    // of one XCD are consecutive, so query heads sharing a K/V head run there
-    // together. (Ordering kv-head-group major instead measured ~1.5% slower.)
-    const int upx = p.units >> 3;
-    const int k = i >> 3;
-    t = k / upx;
-    u = (i & 7) * upx + k % upx;
-  } else {
-    t = i / p.units;
-    u = i % p.units;
-  }
-  Tile w;
-  w.qblk = p.n_qblk - 1 - t;
-  const int hg = u % p.group;
-  int r = u / p.group;
-  w.split = r % p.nsplit;
-  r /= p.nsplit;
-  w.hkv = r % p.HKV;
-  w.b = r / p.HKV;
-  w.h = w.hkv * p.group + hg;
-  return w;
-}
-
-// Work tile of item qblk * units + unit in a persistent launch (the unit
-// decomposition of map_tile, without its XCD grouping).
-__device__ __forceinline__ Tile item_tile(const Params& p, int item) {
-  Tile w;
-  w.qblk = item / p.units;
-  const int u = item % p.units;
-  const int hg = u % p.group;
-  int r = u / p.group;
-  w.split = r % p.nsplit;
-  r /= p.nsplit;
-  w.hkv = r % p.HKV;
-  w.b = r / p.HKV;
-  w.h = w.hkv * p.group + hg;
-  return w;
-}
-
-// Key range [lo, hi) a workgroup with rows [q0, q0 + bm) must visit.
-__device__ __forceinline__ void key_range(const Params& p, int q0, int bm, int split, int& lo,
-                                          int& hi) {
-  lo = split * p.split_len;
-  hi = min(p.Sk, lo + p.split_len);
-  const int last = min(q0 + bm, p.Sq) - 1;
-  if (p.causal) hi = min(hi, last + 1);
-  if (p.window > 0) lo = max(lo, q0 - p.window + 1);
-}
-
-__device__ __forceinline__ bool visible(const Params& p, int i, int j) {
-  return j < p.Sk && (!p.causal || j <= i) && (p.window <= 0 || j > i - p.window);
-}
-
-// Finish one query row: combine the two lane halves' row sums, then write
-// LSE and hand 1/l to `store(partial, row, split, inv)`, which writes O (or
-// the fp32 partial of this key split).
-template <typename StoreFn>
-__device__ __forceinline__ void finish_row(const Params& p, int b, int h, int split, int i,
-                                           int g, float m, float l_lane, StoreFn store) {
-  const float l = l_lane + __shfl_xor(l_lane, 32);
-  const bool any = l > 0.f;
-  const float inv = any ? 1.f / l : 0.f;
-  const float lse = any ? (m + __log2f(l)) * kLn2 : -INFINITY;
-  if (i >= p.Sq) return;
-  const size_t row = (size_t)(b * p.H + h) * p.Sq + i;
-  const bool partial = p.nsplit > 1;
-  // A split row that saw no key needs only its LSE (-inf): the merge skips it.
-  if (!partial || any) store(partial, row, split, inv);
-  if (g == 0) {
-    if (partial)
-      p.Lpart[(size_t)split * p.B * p.H * p.Sq + row] = lse;
-    else
-      p.LSE[row] = lse;
-  }
-}
 
 // ============================================================ block masks
 // Block-sparse form: the key tiles t in [0, n) of a workgroup's range (tile t
@@ -164,12 +78,6 @@ __device__ __forceinline__ int build_tile_list(const unsigned char* mrow, int t0
 __device__ __forceinline__ const unsigned char* mask_row(const Params& p, int b, int h, int hkv,
                                                          int qblk) {
   return p.bmask + b * p.bm_sb + (p.bm_by_kv ? hkv : h) * p.bm_sh + (long long)qblk * p.bm_nkb;
-}
-
-__device__ __forceinline__ float half_max(float x) {
-  // max over lane and lane ^ 32 (the two halves of one query row's keys)
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // ================================================= 16-bit inputs (bf16, fp16)
@@ -209,8 +117,11 @@ void fwd_16b_kernel(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
   const int l32 = lane & 31, g = lane >> 5;
   const Tile w = map_tile(p);
-  const int q0 = w.qblk * kBlockM;
-  const int qw = q0 + wave * 32;
+  // wavefront -> (head w.h + wave % hp, rows q0 + 32 (wave / hp) ..)
+  const int bm = p.bm;                      // query rows per workgroup: kBlockM / hp
+  const int h = w.h + wave % p.hp;
+  const int q0 = w.qblk * bm;
+  const int qw = q0 + (wave / p.hp) * 32;
   const int i = qw + l32;
 
   const E* Qp;
@@ -219,25 +130,25 @@ void fwd_16b_kernel(Params p) {
   long long qr = D;   // element row strides
   int krb = T::ROW, vrb = T::ROW;   // K / V row strides in bytes (strided: multiples of ROW)
   if constexpr (Strided) {
-    Qp = (const E*)p.Q + w.b * p.qs[0] + w.h * p.qs[1];
+    Qp = (const E*)p.Q + w.b * p.qs[0] + h * p.qs[1];
     Kp = (const E*)p.K + w.b * p.ks[0] + w.hkv * p.ks[1];
     Vp = (const E*)p.V + w.b * p.vs[0] + w.hkv * p.vs[1];
     qr = p.qs[2];
     krb = (int)(p.ks[2] * 2);
     vrb = (int)(p.vs[2] * 2);
   } else {
-    Qp = (const E*)p.Q + (size_t)(w.b * p.H + w.h) * p.Sq * D;
+    Qp = (const E*)p.Q + (size_t)(w.b * p.H + h) * p.Sq * D;
     Kp = (const E*)p.K + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
     Vp = (const E*)p.V + (size_t)(w.b * p.HKV + w.hkv) * p.Sk * D;
   }
 
   int lo, hi;
-  key_range(p, q0, kBlockM, w.split, lo, hi);
+  key_range(p, q0, bm, w.split, lo, hi);
   const int t0 = (lo / BN) * BN;
   int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
   __shared__ unsigned short tlist[Sparse ? kMaxListTiles : 1];
   __shared__ int tcount;
-  if constexpr (Sparse)
+  if constexpr (Sparse)   // (block masks: hp = 1, the mask's 128-row blocks)
     n_tiles = build_tile_list(mask_row(p, w.b, w.h, w.hkv, w.qblk), t0, n_tiles, BN, tlist,
                               &tcount, wave, lane);
   // first key of the t-th tile visited
@@ -546,11 +457,11 @@ void fwd_16b_kernel(Params p) {
   // are also fully visible to every row of the block.
   const int full_hi = min(n_tiles, (p.Sk - t0) / BN);
   int u_lo = 0, u_hi = 0;
-  if (!Sparse && q0 + kBlockM <= p.Sq) {   // (block-sparse: tiles are not consecutive)
+  if (!Sparse && q0 + bm <= p.Sq) {   // (block-sparse: tiles are not consecutive)
     u_hi = full_hi;
     if (p.causal) u_hi = min(u_hi, max(0, (q0 - t0 + 1) / BN));
     if (p.window > 0) {
-      const int need = q0 + kBlockM - p.window - t0;       // kt - t0 >= need
+      const int need = q0 + bm - p.window - t0;       // kt - t0 >= need
       u_lo = need > 0 ? (need + BN - 1) / BN : 0;
     }
   }
@@ -575,7 +486,7 @@ void fwd_16b_kernel(Params p) {
   for (; !done; t += 2) done = gen2(t);
 
   // ---- epilogue: lane holds dims 32 db + 8 a + 4 g + (0..3) of row i.
-  finish_row(p, w.b, w.h, w.split, i, g, m_ref, l,
+  finish_row(p, w.b, h, w.split, i, g, m_ref, l,
              [&](bool partial, size_t row, int split, float inv) {
                if (partial) {
                  const size_t rows = (size_t)p.B * p.H * p.Sq;
@@ -590,7 +501,7 @@ void fwd_16b_kernel(Params p) {
                      *(f32x4*)(dst + 32 * db + 8 * a + 4 * g) = v4;
                    }
                } else {
-                 E* dst = Strided ? (E*)p.O + w.b * p.os[0] + w.h * p.os[1] + (long long)i * p.os[2]
+                 E* dst = Strided ? (E*)p.O + w.b * p.os[0] + h * p.os[1] + (long long)i * p.os[2]
                                   : (E*)p.O + row * D;
 #pragma unroll
                  for (int db = 0; db < DB; ++db)

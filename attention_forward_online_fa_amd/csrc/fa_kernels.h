@@ -25,8 +25,15 @@ struct Params {
   int window;
   int nsplit;        // key-axis splits (1 = none)
   int split_len;     // keys per split, a multiple of the key tile
-  int n_qblk;        // ceil(Sq / BM)
-  int units;         // B * H * nsplit
+  int n_qblk;        // ceil(Sq / rows per workgroup)
+  int units;         // B * HKV * packs * nsplit
+  // Query heads per workgroup (16-bit kernel: 1, 2 or 4; fp32 kernel: 1).
+  // Its four wavefronts take hp heads of one kv head times 4 / hp groups of
+  // 32 rows, so a workgroup holds kBlockM / hp query rows of each of its
+  // heads; packs = group / hp workgroups cover a kv head's query heads.
+  int hp;
+  int packs;
+  int bm;            // query rows per workgroup (of each of its hp heads): kBlockM / hp
   int xcd_remap;     // 1: group work so units sharing K/V stay on one XCD
   // Persistent launch (fp32 kernel): nslot workgroups, workgroup s runs the
   // items sched[nslot + 1 + k] for k in [sched[s], sched[s + 1]), item =

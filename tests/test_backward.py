@@ -133,3 +133,35 @@ def test_backward_deterministic():
     b = fa.bwd(q, k, v, o, lse, do, causal=True)
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+# ------------------------------------------------- the benchmarked shape
+def test_backward_benchmark_shape():
+    # bf16 causal GQA B2 H32/8 S4096 D128 (the shape bench.py --pass bwd
+    # times), gradients of two whole kv-head groups against the oracle: dQ of
+    # their 2 x 4 query heads on every row, dK and dV of the two kv heads (the
+    # oracle's backward on a group's slice is exact for that group)
+    import attention_forward_online_fa_amd as fa
+    wl = W.CONFIGS[W.HEADLINE]
+    inp = W.make_inputs(wl)
+    q, k, v = to_device(inp)
+    g_np, bits = W.make_grad_output(inp)
+    do = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    print(f"[backward] {wl.name} (full size)", flush=True)
+    o, lse = fa.fwd(q, k, v, causal=True, scale=wl.scale())
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=True, scale=wl.scale())
+    torch.cuda.synchronize()
+    gsz = wl.H // wl.HKV
+    for b, hk in ((0, 0), (1, wl.HKV - 1)):
+        hs = slice(hk * gsz, (hk + 1) * gsz)
+        ref = attention_backward(inp.q[b:b + 1, hs], inp.k[b:b + 1, hk:hk + 1],
+                                 inp.v[b:b + 1, hk:hk + 1], g_np[b:b + 1, hs], wl.scale(), True, 0)
+        got = (host64(dq[b:b + 1, hs]), host64(dk[b:b + 1, hk:hk + 1]),
+               host64(dv[b:b + 1, hk:hk + 1]))
+        for name, gg, r in zip(("dQ", "dK", "dV"), got, ref):
+            scale_r = max(1.0, float(np.abs(r).max()))
+            err = float(np.abs(gg - r).max())
+            print(f"  b={b} kv head {hk} {name}: max|d|={err:.3e} max|ref|={scale_r:.3e} "
+                  f"(tol {TOL['bf16'] * scale_r:.3e})", flush=True)
+            assert np.all(np.isfinite(gg)), name
+            assert err <= TOL["bf16"] * scale_r, f"{name}: {err:.3e}"
