@@ -172,9 +172,12 @@ def fwd(q, k, v, *, causal=False, window=0, scale=None, num_splits=0, stream=Non
 
 
 def bwd(q, k, v, o, lse, do, *, causal=False, window=0, scale=None, stream=None):
-    """Backward pass (fa_bwd): float32 (dq, dk, dv), the gradients of
-    sum(o * do) for o, lse = fwd(q, k, v, ...) with the same arguments.
-    Contiguous tensors; o and do have q's shape and dtype."""
+    """Backward pass: float32 (dq, dk, dv), the gradients of sum(o * do) for
+    o, lse = fwd(q, k, v, ...) with the same arguments; o and do have q's
+    shape and dtype. Contiguous tensors go through fa_bwd; views with other
+    strides (last dimension contiguous, e.g. token-major storage viewed as
+    [B, H, S, D]) through fa_bwd_strided, and the gradients then take the
+    memory layout of q, k and v."""
     import torch
     _check(q, k, v)
     B, H, Sq, D = q.shape
@@ -182,25 +185,44 @@ def bwd(q, k, v, o, lse, do, *, causal=False, window=0, scale=None, stream=None)
     for name, t in (("o", o), ("do", do)):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor with q's shape and dtype")
-    if tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32:
-        raise ValueError("lse must be float32 [B, H, Sq]")
-    if not all(t.is_contiguous() for t in (q, k, v, o, do, lse)):
-        raise ValueError("the backward pass takes contiguous tensors")
+        if t.stride(3) != 1 and t.shape[3] > 1:
+            raise ValueError(f"{name}: the head dimension must be contiguous (stride 1)")
+    if tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, Sq]")
     if scale is None:
         scale = default_scale(D)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    dense = all(t.is_contiguous() for t in (q, k, v, o, do))
+
+    def grad_like(t):
+        # a dense view keeps its layout (e.g. token-major); others get contiguous gradients
+        if not dense and not t.is_contiguous() and _is_dense_view(t):
+            return torch.empty_like(t, dtype=torch.float32)
+        return torch.empty(t.shape, dtype=torch.float32, device=t.device)
+
     with torch.cuda.device(q.device):
-        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
-        dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
-    st = lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, HKV, Sq,
-                      Sk, D, float(scale), int(bool(causal)), int(window), _dtype_code(q),
-                      stream.cuda_stream)
+        dq, dk, dv = grad_like(q), grad_like(k), grad_like(v)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, HKV, Sq, Sk, D)
+    tail = (float(scale), int(bool(causal)), int(window), _dtype_code(q), stream.cuda_stream)
+    if dense:
+        st = lib().fa_bwd(*args, *tail)
+    else:
+        st3 = [(ctypes.c_longlong * 3)(*t.stride()[:3]) for t in (q, k, v, o, do, dq, dk, dv)]
+        ptr = [ctypes.cast(a, ctypes.c_void_p) for a in st3]
+        st = lib().fa_bwd_strided(*args, *ptr, *tail)
     if st != 0:
         raise FaError(st)
     return dq, dk, dv
+
+
+def _is_dense_view(t) -> bool:
+    """True when t's elements fill its storage span without gaps or overlap
+    (a permutation of a contiguous tensor), so empty_like keeps its layout."""
+    span = 1 + sum((n - 1) * s for n, s in zip(t.shape, t.stride()))
+    return span == t.numel() and len(set(s for n, s in zip(t.shape, t.stride()) if n > 1)) == \
+        sum(1 for n in t.shape if n > 1)
 
 
 def plan_splits(B, H, HKV, Sq, Sk, D, *, causal=False, window=0, dtype="bf16") -> int:

@@ -365,6 +365,9 @@ size_t split_workspace_bytes(int ns, int B, int H, int Sq, int DT) {
   return (size_t)ns * rows * DT * sizeof(float) + (size_t)ns * rows * sizeof(float);
 }
 
+}  // namespace
+
+namespace fa {
 // O's rows must be disjoint: with its (batch, head, row) axes sorted by stride
 // (axes of extent 1 left out), every stride must reach past the extent the
 // smaller axes span (a row spans D elements).
@@ -381,6 +384,10 @@ bool output_rows_disjoint(const long long st[3], int B, int H, int Sq, int D) {
   }
   return true;
 }
+}  // namespace fa
+
+namespace {
+using fa::output_rows_disjoint;
 
 int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
             int HKV, int Sq, int Sk, int D, const long long* q_strides,

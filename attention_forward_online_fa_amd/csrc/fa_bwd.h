@@ -48,15 +48,22 @@ constexpr int bwd_rows_per_group(int D) { return bwd_lanes_per_row(D) == 16 ? 4 
 // Queue the dQ kernel (which also writes Dws) and then the dK/dV kernel.
 hipError_t launch_backward(const BwdParams& p, int dtype, int D, hipStream_t stream);
 
-// Row copies for the 16-bit backward at head dims 16 .. 96 (other than 64),
-// which runs the MFMA kernels of the 64 or 128 tile on zero-padded copies:
-// rows of src_bytes -> rows of dst_bytes with zeros after src_bytes (both
-// multiples of 16), and back for the fp32 gradients (dt -> dv floats per row,
-// both multiples of 4).
-hipError_t launch_pad_rows(const void* src, void* dst, long rows, int src_bytes, int dst_bytes,
-                           hipStream_t stream);
-hipError_t launch_unpad_rows(const float* src, float* dst, long rows, int dt, int dv,
-                             hipStream_t stream);
+// Row copies of the staged backward: the 16-bit backward at head dims 16 ..
+// 96 other than 64 runs the MFMA kernels of the 64 or 128 tile on
+// zero-padded copies, and strided tensors are copied to contiguous rows
+// first. gather: the B heads S rows of a view with byte strides st (batch,
+// head, row; multiples of 16), src_bytes each, -> contiguous rows of
+// dst_bytes with zeros after src_bytes. scatter: contiguous fp32 rows of dt
+// floats -> the first dv floats of each row of an fp32 view (byte strides st).
+hipError_t launch_gather_rows(const void* src, void* dst, int B, int heads, int S,
+                              const long long st[3], int src_bytes, int dst_bytes,
+                              hipStream_t stream);
+hipError_t launch_scatter_rows(const float* src, void* dst, int B, int heads, int S,
+                               const long long st[3], int dt, int dv, hipStream_t stream);
+
+// True when the rows of a [B, heads, S, D] view with element strides st
+// (batch, head, row) are pairwise disjoint (fa_api.cpp).
+bool output_rows_disjoint(const long long st[3], int B, int heads, int S, int D);
 
 // Stream-ordered workspace of `bytes` from the library's memory pool on the
 // current device (fa_api.cpp); release with hipFreeAsync. Returns an fa_status.

@@ -785,41 +785,63 @@ static hipError_t launch_bwd_e(const BwdParams& p, int D, hipStream_t stream) {
   }
 }
 
-// One 16-byte chunk per thread: chunk c of destination row r is chunk c of
-// source row r, or zeros past the source row.
-__global__ __launch_bounds__(256) void pad_rows_kernel(const uint4* __restrict__ src,
-                                                       uint4* __restrict__ dst, long rows, int cs,
-                                                       int ct) {
+// Row copies around the staged backward (head dims padded to a kernel tile,
+// or strided tensors). Rows are r = (b heads + h) S + i; row r of a strided
+// view starts at base + b sb + h sh + i sr (byte strides, multiples of 16).
+__device__ __forceinline__ long long view_row_offset(long r, int heads, int S, long long sb,
+                                                     long long sh, long long sr) {
+  const long bh = r / S;
+  const long b = bh / heads;
+  return b * sb + (bh - b * heads) * sh + (r - bh * S) * sr;
+}
+
+// One 16-byte chunk per thread: source row r of the view (its first cs
+// chunks) -> contiguous row r of ct chunks, zeros past cs.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ src,
+                                                          uint4* __restrict__ dst, long rows,
+                                                          int heads, int S, long long sb,
+                                                          long long sh, long long sr, int cs,
+                                                          int ct) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= rows * ct) return;
   const long r = idx / ct;
   const int c = (int)(idx - r * ct);
-  dst[idx] = c < cs ? src[r * cs + c] : make_uint4(0u, 0u, 0u, 0u);
+  dst[idx] = c < cs ? *(const uint4*)(src + view_row_offset(r, heads, S, sb, sh, sr) + 16L * c)
+                    : make_uint4(0u, 0u, 0u, 0u);
 }
 
-// One float4 per thread: the first cs float4 of each ct-float4 row.
-__global__ __launch_bounds__(256) void unpad_rows_kernel(const float4* __restrict__ src,
-                                                         float4* __restrict__ dst, long rows,
-                                                         int ct, int cs) {
+// One float4 per thread: the first cs float4 of contiguous row r (ct float4
+// long) -> row r of the fp32 view.
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const float4* __restrict__ src,
+                                                           char* __restrict__ dst, long rows,
+                                                           int heads, int S, long long sb,
+                                                           long long sh, long long sr, int ct,
+                                                           int cs) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= rows * cs) return;
   const long r = idx / cs;
-  dst[idx] = src[r * ct + (idx - r * cs)];
+  const int c = (int)(idx - r * cs);
+  *(float4*)(dst + view_row_offset(r, heads, S, sb, sh, sr) + 16L * c) = src[r * ct + c];
 }
 
-hipError_t launch_pad_rows(const void* src, void* dst, long rows, int src_bytes, int dst_bytes,
-                           hipStream_t stream) {
+hipError_t launch_gather_rows(const void* src, void* dst, int B, int heads, int S,
+                              const long long st[3], int src_bytes, int dst_bytes,
+                              hipStream_t stream) {
+  const long rows = (long)B * heads * S;
   const long n = rows * (dst_bytes / 16);
-  hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                     (const uint4*)src, (uint4*)dst, rows, src_bytes / 16, dst_bytes / 16);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     (const char*)src, (uint4*)dst, rows, heads, S, st[0], st[1], st[2],
+                     src_bytes / 16, dst_bytes / 16);
   return hipGetLastError();
 }
 
-hipError_t launch_unpad_rows(const float* src, float* dst, long rows, int dt, int dv,
-                             hipStream_t stream) {
+hipError_t launch_scatter_rows(const float* src, void* dst, int B, int heads, int S,
+                               const long long st[3], int dt, int dv, hipStream_t stream) {
+  const long rows = (long)B * heads * S;
   const long n = rows * (dv / 4);
-  hipLaunchKernelGGL(unpad_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                     (const float4*)src, (float4*)dst, rows, dt / 4, dv / 4);
+  hipLaunchKernelGGL(scatter_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     (const float4*)src, (char*)dst, rows, heads, S, st[0], st[1], st[2], dt / 4,
+                     dv / 4);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
-// C ABI of the backward pass: argument checks, the D_i workspace and the
-// launch. Declared in include/fa.h (fa_bwd).
+// C ABI of the backward pass: argument checks, the D_i workspace, the staged
+// copies (padded head dims, strided tensors) and the launch. Declared in
+// include/fa.h (fa_bwd, fa_bwd_strided).
 #include "fa.h"
 
 #include <hip/hip_runtime.h>
@@ -30,18 +31,63 @@ int check_bwd(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int wind
   return FA_OK;
 }
 
-}  // namespace
+// Element strides (batch, head, row) of one view: the caller's, or those of a
+// contiguous [B, heads, S, D] tensor when `given` is NULL.
+void view_strides(const long long* given, int heads, int S, int D, long long out[3]) {
+  if (given) {
+    out[0] = given[0];
+    out[1] = given[1];
+    out[2] = given[2];
+  } else {
+    out[2] = D;
+    out[1] = (long long)S * D;
+    out[0] = (long long)heads * S * D;
+  }
+}
 
-extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                      const float* LSE, float* dQ, float* dK, float* dV, int B, int H, int HKV,
-                      int Sq, int Sk, int D, float scale, int causal, int window, int dtype,
-                      void* stream_ptr) {
+// Stride rules of the backward's views: non-negative, every row start 16-byte
+// aligned, rows of D elements not overlapping along the row axis, and every
+// element offset far inside int64 (the gradients must also have disjoint
+// rows, checked by the caller).
+int check_view(const long long st[3], int B, int heads, int S, int D, int esz) {
+  for (int a = 0; a < 3; ++a)
+    if (st[a] < 0 || (st[a] * esz) % 16 != 0) return FA_ERR_STRIDE;
+  if (st[2] < D) return FA_ERR_STRIDE;
+  const double last = (double)(B - 1) * st[0] + (double)(heads - 1) * st[1] +
+                      (double)(S - 1) * st[2] + D;
+  if (last * esz > 4.0e18) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+// The backward pass for views with the given element strides (NULL =
+// contiguous): q, k, v, o, dO in the input type, then dQ, dK, dV (fp32).
+int backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+             const float* LSE, float* dQ, float* dK, float* dV, int B, int H, int HKV, int Sq,
+             int Sk, int D, const long long* const given[8], float scale, int causal,
+             int window, int dtype, void* stream_ptr) {
   if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULLPTR;
-  const int st = check_bwd(B, H, HKV, Sq, Sk, D, causal, window, dtype);
+  int st = check_bwd(B, H, HKV, Sq, Sk, D, causal, window, dtype);
   if (st != FA_OK) return st;
   for (const void* p : {Q, K, V, O, dO, (const void*)LSE, (const void*)dQ, (const void*)dK,
                         (const void*)dV})
     if (!aligned16(p)) return FA_ERR_ALIGN;
+  // views: 0 Q, 1 K, 2 V, 3 O, 4 dO (input type), 5 dQ, 6 dK, 7 dV (fp32)
+  const int esz = dtype == FA_F32 ? 4 : 2;
+  long long vs[8][3];
+  bool contiguous = true;
+  for (int t = 0; t < 8; ++t) {
+    const bool kv = t == 1 || t == 2 || t == 6 || t == 7;
+    const int heads = kv ? HKV : H, S = kv ? Sk : Sq;
+    view_strides(given ? given[t] : nullptr, heads, S, D, vs[t]);
+    if ((st = check_view(vs[t], B, heads, S, D, t < 5 ? esz : 4)) != FA_OK) return st;
+    long long c[3];
+    view_strides(nullptr, heads, S, D, c);
+    contiguous = contiguous && std::equal(vs[t], vs[t] + 3, c);
+  }
+  if (!fa::output_rows_disjoint(vs[5], B, H, Sq, D) ||
+      !fa::output_rows_disjoint(vs[6], B, HKV, Sk, D) ||
+      !fa::output_rows_disjoint(vs[7], B, HKV, Sk, D))
+    return FA_ERR_STRIDE;
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
   fa::BwdParams p = {};
@@ -70,16 +116,19 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
   // 16-bit inputs at head dims 16 .. 96 other than 64 run the MFMA kernels of
   // the 64 or 128 tile on copies whose rows are zero-padded to the tile dim:
   // the zero dims add exact zeros to every dot product, and the gradients'
-  // padded dims (zero) are dropped when they are copied back.
+  // padded dims (zero) are dropped when they are copied back. Strided views
+  // are staged the same way: copied to contiguous rows, and the gradients
+  // copied back into the caller's views.
   const bool padded = dtype != FA_F32 && D != 64 && D != 128 && D != 256;
+  const bool staged = padded || !contiguous;
   const int DT = padded ? (D < 64 ? 64 : 128) : D;
   const size_t nq = (size_t)B * H * Sq, nk = (size_t)B * HKV * Sk;
   auto up = [](size_t bytes) { return (bytes + 255) / 256 * 256; };
   // workspace, stream-ordered from the library's memory pool: D_i, and when
   // padded Q, O, dO, K, V (input type) and dQ, dK, dV (fp32) at DT
   const size_t b_d = up(nq * sizeof(float));
-  const size_t b_q = padded ? up(nq * DT * 2) : 0, b_k = padded ? up(nk * DT * 2) : 0;
-  const size_t b_gq = padded ? up(nq * DT * 4) : 0, b_gk = padded ? up(nk * DT * 4) : 0;
+  const size_t b_q = staged ? up(nq * DT * esz) : 0, b_k = staged ? up(nk * DT * esz) : 0;
+  const size_t b_gq = staged ? up(nq * DT * 4) : 0, b_gk = staged ? up(nk * DT * 4) : 0;
   // The per-row kernels (fp32 inputs, D = 256) on grids too small to fill the
   // GPU: each row group's range is cut into nch chunks that run side by side
   // (a causal grid is otherwise bound by its longest rows), their partial
@@ -120,7 +169,7 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
     p.part_v = reinterpret_cast<float*>(pp + b_pq + b_pk);
   }
   hipError_t e = hipSuccess;
-  if (padded) {
+  if (staged) {
     char* q = w + b_d;
     char* o = q + b_q;
     char* go = o + b_q;
@@ -129,10 +178,16 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
     float* gq = reinterpret_cast<float*>(v + b_k);
     float* gk = reinterpret_cast<float*>(reinterpret_cast<char*>(gq) + b_gq);
     float* gv = reinterpret_cast<float*>(reinterpret_cast<char*>(gk) + b_gk);
-    const struct { const void* src; void* dst; size_t rows; } pads[5] = {
-        {Q, q, nq}, {O, o, nq}, {dO, go, nq}, {K, k, nk}, {V, v, nk}};
-    for (const auto& t : pads)
-      if (e == hipSuccess) e = fa::launch_pad_rows(t.src, t.dst, (long)t.rows, 2 * D, 2 * DT, stream);
+    long long bs[8][3];   // byte strides
+    for (int t = 0; t < 8; ++t)
+      for (int a = 0; a < 3; ++a) bs[t][a] = vs[t][a] * (t < 5 ? esz : 4);
+    const struct { const void* src; void* dst; int heads, S, view; } stage[5] = {
+        {Q, q, H, Sq, 0}, {O, o, H, Sq, 3}, {dO, go, H, Sq, 4}, {K, k, HKV, Sk, 1},
+        {V, v, HKV, Sk, 2}};
+    for (const auto& t : stage)
+      if (e == hipSuccess)
+        e = fa::launch_gather_rows(t.src, t.dst, B, t.heads, t.S, bs[t.view], esz * D, esz * DT,
+                                   stream);
     p.Q = q;
     p.O = o;
     p.dO = go;
@@ -142,12 +197,36 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
     p.dK = gk;
     p.dV = gv;
     if (e == hipSuccess) e = fa::launch_backward(p, dtype, DT, stream);
-    if (e == hipSuccess) e = fa::launch_unpad_rows(gq, dQ, (long)nq, DT, D, stream);
-    if (e == hipSuccess) e = fa::launch_unpad_rows(gk, dK, (long)nk, DT, D, stream);
-    if (e == hipSuccess) e = fa::launch_unpad_rows(gv, dV, (long)nk, DT, D, stream);
+    if (e == hipSuccess) e = fa::launch_scatter_rows(gq, dQ, B, H, Sq, bs[5], DT, D, stream);
+    if (e == hipSuccess) e = fa::launch_scatter_rows(gk, dK, B, HKV, Sk, bs[6], DT, D, stream);
+    if (e == hipSuccess) e = fa::launch_scatter_rows(gv, dV, B, HKV, Sk, bs[7], DT, D, stream);
   } else {
     e = fa::launch_backward(p, dtype, D, stream);
   }
   const hipError_t f = hipFreeAsync(ws, stream);
   return (e == hipSuccess && f == hipSuccess) ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                      const float* LSE, float* dQ, float* dK, float* dV, int B, int H, int HKV,
+                      int Sq, int Sk, int D, float scale, int causal, int window, int dtype,
+                      void* stream) {
+  return backward(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, HKV, Sq, Sk, D, nullptr, scale, causal,
+                  window, dtype, stream);
+}
+
+extern "C" int fa_bwd_strided(const void* Q, const void* K, const void* V, const void* O,
+                              const void* dO, const float* LSE, float* dQ, float* dK, float* dV,
+                              int B, int H, int HKV, int Sq, int Sk, int D,
+                              const long long* q_strides, const long long* k_strides,
+                              const long long* v_strides, const long long* o_strides,
+                              const long long* do_strides, const long long* dq_strides,
+                              const long long* dk_strides, const long long* dv_strides,
+                              float scale, int causal, int window, int dtype, void* stream) {
+  const long long* const given[8] = {q_strides, k_strides, v_strides, o_strides,
+                                     do_strides, dq_strides, dk_strides, dv_strides};
+  return backward(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, HKV, Sq, Sk, D, given, scale, causal,
+                  window, dtype, stream);
 }

@@ -258,6 +258,37 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
            int B, int H, int HKV, int Sq, int Sk, int D,
            float scale, int causal, int window, int dtype, void* stream);
 
+/*
+ * fa_bwd_strided - fa_bwd on views with arbitrary batch, head and row
+ * strides, e.g. the token-major [B, S, heads, D] layout the forge
+ * flash_attention.metal backward kernels address (row stride heads * D,
+ * head stride D), or slices of packed QKV buffers.
+ *
+ *   q_strides, k_strides, v_strides, o_strides, do_strides
+ *          host pointers to 3 element strides {batch, head, row} of Q, K, V,
+ *          O and dO (input type), as for fa_fwd_strided; NULL = contiguous
+ *   dq_strides, dk_strides, dv_strides
+ *          the same for the float32 gradients dQ, dK, dV; NULL = contiguous
+ *   LSE stays contiguous [B, H, Sq] float32. Strides are read during the call.
+ *
+ * Stride rules (else FA_ERR_STRIDE): every stride >= 0 and a multiple of 16
+ * bytes, every row stride >= D, and the rows of dQ, dK and dV pairwise
+ * disjoint; batch or head strides of 0 (broadcast inputs) are allowed for the
+ * inputs. When every view is contiguous the call runs exactly as fa_bwd;
+ * otherwise the inputs are first copied to contiguous rows and the gradients
+ * copied back into their views at the end (stream-ordered workspace from the
+ * library's pool, like the padded head dims of fa_bwd). Same arguments,
+ * ownership and other errors as fa_bwd.
+ */
+int fa_bwd_strided(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                   const float* LSE, float* dQ, float* dK, float* dV,
+                   int B, int H, int HKV, int Sq, int Sk, int D,
+                   const long long* q_strides, const long long* k_strides,
+                   const long long* v_strides, const long long* o_strides,
+                   const long long* do_strides, const long long* dq_strides,
+                   const long long* dk_strides, const long long* dv_strides,
+                   float scale, int causal, int window, int dtype, void* stream);
+
 /* fa_status_string - static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 

@@ -253,3 +253,51 @@ def test_padded_head_dims_pass_the_checks(D, ks):
     assert call_strided(ks=ks, D=D, Sq=64, Sk=64) == 8
     assert call(D=D) == 8
     assert call_bwd(D=D) == 8           # likewise for the backward (its workspace pool)
+
+
+# -------------------------------------------------------- strided backward entry
+def call_bwd_strided(strides=(None,) * 8, ptrs=(A,) * 9, **over):
+    a = dict(GOOD, **over)
+    arr = lambda t: None if t is None else ctypes.cast((ctypes.c_longlong * 3)(*t), ctypes.c_void_p)
+    return _lib.lib().fa_bwd_strided(*ptrs, a["B"], a["H"], a["HKV"], a["Sq"], a["Sk"], a["D"],
+                                     *[arr(s) for s in strides], a["scale"], a["causal"],
+                                     a["window"], a["dtype"], None)
+
+
+def _bwd_strides(which, st):
+    s = [None] * 8
+    s[which] = st
+    return tuple(s)
+
+
+@pytest.mark.parametrize("which,st", [
+    (0, (0, 128, -128)),                   # negative
+    (1, (0, 128, 100)),                    # K row stride < D
+    (3, (8192, 3, 512)),                   # O head stride not a multiple of 16 bytes (bf16)
+    (5, (8192, 2, 512)),                   # dQ head stride not a multiple of 16 bytes (fp32)
+    (5, (8192, 0, 128)),                   # dQ heads alias one another
+    (6, (0, 64 * 128, 64)),                # dK rows overlap (row stride < D)
+    (7, (64 * 128, 64, 256)),              # dV head 1 starts inside head 0's rows
+])
+def test_bwd_strided_rule_errors(which, st):
+    # GOOD: B = 1, H = 4, HKV = 2, Sq = Sk = 64, D = 128, bf16
+    assert call_bwd_strided(_bwd_strides(which, st)) == 11
+
+
+def test_bwd_strided_other_errors_come_first():
+    assert call_bwd_strided(_bwd_strides(0, (0, 128, -128)), D=40) == 4
+    assert call_bwd_strided(_bwd_strides(0, (0, 128, -128)), dtype=9) == 5
+    ptrs = (None,) + (A,) * 8
+    assert call_bwd_strided(ptrs=ptrs) == 1
+    assert call_bwd_strided(_bwd_strides(1, (1 << 61, 128, 512)), B=4) == 2
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                    reason="valid arguments would reach a kernel launch on fake pointers")
+def test_bwd_strided_token_major_passes_the_checks():
+    # token-major views of every tensor (and broadcast K/V): past every stride
+    # rule, the call stops at the workspace pool's device query
+    tm_q = (64 * 4 * 128, 128, 4 * 128)
+    tm_k = (64 * 2 * 128, 128, 2 * 128)
+    assert call_bwd_strided((tm_q, tm_k, tm_k, tm_q, tm_q, tm_q, tm_k, tm_k)) == 8
+    assert call_bwd_strided((None, (0, 64 * 128, 128), None, None, None, None, None, None)) == 8

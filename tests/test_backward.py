@@ -3,12 +3,17 @@ gradients, on the same seeded inputs; O and LSE come from the library's own
 forward pass, as a caller would use them.
 
 Tolerance (absolute, scaled by the largest reference magnitude r = max(1,
-max|ref|) of each gradient): fp32 inputs 1e-4 r; bf16 3e-2 r and fp16 1e-2 r.
-The 16-bit bounds come from the forward output and the MFMA operands: the
-backward reads O rounded to the input type, so D_i = dO_i . O_i carries a
-relative error up to 2^-9 (bf16) or 2^-11 (fp16) of sum|dO||O|, every dS_ij =
-P_ij (dP_ij - D_i) inherits it, and P and dS are rounded once more to the
-input type as MFMA operands; the inputs themselves are exact on both sides."""
+max|ref|) of each gradient): bf16 1e-2 r, fp16 2e-3 r, fp32 1e-5 r. The
+16-bit errors come from three roundings to the input type, each of relative
+size at most its unit roundoff u (2^-8 for bf16, 2^-11 for fp16): the backward
+reads O rounded, so D_i = dO_i . O_i is off by up to u sum|dO||O|, which every
+dS_ij = P_ij (dP_ij - D_i) inherits; and P and dS are rounded as MFMA
+operands. The rounding errors of a gradient's many terms have independent
+signs, so its error stays a small multiple of u r: the bounds are 2.56 u
+(bf16) and 4.1 u (fp16), 3.7x and 6.3x the largest errors measured over every
+backward case of the test suite, the benchmark shape included (2.74e-3 r and
+3.15e-4 r). fp32 (per-row kernels, fp32 throughout): 1e-5 r, 8.3x the largest
+measured (1.2e-6 r). The inputs themselves are exact on both sides."""
 import numpy as np
 import pytest
 
@@ -19,7 +24,7 @@ from test_parity import host64, to_device, wl_small
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 3e-2, "f16": 1e-2}
+TOL = {"f32": 1e-5, "bf16": 1e-2, "f16": 2e-3}
 
 
 def grads(wl, seed=0):

@@ -22,7 +22,7 @@ from test_parity import TOL, compare, host64, to_device, wl_small
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-BWD_TOL = {"f32": 1e-4, "bf16": 3e-2, "f16": 1e-2}
+BWD_TOL = {"f32": 1e-5, "bf16": 1e-2, "f16": 2e-3}   # the bounds of test_backward.py
 
 
 def _say(msg):
@@ -165,4 +165,5 @@ def test_backward(case):
         x = host64(x)
         err = float(np.abs(x - r).max())
         tol = BWD_TOL[wl.dtype] * max(1.0, float(np.abs(r).max()))
+        print(f"  {name}: max|d|={err:.3e} (tol {tol:.3e})", flush=True)
         assert np.all(np.isfinite(x)) and err <= tol, f"{name}: {err:.3e} > {tol:.3e}"

@@ -18,7 +18,7 @@ from test_parity import TOL, compare, host64, to_device, wl_small
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-BWD_TOL = {"f32": 1e-4, "bf16": 3e-2, "f16": 1e-2}
+BWD_TOL = {"f32": 1e-5, "bf16": 1e-2, "f16": 2e-3}   # the bounds of test_backward.py
 
 
 def draw(seed):
@@ -91,4 +91,5 @@ def test_random_backward(seed):
         x = host64(x)
         err = float(np.abs(x - r).max()) if r.size else 0.0
         tol = BWD_TOL[wl.dtype] * max(1.0, float(np.abs(r).max()) if r.size else 1.0)
+        print(f"  {name}: max|d|={err:.3e} (tol {tol:.3e})", flush=True)
         assert np.all(np.isfinite(x)) and err <= tol, f"{name}: {err:.3e} > {tol:.3e}"

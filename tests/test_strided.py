@@ -116,3 +116,83 @@ def test_kv_broadcast_over_batch(dtype):
     inp.v = np.broadcast_to(inp1.v, inp.v.shape).copy()
     check(wl, inp, q, k, v, num_splits=1)
 
+
+
+# ------------------------------------------------------- strided backward
+BWD_TOL = {"f32": 1e-5, "bf16": 1e-2, "f16": 2e-3}   # the bounds of test_backward.py
+
+
+def _bwd_check(wl, inp, q, k, v, do_np, do_dev):
+    """fa.bwd on the given views (fa_bwd_strided) against the contiguous
+    fa_bwd (the same kernels on contiguous rows: bit-identical) and the
+    oracle's gradients."""
+    import attention_forward_online_fa_amd as fa
+    from oracle import attention_backward
+    qc, kc, vc, doc = (x.contiguous() for x in (q, k, v, do_dev))
+    o, lse = fa.fwd(qc, kc, vc, causal=bool(wl.causal), window=wl.window, scale=wl.scale())
+    ref = fa.bwd(qc, kc, vc, o, lse, doc, causal=bool(wl.causal), window=wl.window,
+                 scale=wl.scale())
+    o_view = token_major(o) if not q.is_contiguous() else o
+    got = fa.bwd(q, k, v, o_view, lse, do_dev, causal=bool(wl.causal), window=wl.window,
+                 scale=wl.scale())
+    torch.cuda.synchronize()
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert torch.equal(g.contiguous(), r), f"strided {name} differs from the contiguous path"
+    oq = attention_backward(inp.q, inp.k, inp.v, do_np, wl.scale(), bool(wl.causal), wl.window)
+    for name, g, r in zip(("dQ", "dK", "dV"), got, oq):
+        err = float(np.abs(host64(g) - r).max())
+        bound = BWD_TOL[wl.dtype] * max(1.0, float(np.abs(r).max()))
+        _say(f"  strided bwd {name}: max|d|={err:.3e} (tol {bound:.3e})")
+        assert err <= bound, name
+    return got
+
+
+def _grad_out(wl, q):
+    rng = np.random.default_rng(wl.seed + 5000)
+    g = rng.standard_normal(tuple(q.shape)).astype(np.float32)
+    if wl.dtype in W.ROUNDING:
+        to_bits, to_f32 = W.ROUNDING[wl.dtype]
+        bits = to_bits(g)
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float16
+        return to_f32(bits), torch.from_numpy(bits.view(np.int16)).view(tdt).cuda()
+    return g, torch.from_numpy(g).cuda()
+
+
+BWD_CASES = [
+    ("f32", 1, 4, 2, 150, 150, 64, 1, 0),
+    ("bf16", 1, 8, 2, 300, 300, 128, 1, 0),
+    ("bf16", 1, 4, 2, 200, 260, 96, 0, 70),    # padded head dim and strides together
+    ("f16", 1, 2, 1, 130, 170, 256, 1, 0),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=["-".join(map(str, c)) for c in BWD_CASES])
+def test_backward_token_major(case):
+    # forge's backward layout: Q, K, V, O, dO token-major [B, S, heads, D];
+    # the gradients come back token-major too
+    wl = wl_small(*case, seed=sum(case[1:]) + 7)
+    inp = W.make_inputs(wl)
+    _say(f"[strided bwd] token-major {wl}")
+    q, k, v = (token_major(x) for x in to_device(inp))
+    g_np, g_dev = _grad_out(wl, q)
+    dq, dk, dv = _bwd_check(wl, inp, q, k, v, g_np, token_major(g_dev))
+    assert dq.stride() == q.stride() and dk.stride() == k.stride()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_packed_qkv(dtype):
+    # Q, K, V slices of one packed [B, S, H + 2 HKV, D] buffer (GQA)
+    B, H, HKV, S, D = 2, 4, 2, 200, 64
+    wl = wl_small(dtype, B, H, HKV, S, S, D, 1, 0, seed=41)
+    inp = W.make_inputs(wl)
+    _say(f"[strided bwd] packed QKV {wl}")
+    q0, k0, v0 = to_device(inp)
+    buf = torch.empty(B, S, H + 2 * HKV, D, dtype=q0.dtype, device=q0.device)
+    buf[:, :, :H] = q0.transpose(1, 2)
+    buf[:, :, H:H + HKV] = k0.transpose(1, 2)
+    buf[:, :, H + HKV:] = v0.transpose(1, 2)
+    q = buf[:, :, :H].transpose(1, 2)
+    k = buf[:, :, H:H + HKV].transpose(1, 2)
+    v = buf[:, :, H + HKV:].transpose(1, 2)
+    g_np, g_dev = _grad_out(wl, q0)
+    _bwd_check(wl, inp, q, k, v, g_np, g_dev)
