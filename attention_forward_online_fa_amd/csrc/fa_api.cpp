@@ -497,7 +497,14 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   const long blocks = units * p.n_qblk;
   if (blocks < 1 || blocks > 2147483647L) return FA_ERR_SHAPE;
   p.units = (int)units;
-  p.xcd_remap = (p.units % 8 == 0) ? 1 : 0;
+  // Sliding windows over G < 8 kv units (G dividing 8) whose query tiles
+  // split into whole snake periods across the R = 8 / G XCDs of a kv unit:
+  // the chunked order of map_tile; otherwise query tile major when the units
+  // split evenly over the 8 XCDs.
+  const int kv_units = p.units / p.packs;
+  const bool chunked = window > 0 && kv_units < 8 && 8 % kv_units == 0 &&
+                       p.n_qblk % (fa::kXcdChunk * 2 * (8 / kv_units)) == 0;
+  p.xcd_remap = chunked ? 2 : (p.units % 8 == 0) ? 1 : 0;
   std::copy(qs, qs + 3, p.qs);
   std::copy(ks, ks + 3, p.ks);
   std::copy(vs, vs + 3, p.vs);

@@ -21,7 +21,29 @@ struct Tile {
 __device__ __forceinline__ Tile map_tile(const Params& p) {
   const int i = blockIdx.x;
   int t, u;
-  if (p.xcd_remap) {
+  if (p.xcd_remap == 2) {
+    // Sliding windows with fewer than 8 kv units (K/V heads times splits):
+    // the R = 8 / G XCDs of kv unit g = x / R share its query tiles in
+    // chunks of kXcdChunk consecutive tiles (every pack of each), dealt in
+    // snake order (r, 2R - 1 - r per period of 2R chunks) so that the light
+    // tiles where the window is still filling spread evenly, and run
+    // heaviest chunk first. The workgroups an XCD runs at once then hold
+    // every query head of one K/V head over one or two runs of consecutive
+    // tiles: their windows overlap and the keys they read at one time stay in
+    // that XCD's L2 (the query-tile-major order below spreads an XCD's
+    // concurrent workgroups over a whole window of keys).
+    const int x = i & 7, k = i >> 3;
+    const int R = 8 / (p.units / p.packs);
+    const int g = x / R, r = x % R;
+    const int per_chunk = kXcdChunk * p.packs;
+    const int s = k / per_chunk, o = k % per_chunk;
+    const int periods = p.n_qblk / (kXcdChunk * 2 * R);
+    const int period = periods - 1 - (s >> 1);
+    const int chunk = period * 2 * R + ((s & 1) ? r : 2 * R - 1 - r);
+    const int qb = chunk * kXcdChunk + kXcdChunk - 1 - o / p.packs;
+    t = p.n_qblk - 1 - qb;
+    u = g * p.packs + o % p.packs;
+  } else if (p.xcd_remap) {
     // Block i runs on XCD i % 8 as that XCD's (i / 8)-th block. Give XCD x
     // the contiguous unit range [x U/8, (x+1) U/8).
     // Within an XCD: query tile major (heaviest first), then unit; the units

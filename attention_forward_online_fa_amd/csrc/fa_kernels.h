@@ -34,7 +34,8 @@ struct Params {
   int hp;
   int packs;
   int bm;            // query rows per workgroup (of each of its hp heads): kBlockM / hp
-  int xcd_remap;     // 1: group work so units sharing K/V stay on one XCD
+  int xcd_remap;     // 1: units sharing K/V stay on one XCD (query tile major);
+                     // 2: sliding windows over fewer than 8 kv units (see map_tile)
   // Persistent launch (fp32 kernel): nslot workgroups, workgroup s runs the
   // items sched[nslot + 1 + k] for k in [sched[s], sched[s + 1]), item =
   // qblk * units + unit. Null: one workgroup per item in the default order.
@@ -72,6 +73,8 @@ constexpr int kMaxListTiles = 2048;
 
 // Tile shape per (dtype, D): query rows per workgroup and keys per K/V tile.
 constexpr int kBlockM = 128;
+// Query tiles per chunk of the sliding-window XCD order (Params::xcd_remap 2).
+constexpr int kXcdChunk = 8;
 int key_tile(int dtype, int D);
 int block_m(int dtype, int D);
 // Workgroups of the fp32 kernel (in the given form) that fit on one CU at

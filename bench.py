@@ -41,7 +41,8 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # MI355X dense MFM
 # It counts packed fp32 FMAs; code built without them (as this library is) tops out at half.
 PEAK_VALU_F32 = 157.3
 KERNEL_SOURCES = [os.path.join(ROOT, "attention_forward_online_fa_amd", "csrc", f)
-                  for f in ("fa_fwd.hip", "fa_api.cpp", "fa_kernels.h", "fa_tile.h")]
+                  for f in ("fa_fwd.hip", "fa_fwd_common.h", "fa_api.cpp", "fa_kernels.h",
+                            "fa_tile.h")]
 
 
 def row_counts(wl: W.Workload, i: np.ndarray, mask_bh=None) -> np.ndarray:

@@ -110,6 +110,10 @@ SMALL = [
     ("bf16", 1, 4, 1, 1536, 1536, 128, 1, 0),
     ("bf16", 1, 2, 2, 256, 1500, 128, 0, 0),
     ("bf16", 2, 2, 1, 333, 1111, 128, 0, 500),
+    # sliding windows over 4 kv units: the chunked XCD order of the work
+    # mapping (query-tile chunks dealt in snake order over two XCDs per kv unit)
+    ("bf16", 1, 8, 4, 2048, 2048, 128, 1, 300),
+    ("f32", 1, 4, 4, 4096, 4096, 64, 1, 500),
     # float16 inputs (same kernel as bfloat16, fp16 MFMA and fp16 P)
     ("f16", 1, 1, 1, 128, 128, 64, 0, 0),
     ("f16", 2, 4, 2, 300, 300, 64, 1, 0),
