@@ -12,8 +12,9 @@ operands. The rounding errors of a gradient's many terms have independent
 signs, so its error stays a small multiple of u r: the bounds are 2.56 u
 (bf16) and 4.1 u (fp16), 3.7x and 6.3x the largest errors measured over every
 backward case of the test suite, the benchmark shape included (2.74e-3 r and
-3.15e-4 r). fp32 (per-row kernels, fp32 throughout): 1e-5 r, 8.3x the largest
-measured (1.2e-6 r). The inputs themselves are exact on both sides."""
+3.15e-4 r). fp32 (fp32 MFMA and per-row kernels, fp32 throughout): 1e-5 r, 5x
+the largest measured (2.0e-6 r). The inputs themselves are exact on both
+sides."""
 import numpy as np
 import pytest
 
