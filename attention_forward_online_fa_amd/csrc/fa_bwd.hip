@@ -337,13 +337,14 @@ void bwd_dkdv_kernel(BwdParams p) {
 // with the V swizzle for K^T; V is read by rows only.
 // D_i = dO_i . O_i is formed here and written for the dK/dV kernel.
 template <typename E, int D>
-__global__ __launch_bounds__(kBwdThreads, 2)
+__global__ __launch_bounds__(kBwdThreads, D <= 128 ? 2 : 1)
 void bwd_dq_mfma_kernel(BwdParams p) {
   constexpr int BN = 32;
   using T = Bf16Tile<D, BN>;
   using X = Elt<E>;
   typedef typename X::x8 e16x8;
-  static_assert(D <= 128, "one offset register per K operand step");
+  // D = 256: one wavefront per SIMD (the dQ^T accumulators, 128 registers, in AGPRs)
+  static_assert(D == 64 || D == 128 || D == 256, "MFMA tile dims");
   __shared__ __attribute__((aligned(1024))) char kbuf0[T::TILE];
   __shared__ __attribute__((aligned(1024))) char kbuf1[T::TILE];
   __shared__ __attribute__((aligned(1024))) char ktbuf0[T::TILE];   // K again, V swizzle
@@ -518,12 +519,18 @@ __global__ __launch_bounds__(kBwdThreads, 1)
 void bwd_dkdv_mfma_kernel(BwdParams p) {
   // 64 query rows per copied tile, worked as two independent 32-row halves
   // between barriers, so one half's MFMAs can issue under the other's
-  // exponentials (one wavefront per SIMD leaves no other wavefront to do it)
-  constexpr int BM = 64, HM = 32;
+  // exponentials (one wavefront per SIMD leaves no other wavefront to do it).
+  // D = 256 is blocked along the output dims: a workgroup accumulates dK and
+  // dV for DO = 128 of the 256 dims (blockIdx.x % 2 picks which) while its
+  // score products S and dP take all 256; its Q/dO tiles are 32 rows (the
+  // four copies of a 64-row tile would not fit in LDS).
+  constexpr int DO = D <= 128 ? D : 128;         // output dims per workgroup
+  constexpr int DBO = DO / 32;                   // output dim blocks per workgroup
+  constexpr int BM = D <= 128 ? 64 : 32, HM = 32, NH = BM / HM;
   using T = Bf16Tile<D, BM>;
   using X = Elt<E>;
   typedef typename X::x8 e16x8;
-  static_assert(D <= 128, "one offset register per operand step");
+  static_assert(D == 64 || D == 128 || D == 256, "MFMA tile dims");
   // Q and dO tiles twice each: K swizzle for the row reads, V swizzle for the
   // transposed reads (see the dQ kernel)
   __shared__ __attribute__((aligned(1024))) char qbuf0[T::TILE];
@@ -534,15 +541,17 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char obuf1[T::TILE];
   __shared__ __attribute__((aligned(1024))) char otbuf0[T::TILE];
   __shared__ __attribute__((aligned(1024))) char otbuf1[T::TILE];
-  __shared__ __attribute__((aligned(16))) float lbuf0[2 * BM];   // [0, 64): base-2 LSE, [64, 128): D
+  __shared__ __attribute__((aligned(16))) float lbuf0[2 * BM];   // [0, BM): base-2 LSE, [BM, 2 BM): D
   __shared__ __attribute__((aligned(16))) float lbuf1[2 * BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int units = p.B * p.HKV;
-  const int kblk = blockIdx.x / units;   // ascending: under a causal mask the first keys see most rows
-  const int u = blockIdx.x % units;
+  const int ob = blockIdx.x % (D / DO);               // output dim block: dims DO ob ..
+  const int bid = blockIdx.x / (D / DO);
+  const int kblk = bid / units;   // ascending: under a causal mask the first keys see most rows
+  const int u = bid % units;
   const int hkv = u % p.HKV, b = u / p.HKV;
   const int gh = p.H / p.HKV;
   const int k0 = kblk * 128, kw = k0 + wave * 32, j = kw + l32;
@@ -582,7 +591,7 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
       dma16(ob, bytes, voff ^ T::dma_xor(k, false), od + off);
       dma16(ob, bytes, voff_t ^ T::dma_xor(k, true), otd + off);
     }
-    if (wave < 2) ld[wave * BM + lane] = x;
+    if (wave < 2 && lane < BM) ld[wave * BM + lane] = x;
   };
   if (n_tiles > 0) issue(0, qbuf0, qtbuf0, obuf0, otbuf0, lbuf0);
 
@@ -607,16 +616,16 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   for (int t = 0; t < T::DC; ++t) roff[t] = qrow * T::ROW + (((2 * t + g) ^ T::swz_k(qrow)) << 4);
   const int blk = lane >> 4, li = lane & 15;
   const int vrow = 8 * g + (li >> 2);
-  int troff[T::DB];
+  int troff[DBO];   // the output dim blocks DBO ob + db
 #pragma unroll
-  for (int db = 0; db < T::DB; ++db) {
-    const int chunk = 4 * db + 2 * (blk & 1) + ((li & 3) >> 1);
+  for (int db = 0; db < DBO; ++db) {
+    const int chunk = 4 * (DBO * ob + db) + 2 * (blk & 1) + ((li & 3) >> 1);
     troff[db] = vrow * T::ROW + ((chunk ^ T::swz_v(vrow)) << 4) + 8 * (li & 1);
   }
 
-  f32x16 dk[T::DB], dv[T::DB];
+  f32x16 dk[DBO], dv[DBO];
 #pragma unroll
-  for (int db = 0; db < T::DB; ++db) dk[db] = dv[db] = f32x16{};
+  for (int db = 0; db < DBO; ++db) dk[db] = dv[db] = f32x16{};
 
   auto step = [&](int t, const char* Qc, const char* QTc, const char* Oc, const char* OTc,
                   const float* Lc, char* Qn, char* QTn, char* On, char* OTn,
@@ -627,9 +636,9 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
     if (kw >= p.Sk || (p.causal && r0 + BM - 1 < kw) ||
         (p.window > 0 && r0 > kw + 31 + p.window - 1))
       return;
-    f32x16 sc[2], dp[2];
+    f32x16 sc[NH], dp[NH];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < NH; ++hh) {
       sc[hh] = f32x16{};
       dp[hh] = f32x16{};
 #pragma unroll
@@ -642,9 +651,9 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
     }
     const bool edge = (kw + 31 >= p.Sk) || (p.causal && r0 < kw + 31) ||
                       (p.window > 0 && r0 + BM - 1 > kw + p.window - 1);
-    typename X::x8 pp[2][2], ds[2][2];
+    typename X::x8 pp[NH][2], ds[NH][2];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < NH; ++hh) {
       // element v holds query row r0 + 32 hh + 8g + c, c = 16 (v / 8) + v % 8
       f32x4 lq[4], dq4[4];
 #pragma unroll
@@ -667,18 +676,18 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
       }
     }
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+    for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        e16x8 ao[T::DB], aq[T::DB];
+        e16x8 ao[DBO], aq[DBO];
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db) {
+        for (int db = 0; db < DBO; ++db) {
           const int o = troff[db] + (HM * hh + 16 * c) * T::ROW;
           ao[db] = read_v_pair<e16x8>(OTc, o, o + 4 * T::ROW);
           aq[db] = read_v_pair<e16x8>(QTc, o, o + 4 * T::ROW);
         }
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db) {
+        for (int db = 0; db < DBO; ++db) {
           dv[db] = X::mfma(ao[db], pp[hh][c], dv[db]);
           dk[db] = X::mfma(aq[db], ds[hh][c], dk[db]);
         }
@@ -691,12 +700,12 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
       step(t + 1, qbuf1, qtbuf1, obuf1, otbuf1, lbuf1, qbuf0, qtbuf0, obuf0, otbuf0, lbuf0);
   }
 
-  // lane holds dims 32 db + 8 a + 4 g + (0..3) of key j
+  // lane holds dims DO ob + 32 db + 8 a + 4 g + (0..3) of key j
   if (key_ok) {
-    float* odk = p.dK + krow * D;
-    float* odv = p.dV + krow * D;
+    float* odk = p.dK + krow * D + DO * ob;
+    float* odv = p.dV + krow * D + DO * ob;
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db)
+    for (int db = 0; db < DBO; ++db)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const f32x4 k4 = {dk[db][4 * a] * p.scale, dk[db][4 * a + 1] * p.scale,
@@ -1104,7 +1113,8 @@ static hipError_t sum_parts(const float* part, float* out, long n, int nch, floa
 template <typename E, int D>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   constexpr bool f32_mfma = sizeof(E) == 4 && bwd_f32_mfma(D);
-  if constexpr (sizeof(E) == 2 && (D == 64 || D == 128)) {
+  constexpr bool b16_mfma = sizeof(E) == 2 && (D == 64 || D == 128 || D == 256);
+  if constexpr (b16_mfma) {
     hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D>), dim3((unsigned)((long)p.B * p.H * p.n_qblk)),
                        dim3(kBwdThreads), 0, stream, p);
   } else if constexpr (f32_mfma) {
@@ -1123,8 +1133,9 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
     e = sum_parts(p.part_q, p.dQ, (long)p.B * p.H * p.Sq * D, p.nch, p.scale, stream);
     if (e != hipSuccess) return e;
   }
-  if constexpr (sizeof(E) == 2 && (D == 64 || D == 128)) {
-    const long kblocks = (long)p.B * p.HKV * ((p.Sk + 127) / 128);
+  if constexpr (b16_mfma) {
+    // (D = 256: two workgroups per key block, one per half of the output dims)
+    const long kblocks = (long)p.B * p.HKV * ((p.Sk + 127) / 128) * (D == 256 ? 2 : 1);
     hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D>), dim3((unsigned)kblocks), dim3(kBwdThreads), 0,
                        stream, p);
   } else if constexpr (f32_mfma) {

@@ -129,14 +129,14 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
   const size_t b_d = up(nq * sizeof(float));
   const size_t b_q = staged ? up(nq * DT * esz) : 0, b_k = staged ? up(nk * DT * esz) : 0;
   const size_t b_gq = staged ? up(nq * DT * 4) : 0, b_gk = staged ? up(nk * DT * 4) : 0;
-  // The per-row kernels (fp32 inputs at D = 16, 48, 80 and 256; 16-bit D = 256) on grids too small to fill the
+  // The per-row kernels (fp32 inputs at D = 16, 48, 80 and 256) on grids too small to fill the
   // GPU: each row group's range is cut into nch chunks that run side by side
   // (a causal grid is otherwise bound by its longest rows), their partial
   // sums added up afterwards in chunk order (deterministic). A group's range
   // spans at most `span` + R - 1 keys (query rows): the ranges of its R
   // adjacent rows.
   p.nch = 1;
-  if ((dtype == FA_F32 && !fa::bwd_f32_mfma(D)) || D == 256) {
+  if (dtype == FA_F32 && !fa::bwd_f32_mfma(D)) {
     const int R = fa::bwd_rows_per_group(D);
     const long groups = (long)B * H * ((Sq + R - 1) / R);
     const long target = 1L << 18;   // row groups that fill the GPU several times over

@@ -160,10 +160,10 @@ def bench_backward(args, wl, inp, q, k, v, torch, fa):
     ms_per_step = wall * 1e3 / args.steps
     per_step = per_step_events(step, stream, 20)
     flops = 2.5 * counted_flops(wl)          # 10 D per visible pair
-    # MFMA backward kernels: 16-bit inputs at D <= 128 (head dims other than 64
-    # and 128 on zero-padded copies) and fp32 inputs at D = 32, 64, 96, 128;
-    # the rest (D = 256, fp32 D = 16, 48, 80) run the per-row VALU kernels
-    if (wl.dtype != "f32" and wl.D <= 128) or (wl.dtype == "f32" and wl.D in (32, 64, 96, 128)):
+    # MFMA backward kernels: 16-bit inputs (head dims other than 64, 128 and
+    # 256 on zero-padded copies) and fp32 inputs at D = 32, 64, 96, 128; the
+    # rest (fp32 D = 16, 48, 80, 256) run the per-row VALU kernels
+    if wl.dtype != "f32" or wl.D in (32, 64, 96, 128):
         bound, peak = "mfma", PEAK_TFLOPS[wl.dtype]
     else:
         bound, peak = "alu", PEAK_VALU_F32

@@ -66,24 +66,36 @@ CASES = [
 ]
 
 
-# several query tiles and key blocks for the MFMA kernels (16-bit, D <= 128)
+# several query tiles and key blocks for the MFMA kernels (16-bit; at D = 256
+# the dK/dV kernel takes half of the output dims per workgroup)
 CASES += [
+    ("bf16", 1, 4, 2, 700, 900, 256, 1, 0),
+    ("f16", 1, 2, 1, 500, 1300, 256, 0, 200),
     ("bf16", 1, 8, 2, 1024, 1024, 128, 1, 0),
     ("bf16", 1, 4, 4, 700, 1100, 64, 0, 0),
     ("f16", 1, 4, 1, 1000, 1000, 128, 1, 300),
     ("bf16", 2, 2, 1, 900, 600, 128, 0, 250),
 ]
 
-# small grids on the per-row kernels (fp32, D = 256): the rows' ranges run in
-# up to eight chunks whose partial sums are added afterwards
+# small grids on the per-row kernels (fp32 at D = 16, 48, 80, 256): the rows'
+# ranges run in up to eight chunks whose partial sums are added afterwards
 CASES += [
-    ("f32", 1, 2, 1, 1024, 1024, 64, 1, 0),      # eight chunks, causal
-    ("f32", 1, 2, 2, 600, 900, 32, 0, 100),      # a window alone: ranges up to Sk / Sq
-    ("f32", 1, 4, 1, 800, 800, 96, 1, 300),      # causal band of 300
-    ("bf16", 1, 2, 1, 600, 700, 256, 0, 0),      # D = 256: two rows per 32-lane group
+    ("f32", 1, 2, 1, 1024, 1024, 48, 1, 0),      # eight chunks, causal
+    ("f32", 1, 2, 2, 600, 900, 16, 0, 100),      # a window alone: ranges up to Sk / Sq
+    ("f32", 1, 4, 1, 800, 800, 80, 1, 300),      # causal band of 300
+    ("f32", 1, 2, 1, 600, 700, 256, 0, 0),       # D = 256: two rows per 32-lane group
     # odd Sq and Sk at D = 256: the last group of each kernel holds one row
-    ("bf16", 1, 2, 1, 91, 121, 256, 1, 30),
+    ("f32", 1, 2, 1, 91, 121, 256, 1, 30),
     ("f32", 1, 2, 2, 77, 133, 256, 0, 0),
+]
+
+# the same shapes on the MFMA kernels (fp32 at D = 64, 32, 96; bf16 at D = 256)
+CASES += [
+    ("f32", 1, 2, 1, 1024, 1024, 64, 1, 0),
+    ("f32", 1, 2, 2, 600, 900, 32, 0, 100),
+    ("f32", 1, 4, 1, 800, 800, 96, 1, 300),
+    ("bf16", 1, 2, 1, 600, 700, 256, 0, 0),
+    ("bf16", 1, 2, 1, 91, 121, 256, 1, 30),     # odd Sq and Sk
 ]
 
 
@@ -116,10 +128,12 @@ def test_backward_empty_rows_and_unseen_keys(dtype):
             assert float(np.abs(g - r).max()) <= TOL[dtype] * max(1.0, float(np.abs(r).max()))
 
 
-def test_backward_deterministic_fp32_chunked():
-    # fp32 on a small grid: chunked ranges, partial sums added in a fixed order
+@pytest.mark.parametrize("D", [48, 64])
+def test_backward_deterministic_fp32_chunked(D):
+    # fp32 on a small grid: at D = 48 the per-row kernels' chunked ranges,
+    # partial sums added in a fixed order; at D = 64 the fp32 MFMA kernels
     import attention_forward_online_fa_amd as fa
-    wl = wl_small("f32", 1, 2, 1, 900, 900, 64, 1, 0, seed=6)
+    wl = wl_small("f32", 1, 2, 1, 900, 900, D, 1, 0, seed=6)
     q, k, v = to_device(W.make_inputs(wl))
     do = torch.randn_like(q)
     o, lse = fa.fwd(q, k, v, causal=True)
