@@ -552,6 +552,11 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
 }  // namespace
 
 namespace fa {
+int device_cus() {
+  DeviceState* ds = nullptr;
+  return device_state(&ds) == FA_OK ? ds->num_cus : 0;
+}
+
 int forward_fixed_workspace(const void* Q, const void* K, const void* V, void* O, float* LSE,
                             int B, int H, int HKV, int Sq, int Sk, int D, float scale,
                             int causal, int window, int dtype, int num_splits, void* stream,

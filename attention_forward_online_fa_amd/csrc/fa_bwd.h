@@ -27,11 +27,14 @@ struct BwdParams {
   float sl_abs;
   int neg_q;
   int n_qblk;
-  // Per-row kernels (fp32 inputs, D = 256) on small grids: each row group's
-  // range is cut into nch chunks of chunk_q keys (dQ kernel) or chunk_k query
-  // rows (dK/dV kernel), one per blockIdx.y; chunk c writes unscaled partial
-  // sums to part_q [nch][B H Sq][D] and part_k, part_v [nch][B HKV Sk][D],
-  // which are then added up in chunk order. nch = 1: gradients written directly.
+  // Small grids: the key range is cut into nch chunks, one per blockIdx.y,
+  // whose unscaled partial sums are added up in chunk order afterwards (nch =
+  // 1: gradients written directly). Per-row kernels: each row group's range
+  // in chunks of chunk_q keys (dQ) or chunk_k query rows (dK/dV), partial sums
+  // to part_q [nch][B H Sq][D] and part_k, part_v [nch][B HKV Sk][D]. MFMA
+  // dQ kernels: key chunk c = [c chunk_q, (c + 1) chunk_q) (chunk_q a
+  // multiple of the 32-key tile), partial sums to part_q; their dK/dV
+  // kernels never split.
   int nch, chunk_q, chunk_k;
   float* part_q;
   float* part_k;
@@ -68,6 +71,9 @@ hipError_t launch_scatter_rows(const float* src, void* dst, int B, int heads, in
 // True when the rows of a [B, heads, S, D] view with element strides st
 // (batch, head, row) are pairwise disjoint (fa_api.cpp).
 bool output_rows_disjoint(const long long st[3], int B, int heads, int S, int D);
+
+// Compute units of the current device (cached; fa_api.cpp), 0 on error.
+int device_cus();
 
 // Stream-ordered workspace of `bytes` from the library's memory pool on the
 // current device (fa_api.cpp); release with hipFreeAsync. Returns an fa_status.

@@ -370,10 +370,15 @@ void bwd_dq_mfma_kernel(BwdParams p) {
   const E* Kp = (const E*)p.K + ((long)b * p.HKV + hkv) * p.Sk * D;
   const E* Vp = (const E*)p.V + ((long)b * p.HKV + hkv) * p.Sk * D;
 
-  // key range of the block
+  // key range of the block; on small grids only key chunk blockIdx.y of it
+  // (chunk_q is a multiple of BN, so the chunks split the key tiles exactly)
   int lo = 0, hi = p.Sk;
   if (p.causal) hi = min(hi, min(q0 + 128, p.Sq));
   if (p.window > 0) lo = max(0, q0 - p.window + 1);
+  if (p.nch > 1) {
+    lo = max(lo, (int)blockIdx.y * p.chunk_q);
+    hi = min(hi, ((int)blockIdx.y + 1) * p.chunk_q);
+  }
   const int t0 = (lo / BN) * BN;
   const int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
 
@@ -489,18 +494,22 @@ void bwd_dq_mfma_kernel(BwdParams p) {
     if (t + 1 < n_tiles) step(t + 1, kbuf1, ktbuf1, vbuf1, kbuf0, ktbuf0, vbuf0);
   }
 
-  // lane holds dims 32 db + 8 a + 4 g + (0..3) of row i
+  // lane holds dims 32 db + 8 a + 4 g + (0..3) of row i; a key chunk writes
+  // its unscaled partial sums, added up in chunk order afterwards
   if (row_ok) {
-    float* dst = p.dQ + row * D;
+    const bool part = p.nch > 1;
+    const float sc = part ? 1.f : p.scale;
+    float* dst = part ? p.part_q + ((long)blockIdx.y * p.B * p.H * p.Sq + row) * D
+                      : p.dQ + row * D;
 #pragma unroll
     for (int db = 0; db < T::DB; ++db)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const f32x4 v4 = {dq[db][4 * a] * p.scale, dq[db][4 * a + 1] * p.scale,
-                          dq[db][4 * a + 2] * p.scale, dq[db][4 * a + 3] * p.scale};
+        const f32x4 v4 = {dq[db][4 * a] * sc, dq[db][4 * a + 1] * sc,
+                          dq[db][4 * a + 2] * sc, dq[db][4 * a + 3] * sc};
         *(f32x4*)(dst + 32 * db + 8 * a + 4 * g) = v4;
       }
-    if (g == 0) p.Dws[row] = Di;
+    if (g == 0 && blockIdx.y == 0) p.Dws[row] = Di;
   }
 }
 
@@ -787,6 +796,10 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
   int lo = 0, hi = p.Sk;
   if (p.causal) hi = min(hi, min(q0 + 128, p.Sq));
   if (p.window > 0) lo = max(0, q0 - p.window + 1);
+  if (p.nch > 1) {   // key chunk blockIdx.y (chunk_q: a multiple of BN)
+    lo = max(lo, (int)blockIdx.y * p.chunk_q);
+    hi = min(hi, ((int)blockIdx.y + 1) * p.chunk_q);
+  }
   const int t0 = (lo / BN) * BN;
   const int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
 
@@ -889,25 +902,29 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
     __syncthreads();
   }
 
-  // element v of block db: dim (D/32)(8 (v / 4) + 4 g + v % 4) + db of row i
+  // element v of block db: dim (D/32)(8 (v / 4) + 4 g + v % 4) + db of row i;
+  // a key chunk writes its unscaled partial sums
   if (row_ok) {
-    float* dst = p.dQ + row * D;
+    const bool part = p.nch > 1;
+    const float sc = part ? 1.f : p.scale;
+    float* dst = part ? p.part_q + ((long)blockIdx.y * p.B * p.H * p.Sq + row) * D
+                      : p.dQ + row * D;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       float* d0 = dst + T::DB * (8 * (v >> 2) + 4 * g + (v & 3));
       if constexpr (T::DB % 4 == 0) {
 #pragma unroll
         for (int c4 = 0; c4 < T::DB / 4; ++c4) {
-          const f32x4 x = {dq[4 * c4][v] * p.scale, dq[4 * c4 + 1][v] * p.scale,
-                           dq[4 * c4 + 2][v] * p.scale, dq[4 * c4 + 3][v] * p.scale};
+          const f32x4 x = {dq[4 * c4][v] * sc, dq[4 * c4 + 1][v] * sc,
+                           dq[4 * c4 + 2][v] * sc, dq[4 * c4 + 3][v] * sc};
           *(f32x4*)(d0 + 4 * c4) = x;
         }
       } else {
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db) d0[db] = dq[db][v] * p.scale;
+        for (int db = 0; db < T::DB; ++db) d0[db] = dq[db][v] * sc;
       }
     }
-    if (g == 0) p.Dws[row] = Di;
+    if (g == 0 && blockIdx.y == 0) p.Dws[row] = Di;
   }
 }
 
@@ -1114,11 +1131,14 @@ template <typename E, int D>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   constexpr bool f32_mfma = sizeof(E) == 4 && bwd_f32_mfma(D);
   constexpr bool b16_mfma = sizeof(E) == 2 && (D == 64 || D == 128 || D == 256);
+  // (MFMA dQ kernels: blockIdx.y = key chunk when p.nch > 1)
   if constexpr (b16_mfma) {
-    hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D>), dim3((unsigned)((long)p.B * p.H * p.n_qblk)),
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D>),
+                       dim3((unsigned)((long)p.B * p.H * p.n_qblk), (unsigned)p.nch),
                        dim3(kBwdThreads), 0, stream, p);
   } else if constexpr (f32_mfma) {
-    hipLaunchKernelGGL((bwd_dq_f32_mfma_kernel<D>), dim3((unsigned)((long)p.B * p.H * p.n_qblk)),
+    hipLaunchKernelGGL((bwd_dq_f32_mfma_kernel<D>),
+                       dim3((unsigned)((long)p.B * p.H * p.n_qblk), (unsigned)p.nch),
                        dim3(kBwdThreads), 0, stream, p);
   } else {
     constexpr int R = rows_per_group<D>(), GPB = kBwdThreads / bwd_lanes_per_row(D);
@@ -1150,7 +1170,9 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
                        dim3(kBwdThreads), 0, stream, p);
   }
   e = hipGetLastError();
-  if (e != hipSuccess || p.nch == 1) return e;
+  // (the MFMA dK/dV kernels write dK and dV directly; chunks split only the
+  // per-row kernels' key ranges)
+  if (e != hipSuccess || p.nch == 1 || b16_mfma || f32_mfma) return e;
   const long nk = (long)p.B * p.HKV * p.Sk * D;
   e = sum_parts(p.part_k, p.dK, nk, p.nch, p.scale, stream);
   if (e != hipSuccess) return e;

@@ -153,9 +153,26 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
     }
     p.chunk_q = (int)((span_q + p.nch - 1) / p.nch);
     p.chunk_k = (int)((span_k + p.nch - 1) / p.nch);
+  } else {
+    // MFMA kernels: when the dQ kernel has fewer query tiles than two per
+    // CU, cut the key axis into chunks of whole 32-key tiles (at least 16
+    // tiles each, at most 16 chunks, workspace at most 512 MiB)
+    const int cus = fa::device_cus();
+    if (cus <= 0) return FA_ERR_HIP;
+    const long qwg = (long)B * H * p.n_qblk;
+    const long tiles = (Sk + 31) / 32;
+    if (qwg < 2L * cus) {
+      long n = std::min({(2L * cus + qwg - 1) / qwg, tiles / 16, 16L});
+      while (n > 1 && (double)n * nq * DT * 4 > 512.0 * (1 << 20)) --n;
+      if (n > 1) {
+        p.chunk_q = (int)((tiles + n - 1) / n) * 32;
+        p.nch = (int)((Sk + p.chunk_q - 1) / p.chunk_q);
+      }
+    }
   }
-  const size_t b_pq = p.nch > 1 ? up((size_t)p.nch * nq * D * 4) : 0;
-  const size_t b_pk = p.nch > 1 ? up((size_t)p.nch * nk * D * 4) : 0;
+  const bool per_row = dtype == FA_F32 && !fa::bwd_f32_mfma(D);
+  const size_t b_pq = p.nch > 1 ? up((size_t)p.nch * nq * DT * 4) : 0;
+  const size_t b_pk = p.nch > 1 && per_row ? up((size_t)p.nch * nk * D * 4) : 0;
   void* ws = nullptr;
   const int wst = fa::library_workspace(b_d + 3 * b_q + 2 * b_k + b_gq + 2 * b_gk + b_pq + 2 * b_pk,
                                         stream, &ws);

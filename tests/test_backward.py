@@ -89,6 +89,16 @@ CASES += [
     ("f32", 1, 2, 2, 77, 133, 256, 0, 0),
 ]
 
+# few query tiles on the MFMA kernels: the dQ kernel splits the key axis into
+# chunks of whole key tiles whose partial sums are added in chunk order
+CASES += [
+    ("bf16", 1, 2, 1, 200, 4000, 128, 0, 0),
+    ("bf16", 1, 2, 1, 200, 4000, 128, 1, 0),     # causal: every chunk past key 200 is empty
+    ("f32", 1, 2, 2, 300, 3000, 64, 0, 500),
+    ("bf16", 1, 1, 1, 256, 2048, 256, 0, 0),
+    ("f16", 1, 4, 2, 130, 2600, 96, 1, 900),     # padded head dim, window and key chunks
+]
+
 # the same shapes on the MFMA kernels (fp32 at D = 64, 32, 96; bf16 at D = 256)
 CASES += [
     ("f32", 1, 2, 1, 1024, 1024, 64, 1, 0),
