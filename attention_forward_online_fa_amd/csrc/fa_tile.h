@@ -69,6 +69,9 @@ __device__ __forceinline__ int perm_row(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// Swizzle modes of a tile copy (Bf16Tile::swz).
+constexpr int kSwzK = 0, kSwzV = 1, kSwzB = 2;
+
 template <int D, int BN>
 struct Bf16Tile {
   static constexpr int DC = D / 16;      // k-steps of the S MFMA
@@ -83,30 +86,57 @@ struct Bf16Tile {
   static constexpr int NIW = NI / 4;             // ... per wavefront
   static_assert(NI % 4 == 0, "each wavefront issues the same number of DMA instructions");
 
+  // Swizzles (XOR on a row's 16-byte chunk index), by read pattern:
   // K reads: 16 lanes read one chunk of 16 different keys -> XOR with the key.
   static constexpr int swz_k(int key) { return CPR >= 16 ? (key & 15) : ((key >> 1) & 7); }
   // V transpose reads: 32 lanes read 4 chunks of 4 consecutive keys -> move
   // each key of the group of 4 to its own group of 4 chunks.
   static constexpr int swz_v(int key) { return CPR >= 16 ? 4 * (key & 3) : 4 * ((key >> 1) & 1); }
+  // Both patterns on one copy (CPR >= 16): the low four bits of the row,
+  // their two halves swapped. Any bijection of those bits serves the row
+  // reads; this one also gives the four consecutive rows of a transposed read
+  // four different chunk groups (bits 2-3 of the chunk index), with the two
+  // chunks each row reads differing in bit 0. Rows r and r + 4 then differ by
+  // 1 in the XOR when r % 8 < 4 (bit 2 of r is 0).
+  static constexpr int swz_b(int key) { return ((key & 3) << 2) | ((key >> 2) & 3); }
+  static constexpr int swz(int key, int mode) {
+    return mode == kSwzK ? swz_k(key) : mode == kSwzV ? swz_v(key) : swz_b(key);
+  }
   // Tile byte offset that LDS chunk P of a copy reads: logical chunk
   // (P % CPR) ^ swz(row) of row P / CPR.
-  static constexpr int chunk_off(int P, bool v) {
-    return ((P % CPR) ^ (v ? swz_v(P / CPR) : swz_k(P / CPR))) << 4;
-  }
-  static constexpr int dma_off(int P, bool v) { return (P / CPR) * ROW + chunk_off(P, v); }
+  static constexpr int chunk_off(int P, int mode) { return ((P % CPR) ^ swz(P / CPR, mode)) << 4; }
+  static constexpr int dma_off(int P, int mode) { return (P / CPR) * ROW + chunk_off(P, mode); }
   // The offsets of copy instruction k (chunks 64k.. of a wavefront's share)
   // differ from those of instruction 0 by the same XOR in every lane: the row
-  // step and the swizzle touch disjoint bits. One register per buffer then
-  // holds a lane's offsets.
-  static constexpr int dma_xor(int k, bool v) { return dma_off(64 * k, v) ^ dma_off(0, v); }
+  // step and the swizzle touch disjoint bits (checked below). One register
+  // per buffer then holds a lane's offsets.
+  static constexpr int dma_xor(int k, int mode) { return dma_off(64 * k, mode) ^ dma_off(0, mode); }
+  static constexpr bool xor_property(int mode) {
+    for (int k = 0; k < NI; ++k)
+      for (int lane = 0; lane < 64; ++lane)
+        if ((dma_off(64 * k + lane, mode) ^ dma_off(lane, mode)) != dma_xor(k, mode)) return false;
+    return true;
+  }
+
   // Strided rows (a row stride R that is a multiple of ROW): the row part of
   // an offset, row * R, no longer fits the XOR. It is additive instead
   // (instruction k adds k * RPI * R, uniform) and stays in the vector offset,
   // which the buffer range check covers; the chunk part keeps its
   // per-instruction XOR.
   static constexpr int RPI = 64 / CPR;                   // rows per copy instruction
-  static constexpr int chunk_xor(int k, bool v) { return dma_xor(k, v) & (ROW - 1); }
+  static constexpr int chunk_xor(int k, int mode) { return dma_xor(k, mode) & (ROW - 1); }
 };
+
+// The XOR property of the copy offsets for every tile shape the kernels use.
+template <int D, int BN>
+constexpr bool tile_offsets_by_xor() {
+  using T = Bf16Tile<D, BN>;
+  return T::xor_property(kSwzK) && T::xor_property(kSwzV) && (T::CPR < 16 || T::xor_property(kSwzB));
+}
+static_assert(tile_offsets_by_xor<64, 64>() && tile_offsets_by_xor<128, 32>() &&
+                  tile_offsets_by_xor<256, 32>() && tile_offsets_by_xor<64, 32>() &&
+                  tile_offsets_by_xor<128, 64>(),
+              "copy offsets of instruction k: instruction 0's XOR a lane-independent constant");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
