@@ -333,10 +333,8 @@ void bwd_dkdv_kernel(BwdParams p) {
 //                          packed to the input type as the forward packs P)
 // The K tile is read both by rows (S^T) and transposed (K^T). With either the
 // forward's K swizzle or its V swizzle alone, half the LDS cycles went to bank
-// conflicts; at D >= 128 the tiles take the swizzle that serves both patterns
-// (Bf16Tile::swz_b) and K is copied once. At D = 64 (rows of 128 bytes) the K
-// tile is copied twice, with the K swizzle for S^T and the V swizzle for K^T.
-// V is read by rows only.
+// conflicts; the tiles take the swizzle that serves both patterns
+// (Bf16Tile::swz_b), so K is copied once. V is read by rows only.
 // D_i = dO_i . O_i is formed here and written for the dK/dV kernel.
 template <typename E, int D>
 __global__ __launch_bounds__(kBwdThreads, D <= 128 ? 2 : 1)
@@ -347,13 +345,8 @@ void bwd_dq_mfma_kernel(BwdParams p) {
   typedef typename X::x8 e16x8;
   // D = 256: one wavefront per SIMD (the dQ^T accumulators, 128 registers, in AGPRs)
   static_assert(D == 64 || D == 128 || D == 256, "MFMA tile dims");
-  // one copy of K for both read patterns (D >= 128), else two
-  constexpr bool OneK = T::CPR >= 16;
-  constexpr int SR = OneK ? kSwzB : kSwzK, ST = OneK ? kSwzB : kSwzV;   // row / transposed reads
   __shared__ __attribute__((aligned(1024))) char kbuf0[T::TILE];
   __shared__ __attribute__((aligned(1024))) char kbuf1[T::TILE];
-  __shared__ __attribute__((aligned(1024))) char ktbuf0[OneK ? 16 : T::TILE];   // K again, V swizzle
-  __shared__ __attribute__((aligned(1024))) char ktbuf1[OneK ? 16 : T::TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf0[T::TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf1[T::TILE];
 
@@ -387,21 +380,19 @@ void bwd_dq_mfma_kernel(BwdParams p) {
   const int t0 = (lo / BN) * BN;
   const int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
 
-  const int voff = T::dma_off(64 * wave * T::NIW + lane, SR);
-  const int voff_t = T::dma_off(64 * wave * T::NIW + lane, ST);
-  auto issue = [&](int kt, char* kd, char* ktd, char* vd) {
+  const int voff = T::dma_off(64 * wave * T::NIW + lane, kSwzB);
+  auto issue = [&](int kt, char* kd, char* vd) {
     const unsigned bytes = (unsigned)min((long)(p.Sk - kt) * T::ROW, 0x7fffffffL);
     const E* kb = Kp + (size_t)kt * D;
     const E* vb = Vp + (size_t)kt * D;
 #pragma unroll
     for (int k = 0; k < T::NIW; ++k) {
       const int off = (wave * T::NIW + k) * 1024;
-      dma16(kb, bytes, voff ^ T::dma_xor(k, SR), kd + off);
-      if constexpr (!OneK) dma16(kb, bytes, voff_t ^ T::dma_xor(k, ST), ktd + off);
-      dma16(vb, bytes, voff ^ T::dma_xor(k, SR), vd + off);
+      dma16(kb, bytes, voff ^ T::dma_xor(k, kSwzB), kd + off);
+      dma16(vb, bytes, voff ^ T::dma_xor(k, kSwzB), vd + off);
     }
   };
-  if (n_tiles > 0) issue(t0, kbuf0, ktbuf0, vbuf0);
+  if (n_tiles > 0) issue(t0, kbuf0, vbuf0);
 
   // Q and dO rows as B operands (k-slot (g, e) of step t is dim 16t + 8g + e);
   // D_i from the same dims of O, summed over the two lane halves.
@@ -434,29 +425,26 @@ void bwd_dq_mfma_kernel(BwdParams p) {
   const int krow = perm_row(l32);
   int koff[T::DC];
 #pragma unroll
-  for (int t = 0; t < T::DC; ++t) koff[t] = krow * T::ROW + (((2 * t + g) ^ T::swz(krow, SR)) << 4);
-  // transposed reads, as the forward reads V^T: rows vrow and vrow + 4 (the
-  // second read) share the V swizzle; under swz_b their XORs differ in bit 0
-  // (vrow % 8 < 4), i.e. the second offset flips byte-offset bit 4
+  for (int t = 0; t < T::DC; ++t) koff[t] = krow * T::ROW + (((2 * t + g) ^ T::swz_b(krow)) << 4);
+  // transposed reads, as the forward reads V^T: the second read is 4 rows on,
+  // where the XOR differs in bit 0 (vrow % 8 < 4): byte-offset bit 4 flips
   const int blk = lane >> 4, li = lane & 15;
   const int vrow = 8 * g + (li >> 2);
   int ktoff[T::DB];
 #pragma unroll
   for (int db = 0; db < T::DB; ++db) {
     const int chunk = 4 * db + 2 * (blk & 1) + ((li & 3) >> 1);
-    ktoff[db] = vrow * T::ROW + ((chunk ^ T::swz(vrow, ST)) << 4) + 8 * (li & 1);
+    ktoff[db] = vrow * T::ROW + ((chunk ^ T::swz_b(vrow)) << 4) + 8 * (li & 1);
   }
-  auto kt_second = [&](int o) { return OneK ? ((o + 4 * T::ROW) ^ 16) : o + 4 * T::ROW; };
 
   f32x16 dq[T::DB];
 #pragma unroll
   for (int db = 0; db < T::DB; ++db) dq[db] = f32x16{};
 
-  auto step = [&](int t, const char* Kc, const char* KTc, const char* Vc, char* Kn, char* KTn,
-                  char* Vn) __attribute__((always_inline)) {
+  auto step = [&](int t, const char* Kc, const char* Vc, char* Kn, char* Vn) __attribute__((always_inline)) {
     const int kt = t0 + t * BN;
     wait_dma_and_sync();
-    if (t + 1 < n_tiles) issue(kt + BN, Kn, KTn, Vn);
+    if (t + 1 < n_tiles) issue(kt + BN, Kn, Vn);
     if (qw >= p.Sq || (p.causal && kt > qw + 31) ||
         (p.window > 0 && kt + BN - 1 < qw - p.window + 1))
       return;
@@ -489,7 +477,7 @@ void bwd_dq_mfma_kernel(BwdParams p) {
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) {
         const int o = ktoff[db] + 16 * c * T::ROW;
-        a[db] = read_v_pair<e16x8>(OneK ? Kc : KTc, o, kt_second(o));
+        a[db] = read_v_pair<e16x8>(Kc, o, (o + 4 * T::ROW) ^ 16);
       }
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) dq[db] = X::mfma(a[db], dsf[c], dq[db]);
@@ -497,8 +485,8 @@ void bwd_dq_mfma_kernel(BwdParams p) {
   };
 
   for (int t = 0; t < n_tiles; t += 2) {
-    step(t, kbuf0, ktbuf0, vbuf0, kbuf1, ktbuf1, vbuf1);
-    if (t + 1 < n_tiles) step(t + 1, kbuf1, ktbuf1, vbuf1, kbuf0, ktbuf0, vbuf0);
+    step(t, kbuf0, vbuf0, kbuf1, vbuf1);
+    if (t + 1 < n_tiles) step(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
   }
 
   // lane holds dims 32 db + 8 a + 4 g + (0..3) of row i; a key chunk writes
@@ -547,19 +535,12 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   using X = Elt<E>;
   typedef typename X::x8 e16x8;
   static_assert(D == 64 || D == 128 || D == 256, "MFMA tile dims");
-  // Q and dO tiles are read by rows and transposed: at D >= 128 one copy each
-  // with the swizzle that serves both, at D = 64 two copies each (K swizzle
-  // for the row reads, V swizzle for the transposed reads; see the dQ kernel)
-  constexpr bool One = T::CPR >= 16;
-  constexpr int SR = One ? kSwzB : kSwzK, ST = One ? kSwzB : kSwzV;
+  // Q and dO tiles are read by rows and transposed: one copy each, with the
+  // swizzle that serves both (see the dQ kernel)
   __shared__ __attribute__((aligned(1024))) char qbuf0[T::TILE];
   __shared__ __attribute__((aligned(1024))) char qbuf1[T::TILE];
-  __shared__ __attribute__((aligned(1024))) char qtbuf0[One ? 16 : T::TILE];
-  __shared__ __attribute__((aligned(1024))) char qtbuf1[One ? 16 : T::TILE];
   __shared__ __attribute__((aligned(1024))) char obuf0[T::TILE];
   __shared__ __attribute__((aligned(1024))) char obuf1[T::TILE];
-  __shared__ __attribute__((aligned(1024))) char otbuf0[One ? 16 : T::TILE];
-  __shared__ __attribute__((aligned(1024))) char otbuf1[One ? 16 : T::TILE];
   __shared__ __attribute__((aligned(16))) float lbuf0[2 * BM];   // [0, BM): base-2 LSE, [BM, 2 BM): D
   __shared__ __attribute__((aligned(16))) float lbuf1[2 * BM];
 
@@ -585,9 +566,8 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   const int n_rt = r_hi > r_lo ? (r_hi - rt0 + BM - 1) / BM : 0;
   const int n_tiles = n_rt * gh;   // (query head, row tile) pairs
 
-  const int voff = T::dma_off(64 * wave * T::NIW + lane, SR);
-  const int voff_t = T::dma_off(64 * wave * T::NIW + lane, ST);
-  auto issue = [&](int t, char* qd, char* qtd, char* od, char* otd, float* ld) {
+  const int voff = T::dma_off(64 * wave * T::NIW + lane, kSwzB);
+  auto issue = [&](int t, char* qd, char* od, float* ld) {
     const int h = hkv * gh + t / n_rt, r0 = rt0 + (t % n_rt) * BM;
     const long base = ((long)b * p.H + h) * p.Sq;
     // the tile rows' base-2 LSE (wave 0) and D (wave 1), loaded first
@@ -605,14 +585,12 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
 #pragma unroll
     for (int k = 0; k < T::NIW; ++k) {
       const int off = (wave * T::NIW + k) * 1024;
-      dma16(qb, bytes, voff ^ T::dma_xor(k, SR), qd + off);
-      if constexpr (!One) dma16(qb, bytes, voff_t ^ T::dma_xor(k, ST), qtd + off);
-      dma16(ob, bytes, voff ^ T::dma_xor(k, SR), od + off);
-      if constexpr (!One) dma16(ob, bytes, voff_t ^ T::dma_xor(k, ST), otd + off);
+      dma16(qb, bytes, voff ^ T::dma_xor(k, kSwzB), qd + off);
+      dma16(ob, bytes, voff ^ T::dma_xor(k, kSwzB), od + off);
     }
     if (wave < 2 && lane < BM) ld[wave * BM + lane] = x;
   };
-  if (n_tiles > 0) issue(0, qbuf0, qtbuf0, obuf0, otbuf0, lbuf0);
+  if (n_tiles > 0) issue(0, qbuf0, obuf0, lbuf0);
 
   // K and V rows as B operands (k-slot (g, e) of step t is dim 16t + 8g + e)
   e16x8 kf[T::DC], vf[T::DC];
@@ -632,28 +610,25 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   const int qrow = perm_row(l32);
   int roff[T::DC];
 #pragma unroll
-  for (int t = 0; t < T::DC; ++t) roff[t] = qrow * T::ROW + (((2 * t + g) ^ T::swz(qrow, SR)) << 4);
+  for (int t = 0; t < T::DC; ++t) roff[t] = qrow * T::ROW + (((2 * t + g) ^ T::swz_b(qrow)) << 4);
   const int blk = lane >> 4, li = lane & 15;
   const int vrow = 8 * g + (li >> 2);
   int troff[DBO];   // the output dim blocks DBO ob + db
 #pragma unroll
   for (int db = 0; db < DBO; ++db) {
     const int chunk = 4 * (DBO * ob + db) + 2 * (blk & 1) + ((li & 3) >> 1);
-    troff[db] = vrow * T::ROW + ((chunk ^ T::swz(vrow, ST)) << 4) + 8 * (li & 1);
+    troff[db] = vrow * T::ROW + ((chunk ^ T::swz_b(vrow)) << 4) + 8 * (li & 1);
   }
-  // second transposed read, 4 rows on (swz_b: the chunk XOR flips bit 0)
-  auto t_second = [&](int o) { return One ? ((o + 4 * T::ROW) ^ 16) : o + 4 * T::ROW; };
 
   f32x16 dk[DBO], dv[DBO];
 #pragma unroll
   for (int db = 0; db < DBO; ++db) dk[db] = dv[db] = f32x16{};
 
-  auto step = [&](int t, const char* Qc, const char* QTc, const char* Oc, const char* OTc,
-                  const float* Lc, char* Qn, char* QTn, char* On, char* OTn,
+  auto step = [&](int t, const char* Qc, const char* Oc, const float* Lc, char* Qn, char* On,
                   float* Ln) __attribute__((always_inline)) {
     const int r0 = rt0 + (t % n_rt) * BM;
     wait_dma_and_sync();
-    if (t + 1 < n_tiles) issue(t + 1, Qn, QTn, On, OTn, Ln);
+    if (t + 1 < n_tiles) issue(t + 1, Qn, On, Ln);
     if (kw >= p.Sk || (p.causal && r0 + BM - 1 < kw) ||
         (p.window > 0 && r0 > kw + 31 + p.window - 1))
       return;
@@ -703,9 +678,10 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
         e16x8 ao[DBO], aq[DBO];
 #pragma unroll
         for (int db = 0; db < DBO; ++db) {
+          // (the second read is 4 rows on, where the XOR differs in bit 0)
           const int o = troff[db] + (HM * hh + 16 * c) * T::ROW;
-          ao[db] = read_v_pair<e16x8>(One ? Oc : OTc, o, t_second(o));
-          aq[db] = read_v_pair<e16x8>(One ? Qc : QTc, o, t_second(o));
+          ao[db] = read_v_pair<e16x8>(Oc, o, (o + 4 * T::ROW) ^ 16);
+          aq[db] = read_v_pair<e16x8>(Qc, o, (o + 4 * T::ROW) ^ 16);
         }
 #pragma unroll
         for (int db = 0; db < DBO; ++db) {
@@ -716,9 +692,8 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   };
 
   for (int t = 0; t < n_tiles; t += 2) {
-    step(t, qbuf0, qtbuf0, obuf0, otbuf0, lbuf0, qbuf1, qtbuf1, obuf1, otbuf1, lbuf1);
-    if (t + 1 < n_tiles)
-      step(t + 1, qbuf1, qtbuf1, obuf1, otbuf1, lbuf1, qbuf0, qtbuf0, obuf0, otbuf0, lbuf0);
+    step(t, qbuf0, obuf0, lbuf0, qbuf1, obuf1, lbuf1);
+    if (t + 1 < n_tiles) step(t + 1, qbuf1, obuf1, lbuf1, qbuf0, obuf0, lbuf0);
   }
 
   // lane holds dims DO ob + 32 db + 8 a + 4 g + (0..3) of key j

@@ -92,13 +92,15 @@ struct Bf16Tile {
   // V transpose reads: 32 lanes read 4 chunks of 4 consecutive keys -> move
   // each key of the group of 4 to its own group of 4 chunks.
   static constexpr int swz_v(int key) { return CPR >= 16 ? 4 * (key & 3) : 4 * ((key >> 1) & 1); }
-  // Both patterns on one copy (CPR >= 16): the low four bits of the row,
-  // their two halves swapped. Any bijection of those bits serves the row
-  // reads; this one also gives the four consecutive rows of a transposed read
-  // four different chunk groups (bits 2-3 of the chunk index), with the two
-  // chunks each row reads differing in bit 0. Rows r and r + 4 then differ by
-  // 1 in the XOR when r % 8 < 4 (bit 2 of r is 0).
-  static constexpr int swz_b(int key) { return ((key & 3) << 2) | ((key >> 2) & 3); }
+  // Both patterns on one copy: a bit permutation of the row bits that the
+  // row reads need distinct (CPR >= 16: the low four bits, their two halves
+  // swapped; CPR = 8, two rows per 256 bytes: bits 1-3, bit 1 moved to the
+  // top). Any bijection of those bits serves the row reads; these also put
+  // the rows of a transposed read on different chunk groups. Rows r and r + 4
+  // differ by 1 in the XOR when r % 8 < 4 (bit 2 of r is 0).
+  static constexpr int swz_b(int key) {
+    return CPR >= 16 ? ((key & 3) << 2) | ((key >> 2) & 3) : (((key >> 1) & 1) << 2) | ((key >> 2) & 3);
+  }
   static constexpr int swz(int key, int mode) {
     return mode == kSwzK ? swz_k(key) : mode == kSwzV ? swz_v(key) : swz_b(key);
   }
@@ -131,7 +133,8 @@ struct Bf16Tile {
 template <int D, int BN>
 constexpr bool tile_offsets_by_xor() {
   using T = Bf16Tile<D, BN>;
-  return T::xor_property(kSwzK) && T::xor_property(kSwzV) && (T::CPR < 16 || T::xor_property(kSwzB));
+  return T::xor_property(kSwzK) && T::xor_property(kSwzV) && T::xor_property(kSwzB) &&
+         T::swz_b(4) == 1;
 }
 static_assert(tile_offsets_by_xor<64, 64>() && tile_offsets_by_xor<128, 32>() &&
                   tile_offsets_by_xor<256, 32>() && tile_offsets_by_xor<64, 32>() &&
