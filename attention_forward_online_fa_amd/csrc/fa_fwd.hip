@@ -446,23 +446,30 @@ void fwd_16b_kernel(Params p) {
   // next tile exists with BN keys below Sk, so the step needs no skip, mask or
   // bounds decisions.
   auto step_in = [&](int t, const char* Kc, const char* Vc, char* Kn, char* Vn) __attribute__((always_inline)) {
-    const int kt = t0 + t * BN;
     wait_dma_and_sync();
-    issue(kt + BN, Kn, Vn, true);
+    issue(tile_kt(t + 1), Kn, Vn, true);
     qk(Kc);
     softmax();
     pv(Vc);
   };
-  // Tiles [0, full_hi) exist and hold BN keys below Sk; tiles [u_lo, u_hi)
-  // are also fully visible to every row of the block.
-  const int full_hi = min(n_tiles, (p.Sk - t0) / BN);
+  // Visited tiles [0, full_hi) hold BN keys below Sk; tiles [u_lo, u_hi) are
+  // also fully visible to every row of the block. (Block masks: the visited
+  // tiles are ascending, so only the last can be partial; without a causal
+  // or window mask every visited tile is fully visible.)
+  int full_hi = min(n_tiles, (p.Sk - t0) / BN);
+  if constexpr (Sparse)
+    full_hi = (n_tiles > 0 && tile_kt(n_tiles - 1) + BN > p.Sk) ? n_tiles - 1 : n_tiles;
   int u_lo = 0, u_hi = 0;
-  if (!Sparse && q0 + bm <= p.Sq) {   // (block-sparse: tiles are not consecutive)
-    u_hi = full_hi;
-    if (p.causal) u_hi = min(u_hi, max(0, (q0 - t0 + 1) / BN));
-    if (p.window > 0) {
-      const int need = q0 + bm - p.window - t0;       // kt - t0 >= need
-      u_lo = need > 0 ? (need + BN - 1) / BN : 0;
+  if (q0 + bm <= p.Sq) {
+    if constexpr (Sparse) {
+      if (!p.causal && p.window <= 0) u_hi = full_hi;
+    } else {
+      u_hi = full_hi;
+      if (p.causal) u_hi = min(u_hi, max(0, (q0 - t0 + 1) / BN));
+      if (p.window > 0) {
+        const int need = q0 + bm - p.window - t0;       // kt - t0 >= need
+        u_lo = need > 0 ? (need + BN - 1) / BN : 0;
+      }
     }
   }
   // steps t and t+1 both interior, and the tiles they copy (t+1, t+2) full

@@ -119,3 +119,50 @@ def test_schedule_rejects_partial_copy():
         return schedule(n, u_lo, min(u_hi, n - 1), n)
     with pytest.raises(AssertionError):
         check_shape(200, 700, 0, 0, 64, 2, sched=buggy)
+
+
+def check_sparse(Sq, Sk, causal, window, BN, nsplit, rng, sched=None):
+    """Block-sparse form: the workgroup visits a sorted subset of its range's
+    key tiles (its mask's nonzero blocks); position t of that list is the
+    tile at key list[t]. Without a causal or window mask the kernel takes the
+    interior step on every list position whose tile, and the next one it
+    copies, are full; only the last listed tile can be partial."""
+    sched = sched or schedule
+    sk_tiles = (Sk + BN - 1) // BN
+    ns = min(nsplit, sk_tiles)
+    split_len = ((sk_tiles + ns - 1) // ns) * BN
+    ns = (Sk + split_len - 1) // split_len
+    n_interior = 0
+    for q0 in range(0, Sq, BM):
+        for split in range(ns):
+            lo, hi = key_range(Sq, Sk, causal, window, q0, ns, split_len, split)
+            t0 = (lo // BN) * BN
+            n_all = (hi - t0 + BN - 1) // BN if hi > lo else 0
+            keep = [t for t in range(n_all) if rng.random() < 0.6]
+            kts = [t0 + BN * t for t in keep]
+            n = len(kts)
+            full_hi = n - 1 if n > 0 and kts[-1] + BN > Sk else n
+            u_lo = u_hi = 0
+            if q0 + BM <= Sq and not causal and window <= 0:
+                u_hi = full_hi
+            steps = sched(n, u_lo, u_hi, full_hi)
+            assert [t for _, t in steps] == list(range(n))
+            for kind, t in steps:
+                if kind != "interior":
+                    continue
+                n_interior += 1
+                kt = kts[t]
+                assert not causal and window == 0 and q0 + BM <= Sq
+                assert lo <= kt and kt + BN <= min(hi, Sk)
+                assert t + 1 < n and kts[t + 1] + BN <= Sk   # the copied tile is full
+    return n_interior
+
+
+def test_schedule_block_sparse_random():
+    rng = random.Random(20261203)
+    total = 0
+    for _ in range(200):
+        total += check_sparse(rng.randint(1, 1500), rng.randint(1, 1500), rng.randint(0, 1),
+                              rng.choice([0, 0, 1, 100]), rng.choice([32, 64]),
+                              rng.choice([1, 1, 2, 3]), rng)
+    assert total > 0
