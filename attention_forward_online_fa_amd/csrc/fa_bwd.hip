@@ -5,9 +5,9 @@
 //   P_ij  = exp(scale q_i.k_j - LSE_i)            (visible keys only)
 //   D_i   = dO_i . O_i                            (the FA2 identity)
 //   dS_ij = P_ij (dO_i . v_j - D_i)
-//   dQ_i  = scale sum_j dS_ij k_j                 (kernel bwd_dq_kernel)
+//   dQ_i  = scale sum_j dS_ij k_j                 (the dQ kernels)
 //   dV_j  = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i
-//                                                 (kernel bwd_dkdv_kernel)
+//                                                 (the dK/dV kernels)
 // with dK and dV summed over the query heads of a kv head. Every dK/dV row
 // has a single owner that sums its contributions in a fixed order, so no
 // atomics are needed and the result is deterministic (the approach of the
@@ -15,17 +15,22 @@
 // query row by the dQ kernel and handed to the dK/dV kernel through a
 // workspace.
 //
-// Work decomposition: a group of G = 4, 8, 16 or 32 lanes (the fewest that
-// keep D / G <= 8) owns R consecutive rows of one head (bwd_rows_per_group:
-// 4 with 16 lanes, else 2):
-// query rows in the dQ kernel, key rows in the dK/dV kernel. A lane holds
-// D / G consecutive elements of each row vector; dot products reduce over
-// the group with two to four DPP steps (and one lane permute at G = 32). This is the pages'
-// thread-per-row design mapped to wavefronts, on the VALU (no MFMA): exact to
-// fp32 rounding, used for fp32 inputs and D = 256; the MFMA kernels below
-// serve 16-bit inputs at D = 64 and 128. On small grids the per-row kernels
-// run each group's range in chunks (blockIdx.y) whose partial sums
-// sum_parts_kernel adds in chunk order.
+// Three kernel families:
+// - 16-bit inputs: MFMA kernels (bwd_dq_mfma_kernel, bwd_dkdv_mfma_kernel) at
+//   D = 64, 128 and 256; other head dims run them on zero-padded copies.
+// - fp32 inputs at D = 32, 64, 96, 128: MFMA kernels on v_mfma_f32_32x32x2_f32
+//   (bwd_dq_f32_mfma_kernel, bwd_dkdv_f32_mfma_kernel).
+// - fp32 inputs at D = 16, 48, 80, 256: the per-row kernels below (bwd_dq_kernel,
+//   bwd_dkdv_kernel), the pages' thread-per-row design mapped to wavefronts on
+//   the VALU: a group of G = 4, 8, 16 or 32 lanes (the fewest that keep D / G
+//   <= 8) owns R consecutive rows of one head (bwd_rows_per_group: 4 with 16
+//   lanes, else 2), query rows in the dQ kernel, key rows in the dK/dV kernel.
+//   A lane holds D / G consecutive elements of each row vector; dot products
+//   reduce over the group with two to four DPP steps (and one lane permute at
+//   G = 32).
+// On small grids the per-row kernels run each group's range in chunks
+// (blockIdx.y), and the MFMA dQ kernels the key axis in chunks, whose partial
+// sums sum_parts_kernel adds in chunk order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
