@@ -250,6 +250,10 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run a plain device-to-device copy of MIB "
                          "MiB (reference for scaling HBM byte counters)")
+    ap.add_argument("--gemm-ceiling", type=int, default=0, metavar="N",
+                    help="instead of attention, time a dense bf16 N x N x N product "
+                         "(torch.matmul, i.e. hipBLASLt) for reference: what the chip "
+                         "sustains on dense bf16 matrix work under its power limit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -269,6 +273,33 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n,
                           "launches": max(args.steps, 1)}), flush=True)
+        return
+
+    if args.gemm_ceiling:
+        n = args.gemm_ceiling
+        g = torch.Generator(device="cpu").manual_seed(1)
+        a = torch.randn(n, n, generator=g).to(torch.bfloat16).cuda()
+        b = torch.randn(n, n, generator=g).to(torch.bfloat16).cuda().t().contiguous()
+        c = torch.empty(n, n, dtype=torch.bfloat16, device="cuda")
+        for _ in range(max(args.warmup, 1)):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        t_warm = time.perf_counter() + args.warmup_seconds
+        while time.perf_counter() < t_warm:
+            torch.matmul(a, b, out=c)
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+        print(json.dumps({"metric": "dense bf16 GEMM TFLOP/s (torch.matmul), reference only",
+                          "n": n, "ms_per_gemm": round(ms, 5), "tflops": round(tf, 1),
+                          "frac_of_bf16_peak": round(tf / PEAK_TFLOPS["bf16"], 4),
+                          "steps": args.steps}), flush=True)
         return
 
     wl = W.CONFIGS[args.config]
