@@ -39,6 +39,14 @@ struct BwdParams {
   float* part_q;
   float* part_k;
   float* part_v;
+  // General form of the 16-bit MFMA kernels (gen = 1): the tensors are views
+  // with these element strides (batch, head, row; the head dim contiguous),
+  // Q, K, V, O, dO in the input type and dQ, dK, dV in fp32, with head dim
+  // dv (a multiple of 16, at most the kernel's tile dim D): the kernels read
+  // the dims from dv on as zeros and write only the first dv. gen = 0:
+  // contiguous [B, heads, S, D] tensors, strides unused.
+  int gen, dv;
+  long long qs[3], ks[3], vs[3], os[3], dos[3], dqs[3], dks[3], dvs[3];
 };
 
 // Group shape of the per-row kernels (fp32 inputs, D = 256): lanes per row
@@ -55,10 +63,9 @@ constexpr bool bwd_f32_mfma(int D) { return D == 32 || D == 64 || D == 96 || D =
 // Queue the dQ kernel (which also writes Dws) and then the dK/dV kernel.
 hipError_t launch_backward(const BwdParams& p, int dtype, int D, hipStream_t stream);
 
-// Row copies of the staged backward: the 16-bit backward at head dims 16 ..
-// 96 other than 64 runs the MFMA kernels of the 64 or 128 tile on
-// zero-padded copies, and strided tensors are copied to contiguous rows
-// first. gather: the B heads S rows of a view with byte strides st (batch,
+// Row copies of the staged backward (fp32 views, and 16-bit views whose row
+// strides exceed what the general form's copy offsets allow): inputs copied
+// to contiguous zero-padded rows first, gradients copied back. gather: the B heads S rows of a view with byte strides st (batch,
 // head, row; multiples of 16), src_bytes each, -> contiguous rows of
 // dst_bytes with zeros after src_bytes. scatter: contiguous fp32 rows of dt
 // floats -> the first dv floats of each row of an fp32 view (byte strides st).

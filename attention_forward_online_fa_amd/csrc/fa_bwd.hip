@@ -17,7 +17,8 @@
 //
 // Three kernel families:
 // - 16-bit inputs: MFMA kernels (bwd_dq_mfma_kernel, bwd_dkdv_mfma_kernel) at
-//   D = 64, 128 and 256; other head dims run them on zero-padded copies.
+//   tile dims 64, 128 and 256; in their general form they read views with
+//   strides and head dims below the tile dim (those dims read as zeros).
 // - fp32 inputs at D = 32, 64, 96, 128: MFMA kernels on v_mfma_f32_32x32x2_f32
 //   (bwd_dq_f32_mfma_kernel, bwd_dkdv_f32_mfma_kernel).
 // - fp32 inputs at D = 16, 48, 80, 256: the per-row kernels below (bwd_dq_kernel,
@@ -38,6 +39,11 @@
 #include "fa_tile.h"
 
 namespace fa {
+
+// General-form copies: an offset past any buffer range (its chunk lands in LDS
+// as zeros) and the largest range given to a copy (below that offset).
+constexpr int kBwdOutOfRange = 0x7ffffff0;
+constexpr long long kBwdMaxRange = 0x7fff0000LL;
 
 constexpr int kBwdThreads = 256;   // 4 wavefronts x 4 rows
 
@@ -341,7 +347,7 @@ void bwd_dkdv_kernel(BwdParams p) {
 // conflicts; the tiles take the swizzle that serves both patterns
 // (Bf16Tile::swz_b), so K is copied once. V is read by rows only.
 // D_i = dO_i . O_i is formed here and written for the dK/dV kernel.
-template <typename E, int D>
+template <typename E, int D, bool Gen>
 __global__ __launch_bounds__(kBwdThreads, D <= 128 ? 2 : 1)
 void bwd_dq_mfma_kernel(BwdParams p) {
   constexpr int BN = 32;
@@ -367,11 +373,27 @@ void bwd_dq_mfma_kernel(BwdParams p) {
   const bool row_ok = i < p.Sq;
   const long row = ((long)b * p.H + h) * p.Sq + i;
 
-  const E* Qh = (const E*)p.Q + ((long)b * p.H + h) * p.Sq * D;
-  const E* Oh = (const E*)p.O + ((long)b * p.H + h) * p.Sq * D;
-  const E* dOh = (const E*)p.dO + ((long)b * p.H + h) * p.Sq * D;
-  const E* Kp = (const E*)p.K + ((long)b * p.HKV + hkv) * p.Sk * D;
-  const E* Vp = (const E*)p.V + ((long)b * p.HKV + hkv) * p.Sk * D;
+  // row starts: contiguous tensors, or (general form) the views' strides
+  const E *Qh, *Oh, *dOh, *Kp, *Vp;
+  long long qr = D, orow = D, dor = D, kr = D, vr = D;   // element row strides
+  if constexpr (Gen) {
+    Qh = (const E*)p.Q + b * p.qs[0] + h * p.qs[1];
+    Oh = (const E*)p.O + b * p.os[0] + h * p.os[1];
+    dOh = (const E*)p.dO + b * p.dos[0] + h * p.dos[1];
+    Kp = (const E*)p.K + b * p.ks[0] + hkv * p.ks[1];
+    Vp = (const E*)p.V + b * p.vs[0] + hkv * p.vs[1];
+    qr = p.qs[2];
+    orow = p.os[2];
+    dor = p.dos[2];
+    kr = p.ks[2];
+    vr = p.vs[2];
+  } else {
+    Qh = (const E*)p.Q + ((long)b * p.H + h) * p.Sq * D;
+    Oh = (const E*)p.O + ((long)b * p.H + h) * p.Sq * D;
+    dOh = (const E*)p.dO + ((long)b * p.H + h) * p.Sq * D;
+    Kp = (const E*)p.K + ((long)b * p.HKV + hkv) * p.Sk * D;
+    Vp = (const E*)p.V + ((long)b * p.HKV + hkv) * p.Sk * D;
+  }
 
   // key range of the block; on small grids only key chunk blockIdx.y of it
   // (chunk_q is a multiple of BN, so the chunks split the key tiles exactly)
@@ -386,15 +408,40 @@ void bwd_dq_mfma_kernel(BwdParams p) {
   const int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
 
   const int voff = T::dma_off(64 * wave * T::NIW + lane, kSwzB);
-  auto issue = [&](int kt, char* kd, char* vd) {
-    const unsigned bytes = (unsigned)min((long)(p.Sk - kt) * T::ROW, 0x7fffffffL);
-    const E* kb = Kp + (size_t)kt * D;
-    const E* vb = Vp + (size_t)kt * D;
+  // general form: each copy instruction's lane offset in full (any row
+  // stride), or past the buffer's range for a chunk at or beyond dim dv,
+  // which then lands in LDS as zeros
+  int pk_off[Gen ? T::NIW : 1], pv_off[Gen ? T::NIW : 1];
+  if constexpr (Gen) {
 #pragma unroll
     for (int k = 0; k < T::NIW; ++k) {
-      const int off = (wave * T::NIW + k) * 1024;
-      dma16(kb, bytes, voff ^ T::dma_xor(k, kSwzB), kd + off);
-      dma16(vb, bytes, voff ^ T::dma_xor(k, kSwzB), vd + off);
+      const int P = 64 * (wave * T::NIW + k) + lane, r = P / T::CPR;
+      const int ck = (P % T::CPR) ^ T::swz_b(r);
+      pk_off[k] = 8 * ck < p.dv ? r * (int)(2 * kr) + 16 * ck : kBwdOutOfRange;
+      pv_off[k] = 8 * ck < p.dv ? r * (int)(2 * vr) + 16 * ck : kBwdOutOfRange;
+    }
+  }
+  auto issue = [&](int kt, char* kd, char* vd) {
+    const E* kb = Kp + kt * kr;
+    const E* vb = Vp + kt * vr;
+    if constexpr (Gen) {
+      // valid bytes from the tile's first row: up to the end of row Sk - 1
+      const unsigned kbytes = (unsigned)min((long long)(p.Sk - kt - 1) * 2 * kr + 2 * p.dv, kBwdMaxRange);
+      const unsigned vbytes = (unsigned)min((long long)(p.Sk - kt - 1) * 2 * vr + 2 * p.dv, kBwdMaxRange);
+#pragma unroll
+      for (int k = 0; k < T::NIW; ++k) {
+        const int off = (wave * T::NIW + k) * 1024;
+        dma16(kb, kbytes, pk_off[k], kd + off);
+        dma16(vb, vbytes, pv_off[k], vd + off);
+      }
+    } else {
+      const unsigned bytes = (unsigned)min((long)(p.Sk - kt) * T::ROW, 0x7fffffffL);
+#pragma unroll
+      for (int k = 0; k < T::NIW; ++k) {
+        const int off = (wave * T::NIW + k) * 1024;
+        dma16(kb, bytes, voff ^ T::dma_xor(k, kSwzB), kd + off);
+        dma16(vb, bytes, voff ^ T::dma_xor(k, kSwzB), vd + off);
+      }
     }
   };
   if (n_tiles > 0) issue(t0, kbuf0, vbuf0);
@@ -405,10 +452,11 @@ void bwd_dq_mfma_kernel(BwdParams p) {
   float dd = 0.f;
 #pragma unroll
   for (int t = 0; t < T::DC; ++t) {
-    if (row_ok) {
-      qf[t] = *(const e16x8*)(Qh + (size_t)i * D + 16 * t + 8 * g);
-      dof[t] = *(const e16x8*)(dOh + (size_t)i * D + 16 * t + 8 * g);
-      const e16x8 ov = *(const e16x8*)(Oh + (size_t)i * D + 16 * t + 8 * g);
+    // (general form: the dims from dv on, a multiple of 16, are zeros)
+    if (row_ok && (!Gen || 16 * t < p.dv)) {
+      qf[t] = *(const e16x8*)(Qh + i * qr + 16 * t + 8 * g);
+      dof[t] = *(const e16x8*)(dOh + i * dor + 16 * t + 8 * g);
+      const e16x8 ov = *(const e16x8*)(Oh + i * orow + 16 * t + 8 * g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dd = fmaf((float)dof[t][e], (float)ov[e], dd);
     } else {
@@ -496,15 +544,19 @@ void bwd_dq_mfma_kernel(BwdParams p) {
 
   // lane holds dims 32 db + 8 a + 4 g + (0..3) of row i; a key chunk writes
   // its unscaled partial sums, added up in chunk order afterwards
+  // (general form: dQ is a view with strides p.dqs, written in its first dv dims)
   if (row_ok) {
     const bool part = p.nch > 1;
     const float sc = part ? 1.f : p.scale;
     float* dst = part ? p.part_q + ((long)blockIdx.y * p.B * p.H * p.Sq + row) * D
-                      : p.dQ + row * D;
+                 : Gen ? p.dQ + b * p.dqs[0] + h * p.dqs[1] + i * p.dqs[2]
+                       : p.dQ + row * D;
+    const int dlim = Gen && !part ? p.dv : D;
 #pragma unroll
     for (int db = 0; db < T::DB; ++db)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
+        if (32 * db + 8 * a + 4 * g >= dlim) continue;
         const f32x4 v4 = {dq[db][4 * a] * sc, dq[db][4 * a + 1] * sc,
                           dq[db][4 * a + 2] * sc, dq[db][4 * a + 3] * sc};
         *(f32x4*)(dst + 32 * db + 8 * a + 4 * g) = v4;
@@ -523,7 +575,7 @@ void bwd_dq_mfma_kernel(BwdParams p) {
 //   P  = exp2(S |scale| log2 e - LSE log2 e),  dS = P (dP - D)
 //   dV^T += dO^T P,  dK^T += Q^T dS   (A: transposed reads of the dO / Q
 //                                      tiles, B: P / dS packed to the input type)
-template <typename E, int D>
+template <typename E, int D, bool Gen>
 __global__ __launch_bounds__(kBwdThreads, 1)
 void bwd_dkdv_mfma_kernel(BwdParams p) {
   // 64 query rows per copied tile, worked as two independent 32-row halves
@@ -572,6 +624,20 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   const int n_tiles = n_rt * gh;   // (query head, row tile) pairs
 
   const int voff = T::dma_off(64 * wave * T::NIW + lane, kSwzB);
+  // general form (views with strides, head dim dv): each copy instruction's
+  // lane offset in full, or past the buffer's range for a chunk at or beyond
+  // dim dv (zeros in LDS)
+  const long long qr = Gen ? p.qs[2] : D, dor = Gen ? p.dos[2] : D;   // element row strides
+  int pq_off[Gen ? T::NIW : 1], po_off[Gen ? T::NIW : 1];
+  if constexpr (Gen) {
+#pragma unroll
+    for (int k = 0; k < T::NIW; ++k) {
+      const int P = 64 * (wave * T::NIW + k) + lane, r = P / T::CPR;
+      const int ck = (P % T::CPR) ^ T::swz_b(r);
+      pq_off[k] = 8 * ck < p.dv ? r * (int)(2 * qr) + 16 * ck : kBwdOutOfRange;
+      po_off[k] = 8 * ck < p.dv ? r * (int)(2 * dor) + 16 * ck : kBwdOutOfRange;
+    }
+  }
   auto issue = [&](int t, char* qd, char* od, float* ld) {
     const int h = hkv * gh + t / n_rt, r0 = rt0 + (t % n_rt) * BM;
     const long base = ((long)b * p.H + h) * p.Sq;
@@ -584,14 +650,28 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
     } else if (wave == 1) {
       x = r < p.Sq ? p.Dws[base + r] : 0.f;
     }
-    const unsigned bytes = (unsigned)min((long)(p.Sq - r0) * T::ROW, 0x7fffffffL);
-    const E* qb = (const E*)p.Q + (base + r0) * D;
-    const E* ob = (const E*)p.dO + (base + r0) * D;
+    if constexpr (Gen) {
+      const E* qb = (const E*)p.Q + b * p.qs[0] + h * p.qs[1] + r0 * qr;
+      const E* ob = (const E*)p.dO + b * p.dos[0] + h * p.dos[1] + r0 * dor;
+      // valid bytes from the tile's first row: up to the end of row Sq - 1
+      const unsigned qbytes = (unsigned)min((long long)(p.Sq - r0 - 1) * 2 * qr + 2 * p.dv, kBwdMaxRange);
+      const unsigned obytes = (unsigned)min((long long)(p.Sq - r0 - 1) * 2 * dor + 2 * p.dv, kBwdMaxRange);
 #pragma unroll
-    for (int k = 0; k < T::NIW; ++k) {
-      const int off = (wave * T::NIW + k) * 1024;
-      dma16(qb, bytes, voff ^ T::dma_xor(k, kSwzB), qd + off);
-      dma16(ob, bytes, voff ^ T::dma_xor(k, kSwzB), od + off);
+      for (int k = 0; k < T::NIW; ++k) {
+        const int off = (wave * T::NIW + k) * 1024;
+        dma16(qb, qbytes, pq_off[k], qd + off);
+        dma16(ob, obytes, po_off[k], od + off);
+      }
+    } else {
+      const unsigned bytes = (unsigned)min((long)(p.Sq - r0) * T::ROW, 0x7fffffffL);
+      const E* qb = (const E*)p.Q + (base + r0) * D;
+      const E* ob = (const E*)p.dO + (base + r0) * D;
+#pragma unroll
+      for (int k = 0; k < T::NIW; ++k) {
+        const int off = (wave * T::NIW + k) * 1024;
+        dma16(qb, bytes, voff ^ T::dma_xor(k, kSwzB), qd + off);
+        dma16(ob, bytes, voff ^ T::dma_xor(k, kSwzB), od + off);
+      }
     }
     if (wave < 2 && lane < BM) ld[wave * BM + lane] = x;
   };
@@ -599,10 +679,16 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
 
   // K and V rows as B operands (k-slot (g, e) of step t is dim 16t + 8g + e)
   e16x8 kf[T::DC], vf[T::DC];
+  const E* krp = Gen ? (const E*)p.K + b * p.ks[0] + hkv * p.ks[1] + j * p.ks[2]
+                     : (const E*)p.K + krow * D;
+  const E* vrp = Gen ? (const E*)p.V + b * p.vs[0] + hkv * p.vs[1] + j * p.vs[2]
+                     : (const E*)p.V + krow * D;
 #pragma unroll
   for (int t = 0; t < T::DC; ++t) {
-    kf[t] = key_ok ? *(const e16x8*)((const E*)p.K + krow * D + 16 * t + 8 * g) : e16x8{};
-    vf[t] = key_ok ? *(const e16x8*)((const E*)p.V + krow * D + 16 * t + 8 * g) : e16x8{};
+    // (general form: the dims from dv on, a multiple of 16, are zeros)
+    const bool ok = key_ok && (!Gen || 16 * t < p.dv);
+    kf[t] = ok ? *(const e16x8*)(krp + 16 * t + 8 * g) : e16x8{};
+    vf[t] = ok ? *(const e16x8*)(vrp + 16 * t + 8 * g) : e16x8{};
     if (p.neg_q) {   // negative scale: -K and |scale| (exact sign flips)
       u32x4 bits = __builtin_bit_cast(u32x4, kf[t]) ^ 0x80008000u;
       kf[t] = __builtin_bit_cast(e16x8, bits);
@@ -701,14 +787,17 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
     if (t + 1 < n_tiles) step(t + 1, qbuf1, obuf1, lbuf1, qbuf0, obuf0, lbuf0);
   }
 
-  // lane holds dims DO ob + 32 db + 8 a + 4 g + (0..3) of key j
+  // lane holds dims DO ob + 32 db + 8 a + 4 g + (0..3) of key j (general
+  // form: views with strides p.dks / p.dvs, written in their first dv dims)
   if (key_ok) {
-    float* odk = p.dK + krow * D + DO * ob;
-    float* odv = p.dV + krow * D + DO * ob;
+    float* odk = (Gen ? p.dK + b * p.dks[0] + hkv * p.dks[1] + j * p.dks[2] : p.dK + krow * D) + DO * ob;
+    float* odv = (Gen ? p.dV + b * p.dvs[0] + hkv * p.dvs[1] + j * p.dvs[2] : p.dV + krow * D) + DO * ob;
+    const int dlim = (Gen ? p.dv : D) - DO * ob;
 #pragma unroll
     for (int db = 0; db < DBO; ++db)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
+        if (32 * db + 8 * a + 4 * g >= dlim) continue;
         const f32x4 k4 = {dk[db][4 * a] * p.scale, dk[db][4 * a + 1] * p.scale,
                           dk[db][4 * a + 2] * p.scale, dk[db][4 * a + 3] * p.scale};
         const f32x4 v4 = {dv[db][4 * a], dv[db][4 * a + 1], dv[db][4 * a + 2], dv[db][4 * a + 3]};
@@ -1125,9 +1214,11 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   constexpr bool b16_mfma = sizeof(E) == 2 && (D == 64 || D == 128 || D == 256);
   // (MFMA dQ kernels: blockIdx.y = key chunk when p.nch > 1)
   if constexpr (b16_mfma) {
-    hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D>),
-                       dim3((unsigned)((long)p.B * p.H * p.n_qblk), (unsigned)p.nch),
-                       dim3(kBwdThreads), 0, stream, p);
+    const dim3 grid((unsigned)((long)p.B * p.H * p.n_qblk), (unsigned)p.nch);
+    if (p.gen)
+      hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D, true>), grid, dim3(kBwdThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D, false>), grid, dim3(kBwdThreads), 0, stream, p);
   } else if constexpr (f32_mfma) {
     hipLaunchKernelGGL((bwd_dq_f32_mfma_kernel<D>),
                        dim3((unsigned)((long)p.B * p.H * p.n_qblk), (unsigned)p.nch),
@@ -1148,8 +1239,12 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   if constexpr (b16_mfma) {
     // (D = 256: two workgroups per key block, one per half of the output dims)
     const long kblocks = (long)p.B * p.HKV * ((p.Sk + 127) / 128) * (D == 256 ? 2 : 1);
-    hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D>), dim3((unsigned)kblocks), dim3(kBwdThreads), 0,
-                       stream, p);
+    if (p.gen)
+      hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, true>), dim3((unsigned)kblocks), dim3(kBwdThreads),
+                         0, stream, p);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, false>), dim3((unsigned)kblocks), dim3(kBwdThreads),
+                         0, stream, p);
   } else if constexpr (f32_mfma) {
     const long kblocks = (long)p.B * p.HKV * ((p.Sk + 127) / 128);
     hipLaunchKernelGGL((bwd_dkdv_f32_mfma_kernel<D>), dim3((unsigned)kblocks), dim3(kBwdThreads),

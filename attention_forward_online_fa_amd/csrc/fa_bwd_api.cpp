@@ -114,21 +114,32 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
   p.n_qblk = (Sq + 127) / 128;
   if ((double)B * H * p.n_qblk > 2147483647.0) return FA_ERR_SHAPE;
   // 16-bit inputs at head dims 16 .. 96 other than 64 run the MFMA kernels of
-  // the 64 or 128 tile on copies whose rows are zero-padded to the tile dim:
-  // the zero dims add exact zeros to every dot product, and the gradients'
-  // padded dims (zero) are dropped when they are copied back. Strided views
-  // are staged the same way: copied to contiguous rows, and the gradients
-  // copied back into the caller's views.
-  const bool padded = dtype != FA_F32 && D != 64 && D != 128 && D != 256;
-  const bool staged = padded || !contiguous;
-  const int DT = padded ? (D < 64 ? 64 : 128) : D;
+  // the 64 or 128 tile with the dims from D on held as zeros (they add exact
+  // zeros to every dot product, and the gradients' extra dims are not
+  // written). The 16-bit MFMA kernels read such head dims, and strided views,
+  // directly (their general form: per-view strides, copy offsets formed in
+  // full, chunks at or beyond D read as zeros), as long as every row stride
+  // keeps a tile's copy offsets far inside 32 bits. Otherwise, and for fp32
+  // views, the inputs are staged: copied to contiguous zero-padded rows, and
+  // the gradients copied back into the caller's views.
+  const int DT16 = D <= 64 ? 64 : D <= 128 ? 128 : 256;
+  bool gen = false;
+  if (dtype != FA_F32 && (!contiguous || D != DT16)) {
+    long long mx = 0;
+    for (int t = 0; t < 5; ++t) mx = std::max(mx, vs[t][2]);
+    gen = mx <= (1LL << 22);   // 64 rows x 2 bytes x 2^22 = 2^29 bytes per tile
+  }
+  const bool padded = dtype != FA_F32 && D != DT16;
+  const bool staged = !gen && (padded || !contiguous);
+  const int DT = padded ? DT16 : D;
   const size_t nq = (size_t)B * H * Sq, nk = (size_t)B * HKV * Sk;
   auto up = [](size_t bytes) { return (bytes + 255) / 256 * 256; };
   // workspace, stream-ordered from the library's memory pool: D_i, and when
   // padded Q, O, dO, K, V (input type) and dQ, dK, dV (fp32) at DT
   const size_t b_d = up(nq * sizeof(float));
   const size_t b_q = staged ? up(nq * DT * esz) : 0, b_k = staged ? up(nk * DT * esz) : 0;
-  const size_t b_gq = staged ? up(nq * DT * 4) : 0, b_gk = staged ? up(nk * DT * 4) : 0;
+  const size_t b_gk = staged ? up(nk * DT * 4) : 0;
+  size_t b_gq = staged ? up(nq * DT * 4) : 0;   // (the general form's key chunks also use it)
   // The per-row kernels (fp32 inputs at D = 16, 48, 80 and 256) on grids too small to fill the
   // GPU: each row group's range is cut into nch chunks that run side by side
   // (a causal grid is otherwise bound by its longest rows), their partial
@@ -170,6 +181,7 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
       }
     }
   }
+  if (gen && p.nch > 1) b_gq = up(nq * DT * 4);   // summed dQ before it goes to the view
   const bool per_row = dtype == FA_F32 && !fa::bwd_f32_mfma(D);
   const size_t b_pq = p.nch > 1 ? up((size_t)p.nch * nq * DT * 4) : 0;
   const size_t b_pk = p.nch > 1 && per_row ? up((size_t)p.nch * nk * D * 4) : 0;
@@ -217,6 +229,26 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
     if (e == hipSuccess) e = fa::launch_scatter_rows(gq, dQ, B, H, Sq, bs[5], DT, D, stream);
     if (e == hipSuccess) e = fa::launch_scatter_rows(gk, dK, B, HKV, Sk, bs[6], DT, D, stream);
     if (e == hipSuccess) e = fa::launch_scatter_rows(gv, dV, B, HKV, Sk, bs[7], DT, D, stream);
+  } else if (gen) {
+    p.gen = 1;
+    p.dv = D;
+    std::copy(vs[0], vs[0] + 3, p.qs);
+    std::copy(vs[1], vs[1] + 3, p.ks);
+    std::copy(vs[2], vs[2] + 3, p.vs);
+    std::copy(vs[3], vs[3] + 3, p.os);
+    std::copy(vs[4], vs[4] + 3, p.dos);
+    std::copy(vs[5], vs[5] + 3, p.dqs);
+    std::copy(vs[6], vs[6] + 3, p.dks);
+    std::copy(vs[7], vs[7] + 3, p.dvs);
+    // with key chunks the chunk sum lands in contiguous rows first
+    float* gq = p.nch > 1 ? reinterpret_cast<float*>(w + b_d + 3 * b_q + 2 * b_k) : nullptr;
+    if (gq) p.dQ = gq;
+    e = fa::launch_backward(p, dtype, DT, stream);
+    if (e == hipSuccess && gq) {
+      long long bs[3];
+      for (int a = 0; a < 3; ++a) bs[a] = vs[5][a] * 4;
+      e = fa::launch_scatter_rows(gq, dQ, B, H, Sq, bs, DT, D, stream);
+    }
   } else {
     e = fa::launch_backward(p, dtype, D, stream);
   }

@@ -274,10 +274,12 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
  * Stride rules (else FA_ERR_STRIDE): every stride >= 0 and a multiple of 16
  * bytes, every row stride >= D, and the rows of dQ, dK and dV pairwise
  * disjoint; batch or head strides of 0 (broadcast inputs) are allowed for the
- * inputs. When every view is contiguous the call runs exactly as fa_bwd;
- * otherwise the inputs are first copied to contiguous rows and the gradients
- * copied back into their views at the end (stream-ordered workspace from the
- * library's pool, like the padded head dims of fa_bwd). Same arguments,
+ * inputs. When every view is contiguous the call runs exactly as fa_bwd.
+ * Otherwise bfloat16 and float16 views are read and written in place by the
+ * kernels, as long as every row stride of Q, K, V, O, dO is at most 2^22
+ * elements; fp32 views (and 16-bit ones with longer rows) are first copied to
+ * contiguous rows and their gradients copied back into the views at the end
+ * (stream-ordered workspace from the library's pool). Same arguments,
  * ownership and other errors as fa_bwd.
  */
 int fa_bwd_strided(const void* Q, const void* K, const void* V, const void* O, const void* dO,

@@ -163,6 +163,8 @@ BWD_CASES = [
     ("bf16", 1, 8, 2, 300, 300, 128, 1, 0),
     ("bf16", 1, 4, 2, 200, 260, 96, 0, 70),    # padded head dim and strides together
     ("f16", 1, 2, 1, 130, 170, 256, 1, 0),
+    ("bf16", 1, 2, 1, 130, 2200, 128, 0, 0),   # key chunks of the dQ kernel on views
+    ("f16", 1, 4, 2, 200, 300, 48, 1, 0),      # head dim 48 (the 64 tile) on views
 ]
 
 
