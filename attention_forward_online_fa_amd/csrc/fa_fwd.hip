@@ -167,7 +167,10 @@ void fwd_16b_kernel(Params p) {
   // Padded rows: each copy instruction's lane offset in full (a row stride
   // need not be a multiple of the tile row), or one past the buffer's range
   // for a chunk at or beyond dim DV, which then lands in LDS as zeros.
+  // (a copy's range is capped below kOutOfRange, so such a chunk is entirely
+  // out of range however long the key axis)
   constexpr int kOutOfRange = 0x7ffffff0;
+  constexpr long long kMaxRange = 0x7fff0000LL;
   int pk_off[Pad ? T::NIW : 1], pv_off[Pad ? T::NIW : 1];
   if constexpr (Pad) {
 #pragma unroll
@@ -183,9 +186,9 @@ void fwd_16b_kernel(Params p) {
       // valid bytes from the tile's first row: up to the end of row Sk - 1
       constexpr int rb = 2 * DV;
       const unsigned kbytes = full ? (unsigned)((BN - 1) * krb + rb)
-                                   : (unsigned)min((long long)(p.Sk - kt - 1) * krb + rb, 0x7fffffffLL);
+                                   : (unsigned)min((long long)(p.Sk - kt - 1) * krb + rb, kMaxRange);
       const unsigned vbytes = full ? (unsigned)((BN - 1) * vrb + rb)
-                                   : (unsigned)min((long long)(p.Sk - kt - 1) * vrb + rb, 0x7fffffffLL);
+                                   : (unsigned)min((long long)(p.Sk - kt - 1) * vrb + rb, kMaxRange);
       const E* kb = Kp + (long long)kt * p.ks[2];
       const E* vb = Vp + (long long)kt * p.vs[2];
 #pragma unroll
@@ -197,9 +200,9 @@ void fwd_16b_kernel(Params p) {
     } else if constexpr (Strided) {
       // valid bytes from the tile's first row: up to the end of row Sk - 1
       const unsigned kbytes = full ? (unsigned)((BN - 1) * krb + T::ROW)
-                                   : (unsigned)min((long long)(p.Sk - kt - 1) * krb + T::ROW, 0x7fffffffLL);
+                                   : (unsigned)min((long long)(p.Sk - kt - 1) * krb + T::ROW, kMaxRange);
       const unsigned vbytes = full ? (unsigned)((BN - 1) * vrb + T::ROW)
-                                   : (unsigned)min((long long)(p.Sk - kt - 1) * vrb + T::ROW, 0x7fffffffLL);
+                                   : (unsigned)min((long long)(p.Sk - kt - 1) * vrb + T::ROW, kMaxRange);
       const E* kb = Kp + (long long)kt * p.ks[2];
       const E* vb = Vp + (long long)kt * p.vs[2];
 #pragma unroll

@@ -167,3 +167,28 @@ def test_backward(case):
         tol = BWD_TOL[wl.dtype] * max(1.0, float(np.abs(r).max()))
         print(f"  {name}: max|d|={err:.3e} (tol {tol:.3e})", flush=True)
         assert np.all(np.isfinite(x)) and err <= tol, f"{name}: {err:.3e} > {tol:.3e}"
+
+
+def test_padded_keys_with_a_copy_range_past_2gb():
+    # K/V rows 32 KB apart over 65536 keys: for the early key tiles the bytes
+    # from the tile's first row to the end of K exceed 2 GB, so a copy's range
+    # is capped; the padded dims' chunks (sent out of range) must still read
+    # as zeros. 64 query rows, head dim 96 (the 128 tile's padded form).
+    import attention_forward_online_fa_amd as fa
+    D, Sq, Sk, rs = 96, 64, 65536, 16448
+    wl = wl_small("bf16", 1, 1, 1, Sq, Sk, D, 0, 0, name="long-stride", seed=3)
+    inp = W.make_inputs(wl)
+    q, k, v = to_device(inp)
+    _say(f"[head dims] {wl} K/V row stride {rs} elements")
+    kbuf = torch.full((Sk, rs), 3.0, dtype=k.dtype, device=k.device)   # nonzero filler
+    vbuf = torch.full((Sk, rs), 3.0, dtype=v.dtype, device=v.device)
+    kbuf[:, :D] = k[0, 0]
+    vbuf[:, :D] = v[0, 0]
+    kv = kbuf[:, :D].unsqueeze(0).unsqueeze(0)
+    vv = vbuf[:, :D].unsqueeze(0).unsqueeze(0)
+    assert kv.stride(2) == rs and (Sk - 1) * rs * 2 > 2 ** 31
+    o, lse = fa.fwd(q, kv, vv, causal=False, scale=wl.scale(), num_splits=1)
+    torch.cuda.synchronize()
+    O, L = attention(inp.q, inp.k, inp.v, wl.scale(), False, 0)
+    compare(host64(o), host64(lse), O, L, TOL[wl.dtype], wl.name)
+    del kbuf, vbuf
