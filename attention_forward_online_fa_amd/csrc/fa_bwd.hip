@@ -513,15 +513,25 @@ void bwd_dq_mfma_kernel(BwdParams p) {
     const bool edge = (kt + BN > p.Sk) || (p.causal && kt + BN - 1 > qw) ||
                       (p.window > 0 && kt < qw + 31 - p.window + 1);
     typename X::x8 dsf[2];
+    // the mask in one branch (a test per element inside the exponential
+    // loop became a branch per element on every tile); the row index goes
+    // through an empty asm so that the test stays behind the branch
+    float xs[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) xs[v] = fmaf(s[v], sl, -L2);
+    if (edge) {
+      int ii = i;
+      asm volatile("" : "+v"(ii));
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int j = kt + 8 * g + 16 * (v >> 3) + (v & 7);
+        const bool vis = j < p.Sk && (!p.causal || j <= ii) && (p.window <= 0 || j > ii - p.window);
+        xs[v] = vis ? xs[v] : -INFINITY;
+      }
+    }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      float x = fmaf(s[v], sl, -L2);
-      if (edge) {
-        const int j = kt + 8 * g + 16 * (v >> 3) + (v & 7);
-        const bool vis = j < p.Sk && (!p.causal || j <= i) && (p.window <= 0 || j > i - p.window);
-        x = vis ? x : -INFINITY;
-      }
-      const float pr = __builtin_amdgcn_exp2f(x);
+      const float pr = __builtin_amdgcn_exp2f(xs[v]);
       dsf[v >> 3][v & 7] = (E)(pr * (dp[v] - Di));
     }
 #pragma unroll
@@ -638,8 +648,7 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
       po_off[k] = 8 * ck < p.dv ? r * (int)(2 * dor) + 16 * ck : kBwdOutOfRange;
     }
   }
-  auto issue = [&](int t, char* qd, char* od, float* ld) {
-    const int h = hkv * gh + t / n_rt, r0 = rt0 + (t % n_rt) * BM;
+  auto issue = [&](int h, int r0, char* qd, char* od, float* ld) {
     const long base = ((long)b * p.H + h) * p.Sq;
     // the tile rows' base-2 LSE (wave 0) and D (wave 1), loaded first
     const int r = r0 + lane;
@@ -675,7 +684,12 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
     }
     if (wave < 2 && lane < BM) ld[wave * BM + lane] = x;
   };
-  if (n_tiles > 0) issue(0, qbuf0, obuf0, lbuf0);
+  // tiles in (query head, row tile) order, followed by a cursor: the head
+  // and rows of the tile last issued, and the rows of the tile being worked
+  // (no divisions per tile)
+  int ih = hkv * gh, ir = rt0, cur_r0 = rt0;
+  const int rt_end = rt0 + n_rt * BM;
+  if (n_tiles > 0) issue(ih, ir, qbuf0, obuf0, lbuf0);
 
   // K and V rows as B operands (k-slot (g, e) of step t is dim 16t + 8g + e)
   e16x8 kf[T::DC], vf[T::DC];
@@ -717,9 +731,17 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
 
   auto step = [&](int t, const char* Qc, const char* Oc, const float* Lc, char* Qn, char* On,
                   float* Ln) __attribute__((always_inline)) {
-    const int r0 = rt0 + (t % n_rt) * BM;
+    const int r0 = cur_r0;
     wait_dma_and_sync();
-    if (t + 1 < n_tiles) issue(t + 1, Qn, On, Ln);
+    if (t + 1 < n_tiles) {
+      ir += BM;
+      if (ir >= rt_end) {
+        ir = rt0;
+        ++ih;
+      }
+      issue(ih, ir, Qn, On, Ln);
+      cur_r0 = ir;
+    }
     if (kw >= p.Sk || (p.causal && r0 + BM - 1 < kw) ||
         (p.window > 0 && r0 > kw + 31 + p.window - 1))
       return;
@@ -749,15 +771,23 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
         lq[h4] = *(const f32x4*)(Lc + rr);
         dq4[h4] = *(const f32x4*)(Lc + BM + rr);
       }
+      // the mask in one branch per half, as in the dQ kernel
+      float xs[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) xs[v] = fmaf(sc[hh][v], sl, -lq[v >> 2][v & 3]);
+      if (edge) {
+        int jj = j;
+        asm volatile("" : "+v"(jj));
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = r0 + HM * hh + 8 * g + 16 * (v >> 3) + (v & 7);
+          const bool vis = jj < p.Sk && (!p.causal || jj <= r) && (p.window <= 0 || jj > r - p.window);
+          xs[v] = vis ? xs[v] : -INFINITY;
+        }
+      }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float x = fmaf(sc[hh][v], sl, -lq[v >> 2][v & 3]);
-        if (edge) {
-          const int r = r0 + HM * hh + 8 * g + 16 * (v >> 3) + (v & 7);
-          const bool vis = j < p.Sk && (!p.causal || j <= r) && (p.window <= 0 || j > r - p.window);
-          x = vis ? x : -INFINITY;
-        }
-        const float pr = __builtin_amdgcn_exp2f(x);
+        const float pr = __builtin_amdgcn_exp2f(xs[v]);
         pp[hh][v >> 3][v & 7] = (E)pr;
         ds[hh][v >> 3][v & 7] = (E)(pr * (dp[hh][v] - dq4[v >> 2][v & 3]));
       }
@@ -959,15 +989,35 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
       const bool edge = (kt + BN > p.Sk) || (p.causal && kt + BN - 1 > qw) ||
                         (p.window > 0 && kt < qw + 31 - p.window + 1);
       float ds[16];
+      if constexpr (D <= 64) {
+        // the mask in one branch, as in the 16-bit kernels (at D = 128, one
+        // wavefront per SIMD, the test inside the loop measured faster)
+        float xs[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = fmaf(s[v], sl, -L2);
+        for (int v = 0; v < 16; ++v) xs[v] = fmaf(s[v], sl, -L2);
         if (edge) {
-          const int j = kt + 8 * (v >> 2) + 4 * g + (v & 3);
-          const bool vis = j < p.Sk && (!p.causal || j <= i) && (p.window <= 0 || j > i - p.window);
-          x = vis ? x : -INFINITY;
+          int ii = i;
+          asm volatile("" : "+v"(ii));
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int j = kt + 8 * (v >> 2) + 4 * g + (v & 3);
+            const bool vis = j < p.Sk && (!p.causal || j <= ii) && (p.window <= 0 || j > ii - p.window);
+            xs[v] = vis ? xs[v] : -INFINITY;
+          }
         }
-        ds[v] = __builtin_amdgcn_exp2f(x) * (dp[v] - Di);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ds[v] = __builtin_amdgcn_exp2f(xs[v]) * (dp[v] - Di);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float x = fmaf(s[v], sl, -L2);
+          if (edge) {
+            const int j = kt + 8 * (v >> 2) + 4 * g + (v & 3);
+            const bool vis = j < p.Sk && (!p.causal || j <= i) && (p.window <= 0 || j > i - p.window);
+            x = vis ? x : -INFINITY;
+          }
+          ds[v] = __builtin_amdgcn_exp2f(x) * (dp[v] - Di);
+        }
       }
       // dQ^T += K^T dS^T: step u takes key 8 (u / 4) + 4 g + u % 4
 #pragma unroll
@@ -1126,17 +1176,38 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
       const bool edge = (kw + 31 >= p.Sk) || (p.causal && r0 < kw + 31) ||
                         (p.window > 0 && r0 + BM - 1 > kw + p.window - 1);
       float pr[16], ds[16];
+      if constexpr (D <= 64) {   // the mask in one branch, as in the dQ kernel
+        float xs[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rr = 8 * (v >> 2) + 4 * g + (v & 3);
-        float x = fmaf(s[v], sl, -Ls[rr]);
+        for (int v = 0; v < 16; ++v) xs[v] = fmaf(s[v], sl, -Ls[8 * (v >> 2) + 4 * g + (v & 3)]);
         if (edge) {
-          const int r = r0 + rr;
-          const bool vis = j < p.Sk && (!p.causal || j <= r) && (p.window <= 0 || j > r - p.window);
-          x = vis ? x : -INFINITY;
+          int jj = j;
+          asm volatile("" : "+v"(jj));
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = r0 + 8 * (v >> 2) + 4 * g + (v & 3);
+            const bool vis = jj < p.Sk && (!p.causal || jj <= r) && (p.window <= 0 || jj > r - p.window);
+            xs[v] = vis ? xs[v] : -INFINITY;
+          }
         }
-        pr[v] = __builtin_amdgcn_exp2f(x);
-        ds[v] = pr[v] * (dp[v] - Dl[rr]);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          pr[v] = __builtin_amdgcn_exp2f(xs[v]);
+          ds[v] = pr[v] * (dp[v] - Dl[8 * (v >> 2) + 4 * g + (v & 3)]);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rr = 8 * (v >> 2) + 4 * g + (v & 3);
+          float x = fmaf(s[v], sl, -Ls[rr]);
+          if (edge) {
+            const int r = r0 + rr;
+            const bool vis = j < p.Sk && (!p.causal || j <= r) && (p.window <= 0 || j > r - p.window);
+            x = vis ? x : -INFINITY;
+          }
+          pr[v] = __builtin_amdgcn_exp2f(x);
+          ds[v] = pr[v] * (dp[v] - Dl[rr]);
+        }
       }
       // dV^T += dO^T P, dK^T += Q^T dS: step u takes row 8 (u / 4) + 4 g + u % 4
 #pragma unroll
