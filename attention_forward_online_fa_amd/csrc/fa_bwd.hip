@@ -758,6 +758,16 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
         dp[hh] = X::mfma(ao, vf[t2], dp[hh]);
       }
     }
+    // operand reads four products ahead of their MFMAs (the scheduler's own
+    // order read one or two ahead, and one wavefront per SIMD left the LDS
+    // latency exposed)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int k = 0; k < 2 * NH * T::DC - 4; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     const bool edge = (kw + 31 >= p.Sk) || (p.causal && r0 < kw + 31) ||
                       (p.window > 0 && r0 + BM - 1 > kw + p.window - 1);
     typename X::x8 pp[NH][2], ds[NH][2];
