@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 # Hash of the sources and flags a library was built from, written beside it.
 HASH_PATH = LIB_PATH + ".srchash"
 SOURCES = [os.path.join(CSRC, "fa_fwd.hip"), os.path.join(CSRC, "fa_api.cpp"),
-           os.path.join(CSRC, "fa_bwd.hip"), os.path.join(CSRC, "fa_bwd_api.cpp"),
+           os.path.join(CSRC, "fa_bwd.hip"), os.path.join(CSRC, "fa_bwd_f32.hip"),
+           os.path.join(CSRC, "fa_bwd_api.cpp"),
            os.path.join(CSRC, "fa_noalloc.hip")]
 
 ARCH = "gfx950"
@@ -32,7 +33,9 @@ HIP_FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 # Per-source compiler flags on top of HIP_FLAGS (by file name).
-FILE_FLAGS: dict = {}
+# fa_bwd_f32.hip: VGPR-form MFMAs (the fp32 D = 128 backward kernels run one
+# wavefront per SIMD, where the default AGPR form costs register moves).
+FILE_FLAGS: dict = {"fa_bwd_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def source_files() -> list:

@@ -60,8 +60,16 @@ constexpr int bwd_rows_per_group(int D) { return bwd_lanes_per_row(D) == 16 ? 4 
 // 48, 80 and 256 the per-row kernels); 16-bit inputs always run MFMA kernels.
 constexpr bool bwd_f32_mfma(int D) { return D == 32 || D == 64 || D == 96 || D == 128; }
 
+constexpr int kBwdThreads = 256;   // threads per backward workgroup (4 wavefronts)
+constexpr float kLog2e = 1.4426950408889634f;
+
 // Queue the dQ kernel (which also writes Dws) and then the dK/dV kernel.
 hipError_t launch_backward(const BwdParams& p, int dtype, int D, hipStream_t stream);
+
+// The fp32 MFMA kernels (fa_bwd_f32.hip; D one of bwd_f32_mfma's dims): the
+// dQ kernel (key chunks on blockIdx.y when p.nch > 1) and the dK/dV kernel.
+hipError_t launch_bwd_f32_mfma_dq(const BwdParams& p, int D, hipStream_t stream);
+hipError_t launch_bwd_f32_mfma_dkdv(const BwdParams& p, int D, hipStream_t stream);
 
 // Row copies of the staged backward (fp32 views, and 16-bit views whose row
 // strides exceed what the general form's copy offsets allow): inputs copied
