@@ -505,6 +505,17 @@ void bwd_dq_mfma_kernel(BwdParams p) {
       s = X::mfma(ak, qf[t2], s);
       dp = X::mfma(av, dof[t2], dp);
     }
+    if constexpr (D == 256) {
+      // one wavefront per SIMD: operand reads eight products ahead (at two
+      // wavefronts per SIMD the other one hides the latency; measured equal)
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int k = 0; k < 2 * T::DC - 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
     // element v holds key kt + 8g + c, c = 16 (v / 8) + v % 8
     const bool edge = (kt + BN > p.Sk) || (p.causal && kt + BN - 1 > qw) ||
                       (p.window > 0 && kt < qw + 31 - p.window + 1);
