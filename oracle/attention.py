@@ -184,8 +184,12 @@ def visible_count(Sq: int, Sk: int, causal: bool, window: int) -> np.ndarray:
     return np.maximum(hi - lo, 0)
 
 
-def attention_backward(Q, K, V, dO, scale: float, causal: bool = False, window: int = 0):
-    """Gradients (dQ, dK, dV) of L = sum(O * dO), all fp64, for O = attention(...).
+def attention_backward(Q, K, V, dO, scale: float, causal: bool = False, window: int = 0,
+                       block_mask=None, block_q: int = MASK_BLOCK_Q, block_k: int = MASK_BLOCK_K):
+    """Gradients (dQ, dK, dV) of L = sum(O * dO), all fp64, for O = attention(...)
+    with the same arguments (block_mask, block_q, block_k as in ``attention``:
+    a key is visible only where the causal and window rules and the mask's
+    block byte all allow it; masked pairs have P = 0 and get no gradient).
 
     From the definition (forge ``flash_attention.metal`` backward section): with
     P the masked softmax of scale * Q K^T (P_ij = exp(s_ij - LSE_i) on the
@@ -208,14 +212,19 @@ def attention_backward(Q, K, V, dO, scale: float, causal: bool = False, window: 
     assert H % HKV == 0, "H must be a multiple of HKV"
     g = H // HKV
     scale = float(np.float64(scale))
-    vis = visible_mask(np.arange(Sq), Sk, causal, window)
-    nonempty = vis.any(axis=1)
+    rows = np.arange(Sq)
+    vis_rule = visible_mask(rows, Sk, causal, window)
     dQ = np.zeros_like(Q)
     dK = np.zeros_like(K)
     dV = np.zeros_like(V)
     for b in range(B):
         for h in range(H):
             hk = h // g
+            vis = vis_rule
+            if block_mask is not None:
+                vis = vis_rule & block_visible(_mask_slice(block_mask, b, h, hk, H), rows, Sk,
+                                               block_q, block_k)
+            nonempty = vis.any(axis=1)
             S = np.where(vis, scale * (Q[b, h] @ K[b, hk].T), -np.inf)
             m = np.where(nonempty, S.max(axis=1, initial=-np.inf), 0.0)
             E = np.exp(S - m[:, None])
