@@ -171,13 +171,15 @@ def fwd(q, k, v, *, causal=False, window=0, scale=None, num_splits=0, stream=Non
                     num_splits=num_splits, stream=stream, block_mask=block_mask)
 
 
-def bwd(q, k, v, o, lse, do, *, causal=False, window=0, scale=None, stream=None):
+def bwd(q, k, v, o, lse, do, *, causal=False, window=0, scale=None, stream=None,
+        block_mask=None):
     """Backward pass: float32 (dq, dk, dv), the gradients of sum(o * do) for
     o, lse = fwd(q, k, v, ...) with the same arguments; o and do have q's
     shape and dtype. Contiguous tensors go through fa_bwd; views with other
     strides (last dimension contiguous, e.g. token-major storage viewed as
     [B, H, S, D]) through fa_bwd_strided, and the gradients then take the
-    memory layout of q, k and v."""
+    memory layout of q, k and v. A block mask (as for fwd; contiguous tensors)
+    runs fa_bwd_block_sparse."""
     import torch
     _check(q, k, v)
     B, H, Sq, D = q.shape
@@ -206,7 +208,13 @@ def bwd(q, k, v, o, lse, do, *, causal=False, window=0, scale=None, stream=None)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, HKV, Sq, Sk, D)
     tail = (float(scale), int(bool(causal)), int(window), _dtype_code(q), stream.cuda_stream)
-    if dense:
+    if block_mask is not None:
+        if not dense:
+            raise ValueError("block_mask needs contiguous q, k, v, o, do")
+        _check_mask(block_mask, B, H, HKV, Sq, Sk, q)
+        st = lib().fa_bwd_block_sparse(*args, block_mask.data_ptr(), block_mask.shape[0],
+                                       block_mask.shape[1], *tail)
+    elif dense:
         st = lib().fa_bwd(*args, *tail)
     else:
         st3 = [(ctypes.c_longlong * 3)(*t.stride()[:3]) for t in (q, k, v, o, do, dq, dk, dv)]

@@ -36,6 +36,8 @@ SIGNATURES = {
                     _P]),
     "fa_bwd_strided": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                             _P, _P, _P, _P, _P, _P, _P, _P, _F, _I, _I, _I, _P]),
+    "fa_bwd_block_sparse": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                 _P, _I, _I, _F, _I, _I, _I, _P]),
     "fa_plan_splits": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "fa_schedule_table": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),

@@ -47,7 +47,22 @@ struct BwdParams {
   // contiguous [B, heads, S, D] tensors, strides unused.
   int gen, dv;
   long long qs[3], ks[3], vs[3], os[3], dos[3], dqs[3], dks[3], dvs[3];
+  // Block mask (fa_bwd_block_sparse; NULL otherwise): one byte per
+  // (kBwdMaskQ query rows, kBwdMaskK keys) block, contiguous
+  // [mask batch][mask heads][bm_nqb][bm_nkb]; bm_sb / bm_sh are the batch and
+  // head strides in bytes (0 for an axis of extent 1) and bm_by_q says
+  // whether the head axis is indexed by the query head (else the kv head).
+  const unsigned char* bmask;
+  long long bm_sb, bm_sh;
+  int bm_nqb, bm_nkb, bm_by_q;
 };
+
+// Block-mask granularity (the forward's: FA_MASK_BLOCK_Q x FA_MASK_BLOCK_K).
+constexpr int kBwdMaskQ = 128, kBwdMaskK = 64;
+// Longest visible-tile list a masked backward workgroup keeps in LDS: key
+// tiles of a dQ workgroup (chunks of the key axis beyond that), and
+// (query head, 128-row block) pairs of a dK/dV workgroup.
+constexpr int kBwdMaxList = 8192;
 
 // Group shape of the per-row kernels (fp32 inputs, D = 256): lanes per row
 // (a group holds D / lanes elements of each row vector per lane: the fewest

@@ -36,6 +36,7 @@
 #include <stdint.h>
 
 #include "fa_bwd.h"
+#include "fa_bwd_device.h"
 #include "fa_tile.h"
 
 namespace fa {
@@ -107,7 +108,7 @@ template <int D>
 constexpr int rows_per_group() { return bwd_rows_per_group(D); }
 
 // D_i, then dQ_i, for R consecutive query rows (b, h, i0 ..) per 16-lane group.
-template <typename E, int D>
+template <typename E, int D, bool Msk>
 __global__ __launch_bounds__(kBwdThreads)
 void bwd_dq_kernel(BwdParams p) {
   constexpr int G = bwd_lanes_per_row(D), NE = D / G, R = rows_per_group<D>();
@@ -125,10 +126,12 @@ void bwd_dq_kernel(BwdParams p) {
 
   float q[R][NE], go[R][NE], dq[R][NE], Di[R], L2[R];
   int rlo[R], rhi[R];
+  const unsigned char* mrow[R];   // (block mask: each row's mask row)
   int lo = p.Sk, hi = 0;   // union of the rows' visible keys
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int i = i0 + r;
+    if constexpr (Msk) mrow[r] = bwd_mask_row(p, b, h, hk, min(i, p.Sq - 1) / kBwdMaskQ);
     rlo[r] = 0;
     rhi[r] = 0;
     float dd = 0.f;
@@ -192,7 +195,7 @@ void bwd_dq_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const bool in = j >= rlo[r] && j < rhi[r];
+      const bool in = j >= rlo[r] && j < rhi[r] && (!Msk || mrow[r][j / kBwdMaskK] != 0);
       const float pr = in ? __builtin_amdgcn_exp2f(fmaf(s[r], sl, -L2[r])) : 0.f;
       const float ds = pr * (dp[r] - Di[r]);
 #pragma unroll
@@ -218,7 +221,7 @@ void bwd_dq_kernel(BwdParams p) {
 
 // dK_j and dV_j for R consecutive key rows (b, hk, j0 ..) per 16-lane group,
 // over the query heads of kv head hk and the query rows that see each key.
-template <typename E, int D>
+template <typename E, int D, bool Msk>
 __global__ __launch_bounds__(kBwdThreads)
 void bwd_dkdv_kernel(BwdParams p) {
   constexpr int G = bwd_lanes_per_row(D), NE = D / G, R = rows_per_group<D>();
@@ -298,10 +301,11 @@ void bwd_dkdv_kernel(BwdParams p) {
         s[r] = group_sum<G>(s[r]);
         dp[r] = group_sum<G>(dp[r]);
       }
+      const unsigned char* mrow = Msk ? bwd_mask_row(p, b, h, hk, i / kBwdMaskQ) : nullptr;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         // a row that sees key j is not empty, so its LSE is finite
-        const bool in = i >= rlo[r] && i < rhi[r];
+        const bool in = i >= rlo[r] && i < rhi[r] && (!Msk || mrow[(j0 + r) / kBwdMaskK] != 0);
         const float pr = in ? __builtin_amdgcn_exp2f(fmaf(s[r], sl, -Li * kLog2e)) : 0.f;
         const float ds = pr * (dp[r] - Di);
 #pragma unroll
@@ -343,7 +347,7 @@ void bwd_dkdv_kernel(BwdParams p) {
 // conflicts; the tiles take the swizzle that serves both patterns
 // (Bf16Tile::swz_b), so K is copied once. V is read by rows only.
 // D_i = dO_i . O_i is formed here and written for the dK/dV kernel.
-template <typename E, int D, bool Gen>
+template <typename E, int D, bool Gen, bool Msk>
 __global__ __launch_bounds__(kBwdThreads, D <= 128 ? 2 : 1)
 void bwd_dq_mfma_kernel(BwdParams p) {
   constexpr int BN = 32;
@@ -401,7 +405,27 @@ void bwd_dq_mfma_kernel(BwdParams p) {
     hi = min(hi, ((int)blockIdx.y + 1) * p.chunk_q);
   }
   const int t0 = (lo / BN) * BN;
-  const int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
+  const int n_cand = hi > lo ? (hi - t0 + BN - 1) / BN : 0;   // key tiles of the range
+  // block mask: only the tiles whose mask byte is nonzero are copied and
+  // computed, listed in portions of up to kBwdMaxList tiles
+  __shared__ unsigned tlist[Msk ? kBwdMaxList : 1];
+  __shared__ int tsh[2];
+  int n_tiles = n_cand, c_next = n_cand;
+  const unsigned char* mrow = nullptr;
+  if constexpr (Msk) {
+    mrow = bwd_mask_row(p, b, h, hkv, qblk);
+    n_tiles = bwd_build_list(
+        0, n_cand, tlist, tsh, wave, lane,
+        [&](int t) { return mrow[(t0 + t * BN) / kBwdMaskK] != 0; }, [](int t) { return (unsigned)t; },
+        &c_next);
+  }
+  // first key of the t-th tile visited
+  auto tile_kt = [&](int t) {
+    if constexpr (Msk)
+      return t0 + BN * (int)__builtin_amdgcn_readfirstlane(tlist[t]);
+    else
+      return t0 + t * BN;
+  };
 
   const int voff = T::dma_off(64 * wave * T::NIW + lane, kSwzB);
   // general form: each copy instruction's lane offset in full (any row
@@ -440,7 +464,7 @@ void bwd_dq_mfma_kernel(BwdParams p) {
       }
     }
   };
-  if (n_tiles > 0) issue(t0, kbuf0, vbuf0);
+  if (n_tiles > 0) issue(tile_kt(0), kbuf0, vbuf0);
 
   // Q and dO rows as B operands (k-slot (g, e) of step t is dim 16t + 8g + e);
   // D_i from the same dims of O, summed over the two lane halves.
@@ -491,9 +515,9 @@ void bwd_dq_mfma_kernel(BwdParams p) {
   for (int db = 0; db < T::DB; ++db) dq[db] = f32x16{};
 
   auto step = [&](int t, const char* Kc, const char* Vc, char* Kn, char* Vn) __attribute__((always_inline)) {
-    const int kt = t0 + t * BN;
+    const int kt = tile_kt(t);
     wait_dma_and_sync();
-    if (t + 1 < n_tiles) issue(kt + BN, Kn, Vn);
+    if (t + 1 < n_tiles) issue(tile_kt(t + 1), Kn, Vn);
     if (qw >= p.Sq || (p.causal && kt > qw + 31) ||
         (p.window > 0 && kt + BN - 1 < qw - p.window + 1))
       return;
@@ -554,9 +578,19 @@ void bwd_dq_mfma_kernel(BwdParams p) {
     }
   };
 
-  for (int t = 0; t < n_tiles; t += 2) {
-    step(t, kbuf0, vbuf0, kbuf1, vbuf1);
-    if (t + 1 < n_tiles) step(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
+  for (;;) {
+    for (int t = 0; t < n_tiles; t += 2) {
+      step(t, kbuf0, vbuf0, kbuf1, vbuf1);
+      if (t + 1 < n_tiles) step(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
+    }
+    if (c_next >= n_cand) break;
+    if constexpr (Msk) {   // the next portion of the list
+      n_tiles = bwd_build_list(
+          c_next, n_cand, tlist, tsh, wave, lane,
+          [&](int t) { return mrow[(t0 + t * BN) / kBwdMaskK] != 0; },
+          [](int t) { return (unsigned)t; }, &c_next);
+      if (n_tiles > 0) issue(tile_kt(0), kbuf0, vbuf0);
+    }
   }
 
   // lane holds dims 32 db + 8 a + 4 g + (0..3) of row i; a key chunk writes
@@ -592,7 +626,7 @@ void bwd_dq_mfma_kernel(BwdParams p) {
 //   P  = exp2(S |scale| log2 e - LSE log2 e),  dS = P (dP - D)
 //   dV^T += dO^T P,  dK^T += Q^T dS   (A: transposed reads of the dO / Q
 //                                      tiles, B: P / dS packed to the input type)
-template <typename E, int D, bool Gen>
+template <typename E, int D, bool Gen, bool Msk>
 __global__ __launch_bounds__(kBwdThreads, 1)
 void bwd_dkdv_mfma_kernel(BwdParams p) {
   // 64 query rows per copied tile, worked as two independent 32-row halves
@@ -638,7 +672,27 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   if (p.window > 0) r_hi = min(p.Sq, k0 + 128 + p.window - 1);
   const int rt0 = (r_lo / BM) * BM;
   const int n_rt = r_hi > r_lo ? (r_hi - rt0 + BM - 1) / BM : 0;
-  const int n_tiles = n_rt * gh;   // (query head, row tile) pairs
+  const int n_cand = n_rt * gh;   // (query head, row tile) pairs
+  // block mask: only the pairs whose mask byte is nonzero for one of the
+  // block's two key columns are copied, listed in portions of up to
+  // kBwdMaxList entries (query head << 22 | row tile << 2 | a flag per
+  // column); a wavefront computes only where its own column's flag is set
+  __shared__ unsigned tlist[Msk ? kBwdMaxList : 1];
+  __shared__ int tsh[2];
+  const int kb0 = k0 / kBwdMaskK;
+  auto pair_flags = [&](int c) {
+    const int hl = c / n_rt, r0 = rt0 + (c % n_rt) * BM;
+    const unsigned char* m = bwd_mask_row(p, b, hkv * gh + hl, hkv, r0 / kBwdMaskQ);
+    return (m[kb0] != 0 ? 1u : 0u) | (kb0 + 1 < p.bm_nkb && m[kb0 + 1] != 0 ? 2u : 0u);
+  };
+  auto list_portion = [&](int c0, int* next) {
+    return bwd_build_list(
+        c0, n_cand, tlist, tsh, wave, lane, [&](int c) { return pair_flags(c) != 0; },
+        [&](int c) { return (unsigned)(c / n_rt) << 22 | (unsigned)(c % n_rt) << 2 | pair_flags(c); },
+        next);
+  };
+  int n_tiles = n_cand, c_next = n_cand;
+  if constexpr (Msk) n_tiles = list_portion(0, &c_next);
 
   const int voff = T::dma_off(64 * wave * T::NIW + lane, kSwzB);
   // general form (views with strides, head dim dv): each copy instruction's
@@ -695,7 +749,17 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   // and rows of the tile last issued, and the rows of the tile being worked
   // (no divisions per tile)
   int ih = hkv * gh, ir = rt0, cur_r0 = rt0;
+  unsigned cur_fl = 3;   // (block mask: the current pair's column flags)
   const int rt_end = rt0 + n_rt * BM;
+  auto from_list = [&](int t) {   // the cursor at list entry t
+    const unsigned e = __builtin_amdgcn_readfirstlane(tlist[t]);
+    ih = hkv * gh + (int)(e >> 22);
+    ir = rt0 + (int)((e >> 2) & 0xfffffu) * BM;
+    return e & 3u;
+  };
+  if constexpr (Msk)
+    if (n_tiles > 0) cur_fl = from_list(0);
+  cur_r0 = ir;
   if (n_tiles > 0) issue(ih, ir, qbuf0, obuf0, lbuf0);
 
   // K and V rows as B operands (k-slot (g, e) of step t is dim 16t + 8g + e)
@@ -739,18 +803,23 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   auto step = [&](int t, const char* Qc, const char* Oc, const float* Lc, char* Qn, char* On,
                   float* Ln) __attribute__((always_inline)) {
     const int r0 = cur_r0;
+    const unsigned fl = cur_fl;
     wait_dma_and_sync();
     if (t + 1 < n_tiles) {
-      ir += BM;
-      if (ir >= rt_end) {
-        ir = rt0;
-        ++ih;
+      if constexpr (Msk) {
+        cur_fl = from_list(t + 1);
+      } else {
+        ir += BM;
+        if (ir >= rt_end) {
+          ir = rt0;
+          ++ih;
+        }
       }
       issue(ih, ir, Qn, On, Ln);
       cur_r0 = ir;
     }
     if (kw >= p.Sk || (p.causal && r0 + BM - 1 < kw) ||
-        (p.window > 0 && r0 > kw + 31 + p.window - 1))
+        (p.window > 0 && r0 > kw + 31 + p.window - 1) || (Msk && !((fl >> (wave >> 1)) & 1u)))
       return;
     f32x16 sc[NH], dp[NH];
 #pragma unroll
@@ -829,9 +898,20 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
       }
   };
 
-  for (int t = 0; t < n_tiles; t += 2) {
-    step(t, qbuf0, obuf0, lbuf0, qbuf1, obuf1, lbuf1);
-    if (t + 1 < n_tiles) step(t + 1, qbuf1, obuf1, lbuf1, qbuf0, obuf0, lbuf0);
+  for (;;) {
+    for (int t = 0; t < n_tiles; t += 2) {
+      step(t, qbuf0, obuf0, lbuf0, qbuf1, obuf1, lbuf1);
+      if (t + 1 < n_tiles) step(t + 1, qbuf1, obuf1, lbuf1, qbuf0, obuf0, lbuf0);
+    }
+    if (c_next >= n_cand) break;
+    if constexpr (Msk) {   // the next portion of the list
+      n_tiles = list_portion(c_next, &c_next);
+      if (n_tiles > 0) {
+        cur_fl = from_list(0);
+        cur_r0 = ir;
+        issue(ih, ir, qbuf0, obuf0, lbuf0);
+      }
+    }
   }
 
   // lane holds dims DO ob + 32 db + 8 a + 4 g + (0..3) of key j (general
@@ -886,19 +966,23 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   // (MFMA dQ kernels: blockIdx.y = key chunk when p.nch > 1)
   if constexpr (b16_mfma) {
     const dim3 grid((unsigned)((long)p.B * p.H * p.n_qblk), (unsigned)p.nch);
-    if (p.gen)
-      hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D, true>), grid, dim3(kBwdThreads), 0, stream, p);
+    if (p.bmask)
+      hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D, false, true>), grid, dim3(kBwdThreads), 0, stream, p);
+    else if (p.gen)
+      hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D, true, false>), grid, dim3(kBwdThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D, false>), grid, dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D, false, false>), grid, dim3(kBwdThreads), 0, stream, p);
   } else if constexpr (f32_mfma) {
     const hipError_t e0 = launch_bwd_f32_mfma_dq(p, D, stream);
     if (e0 != hipSuccess) return e0;
   } else {
     constexpr int R = rows_per_group<D>(), GPB = kBwdThreads / bwd_lanes_per_row(D);
     const long groups = (long)p.B * p.H * ((p.Sq + R - 1) / R);
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D>),
-                       dim3((unsigned)((groups + GPB - 1) / GPB), (unsigned)p.nch),
-                       dim3(kBwdThreads), 0, stream, p);
+    const dim3 grid((unsigned)((groups + GPB - 1) / GPB), (unsigned)p.nch);
+    if (p.bmask)
+      hipLaunchKernelGGL((bwd_dq_kernel<E, D, true>), grid, dim3(kBwdThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<E, D, false>), grid, dim3(kBwdThreads), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -909,21 +993,26 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   if constexpr (b16_mfma) {
     // (D = 256: two workgroups per key block, one per half of the output dims)
     const long kblocks = (long)p.B * p.HKV * ((p.Sk + 127) / 128) * (D == 256 ? 2 : 1);
-    if (p.gen)
-      hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, true>), dim3((unsigned)kblocks), dim3(kBwdThreads),
-                         0, stream, p);
+    if (p.bmask)
+      hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, false, true>), dim3((unsigned)kblocks),
+                         dim3(kBwdThreads), 0, stream, p);
+    else if (p.gen)
+      hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, true, false>), dim3((unsigned)kblocks),
+                         dim3(kBwdThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, false>), dim3((unsigned)kblocks), dim3(kBwdThreads),
-                         0, stream, p);
+      hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, false, false>), dim3((unsigned)kblocks),
+                         dim3(kBwdThreads), 0, stream, p);
   } else if constexpr (f32_mfma) {
     const hipError_t e0 = launch_bwd_f32_mfma_dkdv(p, D, stream);
     if (e0 != hipSuccess) return e0;
   } else {
     constexpr int R = rows_per_group<D>(), GPB = kBwdThreads / bwd_lanes_per_row(D);
     const long groups = (long)p.B * p.HKV * ((p.Sk + R - 1) / R);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>),
-                       dim3((unsigned)((groups + GPB - 1) / GPB), (unsigned)p.nch),
-                       dim3(kBwdThreads), 0, stream, p);
+    const dim3 grid((unsigned)((groups + GPB - 1) / GPB), (unsigned)p.nch);
+    if (p.bmask)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true>), grid, dim3(kBwdThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false>), grid, dim3(kBwdThreads), 0, stream, p);
   }
   e = hipGetLastError();
   // (the MFMA dK/dV kernels write dK and dV directly; chunks split only the

@@ -1,6 +1,6 @@
 // C ABI of the backward pass: argument checks, the D_i workspace, the staged
 // copies (padded head dims, strided tensors) and the launch. Declared in
-// include/fa.h (fa_bwd, fa_bwd_strided).
+// include/fa.h (fa_bwd, fa_bwd_strided, fa_bwd_block_sparse).
 #include "fa.h"
 
 #include <hip/hip_runtime.h>
@@ -59,15 +59,31 @@ int check_view(const long long st[3], int B, int heads, int S, int D, int esz) {
   return FA_OK;
 }
 
+// Block mask of fa_bwd_block_sparse (NULL for the other entry points).
+struct BwdMask {
+  const unsigned char* mask;
+  int batch, heads;
+};
+
 // The backward pass for views with the given element strides (NULL =
 // contiguous): q, k, v, o, dO in the input type, then dQ, dK, dV (fp32).
 int backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
              const float* LSE, float* dQ, float* dK, float* dV, int B, int H, int HKV, int Sq,
              int Sk, int D, const long long* const given[8], float scale, int causal,
-             int window, int dtype, void* stream_ptr) {
-  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULLPTR;
+             int window, int dtype, void* stream_ptr, const BwdMask* bm = nullptr) {
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV || (bm && !bm->mask))
+    return FA_ERR_NULLPTR;
   int st = check_bwd(B, H, HKV, Sq, Sk, D, causal, window, dtype);
   if (st != FA_OK) return st;
+  if (bm) {
+    // block masks: contiguous tensors at the forward's block-mask head dims
+    if ((bm->batch != 1 && bm->batch != B) ||
+        (bm->heads != 1 && bm->heads != HKV && bm->heads != H))
+      return FA_ERR_MASK;
+    if (D != 64 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
+    // the dK/dV kernels' list entries hold a query head of the group in 10 bits
+    if (H / HKV >= 1024) return FA_ERR_SHAPE;
+  }
   for (const void* p : {Q, K, V, O, dO, (const void*)LSE, (const void*)dQ, (const void*)dK,
                         (const void*)dV})
     if (!aligned16(p)) return FA_ERR_ALIGN;
@@ -113,6 +129,15 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
   p.sl_abs = mag > 1e-30 ? (float)mag : 1e-30f;
   p.n_qblk = (Sq + 127) / 128;
   if ((double)B * H * p.n_qblk > 2147483647.0) return FA_ERR_SHAPE;
+  if (bm) {
+    p.bmask = bm->mask;
+    p.bm_nqb = (Sq + fa::kBwdMaskQ - 1) / fa::kBwdMaskQ;
+    p.bm_nkb = (Sk + fa::kBwdMaskK - 1) / fa::kBwdMaskK;
+    const long long slab = (long long)p.bm_nqb * p.bm_nkb;
+    p.bm_sh = bm->heads == 1 ? 0 : slab;
+    p.bm_sb = bm->batch == 1 ? 0 : bm->heads * slab;
+    p.bm_by_q = bm->heads == H ? 1 : 0;
+  }
   // 16-bit inputs at head dims 16 .. 96 other than 64 run the MFMA kernels of
   // the 64 or 128 tile with the dims from D on held as zeros (they add exact
   // zeros to every dot product, and the gradients' extra dims are not
@@ -264,6 +289,17 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
                       void* stream) {
   return backward(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, HKV, Sq, Sk, D, nullptr, scale, causal,
                   window, dtype, stream);
+}
+
+extern "C" int fa_bwd_block_sparse(const void* Q, const void* K, const void* V, const void* O,
+                                   const void* dO, const float* LSE, float* dQ, float* dK,
+                                   float* dV, int B, int H, int HKV, int Sq, int Sk, int D,
+                                   const unsigned char* block_mask, int mask_batch,
+                                   int mask_heads, float scale, int causal, int window, int dtype,
+                                   void* stream) {
+  const BwdMask bm = {block_mask, mask_batch, mask_heads};
+  return backward(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, HKV, Sq, Sk, D, nullptr, scale, causal,
+                  window, dtype, stream, &bm);
 }
 
 extern "C" int fa_bwd_strided(const void* Q, const void* K, const void* V, const void* O,

@@ -10,6 +10,7 @@
 #include <stdint.h>
 
 #include "fa_bwd.h"
+#include "fa_bwd_device.h"
 #include "fa_tile.h"
 
 namespace fa {
@@ -58,7 +59,7 @@ __device__ __forceinline__ void read_db(const float* p, float (&a)[DB]) {
 
 // dQ (and D_i) for fp32 inputs: 128 query rows per workgroup, K/V tiles of 32
 // keys; S^T = K Q^T, dP^T = V dO^T, dS = P (dP - D_i), dQ^T += K^T dS^T.
-template <int D>
+template <int D, bool Msk>
 __global__ __launch_bounds__(kBwdThreads, D <= 64 ? 2 : 1)
 void bwd_dq_f32_mfma_kernel(BwdParams p) {
   using T = F32BwdTile<D>;
@@ -89,7 +90,28 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
     hi = min(hi, ((int)blockIdx.y + 1) * p.chunk_q);
   }
   const int t0 = (lo / BN) * BN;
-  const int n_tiles = hi > lo ? (hi - t0 + BN - 1) / BN : 0;
+  const int n_cand = hi > lo ? (hi - t0 + BN - 1) / BN : 0;   // key tiles of the range
+  // block mask: only the tiles whose mask byte is nonzero, listed in portions
+  __shared__ unsigned tlist[Msk ? kBwdMaxList : 1];
+  __shared__ int tsh[2];
+  int n_tiles = n_cand, c_next = n_cand;
+  const unsigned char* mrow = nullptr;
+  auto list_portion = [&](int c0) {
+    return bwd_build_list(
+        c0, n_cand, tlist, tsh, wave, lane,
+        [&](int t) { return mrow[(t0 + t * BN) / kBwdMaskK] != 0; }, [](int t) { return (unsigned)t; },
+        &c_next);
+  };
+  if constexpr (Msk) {
+    mrow = bwd_mask_row(p, b, h, hkv, qblk);
+    n_tiles = list_portion(0);
+  }
+  auto tile_kt = [&](int t) {   // first key of the t-th tile visited
+    if constexpr (Msk)
+      return t0 + BN * (int)__builtin_amdgcn_readfirstlane(tlist[t]);
+    else
+      return t0 + t * BN;
+  };
 
   // Q and dO rows (dims t + (D/2) g), D_i over the lane's dims and its partner's
   float qf[T::DH], dof[T::DH];
@@ -132,7 +154,7 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
     }
   };
   if (n_tiles > 0) {
-    load_tile(t0);
+    load_tile(tile_kt(0));
     store_tile(0);
   }
   __syncthreads();
@@ -141,11 +163,12 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < T::DB; ++db) dq[db] = f32x16{};
 
+  for (;;) {
   for (int it = 0; it < n_tiles; ++it) {
-    const int kt = t0 + it * BN;
+    const int kt = tile_kt(it);
     const float* Ks = smem[it & 1][0];
     const float* Vs = smem[it & 1][1];
-    if (it + 1 < n_tiles) load_tile(kt + BN);
+    if (it + 1 < n_tiles) load_tile(tile_kt(it + 1));
     const bool skip = qw >= p.Sq || (p.causal && kt > qw + 31) ||
                       (p.window > 0 && kt + BN - 1 < qw - p.window + 1);
     if (!skip) {
@@ -209,6 +232,16 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
     if (it + 1 < n_tiles) store_tile((it + 1) & 1);
     __syncthreads();
   }
+    if (c_next >= n_cand) break;
+    if constexpr (Msk) {   // the next portion of the list
+      n_tiles = list_portion(c_next);
+      if (n_tiles > 0) {
+        load_tile(tile_kt(0));
+        store_tile(0);
+      }
+      __syncthreads();
+    }
+  }
 
   // element v of block db: dim (D/32)(8 (v / 4) + 4 g + v % 4) + db of row i;
   // a key chunk writes its unscaled partial sums
@@ -241,8 +274,8 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
 // of Q and dO (with the rows' base-2 LSE and D_i) over every query head of
 // the kv head: S = Q K^T, dP = dO V^T, dS = P (dP - D), dV^T += dO^T P,
 // dK^T += Q^T dS.
-template <int D>
-__global__ __launch_bounds__(kBwdThreads, D <= 64 ? 2 : 1)
+template <int D, bool Msk>
+__global__ __launch_bounds__(kBwdThreads, D <= 64 && !Msk ? 2 : 1)   // (masked: the list state spills at two)
 void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
   using T = F32BwdTile<D>;
   constexpr int BM = T::BN;   // query rows per tile
@@ -266,7 +299,39 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
   if (p.window > 0) r_hi = min(p.Sq, k0 + 128 + p.window - 1);
   const int rt0 = (r_lo / BM) * BM;
   const int n_rt = r_hi > r_lo ? (r_hi - rt0 + BM - 1) / BM : 0;
-  const int n_tiles = n_rt * gh;   // (query head, row tile) pairs
+  const int n_cand = n_rt * gh;   // (query head, row tile) pairs
+  // block mask: only the pairs whose mask byte is nonzero for one of the
+  // block's two key columns, listed in portions (query head << 22 | row tile
+  // << 2 | a flag per column); a wavefront computes only under its column's flag
+  __shared__ unsigned tlist[Msk ? kBwdMaxList : 1];
+  __shared__ int tsh[2];
+  const int kb0 = k0 / kBwdMaskK;
+  auto pair_flags = [&](int c) {
+    const int hl = c / n_rt, r0 = rt0 + (c % n_rt) * BM;
+    const unsigned char* m = bwd_mask_row(p, b, hkv * gh + hl, hkv, r0 / kBwdMaskQ);
+    return (m[kb0] != 0 ? 1u : 0u) | (kb0 + 1 < p.bm_nkb && m[kb0 + 1] != 0 ? 2u : 0u);
+  };
+  int n_tiles = n_cand, c_next = n_cand;
+  auto list_portion = [&](int c0) {
+    return bwd_build_list(
+        c0, n_cand, tlist, tsh, wave, lane, [&](int c) { return pair_flags(c) != 0; },
+        [&](int c) { return (unsigned)(c / n_rt) << 22 | (unsigned)(c % n_rt) << 2 | pair_flags(c); },
+        &c_next);
+  };
+  if constexpr (Msk) n_tiles = list_portion(0);
+  // query head, first row and column flags of the t-th pair visited
+  auto tile_at = [&](int t, int& hq, int& r0) {
+    if constexpr (Msk) {
+      const unsigned e = __builtin_amdgcn_readfirstlane(tlist[t]);
+      hq = hkv * gh + (int)(e >> 22);
+      r0 = rt0 + (int)((e >> 2) & 0xfffffu) * BM;
+      return e & 3u;
+    } else {
+      hq = hkv * gh + t / n_rt;
+      r0 = rt0 + (t % n_rt) * BM;
+      return 3u;
+    }
+  };
 
   // K and V rows of key j (dims t + (D/2) g)
   float kf[T::DH], vf[T::DH];
@@ -286,7 +351,8 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
   f32x4 qreg[T::IT], oreg[T::IT];
   float lreg = 0.f;
   auto load_tile = [&](int t) __attribute__((always_inline)) {
-    const int hq = hkv * gh + t / n_rt, r0 = rt0 + (t % n_rt) * BM;
+    int hq, r0;
+    tile_at(t, hq, r0);
     const long base = ((long)b * p.H + hq) * p.Sq;
 #pragma unroll
     for (int it = 0; it < T::IT; ++it) {
@@ -326,15 +392,18 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < T::DB; ++db) dk[db] = dv[db] = f32x16{};
 
+  for (;;) {
   for (int t = 0; t < n_tiles; ++t) {
-    const int r0 = rt0 + (t % n_rt) * BM;
+    int hq_unused, r0;
+    const unsigned fl = tile_at(t, hq_unused, r0);
     const float* Qs = smem[t & 1][0];
     const float* Os = smem[t & 1][1];
     const float* Ls = lds_l[t & 1][0];
     const float* Dl = lds_l[t & 1][1];
     if (t + 1 < n_tiles) load_tile(t + 1);
     const bool skip = kw >= p.Sk || (p.causal && r0 + BM - 1 < kw) ||
-                      (p.window > 0 && r0 > kw + 31 + p.window - 1);
+                      (p.window > 0 && r0 > kw + 31 + p.window - 1) ||
+                      (Msk && !((fl >> (wave >> 1)) & 1u));
     if (!skip) {
       f32x16 s = f32x16{}, dp = f32x16{};
       const float* qrow = Qs + l32 * T::LD + T::DH * g;
@@ -403,6 +472,16 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
     if (t + 1 < n_tiles) store_tile((t + 1) & 1);
     __syncthreads();
   }
+    if (c_next >= n_cand) break;
+    if constexpr (Msk) {   // the next portion of the list
+      n_tiles = list_portion(c_next);
+      if (n_tiles > 0) {
+        load_tile(0);
+        store_tile(0);
+      }
+      __syncthreads();
+    }
+  }
 
   // element v of block db: dim (D/32)(8 (v / 4) + 4 g + v % 4) + db of key j
   if (key_ok) {
@@ -433,17 +512,21 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
 
 template <int D>
 static hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_dq_f32_mfma_kernel<D>),
-                     dim3((unsigned)((long)p.B * p.H * p.n_qblk), (unsigned)p.nch),
-                     dim3(kBwdThreads), 0, stream, p);
+  const dim3 grid((unsigned)((long)p.B * p.H * p.n_qblk), (unsigned)p.nch);
+  if (p.bmask)
+    hipLaunchKernelGGL((bwd_dq_f32_mfma_kernel<D, true>), grid, dim3(kBwdThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((bwd_dq_f32_mfma_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
-  const long kblocks = (long)p.B * p.HKV * ((p.Sk + 127) / 128);
-  hipLaunchKernelGGL((bwd_dkdv_f32_mfma_kernel<D>), dim3((unsigned)kblocks), dim3(kBwdThreads),
-                     0, stream, p);
+  const dim3 grid((unsigned)((long)p.B * p.HKV * ((p.Sk + 127) / 128)));
+  if (p.bmask)
+    hipLaunchKernelGGL((bwd_dkdv_f32_mfma_kernel<D, true>), grid, dim3(kBwdThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_f32_mfma_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -244,7 +244,8 @@ int fa_schedule_table(int B, int H, int HKV, int Sq, int Sk, int D,
  *   D, scale, causal, window, dtype: as for fa_fwd; rows with LSE = -inf (no
  *   visible key) get dQ = 0 and contribute nothing.
  *
- * Contiguous tensors only; no block mask. All buffers 16-byte aligned. A
+ * Contiguous tensors only (block masks: fa_bwd_block_sparse). All buffers
+ * 16-byte aligned. A
  * [B, H, Sq] float32 workspace comes from the library's stream-ordered memory
  * pool (the one fa_release trims). For bf16/fp16 inputs at D = 16, 32, 48,
  * 80 or 96 the work runs on copies of Q, K, V, O, dO (and of the fp32
@@ -290,6 +291,32 @@ int fa_bwd_strided(const void* Q, const void* K, const void* V, const void* O, c
                    const long long* do_strides, const long long* dq_strides,
                    const long long* dk_strides, const long long* dv_strides,
                    float scale, int causal, int window, int dtype, void* stream);
+
+/*
+ * fa_bwd_block_sparse - fa_bwd for O and LSE from fa_fwd_block_sparse with the
+ * same arguments: the gradients of sum(O * dO) under the block mask (the
+ * programmable block masks of the metal-flash-attention README,
+ * "Modifications to FlashAttention", through the backward kernels of the
+ * forge flash_attention.metal page).
+ *
+ *   block_mask, mask_batch, mask_heads: as for fa_fwd_block_sparse (device
+ *               bytes [mask_batch][mask_heads][ceil(Sq / FA_MASK_BLOCK_Q)]
+ *               [ceil(Sk / FA_MASK_BLOCK_K)], contiguous; batch axis 1 or B,
+ *               head axis 1, HKV or H)
+ *
+ * A pair (i, j) contributes only where the causal and window rules allow it
+ * AND the mask byte of its block is nonzero; query and key blocks whose byte
+ * is 0 are neither read nor computed, and keys no row sees get dK = dV = 0.
+ * Contiguous tensors, D = 64, 128 or 256, H / HKV < 1024; other arguments,
+ * workspace and errors as fa_bwd, plus FA_ERR_NULLPTR for a NULL mask and
+ * FA_ERR_MASK for other mask axis sizes. The mask is read by the kernels on
+ * `stream` (it must stay valid until they complete) and is not modified.
+ */
+int fa_bwd_block_sparse(const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const float* LSE, float* dQ, float* dK, float* dV,
+                        int B, int H, int HKV, int Sq, int Sk, int D,
+                        const unsigned char* block_mask, int mask_batch, int mask_heads,
+                        float scale, int causal, int window, int dtype, void* stream);
 
 /* fa_status_string - static, human-readable text for a status code. */
 const char* fa_status_string(int status);

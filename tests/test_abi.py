@@ -224,6 +224,35 @@ def test_bwd_argument_errors(over, code):
     assert call_bwd(**over) == code
 
 
+def call_bwd_sparse(ptrs=(A,) * 9, mask=A, mb=1, mh=1, **over):
+    a = dict(GOOD, **over)
+    return _lib.lib().fa_bwd_block_sparse(*ptrs, a["B"], a["H"], a["HKV"], a["Sq"], a["Sk"],
+                                          a["D"], mask, mb, mh, a["scale"], a["causal"],
+                                          a["window"], a["dtype"], None)
+
+
+def test_bwd_block_sparse_null_pointers():
+    assert call_bwd_sparse(mask=None) == 1
+    for which in range(9):
+        ptrs = [A] * 9
+        ptrs[which] = None
+        assert call_bwd_sparse(tuple(ptrs)) == 1
+
+
+@pytest.mark.parametrize("mb,mh", [(2, 1), (0, 1), (1, 3), (1, 0), (1, 8)])
+def test_bwd_block_sparse_bad_mask_axes(mb, mh):
+    # GOOD: B = 1, H = 4, HKV = 2
+    assert call_bwd_sparse(mb=mb, mh=mh) == 12
+
+
+def test_bwd_block_sparse_shape_errors():
+    assert call_bwd_sparse(D=40) == 4
+    assert call_bwd_sparse(D=96) == 4      # block masks: D = 64, 128 or 256
+    assert call_bwd_sparse(D=32, dtype=0) == 4
+    assert call_bwd_sparse(H=4, HKV=3) == 3
+    assert call_bwd_sparse(H=2048, HKV=2, mh=1) == 2   # a kv head's query heads: fewer than 1024
+
+
 @pytest.mark.parametrize("os_", [
     (4 * 64 * 128, 64 * 128, 128),         # contiguous [B, H, S, D]
     (64 * 4 * 128, 128, 4 * 128),          # token-major [B, S, H, D]
