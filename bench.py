@@ -122,23 +122,25 @@ def device_inputs(inp, torch):
 
 
 def bench_backward(args, wl, inp, q, k, v, torch, fa):
-    """Time the backward pass; prints one JSON line."""
-    if inp.block_mask is not None or wl.layout != "bhsd":
-        print("the backward pass takes contiguous tensors without a block mask", file=sys.stderr)
-        sys.exit(2)
+    """Time the backward pass (fa_bwd; fa_bwd_strided on token-major workloads,
+    fa_bwd_block_sparse under a block mask); prints one JSON line."""
     stream = torch.cuda.current_stream()
     scale = wl.scale()
-    o, lse = fa.fwd(q, k, v, causal=bool(wl.causal), window=wl.window, scale=scale)
+    bmask = W.device_mask(inp, torch, "cuda")
+    o, lse = fa.fwd(q, k, v, causal=bool(wl.causal), window=wl.window, scale=scale,
+                    block_mask=bmask)
     g, bits = W.make_grad_output(inp)
     if bits is not None:
         tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float16
-        do = torch.from_numpy(bits.view(np.int16)).view(tdt).cuda()
+        src = torch.from_numpy(bits.view(np.int16)).view(tdt)
     else:
-        do = torch.from_numpy(g).cuda()
+        src = torch.from_numpy(g)
+    do = torch.empty_like(o)        # o's layout: token-major workloads stay token-major
+    do.copy_(src.cuda())
 
     def step():
         fa.bwd(q, k, v, o, lse, do, causal=bool(wl.causal), window=wl.window, scale=scale,
-               stream=stream)
+               stream=stream, block_mask=bmask)
 
     for _ in range(args.warmup):
         step()
@@ -159,7 +161,7 @@ def bench_backward(args, wl, inp, q, k, v, torch, fa):
     ev_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     per_step = per_step_events(step, stream, 20)
-    flops = 2.5 * counted_flops(wl)          # 10 D per visible pair
+    flops = 2.5 * counted_flops(wl, inp.block_mask)          # 10 D per visible pair
     # MFMA backward kernels: 16-bit inputs (head dims other than 64, 128 and
     # 256 on zero-padded copies) and fp32 inputs at D = 32, 64, 96, 128; the
     # rest (fp32 D = 16, 48, 80, 256) run the per-row VALU kernels
@@ -175,7 +177,9 @@ def bench_backward(args, wl, inp, q, k, v, torch, fa):
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "pass": "bwd", "B": wl.B, "H": wl.H, "HKV": wl.HKV,
                    "Sq": wl.Sq, "Sk": wl.Sk, "D": wl.D, "causal": wl.causal,
-                   "window": wl.window, "counted_flops": flops, "parallelism": "single GPU"},
+                   "window": wl.window, "layout": wl.layout,
+                   "block_mask": None if inp.block_mask is None else list(inp.block_mask.shape),
+                   "counted_flops": flops, "parallelism": "single GPU"},
         "roofline": {"bound": bound, "achieved": round(flops / (ev_ms * 1e-3) / 1e12, 3),
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": round(flops / (ev_ms * 1e-3) / 1e12 / peak, 4),
@@ -187,11 +191,14 @@ def bench_backward(args, wl, inp, q, k, v, torch, fa):
         from oracle import attention_backward
         gsz = wl.H // wl.HKV
         sl = W.small(wl, B=1, H=gsz, HKV=1)
+        m = inp.block_mask
+        if m is not None:   # the slice's mask: batch 0, the group's heads
+            m = m[:1, :gsz] if m.shape[1] == wl.H else m[:1, :1]
         t1 = time.perf_counter()
         attention_backward(inp.q[:1, :gsz], inp.k[:1, :1], inp.v[:1, :1], g[:1, :gsz],
-                           scale, bool(wl.causal), wl.window)
+                           scale, bool(wl.causal), wl.window, block_mask=m)
         dt = time.perf_counter() - t1
-        rec["cpu_baseline"] = {"value": round(2.5 * counted_flops(sl) / dt / 1e12, 6),
+        rec["cpu_baseline"] = {"value": round(2.5 * counted_flops(sl, m) / dt / 1e12, 6),
                                "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)),
                                "kind": "oracle",
                                "sample": f"batch 0, kv head 0 and its {gsz} query heads, fp64 "
