@@ -416,7 +416,8 @@ void bwd_dq_mfma_kernel(BwdParams p) {
     mrow = bwd_mask_row(p, b, h, hkv, qblk);
     n_tiles = bwd_build_list(
         0, n_cand, tlist, tsh, wave, lane,
-        [&](int t) { return mrow[(t0 + t * BN) / kBwdMaskK] != 0; }, [](int t) { return (unsigned)t; },
+        [&](int t) { return mrow[(t0 + t * BN) / kBwdMaskK] != 0 ? 1u : 0u; },
+        [](int t, unsigned) { return (unsigned)t; },
         &c_next);
   }
   // first key of the t-th tile visited
@@ -587,8 +588,8 @@ void bwd_dq_mfma_kernel(BwdParams p) {
     if constexpr (Msk) {   // the next portion of the list
       n_tiles = bwd_build_list(
           c_next, n_cand, tlist, tsh, wave, lane,
-          [&](int t) { return mrow[(t0 + t * BN) / kBwdMaskK] != 0; },
-          [](int t) { return (unsigned)t; }, &c_next);
+          [&](int t) { return mrow[(t0 + t * BN) / kBwdMaskK] != 0 ? 1u : 0u; },
+          [](int t, unsigned) { return (unsigned)t; }, &c_next);
       if (n_tiles > 0) issue(tile_kt(0), kbuf0, vbuf0);
     }
   }
@@ -687,8 +688,8 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   };
   auto list_portion = [&](int c0, int* next) {
     return bwd_build_list(
-        c0, n_cand, tlist, tsh, wave, lane, [&](int c) { return pair_flags(c) != 0; },
-        [&](int c) { return (unsigned)(c / n_rt) << 22 | (unsigned)(c % n_rt) << 2 | pair_flags(c); },
+        c0, n_cand, tlist, tsh, wave, lane, pair_flags,
+        [&](int c, unsigned f) { return (unsigned)(c / n_rt) << 22 | (unsigned)(c % n_rt) << 2 | f; },
         next);
   };
   int n_tiles = n_cand, c_next = n_cand;

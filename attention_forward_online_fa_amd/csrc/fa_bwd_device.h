@@ -16,24 +16,34 @@ __device__ __forceinline__ const unsigned char* bwd_mask_row(const BwdParams& p,
   return p.bmask + b * p.bm_sb + (p.bm_by_q ? h : hkv) * p.bm_sh + (long long)qb * p.bm_nkb;
 }
 
-// Block masks: the candidates c in [c0, n) for which vis(c) holds go, in
-// order, to list[] as entry(c), until the list is full (kBwdMaxList
-// entries); wave 0 scans 64 candidates per round with a ballot. Returns the
-// count (uniform) and sets *next to the first candidate not scanned (n once
-// every candidate was). sh is two ints of LDS.
+// Block masks: the candidates c in [c0, n) with nonzero flags vis(c) go, in
+// order, to list[] as entry(c, flags), until the list is full (kBwdMaxList
+// entries); wave 0 scans 64 candidates per ballot round, with the mask reads
+// of four rounds in flight at once. Returns the count (uniform) and sets
+// *next to the first candidate not scanned (n once every candidate was). sh
+// is two ints of LDS.
 template <typename Vis, typename Ent>
 __device__ __forceinline__ int bwd_build_list(int c0, int n, unsigned* list, int* sh, int wave,
                                               int lane, Vis vis, Ent entry, int* next) {
+  constexpr int kAhead = 4;
   __syncthreads();   // the previous list's readers are done with it
   if (wave == 0) {
     int cnt = 0, c = c0;
     while (c < n && cnt + 64 <= kBwdMaxList) {
-      const int t = c + lane;
-      const bool v = t < n && vis(t);
-      const unsigned long long bal = __ballot(v);
-      if (v) list[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = entry(t);
-      cnt += __popcll(bal);
-      c += 64;
+      unsigned f[kAhead];
+#pragma unroll
+      for (int r = 0; r < kAhead; ++r) {
+        const int t = c + 64 * r + lane;
+        f[r] = t < n ? vis(t) : 0u;
+      }
+#pragma unroll
+      for (int r = 0; r < kAhead; ++r) {
+        if (c >= n || cnt + 64 > kBwdMaxList) break;
+        const unsigned long long bal = __ballot(f[r] != 0u);
+        if (f[r] != 0u) list[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = entry(c + lane, f[r]);
+        cnt += __popcll(bal);
+        c += 64;
+      }
     }
     if (lane == 0) {
       sh[0] = cnt;

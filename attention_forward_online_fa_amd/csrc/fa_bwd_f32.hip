@@ -99,7 +99,8 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
   auto list_portion = [&](int c0) {
     return bwd_build_list(
         c0, n_cand, tlist, tsh, wave, lane,
-        [&](int t) { return mrow[(t0 + t * BN) / kBwdMaskK] != 0; }, [](int t) { return (unsigned)t; },
+        [&](int t) { return mrow[(t0 + t * BN) / kBwdMaskK] != 0 ? 1u : 0u; },
+        [](int t, unsigned) { return (unsigned)t; },
         &c_next);
   };
   if constexpr (Msk) {
@@ -314,8 +315,8 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
   int n_tiles = n_cand, c_next = n_cand;
   auto list_portion = [&](int c0) {
     return bwd_build_list(
-        c0, n_cand, tlist, tsh, wave, lane, [&](int c) { return pair_flags(c) != 0; },
-        [&](int c) { return (unsigned)(c / n_rt) << 22 | (unsigned)(c % n_rt) << 2 | pair_flags(c); },
+        c0, n_cand, tlist, tsh, wave, lane, pair_flags,
+        [&](int c, unsigned f) { return (unsigned)(c / n_rt) << 22 | (unsigned)(c % n_rt) << 2 | f; },
         &c_next);
   };
   if constexpr (Msk) n_tiles = list_portion(0);
