@@ -1,6 +1,7 @@
 """GPU parity over seeded random configurations of every forward entry point
 (contiguous, strided and block-sparse, with forced or automatic key splits)
-and of the backward pass, against the fp64 oracle.
+and of every backward entry point (the same three forms), against the fp64
+oracle.
 
 Each case draws dtype, head dim (any supported one), batch, heads and GQA group, query and key
 lengths (ragged, Sq != Sk), causal and window flags, the split count, the
@@ -66,15 +67,69 @@ def test_random_forward(seed):
     compare(host64(o), host64(lse), O, L, TOL[wl.dtype], wl.name)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_backward(seed):
+    # the three backward entry points: fa_bwd (contiguous), fa_bwd_strided
+    # (token-major views, gradients in the same layout), fa_bwd_block_sparse
+    # (a random mask with a random axis form)
     import attention_forward_online_fa_amd as fa
     c = draw(5000 + seed)
     Sq, Sk = min(c["Sq"], 200), min(c["Sk"], 200)
     wl = wl_small(c["dtype"], c["B"], c["H"], c["HKV"], Sq, Sk, c["D"], c["causal"],
                   c["window"], name=f"randbwd{seed}", seed=300 + seed)
     inp = W.make_inputs(wl)
-    print(f"[random] backward seed {seed}: {wl}", flush=True)
+    print(f"[random] backward seed {seed}: {c['kind']} {wl}", flush=True)
+    q, k, v = to_device(inp)
+    g, bits = W.make_grad_output(inp)
+    if bits is not None:
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float16
+        src = torch.from_numpy(bits.view(np.int16)).view(tdt)
+    else:
+        src = torch.from_numpy(g)
+    mask = None
+    if c["kind"] == "strided":
+        q, k, v = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v))
+    elif c["kind"] == "sparse":
+        r = c["rng"]
+        mB = [1, wl.B][r.integers(2)]
+        mH = [1, wl.HKV, wl.H][r.integers(3)]
+        nqb, nkb = -(-wl.Sq // W.MASK_BLOCK_Q), -(-wl.Sk // W.MASK_BLOCK_K)
+        mask = (r.random((mB, mH, nqb, nkb)) < r.uniform(0.2, 0.9)).astype(np.uint8)
+    m = None if mask is None else torch.from_numpy(mask).cuda()
+    o, lse = fa.fwd(q, k, v, causal=bool(wl.causal), window=wl.window, scale=wl.scale(),
+                    block_mask=m)
+    do = torch.empty_like(o)      # o's layout
+    do.copy_(src.cuda())
+    got = fa.bwd(q, k, v, o, lse, do, causal=bool(wl.causal), window=wl.window,
+                 scale=wl.scale(), block_mask=m)
+    torch.cuda.synchronize()
+    ref = attention_backward(inp.q, inp.k, inp.v, g, wl.scale(), bool(wl.causal), wl.window,
+                             block_mask=mask)
+    for name, x, r in zip(("dQ", "dK", "dV"), got, ref):
+        x = host64(x)
+        err = float(np.abs(x - r).max()) if r.size else 0.0
+        tol = BWD_TOL[wl.dtype] * max(1.0, float(np.abs(r).max()) if r.size else 1.0)
+        print(f"  {name}: max|d|={err:.3e} (tol {tol:.3e})", flush=True)
+        assert np.all(np.isfinite(x)) and err <= tol, f"{name}: {err:.3e} > {tol:.3e}"
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_backward_block_mask(seed):
+    # fa_bwd_block_sparse on random shapes (the block-mask head dims), masks
+    # of random density and axis form, causal and window flags
+    import attention_forward_online_fa_amd as fa
+    c = draw(7000 + seed)
+    r = c["rng"]
+    D = [64, 128, 256][r.integers(3)]
+    Sq, Sk = min(c["Sq"] + 100, 400), min(c["Sk"] + 100, 500)
+    wl = wl_small(c["dtype"], c["B"], c["H"], c["HKV"], Sq, Sk, D, c["causal"], c["window"],
+                  name=f"randbwdmask{seed}", seed=400 + seed)
+    inp = W.make_inputs(wl)
+    mB = [1, wl.B][r.integers(2)]
+    mH = [1, wl.HKV, wl.H][r.integers(3)]
+    nqb, nkb = -(-Sq // W.MASK_BLOCK_Q), -(-Sk // W.MASK_BLOCK_K)
+    mask = (r.random((mB, mH, nqb, nkb)) < r.uniform(0.2, 0.9)).astype(np.uint8)
+    print(f"[random] masked backward seed {seed}: {wl} mask {mask.shape}", flush=True)
     q, k, v = to_device(inp)
     g, bits = W.make_grad_output(inp)
     if bits is not None:
@@ -82,14 +137,17 @@ def test_random_backward(seed):
         do = torch.from_numpy(bits.view(np.int16)).view(tdt).cuda()
     else:
         do = torch.from_numpy(g).cuda()
-    o, lse = fa.fwd(q, k, v, causal=bool(wl.causal), window=wl.window, scale=wl.scale())
+    m = torch.from_numpy(mask).cuda()
+    o, lse = fa.fwd(q, k, v, causal=bool(wl.causal), window=wl.window, scale=wl.scale(),
+                    block_mask=m)
     got = fa.bwd(q, k, v, o, lse, do, causal=bool(wl.causal), window=wl.window,
-                 scale=wl.scale())
+                 scale=wl.scale(), block_mask=m)
     torch.cuda.synchronize()
-    ref = attention_backward(inp.q, inp.k, inp.v, g, wl.scale(), bool(wl.causal), wl.window)
-    for name, x, r in zip(("dQ", "dK", "dV"), got, ref):
+    ref = attention_backward(inp.q, inp.k, inp.v, g, wl.scale(), bool(wl.causal), wl.window,
+                             block_mask=mask)
+    for name, x, rr in zip(("dQ", "dK", "dV"), got, ref):
         x = host64(x)
-        err = float(np.abs(x - r).max()) if r.size else 0.0
-        tol = BWD_TOL[wl.dtype] * max(1.0, float(np.abs(r).max()) if r.size else 1.0)
+        err = float(np.abs(x - rr).max())
+        tol = BWD_TOL[wl.dtype] * max(1.0, float(np.abs(rr).max()))
         print(f"  {name}: max|d|={err:.3e} (tol {tol:.3e})", flush=True)
         assert np.all(np.isfinite(x)) and err <= tol, f"{name}: {err:.3e} > {tol:.3e}"
