@@ -31,7 +31,11 @@
 //   G = 32).
 // On small grids the per-row kernels run each group's range in chunks
 // (blockIdx.y), and the MFMA dQ kernels the key axis in chunks, whose partial
-// sums sum_parts_kernel adds in chunk order.
+// sums sum_parts_kernel adds in chunk order. Under a block mask (the block
+// masks of the metal-flash-attention README, "Modifications to
+// FlashAttention"; Msk instances of every kernel) each MFMA workgroup first
+// lists the tiles its mask leaves visible (bwd_build_list) and copies and
+// computes only those; the per-row kernels test the mask byte per pair.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -1,5 +1,6 @@
 /*
- * fa.h - fused attention forward pass for AMD Instinct MI355X (gfx950).
+ * fa.h - fused attention forward pass (and its backward pass) for AMD
+ * Instinct MI355X (gfx950).
  *
  * Computes, for every query row i of every (batch b, query head h):
  *
@@ -21,6 +22,11 @@
  * header comment of the boostr flash.wgsl shader. The online-softmax
  * recurrence (running max m, running sum l, rescale by exp(m_old - m_new))
  * is the one in the forge header comment; nothing of size Sq x Sk is stored.
+ *
+ * Entry points: the forward pass (fa_fwd, fa_fwd_ex, fa_fwd_strided,
+ * fa_fwd_block_sparse, fa_fwd_noalloc) and its backward pass (fa_bwd,
+ * fa_bwd_strided, fa_bwd_block_sparse), with fa_plan_splits,
+ * fa_schedule_table, fa_status_string and fa_release.
  *
  * The library is plain C ABI: no HIP or torch types in any signature.
  */
