@@ -714,17 +714,26 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
       po_off[k] = 8 * ck < p.dv ? r * (int)(2 * dor) + 16 * ck : kBwdOutOfRange;
     }
   }
-  auto issue = [&](int h, int r0, char* qd, char* od, float* ld) {
-    const long base = ((long)b * p.H + h) * p.Sq;
-    // the tile rows' base-2 LSE (wave 0) and D (wave 1), loaded first
-    const int r = r0 + lane;
-    float x = 0.f;
-    if (wave == 0) {
-      x = r < p.Sq ? p.LSE[base + r] * 1.4426950408889634f : INFINITY;
-      if (x == -INFINITY) x = INFINITY;   // a row with no visible key: P = 0
-    } else if (wave == 1) {
-      x = r < p.Sq ? p.Dws[base + r] : 0.f;
+  // the tile rows' LSE (wave 0) and D (wave 1): loaded into xl with the
+  // tile's copies and written to LDS by store_l at the start of the step that
+  // works the tile, after the wait for those copies (converted there too, so
+  // that no instruction waits for the load while the previous tile is worked)
+  float xl = 0.f;
+  auto store_l = [&](float* ld) __attribute__((always_inline)) {
+    if (wave < 2 && lane < BM) {
+      float x = xl;
+      if (wave == 0) {
+        x *= 1.4426950408889634f;             // base 2
+        if (x == -INFINITY) x = INFINITY;     // a row with no visible key: P = 0
+      }
+      ld[wave * BM + lane] = x;
     }
+  };
+  auto issue = [&](int h, int r0, char* qd, char* od) {
+    const long base = ((long)b * p.H + h) * p.Sq;
+    const int r = r0 + lane;
+    if (wave == 0) xl = r < p.Sq ? p.LSE[base + r] : INFINITY;
+    else if (wave == 1) xl = r < p.Sq ? p.Dws[base + r] : 0.f;
     if constexpr (Gen) {
       const E* qb = (const E*)p.Q + b * p.qs[0] + h * p.qs[1] + r0 * qr;
       const E* ob = (const E*)p.dO + b * p.dos[0] + h * p.dos[1] + r0 * dor;
@@ -748,7 +757,6 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
         dma16(ob, bytes, voff ^ T::dma_xor(k, kSwzB), od + off);
       }
     }
-    if (wave < 2 && lane < BM) ld[wave * BM + lane] = x;
   };
   // tiles in (query head, row tile) order, followed by a cursor: the head
   // and rows of the tile last issued, and the rows of the tile being worked
@@ -765,7 +773,7 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   if constexpr (Msk)
     if (n_tiles > 0) cur_fl = from_list(0);
   cur_r0 = ir;
-  if (n_tiles > 0) issue(ih, ir, qbuf0, obuf0, lbuf0);
+  if (n_tiles > 0) issue(ih, ir, qbuf0, obuf0);
 
   // K and V rows as B operands (k-slot (g, e) of step t is dim 16t + 8g + e)
   e16x8 kf[T::DC], vf[T::DC];
@@ -805,11 +813,14 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < DBO; ++db) dk[db] = dv[db] = f32x16{};
 
-  auto step = [&](int t, const char* Qc, const char* Oc, const float* Lc, char* Qn, char* On,
-                  float* Ln) __attribute__((always_inline)) {
+  auto step = [&](int t, const char* Qc, const char* Oc, float* Lc, char* Qn, char* On)
+      __attribute__((always_inline)) {
     const int r0 = cur_r0;
     const unsigned fl = cur_fl;
-    wait_dma_and_sync();
+    // (Lc was last read two steps back, before the previous step's barrier)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    store_l(Lc);
+    __syncthreads();
     if (t + 1 < n_tiles) {
       if constexpr (Msk) {
         cur_fl = from_list(t + 1);
@@ -820,7 +831,7 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
           ++ih;
         }
       }
-      issue(ih, ir, Qn, On, Ln);
+      issue(ih, ir, Qn, On);
       cur_r0 = ir;
     }
     if (kw >= p.Sk || (p.causal && r0 + BM - 1 < kw) ||
@@ -905,8 +916,8 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
 
   for (;;) {
     for (int t = 0; t < n_tiles; t += 2) {
-      step(t, qbuf0, obuf0, lbuf0, qbuf1, obuf1, lbuf1);
-      if (t + 1 < n_tiles) step(t + 1, qbuf1, obuf1, lbuf1, qbuf0, obuf0, lbuf0);
+      step(t, qbuf0, obuf0, lbuf0, qbuf1, obuf1);
+      if (t + 1 < n_tiles) step(t + 1, qbuf1, obuf1, lbuf1, qbuf0, obuf0);
     }
     if (c_next >= n_cand) break;
     if constexpr (Msk) {   // the next portion of the list
@@ -914,7 +925,7 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
       if (n_tiles > 0) {
         cur_fl = from_list(0);
         cur_r0 = ir;
-        issue(ih, ir, qbuf0, obuf0, lbuf0);
+        issue(ih, ir, qbuf0, obuf0);
       }
     }
   }

@@ -348,6 +348,7 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
     }
   }
   const float sl = p.scale * kLog2e;
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   f32x4 qreg[T::IT], oreg[T::IT];
   float lreg = 0.f;
@@ -363,15 +364,13 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
       qreg[it] = ok ? *(const f32x4*)((const float*)p.Q + off) : f32x4{};
       oreg[it] = ok ? *(const f32x4*)((const float*)p.dO + off) : f32x4{};
     }
-    // the tile rows' base-2 LSE (threads 0 .. 31) and D (threads 32 .. 63)
+    // the tile rows' LSE (threads 0 .. 31) and D (threads 32 .. 63), taken
+    // to base 2 by store_tile (converting here would wait for the load, and
+    // with it for every copy of the tile, before the current tile is worked)
     if (tid < 2 * BM) {
       const int r = r0 + (tid & (BM - 1));
-      if (tid < BM) {
-        float x = r < p.Sq ? p.LSE[base + r] * kLog2e : INFINITY;
-        lreg = x == -INFINITY ? INFINITY : x;   // a row with no visible key: P = 0
-      } else {
-        lreg = r < p.Sq ? p.Dws[base + r] : 0.f;
-      }
+      if (tid < BM) lreg = r < p.Sq ? p.LSE[base + r] : INFINITY;
+      else lreg = r < p.Sq ? p.Dws[base + r] : 0.f;
     }
   };
   auto store_tile = [&](int st) __attribute__((always_inline)) {
@@ -381,7 +380,14 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
       *(f32x4*)(&smem[st][0][r * T::LD + 4 * c4]) = qreg[it];
       *(f32x4*)(&smem[st][1][r * T::LD + 4 * c4]) = oreg[it];
     }
-    if (tid < 2 * BM) lds_l[st][tid / BM][tid & (BM - 1)] = lreg;
+    if (tid < 2 * BM) {
+      float x = lreg;
+      if (tid < BM) {
+        x *= kLog2e;
+        if (x == -INFINITY) x = INFINITY;   // a row with no visible key: P = 0
+      }
+      lds_l[st][tid / BM][tid & (BM - 1)] = x;
+    }
   };
   if (n_tiles > 0) {
     load_tile(0);
