@@ -348,6 +348,10 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
     }
   }
   const float sl = p.scale * kLog2e;
+  // vmcnt(0): the K/V loads land here. Left to the compiler, the wait for them
+  // sat before the loop's first MFMA, where it also waited for the next tile's
+  // register loads issued just before (the compiler's count merges the
+  // loop-entry and back-edge paths).
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   f32x4 qreg[T::IT], oreg[T::IT];
