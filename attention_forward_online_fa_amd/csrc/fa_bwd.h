@@ -33,12 +33,17 @@ struct BwdParams {
   // in chunks of chunk_q keys (dQ) or chunk_k query rows (dK/dV), partial sums
   // to part_q [nch][B H Sq][D] and part_k, part_v [nch][B HKV Sk][D]. MFMA
   // dQ kernels: key chunk c = [c chunk_q, (c + 1) chunk_q) (chunk_q a
-  // multiple of the 32-key tile), partial sums to part_q; their dK/dV
-  // kernels never split.
+  // multiple of the 32-key tile), partial sums to part_q.
   int nch, chunk_q, chunk_k;
   float* part_q;
   float* part_k;
   float* part_v;
+  // MFMA dK/dV kernels on small grids (contiguous tensors):
+  // the query rows are cut into nrc chunks [c chunk_r, (c + 1) chunk_r) (chunk_r
+  // a multiple of 128), one per blockIdx.y, each writing unscaled dK and dV
+  // partial sums to part_k / part_v [nrc][B HKV Sk][D], added up in chunk order
+  // afterwards (nrc = 1: dK and dV written directly).
+  int nrc, chunk_r;
   // General form of the 16-bit MFMA kernels (gen = 1): the tensors are views
   // with these element strides (batch, head, row; the head dim contiguous),
   // Q, K, V, O, dO in the input type and dQ, dK, dV in fp32, with head dim

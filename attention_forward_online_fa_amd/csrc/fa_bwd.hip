@@ -671,10 +671,19 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   const bool key_ok = j < p.Sk;
   const long krow = ((long)b * p.HKV + hkv) * p.Sk + j;
 
-  // query rows [r_lo, r_hi) that see some key of the block
+  // query rows [r_lo, r_hi) that see some key of the block (small grids:
+  // within the workgroup's row chunk rc, whose bounds are multiples of 128, so
+  // that no row tile straddles two chunks)
   int r_lo = 0, r_hi = p.Sq;
   if (p.causal) r_lo = min(k0, p.Sq);
   if (p.window > 0) r_hi = min(p.Sq, k0 + 128 + p.window - 1);
+  // (chunks in reverse, so that under a causal mask the latest rows, which
+  // see the most key blocks, are dispatched first)
+  const int rc = p.nrc - 1 - (int)blockIdx.y;
+  if (p.nrc > 1) {
+    r_lo = max(r_lo, rc * p.chunk_r);
+    r_hi = min(r_hi, (rc + 1) * p.chunk_r);
+  }
   const int rt0 = (r_lo / BM) * BM;
   const int n_rt = r_hi > r_lo ? (r_hi - rt0 + BM - 1) / BM : 0;
   const int n_cand = n_rt * gh;   // (query head, row tile) pairs
@@ -931,18 +940,26 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   }
 
   // lane holds dims DO ob + 32 db + 8 a + 4 g + (0..3) of key j (general
-  // form: views with strides p.dks / p.dvs, written in their first dv dims)
+  // form: views with strides p.dks / p.dvs, written in their first dv dims;
+  // row chunks: the unscaled partial sums of chunk rc)
   if (key_ok) {
-    float* odk = (Gen ? p.dK + b * p.dks[0] + hkv * p.dks[1] + j * p.dks[2] : p.dK + krow * D) + DO * ob;
-    float* odv = (Gen ? p.dV + b * p.dvs[0] + hkv * p.dvs[1] + j * p.dvs[2] : p.dV + krow * D) + DO * ob;
-    const int dlim = (Gen ? p.dv : D) - DO * ob;
+    const bool part = p.nrc > 1;   // (contiguous rows of D dims, general form too)
+    const long po = (long)rc * p.B * p.HKV * p.Sk * D;
+    float* odk = (part  ? p.part_k + po + krow * D
+                  : Gen ? p.dK + b * p.dks[0] + hkv * p.dks[1] + j * p.dks[2]
+                        : p.dK + krow * D) + DO * ob;
+    float* odv = (part  ? p.part_v + po + krow * D
+                  : Gen ? p.dV + b * p.dvs[0] + hkv * p.dvs[1] + j * p.dvs[2]
+                        : p.dV + krow * D) + DO * ob;
+    const int dlim = (Gen && !part ? p.dv : D) - DO * ob;
+    const float ks = part ? 1.f : p.scale;
 #pragma unroll
     for (int db = 0; db < DBO; ++db)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         if (32 * db + 8 * a + 4 * g >= dlim) continue;
-        const f32x4 k4 = {dk[db][4 * a] * p.scale, dk[db][4 * a + 1] * p.scale,
-                          dk[db][4 * a + 2] * p.scale, dk[db][4 * a + 3] * p.scale};
+        const f32x4 k4 = {dk[db][4 * a] * ks, dk[db][4 * a + 1] * ks,
+                          dk[db][4 * a + 2] * ks, dk[db][4 * a + 3] * ks};
         const f32x4 v4 = {dv[db][4 * a], dv[db][4 * a + 1], dv[db][4 * a + 2], dv[db][4 * a + 3]};
         *(f32x4*)(odk + 32 * db + 8 * a + 4 * g) = k4;
         *(f32x4*)(odv + 32 * db + 8 * a + 4 * g) = v4;
@@ -1007,17 +1024,19 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if constexpr (b16_mfma) {
-    // (D = 256: two workgroups per key block, one per half of the output dims)
+    // (D = 256: two workgroups per key block, one per half of the output dims;
+    // blockIdx.y: row chunk nrc - 1 - y when p.nrc > 1)
     const long kblocks = (long)p.B * p.HKV * ((p.Sk + 127) / 128) * (D == 256 ? 2 : 1);
+    const dim3 grid((unsigned)kblocks, (unsigned)p.nrc);
     if (p.bmask)
-      hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, false, true>), dim3((unsigned)kblocks),
-                         dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, false, true>), grid, dim3(kBwdThreads), 0,
+                         stream, p);
     else if (p.gen)
-      hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, true, false>), dim3((unsigned)kblocks),
-                         dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, true, false>), grid, dim3(kBwdThreads), 0,
+                         stream, p);
     else
-      hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, false, false>), dim3((unsigned)kblocks),
-                         dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, false, false>), grid, dim3(kBwdThreads), 0,
+                         stream, p);
   } else if constexpr (f32_mfma) {
     const hipError_t e0 = launch_bwd_f32_mfma_dkdv(p, D, stream);
     if (e0 != hipSuccess) return e0;
@@ -1031,13 +1050,14 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
       hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false>), grid, dim3(kBwdThreads), 0, stream, p);
   }
   e = hipGetLastError();
-  // (the MFMA dK/dV kernels write dK and dV directly; chunks split only the
-  // per-row kernels' key ranges)
-  if (e != hipSuccess || p.nch == 1 || b16_mfma || f32_mfma) return e;
+  // partial dK and dV sums: the per-row kernels' key chunks (p.nch), the MFMA
+  // kernels' row chunks (p.nrc)
+  const int nparts = b16_mfma || f32_mfma ? p.nrc : p.nch;
+  if (e != hipSuccess || nparts == 1) return e;
   const long nk = (long)p.B * p.HKV * p.Sk * D;
-  e = sum_parts(p.part_k, p.dK, nk, p.nch, p.scale, stream);
+  e = sum_parts(p.part_k, p.dK, nk, nparts, p.scale, stream);
   if (e != hipSuccess) return e;
-  return sum_parts(p.part_v, p.dV, nk, p.nch, 1.f, stream);
+  return sum_parts(p.part_v, p.dV, nk, nparts, 1.f, stream);
 }
 
 template <typename E>

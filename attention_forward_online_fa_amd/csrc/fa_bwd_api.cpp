@@ -163,7 +163,7 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
   // padded Q, O, dO, K, V (input type) and dQ, dK, dV (fp32) at DT
   const size_t b_d = up(nq * sizeof(float));
   const size_t b_q = staged ? up(nq * DT * esz) : 0, b_k = staged ? up(nk * DT * esz) : 0;
-  const size_t b_gk = staged ? up(nk * DT * 4) : 0;
+  size_t b_gk = staged ? up(nk * DT * 4) : 0;   // (and the general form's row chunks)
   size_t b_gq = staged ? up(nq * DT * 4) : 0;   // (the general form's key chunks also use it)
   // The per-row kernels (fp32 inputs at D = 16, 48, 80 and 256) on grids too small to fill the
   // GPU: each row group's range is cut into nch chunks that run side by side
@@ -208,19 +208,50 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
   }
   if (gen && p.nch > 1) b_gq = up(nq * DT * 4);   // summed dQ before it goes to the view
   const bool per_row = dtype == FA_F32 && !fa::bwd_f32_mfma(D);
+  // MFMA dK/dV kernels: when their workgroups fill less than twice the GPU's
+  // slots (one per CU; two for fp32 at D <= 64) and a workgroup's walk is long
+  // (Sq rows of each of its H / HKV query heads, fp32 counted four times for
+  // its slower products: at least 4096; shorter walks gain less than the
+  // partial sums cost), cut the query rows into chunks of whole 128-row
+  // blocks (a causal grid is otherwise as long as its first key blocks, which
+  // see every row): at most 8, workspace at most 512 MiB. The partial sums are contiguous rows; views (the general form)
+  // get the summed dK and dV from contiguous rows too. A block mask's 128-row
+  // blocks never straddle two chunks, so the same chunks serve it (and an
+  // all-ones mask keeps the dense sums bit for bit).
+  p.nrc = 1;
+  p.chunk_r = Sq;
+  if (!per_row) {
+    const int cus = fa::device_cus();
+    if (cus <= 0) return FA_ERR_HIP;
+    const long wgs = (long)B * HKV * ((Sk + 127) / 128) * (dtype != FA_F32 && DT == 256 ? 2 : 1);
+    const long slots = (long)cus * (dtype == FA_F32 && DT <= 64 ? 2 : 1);
+    const long blocks = (Sq + 127) / 128;
+    const long walk = (long)Sq * (H / HKV) * (dtype == FA_F32 ? 4 : 1);
+    if (wgs < 2 * slots && walk >= 4096) {
+      long n = std::min({(2 * slots + wgs - 1) / wgs, blocks, 8L});
+      while (n > 1 && 2.0 * n * nk * DT * 4 > 512.0 * (1 << 20)) --n;
+      if (n > 1) {
+        p.chunk_r = (int)((blocks + n - 1) / n) * 128;
+        p.nrc = (int)((Sq + p.chunk_r - 1) / p.chunk_r);
+      }
+    }
+  }
+  if (gen && p.nrc > 1) b_gk = up(nk * DT * 4);   // summed dK, dV before they go to the views
   const size_t b_pq = p.nch > 1 ? up((size_t)p.nch * nq * DT * 4) : 0;
-  const size_t b_pk = p.nch > 1 && per_row ? up((size_t)p.nch * nk * D * 4) : 0;
+  const size_t b_pk = p.nch > 1 && per_row ? up((size_t)p.nch * nk * D * 4)
+                      : p.nrc > 1          ? up((size_t)p.nrc * nk * DT * 4)
+                                           : 0;
   void* ws = nullptr;
   const int wst = fa::library_workspace(b_d + 3 * b_q + 2 * b_k + b_gq + 2 * b_gk + b_pq + 2 * b_pk,
                                         stream, &ws);
   if (wst != FA_OK) return wst;
   char* w = static_cast<char*>(ws);
   p.Dws = reinterpret_cast<float*>(w);
-  if (p.nch > 1) {
+  if (p.nch > 1 || p.nrc > 1) {
     char* pp = w + b_d + 3 * b_q + 2 * b_k + b_gq + 2 * b_gk;
-    p.part_q = reinterpret_cast<float*>(pp);
-    p.part_k = reinterpret_cast<float*>(pp + b_pq);
-    p.part_v = reinterpret_cast<float*>(pp + b_pq + b_pk);
+    p.part_q = p.nch > 1 ? reinterpret_cast<float*>(pp) : nullptr;
+    p.part_k = b_pk ? reinterpret_cast<float*>(pp + b_pq) : nullptr;
+    p.part_v = b_pk ? reinterpret_cast<float*>(pp + b_pq + b_pk) : nullptr;
   }
   hipError_t e = hipSuccess;
   if (staged) {
@@ -265,15 +296,24 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
     std::copy(vs[5], vs[5] + 3, p.dqs);
     std::copy(vs[6], vs[6] + 3, p.dks);
     std::copy(vs[7], vs[7] + 3, p.dvs);
-    // with key chunks the chunk sum lands in contiguous rows first
-    float* gq = p.nch > 1 ? reinterpret_cast<float*>(w + b_d + 3 * b_q + 2 * b_k) : nullptr;
+    // with key chunks (dQ) or row chunks (dK, dV) the chunk sums land in
+    // contiguous rows first
+    char* g0 = w + b_d + 3 * b_q + 2 * b_k;
+    float* gq = p.nch > 1 ? reinterpret_cast<float*>(g0) : nullptr;
+    float* gk = p.nrc > 1 ? reinterpret_cast<float*>(g0 + b_gq) : nullptr;
+    float* gv = p.nrc > 1 ? reinterpret_cast<float*>(g0 + b_gq + b_gk) : nullptr;
     if (gq) p.dQ = gq;
-    e = fa::launch_backward(p, dtype, DT, stream);
-    if (e == hipSuccess && gq) {
-      long long bs[3];
-      for (int a = 0; a < 3; ++a) bs[a] = vs[5][a] * 4;
-      e = fa::launch_scatter_rows(gq, dQ, B, H, Sq, bs, DT, D, stream);
+    if (gk) {
+      p.dK = gk;
+      p.dV = gv;
     }
+    e = fa::launch_backward(p, dtype, DT, stream);
+    long long bs[3][3];   // byte strides of the dQ, dK, dV views
+    for (int t = 0; t < 3; ++t)
+      for (int a = 0; a < 3; ++a) bs[t][a] = vs[5 + t][a] * 4;
+    if (e == hipSuccess && gq) e = fa::launch_scatter_rows(gq, dQ, B, H, Sq, bs[0], DT, D, stream);
+    if (e == hipSuccess && gk) e = fa::launch_scatter_rows(gk, dK, B, HKV, Sk, bs[1], DT, D, stream);
+    if (e == hipSuccess && gv) e = fa::launch_scatter_rows(gv, dV, B, HKV, Sk, bs[2], DT, D, stream);
   } else {
     e = fa::launch_backward(p, dtype, D, stream);
   }

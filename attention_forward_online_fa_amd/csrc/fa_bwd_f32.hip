@@ -294,10 +294,18 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
   const bool key_ok = j < p.Sk;
   const long krow = ((long)b * p.HKV + hkv) * p.Sk + j;
 
-  // query rows [r_lo, r_hi) that see some key of the block
+  // query rows [r_lo, r_hi) that see some key of the block (small grids:
+  // within the workgroup's row chunk rc, bounds multiples of 128)
   int r_lo = 0, r_hi = p.Sq;
   if (p.causal) r_lo = min(k0, p.Sq);
   if (p.window > 0) r_hi = min(p.Sq, k0 + 128 + p.window - 1);
+  // (chunks in reverse, so that under a causal mask the latest rows, which
+  // see the most key blocks, are dispatched first)
+  const int rc = p.nrc - 1 - (int)blockIdx.y;
+  if (p.nrc > 1) {
+    r_lo = max(r_lo, rc * p.chunk_r);
+    r_hi = min(r_hi, (rc + 1) * p.chunk_r);
+  }
   const int rt0 = (r_lo / BM) * BM;
   const int n_rt = r_hi > r_lo ? (r_hi - rt0 + BM - 1) / BM : 0;
   const int n_cand = n_rt * gh;   // (query head, row tile) pairs
@@ -495,17 +503,21 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
   }
 
   // element v of block db: dim (D/32)(8 (v / 4) + 4 g + v % 4) + db of key j
+  // (row chunks: the unscaled partial sums of chunk rc)
   if (key_ok) {
-    float* odk = p.dK + krow * D;
-    float* odv = p.dV + krow * D;
+    const bool part = p.nrc > 1;
+    const long po = (long)rc * p.B * p.HKV * p.Sk * D;
+    float* odk = (part ? p.part_k + po : p.dK) + krow * D;
+    float* odv = (part ? p.part_v + po : p.dV) + krow * D;
+    const float ks = part ? 1.f : p.scale;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int m = T::DB * (8 * (v >> 2) + 4 * g + (v & 3));
       if constexpr (T::DB % 4 == 0) {
 #pragma unroll
         for (int c4 = 0; c4 < T::DB / 4; ++c4) {
-          const f32x4 k4 = {dk[4 * c4][v] * p.scale, dk[4 * c4 + 1][v] * p.scale,
-                            dk[4 * c4 + 2][v] * p.scale, dk[4 * c4 + 3][v] * p.scale};
+          const f32x4 k4 = {dk[4 * c4][v] * ks, dk[4 * c4 + 1][v] * ks,
+                            dk[4 * c4 + 2][v] * ks, dk[4 * c4 + 3][v] * ks};
           const f32x4 v4 = {dv[4 * c4][v], dv[4 * c4 + 1][v], dv[4 * c4 + 2][v], dv[4 * c4 + 3][v]};
           *(f32x4*)(odk + m + 4 * c4) = k4;
           *(f32x4*)(odv + m + 4 * c4) = v4;
@@ -513,7 +525,7 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
       } else {
 #pragma unroll
         for (int db = 0; db < T::DB; ++db) {
-          odk[m + db] = dk[db][v] * p.scale;
+          odk[m + db] = dk[db][v] * ks;
           odv[m + db] = dv[db][v];
         }
       }
@@ -533,7 +545,8 @@ static hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
 
 template <int D>
 static hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((long)p.B * p.HKV * ((p.Sk + 127) / 128)));
+  // (blockIdx.y: row chunk nrc - 1 - y when p.nrc > 1)
+  const dim3 grid((unsigned)((long)p.B * p.HKV * ((p.Sk + 127) / 128)), (unsigned)p.nrc);
   if (p.bmask)
     hipLaunchKernelGGL((bwd_dkdv_f32_mfma_kernel<D, true>), grid, dim3(kBwdThreads), 0, stream, p);
   else

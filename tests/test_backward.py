@@ -109,6 +109,21 @@ CASES += [
 ]
 
 
+# small grids whose dK/dV workgroups walk long row ranges (Sq x H / HKV, fp32
+# counted four times, at least 4096): the MFMA dK/dV kernels cut the query
+# rows into chunks of 128-row blocks whose partial sums are added in chunk
+# order (causal, windowed, non-causal with Sq > Sk, ragged Sq, the general
+# form of a padded head dim, D = 256 with two output halves, fp32)
+CASES += [
+    ("bf16", 1, 4, 1, 1100, 700, 64, 0, 0),
+    ("f16", 1, 8, 2, 1040, 1040, 128, 1, 200),
+    ("bf16", 1, 8, 2, 1030, 1030, 96, 1, 0),
+    ("bf16", 1, 4, 2, 2100, 2100, 256, 1, 0),
+    ("f32", 1, 4, 1, 600, 600, 128, 1, 0),
+    ("f32", 1, 2, 2, 1300, 500, 32, 0, 0),
+]
+
+
 @pytest.mark.parametrize("case", CASES, ids=["-".join(map(str, c)) for c in CASES])
 def test_backward_matches_oracle(case):
     wl = wl_small(*case, seed=sum(case[1:]) + 3)

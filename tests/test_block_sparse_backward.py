@@ -66,6 +66,9 @@ CASES = [
     ("f32", 1, 4, 2, 300, 500, 64, 1, 0, "1", "kv"),
     ("f32", 2, 2, 1, 260, 390, 128, 0, 200, "B", "q"),
     ("f32", 1, 2, 1, 190, 330, 256, 1, 0, "1", "1"),    # fp32 D = 256: the per-row kernels
+    # small grids with long row walks: dK/dV row chunks under the mask
+    ("bf16", 1, 8, 2, 1100, 1100, 128, 0, 0, "1", "kv"),
+    ("f32", 1, 4, 1, 700, 700, 64, 1, 0, "1", "q"),
 ]
 
 
@@ -84,14 +87,16 @@ def test_masked_backward_matches_oracle(case, density):
     check(wl, got, ref)
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64), ("bf16", 256)])
-def test_all_ones_mask_equals_dense_backward(dtype, D):
-    # every block visible: the same gradients as fa_bwd, bit for bit
+@pytest.mark.parametrize("dtype,D,Sq", [("bf16", 128, 300), ("f32", 64, 300), ("bf16", 256, 300),
+                                        ("bf16", 128, 1100), ("f32", 64, 1100)])
+def test_all_ones_mask_equals_dense_backward(dtype, D, Sq):
+    # every block visible: the same gradients as fa_bwd, bit for bit (Sq =
+    # 1100: both with dK/dV row chunks)
     import attention_forward_online_fa_amd as fa
-    wl = wl_small(dtype, 1, 4, 2, 300, 400, D, 1, 0, seed=21)
+    wl = wl_small(dtype, 1, 8 if Sq > 1000 else 4, 2, Sq, 400, D, 1, 0, seed=21)
     q, k, v = to_device(W.make_inputs(wl))
     _, do = grad_output(wl, q, 1)
-    ones = torch.ones(1, 1, 3, 7, dtype=torch.uint8, device="cuda")
+    ones = torch.ones(1, 1, -(-Sq // 128), 7, dtype=torch.uint8, device="cuda")
     o, lse = fa.fwd(q, k, v, causal=True)
     a = fa.bwd(q, k, v, o, lse, do, causal=True)
     b = fa.bwd(q, k, v, o, lse, do, causal=True, block_mask=ones)
@@ -118,14 +123,21 @@ def test_unseen_keys_and_empty_rows_get_zero_gradients(dtype):
 def test_dkdv_list_in_portions():
     # one key block seen by 16 query heads x 625 row tiles = 10000 pairs, more
     # than a dK/dV workgroup's list holds (8192): the list is built and worked
-    # in two portions
-    wl = wl_small("bf16", 1, 16, 1, 40000, 64, 64, 0, 0, seed=23)
+    # in two portions. 1024 dK/dV key blocks, so that the grid is too large
+    # for row chunks (and the forward's 2048-tile list still holds the key
+    # axis); only the first 64 keys are visible, so the oracle takes those
+    # alone, and every other key must get dK = dV = 0 exactly
+    Sk = 1024 * 128
+    wl = wl_small("bf16", 1, 16, 1, 40000, Sk, 64, 0, 0, seed=23)
     inp = W.make_inputs(wl)
-    mask = np.ones((1, 1, -(-40000 // 128), 1), dtype=np.uint8)
+    mask = np.zeros((1, 1, -(-40000 // 128), Sk // 64), dtype=np.uint8)
+    mask[0, 0, :, 0] = 1
     mask[0, 0, 7::11, 0] = 0
-    got, dO = masked_grads(wl, inp, mask)
-    ref = attention_backward(inp.q, inp.k, inp.v, dO, wl.scale(), False, 0, block_mask=mask)
-    check(wl, got, ref)
+    (dq, dk, dv), dO = masked_grads(wl, inp, mask)
+    assert np.all(dk[:, :, 64:] == 0) and np.all(dv[:, :, 64:] == 0)
+    ref = attention_backward(inp.q, inp.k[:, :, :64], inp.v[:, :, :64], dO, wl.scale(), False, 0,
+                             block_mask=mask[:, :, :, :1])
+    check(wl, (dq, dk[:, :, :64], dv[:, :, :64]), ref)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

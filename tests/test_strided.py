@@ -165,6 +165,10 @@ BWD_CASES = [
     ("f16", 1, 2, 1, 130, 170, 256, 1, 0),
     ("bf16", 1, 2, 1, 130, 2200, 128, 0, 0),   # key chunks of the dQ kernel on views
     ("f16", 1, 4, 2, 200, 300, 48, 1, 0),      # head dim 48 (the 64 tile) on views
+    # row chunks of the dK/dV kernels on views: the chunk sums go to
+    # contiguous rows, then into the dK / dV views
+    ("bf16", 1, 8, 2, 1030, 1030, 128, 1, 0),
+    ("f32", 1, 4, 1, 600, 600, 64, 1, 100),
 ]
 
 
