@@ -208,27 +208,29 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
   }
   if (gen && p.nch > 1) b_gq = up(nq * DT * 4);   // summed dQ before it goes to the view
   const bool per_row = dtype == FA_F32 && !fa::bwd_f32_mfma(D);
-  // MFMA dK/dV kernels: when their workgroups fill less than twice the GPU's
-  // slots (one per CU; two for fp32 at D <= 64) and a workgroup's walk is long
-  // (Sq rows of each of its H / HKV query heads, fp32 counted four times for
-  // its slower products: at least 4096; shorter walks gain less than the
-  // partial sums cost), cut the query rows into chunks of whole 128-row
-  // blocks (a causal grid is otherwise as long as its first key blocks, which
-  // see every row): at most 8, workspace at most 512 MiB. The partial sums are contiguous rows; views (the general form)
-  // get the summed dK and dV from contiguous rows too. A block mask's 128-row
-  // blocks never straddle two chunks, so the same chunks serve it (and an
-  // all-ones mask keeps the dense sums bit for bit).
+  // MFMA dK/dV kernels: when their workgroups fill less than the GPU's slots
+  // (one per CU; two for fp32 at D <= 64; fp32 counts the slots twice) and a
+  // workgroup's walk is long (Sq rows of each of its H / HKV query heads: at
+  // least 2048, fp32 1024; shorter walks gain less than the partial sums
+  // cost), cut the query rows into chunks of whole 128-row blocks (a causal
+  // grid is otherwise as long as its first key blocks, which see every row):
+  // as many as fill the (doubled) slots, at most 8, workspace at most 512 MiB.
+  // The partial sums are contiguous rows; views (the general form) get the
+  // summed dK and dV from contiguous rows too. A block mask's 128-row blocks
+  // never straddle two chunks, so the same chunks serve it (and an all-ones
+  // mask keeps the dense sums bit for bit).
   p.nrc = 1;
   p.chunk_r = Sq;
   if (!per_row) {
     const int cus = fa::device_cus();
     if (cus <= 0) return FA_ERR_HIP;
     const long wgs = (long)B * HKV * ((Sk + 127) / 128) * (dtype != FA_F32 && DT == 256 ? 2 : 1);
-    const long slots = (long)cus * (dtype == FA_F32 && DT <= 64 ? 2 : 1);
+    const bool f32 = dtype == FA_F32;
+    const long target = (long)cus * (f32 && DT <= 64 ? 2 : 1) * (f32 ? 2 : 1);
     const long blocks = (Sq + 127) / 128;
-    const long walk = (long)Sq * (H / HKV) * (dtype == FA_F32 ? 4 : 1);
-    if (wgs < 2 * slots && walk >= 4096) {
-      long n = std::min({(2 * slots + wgs - 1) / wgs, blocks, 8L});
+    const long walk = (long)Sq * (H / HKV);
+    if (wgs < target && walk >= (f32 ? 1024 : 2048)) {
+      long n = std::min({(target + wgs - 1) / wgs, blocks, 8L});
       while (n > 1 && 2.0 * n * nk * DT * 4 > 512.0 * (1 << 20)) --n;
       if (n > 1) {
         p.chunk_r = (int)((blocks + n - 1) / n) * 128;
