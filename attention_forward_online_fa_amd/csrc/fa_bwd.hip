@@ -967,12 +967,21 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   }
 }
 
-// out = scale * sum over c < nch of part[c] (n4 float4 per part), in chunk order.
+// out = scale * sum over c < nch of part[c] (n4 float4 per part), in chunk
+// order; blockIdx.y = 1 does the same for (part1, out1, scale1) (dK and dV in
+// one launch).
 __global__ __launch_bounds__(256) void sum_parts_kernel(const float4* __restrict__ part,
-                                                        float4* __restrict__ out, long n4, int nch,
-                                                        float scale) {
+                                                        float4* __restrict__ out, float scale,
+                                                        const float4* __restrict__ part1,
+                                                        float4* __restrict__ out1, float scale1,
+                                                        long n4, int nch) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= n4) return;
+  if (blockIdx.y == 1) {
+    part = part1;
+    out = out1;
+    scale = scale1;
+  }
   float4 acc = part[idx];
   for (int c = 1; c < nch; ++c) {
     const float4 x = part[c * n4 + idx];
@@ -984,11 +993,13 @@ __global__ __launch_bounds__(256) void sum_parts_kernel(const float4* __restrict
   out[idx] = make_float4(acc.x * scale, acc.y * scale, acc.z * scale, acc.w * scale);
 }
 
-static hipError_t sum_parts(const float* part, float* out, long n, int nch, float scale,
-                            hipStream_t stream) {
+// One reduction (part1 == nullptr) or two of the same size.
+static hipError_t sum_parts(const float* part, float* out, float scale, const float* part1,
+                            float* out1, float scale1, long n, int nch, hipStream_t stream) {
   const long n4 = n / 4;
-  hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                     (const float4*)part, (float4*)out, n4, nch, scale);
+  const dim3 grid((unsigned)((n4 + 255) / 256), part1 ? 2u : 1u);
+  hipLaunchKernelGGL(sum_parts_kernel, grid, dim3(256), 0, stream, (const float4*)part,
+                     (float4*)out, scale, (const float4*)part1, (float4*)out1, scale1, n4, nch);
   return hipGetLastError();
 }
 
@@ -1020,7 +1031,8 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.nch > 1) {
-    e = sum_parts(p.part_q, p.dQ, (long)p.B * p.H * p.Sq * D, p.nch, p.scale, stream);
+    e = sum_parts(p.part_q, p.dQ, p.scale, nullptr, nullptr, 0.f, (long)p.B * p.H * p.Sq * D,
+                  p.nch, stream);
     if (e != hipSuccess) return e;
   }
   if constexpr (b16_mfma) {
@@ -1055,9 +1067,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const int nparts = b16_mfma || f32_mfma ? p.nrc : p.nch;
   if (e != hipSuccess || nparts == 1) return e;
   const long nk = (long)p.B * p.HKV * p.Sk * D;
-  e = sum_parts(p.part_k, p.dK, nk, nparts, p.scale, stream);
-  if (e != hipSuccess) return e;
-  return sum_parts(p.part_v, p.dV, nk, nparts, 1.f, stream);
+  return sum_parts(p.part_k, p.dK, p.scale, p.part_v, p.dV, 1.f, nk, nparts, stream);
 }
 
 template <typename E>
