@@ -967,21 +967,29 @@ void bwd_dkdv_mfma_kernel(BwdParams p) {
   }
 }
 
-// out = scale * sum over c < nch of part[c] (n4 float4 per part), in chunk
-// order; blockIdx.y = 1 does the same for (part1, out1, scale1) (dK and dV in
-// one launch).
-__global__ __launch_bounds__(256) void sum_parts_kernel(const float4* __restrict__ part,
-                                                        float4* __restrict__ out, float scale,
-                                                        const float4* __restrict__ part1,
-                                                        float4* __restrict__ out1, float scale1,
-                                                        long n4, int nch) {
+// Chunk sums: out = scale * sum over c < nch of part[c] (n4 float4 per part),
+// in chunk order, for up to three tensors (dQ, dK, dV) in one launch, one per
+// blockIdx.y.
+struct SumJob {
+  const float4* part;
+  float4* out;
+  float scale;
+  long n4;
+  int nch;
+};
+struct SumJobs {
+  SumJob j[3];
+};
+
+__global__ __launch_bounds__(256) void sum_parts_kernel(SumJobs jobs) {
+  const SumJob& jb = jobs.j[blockIdx.y];
+  const float4* __restrict__ part = jb.part;
+  float4* __restrict__ out = jb.out;
+  const float scale = jb.scale;
+  const long n4 = jb.n4;
+  const int nch = jb.nch;
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= n4) return;
-  if (blockIdx.y == 1) {
-    part = part1;
-    out = out1;
-    scale = scale1;
-  }
   float4 acc = part[idx];
   for (int c = 1; c < nch; ++c) {
     const float4 x = part[c * n4 + idx];
@@ -993,13 +1001,13 @@ __global__ __launch_bounds__(256) void sum_parts_kernel(const float4* __restrict
   out[idx] = make_float4(acc.x * scale, acc.y * scale, acc.z * scale, acc.w * scale);
 }
 
-// One reduction (part1 == nullptr) or two of the same size.
-static hipError_t sum_parts(const float* part, float* out, float scale, const float* part1,
-                            float* out1, float scale1, long n, int nch, hipStream_t stream) {
-  const long n4 = n / 4;
-  const dim3 grid((unsigned)((n4 + 255) / 256), part1 ? 2u : 1u);
-  hipLaunchKernelGGL(sum_parts_kernel, grid, dim3(256), 0, stream, (const float4*)part,
-                     (float4*)out, scale, (const float4*)part1, (float4*)out1, scale1, n4, nch);
+// The jobs' reductions (n floats each, nch > 1) in one launch; none: nothing.
+static hipError_t sum_parts(const SumJobs& jobs, int njobs, hipStream_t stream) {
+  if (njobs == 0) return hipSuccess;
+  long n4 = 0;
+  for (int t = 0; t < njobs; ++t) n4 = n4 > jobs.j[t].n4 ? n4 : jobs.j[t].n4;
+  const dim3 grid((unsigned)((n4 + 255) / 256), (unsigned)njobs);
+  hipLaunchKernelGGL(sum_parts_kernel, grid, dim3(256), 0, stream, jobs);
   return hipGetLastError();
 }
 
@@ -1030,11 +1038,6 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.nch > 1) {
-    e = sum_parts(p.part_q, p.dQ, p.scale, nullptr, nullptr, 0.f, (long)p.B * p.H * p.Sq * D,
-                  p.nch, stream);
-    if (e != hipSuccess) return e;
-  }
   if constexpr (b16_mfma) {
     // (D = 256: two workgroups per key block, one per half of the output dims;
     // blockIdx.y: row chunk nrc - 1 - y when p.nrc > 1)
@@ -1062,12 +1065,22 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
       hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false>), grid, dim3(kBwdThreads), 0, stream, p);
   }
   e = hipGetLastError();
-  // partial dK and dV sums: the per-row kernels' key chunks (p.nch), the MFMA
-  // kernels' row chunks (p.nrc)
+  if (e != hipSuccess) return e;
+  // the chunk sums, after both kernels, in one launch: dQ over its key chunks
+  // (p.nch), dK and dV over the per-row kernels' key chunks (p.nch) or the
+  // MFMA kernels' row chunks (p.nrc)
+  SumJobs jobs = {};
+  int njobs = 0;
+  if (p.nch > 1)
+    jobs.j[njobs++] = {(const float4*)p.part_q, (float4*)p.dQ, p.scale, (long)p.B * p.H * p.Sq * D / 4,
+                       p.nch};
   const int nparts = b16_mfma || f32_mfma ? p.nrc : p.nch;
-  if (e != hipSuccess || nparts == 1) return e;
-  const long nk = (long)p.B * p.HKV * p.Sk * D;
-  return sum_parts(p.part_k, p.dK, p.scale, p.part_v, p.dV, 1.f, nk, nparts, stream);
+  if (nparts > 1) {
+    const long nk4 = (long)p.B * p.HKV * p.Sk * D / 4;
+    jobs.j[njobs++] = {(const float4*)p.part_k, (float4*)p.dK, p.scale, nk4, nparts};
+    jobs.j[njobs++] = {(const float4*)p.part_v, (float4*)p.dV, 1.f, nk4, nparts};
+  }
+  return sum_parts(jobs, njobs, stream);
 }
 
 template <typename E>
