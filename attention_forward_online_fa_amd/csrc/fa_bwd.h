@@ -76,8 +76,9 @@ constexpr int kBwdMaxList = 8192;
 constexpr int bwd_lanes_per_row(int D) { return D <= 32 ? 4 : D <= 64 ? 8 : D <= 128 ? 16 : 32; }
 constexpr int bwd_rows_per_group(int D) { return bwd_lanes_per_row(D) == 16 ? 4 : 2; }
 
-// fp32 inputs at these head dims run the MFMA backward kernels (fp32 at 16,
-// 48, 80 and 256 the per-row kernels); 16-bit inputs always run MFMA kernels.
+// fp32 inputs at these head dims run the MFMA backward kernels (16, 48 and 80
+// staged into the 32, 64, 96 tiles when the work is large, else the per-row
+// kernels, as at 256); 16-bit inputs always run MFMA kernels.
 constexpr bool bwd_f32_mfma(int D) { return D == 32 || D == 64 || D == 96 || D == 128; }
 
 constexpr int kBwdThreads = 256;   // threads per backward workgroup (4 wavefronts)

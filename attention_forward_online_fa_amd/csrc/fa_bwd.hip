@@ -21,7 +21,9 @@
 //   strides and head dims below the tile dim (those dims read as zeros).
 // - fp32 inputs at D = 32, 64, 96, 128: MFMA kernels on v_mfma_f32_32x32x2_f32
 //   (bwd_dq_f32_mfma_kernel, bwd_dkdv_f32_mfma_kernel, in fa_bwd_f32.hip).
-// - fp32 inputs at D = 16, 48, 80, 256: the per-row kernels below (bwd_dq_kernel,
+// - fp32 inputs at D = 256, and at D = 16, 48, 80 on small problems (larger
+//   ones are staged into the MFMA kernels of the 32, 64, 96 tiles, the extra
+//   dims zero): the per-row kernels below (bwd_dq_kernel,
 //   bwd_dkdv_kernel), the pages' thread-per-row design mapped to wavefronts on
 //   the VALU: a group of G = 4, 8, 16 or 32 lanes (the fewest that keep D / G
 //   <= 8) owns R consecutive rows of one head (bwd_rows_per_group: 4 with 16

@@ -13,6 +13,19 @@
 
 namespace {
 
+// Visible (query row, key) pairs of one head, counted up to `cap`: rows i <
+// Sq see keys j < Sk with j <= i under a causal mask and j > i - window under
+// a window.
+double visible_pairs(int Sq, int Sk, int causal, int window, double cap) {
+  double n = 0;
+  for (long i = 0; i < Sq && n < cap; ++i) {
+    const long hi = causal ? std::min<long>(i + 1, Sk) : Sk;
+    const long lo = window > 0 ? std::max<long>(0, i - window + 1) : 0;
+    if (hi > lo) n += (double)(hi - lo);
+  }
+  return n;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_bwd(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int window, int dtype) {
@@ -154,9 +167,18 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
     for (int t = 0; t < 5; ++t) mx = std::max(mx, vs[t][2]);
     gen = mx <= (1LL << 22);   // 64 rows x 2 bytes x 2^22 = 2^29 bytes per tile
   }
-  const bool padded = dtype != FA_F32 && D != DT16;
+  // fp32 head dims below an fp32 MFMA tile (16, 48, 80) are staged into it
+  // when the work is large enough to pay for the staging copies (B H visible
+  // pairs at least 2^23; smaller problems run faster on the per-row kernels,
+  // whose launch has no copies around it); D = 256 keeps the per-row kernels
+  const int DTF = D <= 32 ? 32 : D <= 64 ? 64 : D <= 96 ? 96 : D <= 128 ? 128 : D;
+  const double pad_work = 8388608.0;
+  const bool f32_pad = dtype == FA_F32 && D != DTF &&
+                       (double)B * H * visible_pairs(Sq, Sk, causal, window, pad_work / ((double)B * H)) >=
+                           pad_work;
+  const bool padded = dtype != FA_F32 ? D != DT16 : f32_pad;
   const bool staged = !gen && (padded || !contiguous);
-  const int DT = padded ? DT16 : D;
+  const int DT = padded ? (dtype != FA_F32 ? DT16 : DTF) : D;
   const size_t nq = (size_t)B * H * Sq, nk = (size_t)B * HKV * Sk;
   auto up = [](size_t bytes) { return (bytes + 255) / 256 * 256; };
   // workspace, stream-ordered from the library's memory pool: D_i, and when
@@ -165,15 +187,15 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
   const size_t b_q = staged ? up(nq * DT * esz) : 0, b_k = staged ? up(nk * DT * esz) : 0;
   size_t b_gk = staged ? up(nk * DT * 4) : 0;   // (and the general form's row chunks)
   size_t b_gq = staged ? up(nq * DT * 4) : 0;   // (the general form's key chunks also use it)
-  // The per-row kernels (fp32 inputs at D = 16, 48, 80 and 256) on grids too small to fill the
+  // The per-row kernels (fp32 inputs at D = 256, and 16, 48, 80 unstaged) on grids too small to fill the
   // GPU: each row group's range is cut into nch chunks that run side by side
   // (a causal grid is otherwise bound by its longest rows), their partial
   // sums added up afterwards in chunk order (deterministic). A group's range
   // spans at most `span` + R - 1 keys (query rows): the ranges of its R
   // adjacent rows.
   p.nch = 1;
-  if (dtype == FA_F32 && !fa::bwd_f32_mfma(D)) {
-    const int R = fa::bwd_rows_per_group(D);
+  if (dtype == FA_F32 && !fa::bwd_f32_mfma(DT)) {
+    const int R = fa::bwd_rows_per_group(DT);
     const long groups = (long)B * H * ((Sq + R - 1) / R);
     const long target = 1L << 18;   // row groups that fill the GPU several times over
     // keys per query row and query rows per key: at most `window` only under
@@ -183,7 +205,7 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
     const long span_k = (band ? std::min(Sq, window) : Sq) + R - 1;
     if (groups < target) {
       long n = std::min({(target + groups - 1) / groups, (std::max(span_q, span_k) + 127) / 128, 8L});
-      const double per_chunk = (double)(nq + 2 * nk) * D * 4;
+      const double per_chunk = (double)(nq + 2 * nk) * DT * 4;
       while (n > 1 && n * per_chunk > 512.0 * (1 << 20)) --n;   // workspace at most 512 MiB
       p.nch = (int)std::max(1L, n);
     }
@@ -207,7 +229,7 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
     }
   }
   if (gen && p.nch > 1) b_gq = up(nq * DT * 4);   // summed dQ before it goes to the view
-  const bool per_row = dtype == FA_F32 && !fa::bwd_f32_mfma(D);
+  const bool per_row = dtype == FA_F32 && !fa::bwd_f32_mfma(DT);
   // MFMA dK/dV kernels: when their workgroups fill less than the GPU's slots
   // (one per CU; two for fp32 at D <= 64; fp32 counts the slots twice) and a
   // workgroup's walk is long (Sq rows of each of its H / HKV query heads: at
@@ -240,7 +262,7 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
   }
   if (gen && p.nrc > 1) b_gk = up(nk * DT * 4);   // summed dK, dV before they go to the views
   const size_t b_pq = p.nch > 1 ? up((size_t)p.nch * nq * DT * 4) : 0;
-  const size_t b_pk = p.nch > 1 && per_row ? up((size_t)p.nch * nk * D * 4)
+  const size_t b_pk = p.nch > 1 && per_row ? up((size_t)p.nch * nk * DT * 4)
                       : p.nrc > 1          ? up((size_t)p.nrc * nk * DT * 4)
                                            : 0;
   void* ws = nullptr;

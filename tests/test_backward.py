@@ -124,6 +124,16 @@ CASES += [
 ]
 
 
+# fp32 head dims 16, 48, 80 with enough work (B H visible pairs at least
+# 2^23): staged into the fp32 MFMA kernels of the 32, 64, 96 tiles, the extra
+# dims zero (the smaller cases above keep the per-row kernels)
+CASES += [
+    ("f32", 1, 8, 2, 1500, 1500, 48, 1, 0),
+    ("f32", 1, 4, 1, 2100, 2100, 16, 0, 300),
+    ("f32", 1, 8, 2, 1500, 1500, 80, 1, 0),
+]
+
+
 @pytest.mark.parametrize("case", CASES, ids=["-".join(map(str, c)) for c in CASES])
 def test_backward_matches_oracle(case):
     wl = wl_small(*case, seed=sum(case[1:]) + 3)

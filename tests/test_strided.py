@@ -169,6 +169,8 @@ BWD_CASES = [
     # contiguous rows, then into the dK / dV views
     ("bf16", 1, 8, 2, 1030, 1030, 128, 1, 0),
     ("f32", 1, 4, 1, 600, 600, 64, 1, 100),
+    # fp32 head dim 48 staged into the 64 tile (enough work for it)
+    ("f32", 1, 8, 2, 1500, 1500, 48, 1, 0),
 ]
 
 
