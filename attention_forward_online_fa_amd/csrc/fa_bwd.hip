@@ -1087,16 +1087,27 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
 
 template <typename E>
 static hipError_t launch_bwd_e(const BwdParams& p, int D, hipStream_t stream) {
-  switch (D) {
-    case 16: return launch_bwd_t<E, 16>(p, stream);
-    case 32: return launch_bwd_t<E, 32>(p, stream);
-    case 48: return launch_bwd_t<E, 48>(p, stream);
-    case 64: return launch_bwd_t<E, 64>(p, stream);
-    case 80: return launch_bwd_t<E, 80>(p, stream);
-    case 96: return launch_bwd_t<E, 96>(p, stream);
-    case 128: return launch_bwd_t<E, 128>(p, stream);
-    case 256: return launch_bwd_t<E, 256>(p, stream);
-    default: return hipErrorInvalidValue;
+  // (16-bit inputs reach here at their tile dims 64, 128, 256 only: other head
+  // dims run those tiles in the general form or staged)
+  if constexpr (sizeof(E) == 2) {
+    switch (D) {
+      case 64: return launch_bwd_t<E, 64>(p, stream);
+      case 128: return launch_bwd_t<E, 128>(p, stream);
+      case 256: return launch_bwd_t<E, 256>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (D) {
+      case 16: return launch_bwd_t<E, 16>(p, stream);
+      case 32: return launch_bwd_t<E, 32>(p, stream);
+      case 48: return launch_bwd_t<E, 48>(p, stream);
+      case 64: return launch_bwd_t<E, 64>(p, stream);
+      case 80: return launch_bwd_t<E, 80>(p, stream);
+      case 96: return launch_bwd_t<E, 96>(p, stream);
+      case 128: return launch_bwd_t<E, 128>(p, stream);
+      case 256: return launch_bwd_t<E, 256>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 
