@@ -38,11 +38,12 @@ struct BwdParams {
   float* part_q;
   float* part_k;
   float* part_v;
-  // MFMA dK/dV kernels on small grids (contiguous tensors):
-  // the query rows are cut into nrc chunks [c chunk_r, (c + 1) chunk_r) (chunk_r
-  // a multiple of 128), one per blockIdx.y, each writing unscaled dK and dV
-  // partial sums to part_k / part_v [nrc][B HKV Sk][D], added up in chunk order
-  // afterwards (nrc = 1: dK and dV written directly).
+  // MFMA dK/dV kernels on small grids: the query rows are cut into nrc
+  // chunks [c chunk_r, (c + 1) chunk_r) (chunk_r a multiple of 128; chunk c =
+  // nrc - 1 - blockIdx.y, the last rows first), each writing unscaled dK and
+  // dV partial sums to contiguous rows part_k / part_v [nrc][B HKV Sk][D]
+  // (the general form too), added up in chunk order afterwards (nrc = 1: dK
+  // and dV written directly).
   int nrc, chunk_r;
   // General form of the 16-bit MFMA kernels (gen = 1): the tensors are views
   // with these element strides (batch, head, row; the head dim contiguous),
