@@ -9,6 +9,8 @@ layout (contiguous or token-major) and, for block-sparse cases, a random mask
 with a random axis form. Shapes stay small enough for the oracle to check
 every row. Tolerances as in test_parity.py (forward) and test_backward.py
 (backward)."""
+import os
+
 import numpy as np
 import pytest
 
@@ -72,13 +74,34 @@ def test_random_backward(seed):
     # the three backward entry points: fa_bwd (contiguous), fa_bwd_strided
     # (token-major views, gradients in the same layout), fa_bwd_block_sparse
     # (a random mask with a random axis form)
-    import attention_forward_online_fa_amd as fa
     c = draw(5000 + seed)
     Sq, Sk = min(c["Sq"], 200), min(c["Sk"], 200)
     wl = wl_small(c["dtype"], c["B"], c["H"], c["HKV"], Sq, Sk, c["D"], c["causal"],
                   c["window"], name=f"randbwd{seed}", seed=300 + seed)
+    _check_backward(c, wl, f"backward seed {seed}")
+
+
+@pytest.mark.parametrize("seed", range(int(os.environ.get("FA_RANDOM_LONG_SEEDS", "8"))))
+def test_random_backward_long_rows(seed):
+    # the same on small grids with long row walks (one batch, few kv heads,
+    # 1000 .. 2200 query rows): the dK/dV row chunks, the dQ key chunks, the
+    # staged fp32 head dims 16 / 48 / 80 and the one reduction launch
+    c = draw(9000 + seed)
+    r = c["rng"]
+    HKV = int(r.integers(1, 3))
+    H = HKV * int(r.choice([1, 2, 4, 8]))
+    while H * c["D"] > 512 and H > HKV:   # (keeps the oracle to seconds)
+        H //= 2
+    Sq, Sk = int(r.integers(1000, 2200)), int(r.integers(200, 1000))
+    wl = wl_small(c["dtype"], 1, H, HKV, Sq, Sk, c["D"], c["causal"], c["window"],
+                  name=f"randbwdlong{seed}", seed=500 + seed)
+    _check_backward(c, wl, f"long-row backward seed {seed}")
+
+
+def _check_backward(c, wl, what):
+    import attention_forward_online_fa_amd as fa
     inp = W.make_inputs(wl)
-    print(f"[random] backward seed {seed}: {c['kind']} {wl}", flush=True)
+    print(f"[random] {what}: {c['kind']} {wl}", flush=True)
     q, k, v = to_device(inp)
     g, bits = W.make_grad_output(inp)
     if bits is not None:
