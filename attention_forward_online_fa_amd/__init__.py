@@ -24,8 +24,8 @@ import math
 from ._lib import (FA_BF16, FA_F16, FA_F32, FA_MASK_BLOCK_K, FA_MASK_BLOCK_Q, FA_MAX_SPLITS,
                    FaError, lib, library_path)
 
-__all__ = ["fwd", "fwd_into", "fwd_noalloc_into", "bwd", "plan_splits", "schedule_table",
-           "release", "FaError",
+__all__ = ["fwd", "fwd_into", "fwd_noalloc_into", "bwd", "plan_splits", "bwd_plan",
+           "schedule_table", "release", "FaError",
            "library_path", "default_scale", "FA_F32", "FA_BF16", "FA_F16", "FA_MAX_SPLITS",
            "FA_MASK_BLOCK_Q", "FA_MASK_BLOCK_K"]
 
@@ -240,6 +240,20 @@ def plan_splits(B, H, HKV, Sq, Sk, D, *, causal=False, window=0, dtype="bf16") -
     if r < 0:
         raise FaError(-r)
     return r
+
+
+def bwd_plan(B, H, HKV, Sq, Sk, D, num_cus, *, causal=False, window=0, dtype="bf16") -> dict:
+    """How the backward pass would run this problem (contiguous tensors, no
+    block mask) on a device with num_cus compute units (host only)."""
+    code = _dtype_name_code(dtype)
+    buf = (ctypes.c_int * 8)()
+    r = lib().fa_bwd_plan(B, H, HKV, Sq, Sk, D, int(bool(causal)), int(window), code, num_cus,
+                          ctypes.cast(buf, ctypes.c_void_p))
+    if r != 0:
+        raise FaError(r)
+    keys = ("head_dim", "general", "staged", "per_row", "key_chunks", "keys_per_chunk",
+            "row_chunks", "rows_per_chunk")
+    return dict(zip(keys, list(buf)))
 
 
 def schedule_table(B, H, HKV, Sq, Sk, D, nslot, *, causal=False, window=0, dtype="f32"):

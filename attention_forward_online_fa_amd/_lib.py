@@ -39,6 +39,7 @@ SIGNATURES = {
     "fa_bwd_block_sparse": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                  _P, _I, _I, _F, _I, _I, _I, _P]),
     "fa_plan_splits": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
+    "fa_bwd_plan": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
     "fa_schedule_table": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_release": (None, []),

@@ -78,6 +78,122 @@ struct BwdMask {
   int batch, heads;
 };
 
+// The backward's plan for one call (host computation only): the tile dim
+// the kernels run at, how the inputs reach them, and the small-grid chunks.
+struct BwdPlan {
+  int DT = 0;
+  bool gen = false, padded = false, staged = false, per_row = false;
+  int nch = 1, chunk_q = 0, chunk_k = 0;   // key chunks (dQ; the per-row kernels: both)
+  int nrc = 1, chunk_r = 0;                // row chunks of the MFMA dK/dV kernels
+};
+
+// contiguous: every tensor in its contiguous [B, heads, S, D] layout;
+// max_row_stride: the largest row stride (elements) of Q, K, V, O, dO;
+// cus: compute units of the device.
+BwdPlan plan_backward(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int window,
+                      int dtype, bool contiguous, long long max_row_stride, int cus) {
+  BwdPlan pl;
+  const long n_qblk = (Sq + 127) / 128;
+  const size_t nq = (size_t)B * H * Sq, nk = (size_t)B * HKV * Sk;
+  // 16-bit inputs at head dims 16 .. 96 other than 64 run the MFMA kernels of
+  // the 64 or 128 tile with the dims from D on held as zeros (they add exact
+  // zeros to every dot product, and the gradients' extra dims are not
+  // written). The 16-bit MFMA kernels read such head dims, and strided views,
+  // directly (their general form: per-view strides, copy offsets formed in
+  // full, chunks at or beyond D read as zeros), as long as every row stride
+  // keeps a tile's copy offsets far inside 32 bits. Otherwise, and for fp32
+  // views, the inputs are staged: copied to contiguous zero-padded rows, and
+  // the gradients copied back into the caller's views.
+  const int DT16 = D <= 64 ? 64 : D <= 128 ? 128 : 256;
+  bool gen = false;
+  if (dtype != FA_F32 && (!contiguous || D != DT16))
+    gen = max_row_stride <= (1LL << 22);   // 64 rows x 2 bytes x 2^22 = 2^29 bytes per tile
+  // fp32 head dims below an fp32 MFMA tile (16, 48, 80) are staged into it
+  // when the work is large enough to pay for the staging copies (B H visible
+  // pairs at least 2^23; smaller problems run faster on the per-row kernels,
+  // whose launch has no copies around it); D = 256 keeps the per-row kernels
+  const int DTF = D <= 32 ? 32 : D <= 64 ? 64 : D <= 96 ? 96 : D <= 128 ? 128 : D;
+  const double pad_work = 8388608.0;
+  const bool f32_pad = dtype == FA_F32 && D != DTF &&
+                       (double)B * H * visible_pairs(Sq, Sk, causal, window, pad_work / ((double)B * H)) >=
+                           pad_work;
+  const bool padded = dtype != FA_F32 ? D != DT16 : f32_pad;
+  const bool staged = !gen && (padded || !contiguous);
+  const int DT = padded ? (dtype != FA_F32 ? DT16 : DTF) : D;
+  // The per-row kernels (fp32 inputs at D = 256, and 16, 48, 80 unstaged) on grids too small to fill the
+  // GPU: each row group's range is cut into nch chunks that run side by side
+  // (a causal grid is otherwise bound by its longest rows), their partial
+  // sums added up afterwards in chunk order (deterministic). A group's range
+  // spans at most `span` + R - 1 keys (query rows): the ranges of its R
+  // adjacent rows.
+  if (dtype == FA_F32 && !fa::bwd_f32_mfma(DT)) {
+    const int R = fa::bwd_rows_per_group(DT);
+    const long groups = (long)B * H * ((Sq + R - 1) / R);
+    const long target = 1L << 18;   // row groups that fill the GPU several times over
+    // keys per query row and query rows per key: at most `window` only under
+    // causal + window (a window alone bounds one side)
+    const bool band = causal && window > 0;
+    const long span_q = (band ? std::min(Sk, window) : Sk) + R - 1;
+    const long span_k = (band ? std::min(Sq, window) : Sq) + R - 1;
+    if (groups < target) {
+      long n = std::min({(target + groups - 1) / groups, (std::max(span_q, span_k) + 127) / 128, 8L});
+      const double per_chunk = (double)(nq + 2 * nk) * DT * 4;
+      while (n > 1 && n * per_chunk > 512.0 * (1 << 20)) --n;   // workspace at most 512 MiB
+      pl.nch = (int)std::max(1L, n);
+    }
+    pl.chunk_q = (int)((span_q + pl.nch - 1) / pl.nch);
+    pl.chunk_k = (int)((span_k + pl.nch - 1) / pl.nch);
+  } else {
+    // MFMA kernels: when the dQ kernel has fewer query tiles than two per
+    // CU, cut the key axis into chunks of whole 32-key tiles (at least 16
+    // tiles each, at most 16 chunks, workspace at most 512 MiB)
+    const long qwg = (long)B * H * n_qblk;
+    const long tiles = (Sk + 31) / 32;
+    if (qwg < 2L * cus) {
+      long n = std::min({(2L * cus + qwg - 1) / qwg, tiles / 16, 16L});
+      while (n > 1 && (double)n * nq * DT * 4 > 512.0 * (1 << 20)) --n;
+      if (n > 1) {
+        pl.chunk_q = (int)((tiles + n - 1) / n) * 32;
+        pl.nch = (int)((Sk + pl.chunk_q - 1) / pl.chunk_q);
+      }
+    }
+  }
+  const bool per_row = dtype == FA_F32 && !fa::bwd_f32_mfma(DT);
+  // MFMA dK/dV kernels: when their workgroups fill less than the GPU's slots
+  // (one per CU; two for fp32 at D <= 64; fp32 counts the slots twice) and a
+  // workgroup's walk is long (Sq rows of each of its H / HKV query heads: at
+  // least 2048, fp32 1024; shorter walks gain less than the partial sums
+  // cost), cut the query rows into chunks of whole 128-row blocks (a causal
+  // grid is otherwise as long as its first key blocks, which see every row):
+  // as many as fill the (doubled) slots, at most 8, workspace at most 512 MiB.
+  // The partial sums are contiguous rows; views (the general form) get the
+  // summed dK and dV from contiguous rows too. A block mask's 128-row blocks
+  // never straddle two chunks, so the same chunks serve it (and an all-ones
+  // mask keeps the dense sums bit for bit).
+  pl.chunk_r = Sq;
+  if (!per_row) {
+    const long wgs = (long)B * HKV * ((Sk + 127) / 128) * (dtype != FA_F32 && DT == 256 ? 2 : 1);
+    const bool f32 = dtype == FA_F32;
+    const long target = (long)cus * (f32 && DT <= 64 ? 2 : 1) * (f32 ? 2 : 1);
+    const long blocks = (Sq + 127) / 128;
+    const long walk = (long)Sq * (H / HKV);
+    if (wgs < target && walk >= (f32 ? 1024 : 2048)) {
+      long n = std::min({(target + wgs - 1) / wgs, blocks, 8L});
+      while (n > 1 && 2.0 * n * nk * DT * 4 > 512.0 * (1 << 20)) --n;
+      if (n > 1) {
+        pl.chunk_r = (int)((blocks + n - 1) / n) * 128;
+        pl.nrc = (int)((Sq + pl.chunk_r - 1) / pl.chunk_r);
+      }
+    }
+  }
+  pl.DT = DT;
+  pl.gen = gen;
+  pl.padded = padded;
+  pl.staged = staged;
+  pl.per_row = per_row;
+  return pl;
+}
+
 // The backward pass for views with the given element strides (NULL =
 // contiguous): q, k, v, o, dO in the input type, then dQ, dK, dV (fp32).
 int backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -151,34 +267,18 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
     p.bm_sb = bm->batch == 1 ? 0 : bm->heads * slab;
     p.bm_by_q = bm->heads == H ? 1 : 0;
   }
-  // 16-bit inputs at head dims 16 .. 96 other than 64 run the MFMA kernels of
-  // the 64 or 128 tile with the dims from D on held as zeros (they add exact
-  // zeros to every dot product, and the gradients' extra dims are not
-  // written). The 16-bit MFMA kernels read such head dims, and strided views,
-  // directly (their general form: per-view strides, copy offsets formed in
-  // full, chunks at or beyond D read as zeros), as long as every row stride
-  // keeps a tile's copy offsets far inside 32 bits. Otherwise, and for fp32
-  // views, the inputs are staged: copied to contiguous zero-padded rows, and
-  // the gradients copied back into the caller's views.
-  const int DT16 = D <= 64 ? 64 : D <= 128 ? 128 : 256;
-  bool gen = false;
-  if (dtype != FA_F32 && (!contiguous || D != DT16)) {
-    long long mx = 0;
-    for (int t = 0; t < 5; ++t) mx = std::max(mx, vs[t][2]);
-    gen = mx <= (1LL << 22);   // 64 rows x 2 bytes x 2^22 = 2^29 bytes per tile
-  }
-  // fp32 head dims below an fp32 MFMA tile (16, 48, 80) are staged into it
-  // when the work is large enough to pay for the staging copies (B H visible
-  // pairs at least 2^23; smaller problems run faster on the per-row kernels,
-  // whose launch has no copies around it); D = 256 keeps the per-row kernels
-  const int DTF = D <= 32 ? 32 : D <= 64 ? 64 : D <= 96 ? 96 : D <= 128 ? 128 : D;
-  const double pad_work = 8388608.0;
-  const bool f32_pad = dtype == FA_F32 && D != DTF &&
-                       (double)B * H * visible_pairs(Sq, Sk, causal, window, pad_work / ((double)B * H)) >=
-                           pad_work;
-  const bool padded = dtype != FA_F32 ? D != DT16 : f32_pad;
-  const bool staged = !gen && (padded || !contiguous);
-  const int DT = padded ? (dtype != FA_F32 ? DT16 : DTF) : D;
+  long long mx = 0;   // the largest row stride of the inputs
+  for (int t = 0; t < 5; ++t) mx = std::max(mx, vs[t][2]);
+  const int cus = fa::device_cus();
+  if (cus <= 0) return FA_ERR_HIP;
+  const BwdPlan pl = plan_backward(B, H, HKV, Sq, Sk, D, causal, window, dtype, contiguous, mx, cus);
+  const bool gen = pl.gen, staged = pl.staged, per_row = pl.per_row;
+  const int DT = pl.DT;
+  p.nch = pl.nch;
+  p.chunk_q = pl.chunk_q;
+  p.chunk_k = pl.chunk_k;
+  p.nrc = pl.nrc;
+  p.chunk_r = pl.chunk_r;
   const size_t nq = (size_t)B * H * Sq, nk = (size_t)B * HKV * Sk;
   auto up = [](size_t bytes) { return (bytes + 255) / 256 * 256; };
   // workspace, stream-ordered from the library's memory pool: D_i, and when
@@ -187,79 +287,7 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
   const size_t b_q = staged ? up(nq * DT * esz) : 0, b_k = staged ? up(nk * DT * esz) : 0;
   size_t b_gk = staged ? up(nk * DT * 4) : 0;   // (and the general form's row chunks)
   size_t b_gq = staged ? up(nq * DT * 4) : 0;   // (the general form's key chunks also use it)
-  // The per-row kernels (fp32 inputs at D = 256, and 16, 48, 80 unstaged) on grids too small to fill the
-  // GPU: each row group's range is cut into nch chunks that run side by side
-  // (a causal grid is otherwise bound by its longest rows), their partial
-  // sums added up afterwards in chunk order (deterministic). A group's range
-  // spans at most `span` + R - 1 keys (query rows): the ranges of its R
-  // adjacent rows.
-  p.nch = 1;
-  if (dtype == FA_F32 && !fa::bwd_f32_mfma(DT)) {
-    const int R = fa::bwd_rows_per_group(DT);
-    const long groups = (long)B * H * ((Sq + R - 1) / R);
-    const long target = 1L << 18;   // row groups that fill the GPU several times over
-    // keys per query row and query rows per key: at most `window` only under
-    // causal + window (a window alone bounds one side)
-    const bool band = causal && window > 0;
-    const long span_q = (band ? std::min(Sk, window) : Sk) + R - 1;
-    const long span_k = (band ? std::min(Sq, window) : Sq) + R - 1;
-    if (groups < target) {
-      long n = std::min({(target + groups - 1) / groups, (std::max(span_q, span_k) + 127) / 128, 8L});
-      const double per_chunk = (double)(nq + 2 * nk) * DT * 4;
-      while (n > 1 && n * per_chunk > 512.0 * (1 << 20)) --n;   // workspace at most 512 MiB
-      p.nch = (int)std::max(1L, n);
-    }
-    p.chunk_q = (int)((span_q + p.nch - 1) / p.nch);
-    p.chunk_k = (int)((span_k + p.nch - 1) / p.nch);
-  } else {
-    // MFMA kernels: when the dQ kernel has fewer query tiles than two per
-    // CU, cut the key axis into chunks of whole 32-key tiles (at least 16
-    // tiles each, at most 16 chunks, workspace at most 512 MiB)
-    const int cus = fa::device_cus();
-    if (cus <= 0) return FA_ERR_HIP;
-    const long qwg = (long)B * H * p.n_qblk;
-    const long tiles = (Sk + 31) / 32;
-    if (qwg < 2L * cus) {
-      long n = std::min({(2L * cus + qwg - 1) / qwg, tiles / 16, 16L});
-      while (n > 1 && (double)n * nq * DT * 4 > 512.0 * (1 << 20)) --n;
-      if (n > 1) {
-        p.chunk_q = (int)((tiles + n - 1) / n) * 32;
-        p.nch = (int)((Sk + p.chunk_q - 1) / p.chunk_q);
-      }
-    }
-  }
   if (gen && p.nch > 1) b_gq = up(nq * DT * 4);   // summed dQ before it goes to the view
-  const bool per_row = dtype == FA_F32 && !fa::bwd_f32_mfma(DT);
-  // MFMA dK/dV kernels: when their workgroups fill less than the GPU's slots
-  // (one per CU; two for fp32 at D <= 64; fp32 counts the slots twice) and a
-  // workgroup's walk is long (Sq rows of each of its H / HKV query heads: at
-  // least 2048, fp32 1024; shorter walks gain less than the partial sums
-  // cost), cut the query rows into chunks of whole 128-row blocks (a causal
-  // grid is otherwise as long as its first key blocks, which see every row):
-  // as many as fill the (doubled) slots, at most 8, workspace at most 512 MiB.
-  // The partial sums are contiguous rows; views (the general form) get the
-  // summed dK and dV from contiguous rows too. A block mask's 128-row blocks
-  // never straddle two chunks, so the same chunks serve it (and an all-ones
-  // mask keeps the dense sums bit for bit).
-  p.nrc = 1;
-  p.chunk_r = Sq;
-  if (!per_row) {
-    const int cus = fa::device_cus();
-    if (cus <= 0) return FA_ERR_HIP;
-    const long wgs = (long)B * HKV * ((Sk + 127) / 128) * (dtype != FA_F32 && DT == 256 ? 2 : 1);
-    const bool f32 = dtype == FA_F32;
-    const long target = (long)cus * (f32 && DT <= 64 ? 2 : 1) * (f32 ? 2 : 1);
-    const long blocks = (Sq + 127) / 128;
-    const long walk = (long)Sq * (H / HKV);
-    if (wgs < target && walk >= (f32 ? 1024 : 2048)) {
-      long n = std::min({(target + wgs - 1) / wgs, blocks, 8L});
-      while (n > 1 && 2.0 * n * nk * DT * 4 > 512.0 * (1 << 20)) --n;
-      if (n > 1) {
-        p.chunk_r = (int)((blocks + n - 1) / n) * 128;
-        p.nrc = (int)((Sq + p.chunk_r - 1) / p.chunk_r);
-      }
-    }
-  }
   if (gen && p.nrc > 1) b_gk = up(nk * DT * 4);   // summed dK, dV before they go to the views
   const size_t b_pq = p.nch > 1 ? up((size_t)p.nch * nq * DT * 4) : 0;
   const size_t b_pk = p.nch > 1 && per_row ? up((size_t)p.nch * nk * DT * 4)
@@ -378,4 +406,16 @@ extern "C" int fa_bwd_strided(const void* Q, const void* K, const void* V, const
                                      do_strides, dq_strides, dk_strides, dv_strides};
   return backward(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, HKV, Sq, Sk, D, given, scale, causal,
                   window, dtype, stream);
+}
+
+extern "C" int fa_bwd_plan(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int window,
+                           int dtype, int num_cus, int* plan) {
+  if (!plan) return FA_ERR_NULLPTR;
+  const int st = check_bwd(B, H, HKV, Sq, Sk, D, causal, window, dtype);
+  if (st != FA_OK) return st;
+  if (num_cus < 1) return FA_ERR_SHAPE;
+  const BwdPlan pl = plan_backward(B, H, HKV, Sq, Sk, D, causal, window, dtype, true, D, num_cus);
+  const int out[8] = {pl.DT, pl.gen, pl.staged, pl.per_row, pl.nch, pl.chunk_q, pl.nrc, pl.chunk_r};
+  for (int t = 0; t < 8; ++t) plan[t] = out[t];
+  return FA_OK;
 }

@@ -25,7 +25,7 @@
  *
  * Entry points: the forward pass (fa_fwd, fa_fwd_ex, fa_fwd_strided,
  * fa_fwd_block_sparse, fa_fwd_noalloc) and its backward pass (fa_bwd,
- * fa_bwd_strided, fa_bwd_block_sparse), with fa_plan_splits,
+ * fa_bwd_strided, fa_bwd_block_sparse), with fa_plan_splits, fa_bwd_plan,
  * fa_schedule_table, fa_status_string and fa_release.
  *
  * The library is plain C ABI: no HIP or torch types in any signature.
@@ -216,6 +216,25 @@ int fa_fwd_block_sparse(const void* Q, const void* K, const void* V, void* O, fl
  */
 int fa_plan_splits(int B, int H, int HKV, int Sq, int Sk, int D,
                    int causal, int window, int dtype);
+
+/*
+ * fa_bwd_plan - how fa_bwd would run this problem (contiguous tensors, no
+ * block mask) on a device with num_cus compute units: host computation only
+ * (no HIP call, so it also runs without a GPU). Writes 8 ints to plan:
+ *   [0] the kernels' head dim (D, or the tile D is zero-padded into),
+ *   [1] 1 when 16-bit inputs run the kernels' general form in place,
+ *   [2] 1 when the inputs are staged into contiguous zero-padded copies,
+ *   [3] 1 when fp32 runs the per-row VALU kernels (else MFMA kernels),
+ *   [4] key chunks (dQ; the per-row kernels' ranges too), [5] keys per chunk,
+ *   [6] query-row chunks of the MFMA dK/dV kernels, [7] rows per chunk (a
+ *       multiple of 128 when [6] > 1),
+ * following the backward's small-grid rules (its dQ key chunks, dK/dV row
+ * chunks and fp32 head-dim staging; the reasons are in fa_bwd_api.cpp).
+ * Returns FA_OK, or the argument error fa_bwd would return (FA_ERR_NULLPTR
+ * for a NULL plan, FA_ERR_SHAPE for num_cus < 1).
+ */
+int fa_bwd_plan(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int window,
+                int dtype, int num_cus, int* plan);
 
 /*
  * fa_schedule_table - the item lists of a persistent launch with nslot
