@@ -79,8 +79,12 @@ constexpr int bwd_rows_per_group(int D) { return bwd_lanes_per_row(D) == 16 ? 4 
 
 // fp32 inputs at these head dims run the MFMA backward kernels (16, 48 and 80
 // staged into the 32, 64, 96 tiles when the work is large, else the per-row
-// kernels, as at 256); 16-bit inputs always run MFMA kernels.
-constexpr bool bwd_f32_mfma(int D) { return D == 32 || D == 64 || D == 96 || D == 128; }
+// kernels; 256 with its dims split over wavefront pairs, except under a block
+// mask, which keeps the per-row kernels there); 16-bit inputs always run MFMA
+// kernels.
+constexpr bool bwd_f32_mfma(int D, bool masked = false) {
+  return D == 32 || D == 64 || D == 96 || D == 128 || (D == 256 && !masked);
+}
 
 constexpr int kBwdThreads = 256;   // threads per backward workgroup (4 wavefronts)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -89,7 +93,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 hipError_t launch_backward(const BwdParams& p, int dtype, int D, hipStream_t stream);
 
 // The fp32 MFMA kernels (fa_bwd_f32.hip; D one of bwd_f32_mfma's dims): the
-// dQ kernel (key chunks on blockIdx.y when p.nch > 1) and the dK/dV kernel.
+// dQ kernel (key chunks on blockIdx.y when p.nch > 1) and the dK/dV kernel
+// (row chunks on blockIdx.y when p.nrc > 1); at D = 256 64 query rows (keys)
+// per workgroup instead of 128.
 hipError_t launch_bwd_f32_mfma_dq(const BwdParams& p, int D, hipStream_t stream);
 hipError_t launch_bwd_f32_mfma_dkdv(const BwdParams& p, int D, hipStream_t stream);
 

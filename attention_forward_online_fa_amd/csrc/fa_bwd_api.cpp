@@ -91,9 +91,11 @@ struct BwdPlan {
 // max_row_stride: the largest row stride (elements) of Q, K, V, O, dO;
 // cus: compute units of the device.
 BwdPlan plan_backward(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int window,
-                      int dtype, bool contiguous, long long max_row_stride, int cus) {
+                      int dtype, bool contiguous, long long max_row_stride, int cus, bool masked) {
   BwdPlan pl;
   const long n_qblk = (Sq + 127) / 128;
+  // fp32 at D = 256 (unmasked): MFMA kernels with 64 query rows (keys) per workgroup
+  const bool f32_256 = dtype == FA_F32 && D == 256 && !masked;
   const size_t nq = (size_t)B * H * Sq, nk = (size_t)B * HKV * Sk;
   // 16-bit inputs at head dims 16 .. 96 other than 64 run the MFMA kernels of
   // the 64 or 128 tile with the dims from D on held as zeros (they add exact
@@ -120,13 +122,14 @@ BwdPlan plan_backward(int B, int H, int HKV, int Sq, int Sk, int D, int causal, 
   const bool padded = dtype != FA_F32 ? D != DT16 : f32_pad;
   const bool staged = !gen && (padded || !contiguous);
   const int DT = padded ? (dtype != FA_F32 ? DT16 : DTF) : D;
-  // The per-row kernels (fp32 inputs at D = 256, and 16, 48, 80 unstaged) on grids too small to fill the
-  // GPU: each row group's range is cut into nch chunks that run side by side
+  // The per-row kernels (fp32 inputs at D = 256 under a block mask, and 16,
+  // 48, 80 unstaged) on grids too small to fill the GPU: each row group's range is cut into nch chunks that run side by side
   // (a causal grid is otherwise bound by its longest rows), their partial
   // sums added up afterwards in chunk order (deterministic). A group's range
   // spans at most `span` + R - 1 keys (query rows): the ranges of its R
   // adjacent rows.
-  if (dtype == FA_F32 && !fa::bwd_f32_mfma(DT)) {
+  const bool per_row = dtype == FA_F32 && !fa::bwd_f32_mfma(DT, masked);
+  if (per_row) {
     const int R = fa::bwd_rows_per_group(DT);
     const long groups = (long)B * H * ((Sq + R - 1) / R);
     const long target = 1L << 18;   // row groups that fill the GPU several times over
@@ -147,7 +150,7 @@ BwdPlan plan_backward(int B, int H, int HKV, int Sq, int Sk, int D, int causal, 
     // MFMA kernels: when the dQ kernel has fewer query tiles than two per
     // CU, cut the key axis into chunks of whole 32-key tiles (at least 16
     // tiles each, at most 16 chunks, workspace at most 512 MiB)
-    const long qwg = (long)B * H * n_qblk;
+    const long qwg = (long)B * H * (f32_256 ? (Sq + 63) / 64 : n_qblk);
     const long tiles = (Sk + 31) / 32;
     if (qwg < 2L * cus) {
       long n = std::min({(2L * cus + qwg - 1) / qwg, tiles / 16, 16L});
@@ -158,9 +161,9 @@ BwdPlan plan_backward(int B, int H, int HKV, int Sq, int Sk, int D, int causal, 
       }
     }
   }
-  const bool per_row = dtype == FA_F32 && !fa::bwd_f32_mfma(DT);
-  // MFMA dK/dV kernels: when their workgroups fill less than the GPU's slots
-  // (one per CU; two for fp32 at D <= 64; fp32 counts the slots twice) and a
+  // MFMA dK/dV kernels: when their workgroups (two per 128 keys at D = 256)
+  // fill less than the GPU's slots (one per CU; two for fp32 at D <= 64; fp32
+  // counts the slots twice) and a
   // workgroup's walk is long (Sq rows of each of its H / HKV query heads: at
   // least 2048, fp32 1024; shorter walks gain less than the partial sums
   // cost), cut the query rows into chunks of whole 128-row blocks (a causal
@@ -172,7 +175,7 @@ BwdPlan plan_backward(int B, int H, int HKV, int Sq, int Sk, int D, int causal, 
   // mask keeps the dense sums bit for bit).
   pl.chunk_r = Sq;
   if (!per_row) {
-    const long wgs = (long)B * HKV * ((Sk + 127) / 128) * (dtype != FA_F32 && DT == 256 ? 2 : 1);
+    const long wgs = (long)B * HKV * ((Sk + 127) / 128) * (DT == 256 ? 2 : 1);
     const bool f32 = dtype == FA_F32;
     const long target = (long)cus * (f32 && DT <= 64 ? 2 : 1) * (f32 ? 2 : 1);
     const long blocks = (Sq + 127) / 128;
@@ -271,7 +274,8 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
   for (int t = 0; t < 5; ++t) mx = std::max(mx, vs[t][2]);
   const int cus = fa::device_cus();
   if (cus <= 0) return FA_ERR_HIP;
-  const BwdPlan pl = plan_backward(B, H, HKV, Sq, Sk, D, causal, window, dtype, contiguous, mx, cus);
+  const BwdPlan pl = plan_backward(B, H, HKV, Sq, Sk, D, causal, window, dtype, contiguous, mx, cus,
+                                    bm != nullptr);
   const bool gen = pl.gen, staged = pl.staged, per_row = pl.per_row;
   const int DT = pl.DT;
   p.nch = pl.nch;
@@ -414,7 +418,7 @@ extern "C" int fa_bwd_plan(int B, int H, int HKV, int Sq, int Sk, int D, int cau
   const int st = check_bwd(B, H, HKV, Sq, Sk, D, causal, window, dtype);
   if (st != FA_OK) return st;
   if (num_cus < 1) return FA_ERR_SHAPE;
-  const BwdPlan pl = plan_backward(B, H, HKV, Sq, Sk, D, causal, window, dtype, true, D, num_cus);
+  const BwdPlan pl = plan_backward(B, H, HKV, Sq, Sk, D, causal, window, dtype, true, D, num_cus, false);
   const int out[8] = {pl.DT, pl.gen, pl.staged, pl.per_row, pl.nch, pl.chunk_q, pl.nrc, pl.chunk_r};
   for (int t = 0; t < 8; ++t) plan[t] = out[t];
   return FA_OK;

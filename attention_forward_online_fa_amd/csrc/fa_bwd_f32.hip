@@ -57,23 +57,69 @@ __device__ __forceinline__ void read_db(const float* p, float (&a)[DB]) {
   }
 }
 
-// dQ (and D_i) for fp32 inputs: 128 query rows per workgroup, K/V tiles of 32
-// keys; S^T = K Q^T, dP^T = V dO^T, dS = P (dP - D_i), dQ^T += K^T dS^T.
+// At D = 256 the head dims are split over a pair of wavefronts (Q and dO rows
+// of 128 dims per lane and the output accumulators of all 256 dims would not
+// fit one wavefront's registers): wavefront w takes rows 32 (w / 2) of its
+// workgroup and dims 128 (w % 2) .. +127 of every product. Each wavefront
+// forms the scores and dP over its own dims; the pair adds its two partial
+// tiles through LDS (the idle stage of the tile buffer), lower dims first, so
+// that both hold the same sums, and each then accumulates the output products
+// of its own dims. One workgroup covers 64 rows (dQ) or 64 keys (dK/dV).
+template <int D>
+struct F32BwdSplit {
+  static constexpr bool SP = D == 256;
+  static constexpr int HD = SP ? D / 2 : D;   // dims of one wavefront's products
+  static constexpr int DHw = HD / 2;          // score k-steps per wavefront
+  static constexpr int DBw = HD / 32;         // output d-blocks per wavefront
+  static constexpr int RW = SP ? 64 : 128;    // query rows (dQ) or keys (dK/dV) per workgroup
+};
+
+// Adds the pair's partial score and dP tiles (SP only): element v of s and dp
+// goes to xb[(32 wave + v) 64 + lane] and [(32 wave + 16 + v) 64 + lane]; the
+// second barrier keeps xb's stage from being refilled before the partner read it.
+__device__ __forceinline__ void f32_pair_sum(float* xb, int wave, int lane, int hf, f32x16& s,
+                                             f32x16& dp) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    xb[(32 * wave + v) * 64 + lane] = s[v];
+    xb[(32 * wave + 16 + v) * 64 + lane] = dp[v];
+  }
+  __syncthreads();
+  const int pw = wave ^ 1;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const float so = xb[(32 * pw + v) * 64 + lane];
+    const float po = xb[(32 * pw + 16 + v) * 64 + lane];
+    s[v] = hf ? so + s[v] : s[v] + so;
+    dp[v] = hf ? po + dp[v] : dp[v] + po;
+  }
+  __syncthreads();
+}
+
+// dQ (and D_i) for fp32 inputs: 128 query rows per workgroup (64 at D = 256),
+// K/V tiles of 32 keys; S^T = K Q^T, dP^T = V dO^T, dS = P (dP - D_i),
+// dQ^T += K^T dS^T.
 template <int D, bool Msk>
 __global__ __launch_bounds__(kBwdThreads, D <= 64 ? 2 : 1)
 void bwd_dq_f32_mfma_kernel(BwdParams p) {
   using T = F32BwdTile<D>;
+  using W = F32BwdSplit<D>;
+  static_assert(!(W::SP && Msk), "block masks at D = 256 run the per-row kernels");
+  static_assert(!W::SP || 4 * 32 * 64 <= T::TILE_F, "the pair sums fit one tile buffer");
   constexpr int BN = T::BN;
   __shared__ __attribute__((aligned(16))) float smem[2][2][T::TILE_F];   // [stage][K, V]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
+  const int rg = W::SP ? wave >> 1 : wave, hf = W::SP ? wave & 1 : 0;
+  const int doff = hf * W::HD;   // first dim of the wavefront's products
   const int units = p.B * p.H;
-  const int qblk = p.n_qblk - 1 - (int)(blockIdx.x / units);   // heaviest query tiles first
+  const int nqb = W::SP ? (p.Sq + W::RW - 1) / W::RW : p.n_qblk;
+  const int qblk = nqb - 1 - (int)(blockIdx.x / units);   // heaviest query tiles first
   const int u = blockIdx.x % units;
   const int h = u % p.H, b = u / p.H;
   const int hkv = h / (p.H / p.HKV);
-  const int q0 = qblk * 128, qw = q0 + wave * 32, i = qw + l32;
+  const int q0 = qblk * W::RW, qw = q0 + rg * 32, i = qw + l32;
   const bool row_ok = i < p.Sq;
   const long row = ((long)b * p.H + h) * p.Sq + i;
   const float* Qh = (const float*)p.Q + ((long)b * p.H + h) * p.Sq * D;
@@ -83,7 +129,7 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
   const float* Vp = (const float*)p.V + ((long)b * p.HKV + hkv) * p.Sk * D;
 
   int lo = 0, hi = p.Sk;
-  if (p.causal) hi = min(hi, min(q0 + 128, p.Sq));
+  if (p.causal) hi = min(hi, min(q0 + W::RW, p.Sq));
   if (p.window > 0) lo = max(0, q0 - p.window + 1);
   if (p.nch > 1) {   // key chunk blockIdx.y (chunk_q: a multiple of BN)
     lo = max(lo, (int)blockIdx.y * p.chunk_q);
@@ -114,20 +160,35 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
       return t0 + t * BN;
   };
 
-  // Q and dO rows (dims t + (D/2) g), D_i over the lane's dims and its partner's
-  float qf[T::DH], dof[T::DH];
+  // Q and dO rows (dims doff + t + (HD/2) g), D_i over the lane's dims and its
+  // partner's (at D = 256 over dims 128 g .. +127 of the whole row, so that
+  // both wavefronts of a pair form the same D_i)
+  float qf[W::DHw], dof[W::DHw];
   float dd = 0.f;
 #pragma unroll
-  for (int t4 = 0; t4 < T::DH / 4; ++t4) {
-    const long off = (long)i * D + T::DH * g + 4 * t4;
+  for (int t4 = 0; t4 < W::DHw / 4; ++t4) {
+    const long off = (long)i * D + doff + W::DHw * g + 4 * t4;
     const f32x4 qv = row_ok ? *(const f32x4*)(Qh + off) : f32x4{};
     const f32x4 dv = row_ok ? *(const f32x4*)(dOh + off) : f32x4{};
-    const f32x4 ov = row_ok ? *(const f32x4*)(Oh + off) : f32x4{};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       qf[4 * t4 + e] = qv[e];
       dof[4 * t4 + e] = dv[e];
-      dd = fmaf(dv[e], ov[e], dd);
+    }
+    if constexpr (!W::SP) {
+      const f32x4 ov = row_ok ? *(const f32x4*)(Oh + off) : f32x4{};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dd = fmaf(dv[e], ov[e], dd);
+    }
+  }
+  if constexpr (W::SP) {
+#pragma unroll 4
+    for (int t4 = 0; t4 < D / 8; ++t4) {
+      const long off = (long)i * D + (D / 2) * g + 4 * t4;
+      const f32x4 dv = row_ok ? *(const f32x4*)(dOh + off) : f32x4{};
+      const f32x4 ov = row_ok ? *(const f32x4*)(Oh + off) : f32x4{};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dd = fmaf(dv[e], ov[e], dd);
     }
   }
   const float Di = dd + __shfl_xor(dd, 32);
@@ -160,9 +221,9 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
   }
   __syncthreads();
 
-  f32x16 dq[T::DB];
+  f32x16 dq[W::DBw];
 #pragma unroll
-  for (int db = 0; db < T::DB; ++db) dq[db] = f32x16{};
+  for (int db = 0; db < W::DBw; ++db) dq[db] = f32x16{};
 
   for (;;) {
   for (int it = 0; it < n_tiles; ++it) {
@@ -172,12 +233,12 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
     if (it + 1 < n_tiles) load_tile(tile_kt(it + 1));
     const bool skip = qw >= p.Sq || (p.causal && kt > qw + 31) ||
                       (p.window > 0 && kt + BN - 1 < qw - p.window + 1);
+    f32x16 s = f32x16{}, dp = f32x16{};
     if (!skip) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-      const float* krow = Ks + l32 * T::LD + T::DH * g;
-      const float* vrow = Vs + l32 * T::LD + T::DH * g;
+      const float* krow = Ks + l32 * T::LD + doff + W::DHw * g;
+      const float* vrow = Vs + l32 * T::LD + doff + W::DHw * g;
 #pragma unroll
-      for (int t4 = 0; t4 < T::DH / 4; ++t4) {
+      for (int t4 = 0; t4 < W::DHw / 4; ++t4) {
         const f32x4 a = *(const f32x4*)(krow + 4 * t4);
         const f32x4 c = *(const f32x4*)(vrow + 4 * t4);
 #pragma unroll
@@ -186,6 +247,10 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
           dp = __builtin_amdgcn_mfma_f32_32x32x2f32(c[e], dof[4 * t4 + e], dp, 0, 0, 0);
         }
       }
+    }
+    // (every wavefront reaches the pair sum's barriers; a skipped pair adds zeros)
+    if constexpr (W::SP) f32_pair_sum(smem[(it + 1) & 1][0], wave, lane, hf, s, dp);
+    if (!skip) {
       // element v holds key kt + 8 (v / 4) + 4 g + v % 4 of row i
       const bool edge = (kt + BN > p.Sk) || (p.causal && kt + BN - 1 > qw) ||
                         (p.window > 0 && kt < qw + 31 - p.window + 1);
@@ -223,10 +288,10 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
       // dQ^T += K^T dS^T: step u takes key 8 (u / 4) + 4 g + u % 4
 #pragma unroll
       for (int u2 = 0; u2 < 16; ++u2) {
-        float ka[T::DB];
-        read_db<T::DB>(Ks + (8 * (u2 >> 2) + 4 * g + (u2 & 3)) * T::LD + T::DB * l32, ka);
+        float ka[W::DBw];
+        read_db<W::DBw>(Ks + (8 * (u2 >> 2) + 4 * g + (u2 & 3)) * T::LD + doff + W::DBw * l32, ka);
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db)
+        for (int db = 0; db < W::DBw; ++db)
           dq[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[db], ds[u2], dq[db], 0, 0, 0);
       }
     }
@@ -244,8 +309,8 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
     }
   }
 
-  // element v of block db: dim (D/32)(8 (v / 4) + 4 g + v % 4) + db of row i;
-  // a key chunk writes its unscaled partial sums
+  // element v of block db: dim doff + (HD/32)(8 (v / 4) + 4 g + v % 4) + db of
+  // row i; a key chunk writes its unscaled partial sums
   if (row_ok) {
     const bool part = p.nch > 1;
     const float sc = part ? 1.f : p.scale;
@@ -253,32 +318,34 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
                       : p.dQ + row * D;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      float* d0 = dst + T::DB * (8 * (v >> 2) + 4 * g + (v & 3));
-      if constexpr (T::DB % 4 == 0) {
+      float* d0 = dst + doff + W::DBw * (8 * (v >> 2) + 4 * g + (v & 3));
+      if constexpr (W::DBw % 4 == 0) {
 #pragma unroll
-        for (int c4 = 0; c4 < T::DB / 4; ++c4) {
+        for (int c4 = 0; c4 < W::DBw / 4; ++c4) {
           const f32x4 x = {dq[4 * c4][v] * sc, dq[4 * c4 + 1][v] * sc,
                            dq[4 * c4 + 2][v] * sc, dq[4 * c4 + 3][v] * sc};
           *(f32x4*)(d0 + 4 * c4) = x;
         }
       } else {
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db) d0[db] = dq[db][v] * sc;
+        for (int db = 0; db < W::DBw; ++db) d0[db] = dq[db][v] * sc;
       }
     }
-    if (g == 0 && blockIdx.y == 0) p.Dws[row] = Di;
+    if (g == 0 && hf == 0 && blockIdx.y == 0) p.Dws[row] = Di;
   }
 }
 
 // dK and dV for fp32 inputs: a workgroup owns 128 keys (4 wavefronts x 32, a
-// lane owns one key) with K and V rows in registers, and walks 32-row tiles
-// of Q and dO (with the rows' base-2 LSE and D_i) over every query head of
-// the kv head: S = Q K^T, dP = dO V^T, dS = P (dP - D), dV^T += dO^T P,
-// dK^T += Q^T dS.
+// lane owns one key; at D = 256 64 keys, each on a wavefront pair) with K and
+// V rows in registers, and walks 32-row tiles of Q and dO (with the rows'
+// base-2 LSE and D_i) over every query head of the kv head: S = Q K^T,
+// dP = dO V^T, dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.
 template <int D, bool Msk>
 __global__ __launch_bounds__(kBwdThreads, D <= 64 && !Msk ? 2 : 1)   // (masked: the list state spills at two)
 void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
   using T = F32BwdTile<D>;
+  using W = F32BwdSplit<D>;
+  static_assert(!(W::SP && Msk), "block masks at D = 256 run the per-row kernels");
   constexpr int BM = T::BN;   // query rows per tile
   __shared__ __attribute__((aligned(16))) float smem[2][2][T::TILE_F];   // [stage][Q, dO]
   __shared__ __attribute__((aligned(16))) float lds_l[2][2][BM];         // [stage][L2, D]
@@ -286,11 +353,13 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int units = p.B * p.HKV;
+  const int rg = W::SP ? wave >> 1 : wave, hf = W::SP ? wave & 1 : 0;
+  const int doff = hf * W::HD;   // first dim of the wavefront's products
   const int kblk = blockIdx.x / units;   // ascending: under a causal mask the first keys see most rows
   const int u = blockIdx.x % units;
   const int hkv = u % p.HKV, b = u / p.HKV;
   const int gh = p.H / p.HKV;
-  const int k0 = kblk * 128, kw = k0 + wave * 32, j = kw + l32;
+  const int k0 = kblk * W::RW, kw = k0 + rg * 32, j = kw + l32;
   const bool key_ok = j < p.Sk;
   const long krow = ((long)b * p.HKV + hkv) * p.Sk + j;
 
@@ -298,7 +367,7 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
   // within the workgroup's row chunk rc, bounds multiples of 128)
   int r_lo = 0, r_hi = p.Sq;
   if (p.causal) r_lo = min(k0, p.Sq);
-  if (p.window > 0) r_hi = min(p.Sq, k0 + 128 + p.window - 1);
+  if (p.window > 0) r_hi = min(p.Sq, k0 + W::RW + p.window - 1);
   // (chunks in reverse, so that under a causal mask the latest rows, which
   // see the most key blocks, are dispatched first)
   const int rc = p.nrc - 1 - (int)blockIdx.y;
@@ -342,11 +411,11 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
     }
   };
 
-  // K and V rows of key j (dims t + (D/2) g)
-  float kf[T::DH], vf[T::DH];
+  // K and V rows of key j (dims doff + t + (HD/2) g)
+  float kf[W::DHw], vf[W::DHw];
 #pragma unroll
-  for (int t4 = 0; t4 < T::DH / 4; ++t4) {
-    const long off = krow * D + T::DH * g + 4 * t4;
+  for (int t4 = 0; t4 < W::DHw / 4; ++t4) {
+    const long off = krow * D + doff + W::DHw * g + 4 * t4;
     const f32x4 kv = key_ok ? *(const f32x4*)((const float*)p.K + off) : f32x4{};
     const f32x4 vv = key_ok ? *(const f32x4*)((const float*)p.V + off) : f32x4{};
 #pragma unroll
@@ -407,9 +476,9 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
   }
   __syncthreads();
 
-  f32x16 dk[T::DB], dv[T::DB];
+  f32x16 dk[W::DBw], dv[W::DBw];
 #pragma unroll
-  for (int db = 0; db < T::DB; ++db) dk[db] = dv[db] = f32x16{};
+  for (int db = 0; db < W::DBw; ++db) dk[db] = dv[db] = f32x16{};
 
   for (;;) {
   for (int t = 0; t < n_tiles; ++t) {
@@ -423,12 +492,12 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
     const bool skip = kw >= p.Sk || (p.causal && r0 + BM - 1 < kw) ||
                       (p.window > 0 && r0 > kw + 31 + p.window - 1) ||
                       (Msk && !((fl >> (wave >> 1)) & 1u));
+    f32x16 s = f32x16{}, dp = f32x16{};
     if (!skip) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-      const float* qrow = Qs + l32 * T::LD + T::DH * g;
-      const float* orow = Os + l32 * T::LD + T::DH * g;
+      const float* qrow = Qs + l32 * T::LD + doff + W::DHw * g;
+      const float* orow = Os + l32 * T::LD + doff + W::DHw * g;
 #pragma unroll
-      for (int t4 = 0; t4 < T::DH / 4; ++t4) {
+      for (int t4 = 0; t4 < W::DHw / 4; ++t4) {
         const f32x4 a = *(const f32x4*)(qrow + 4 * t4);
         const f32x4 c = *(const f32x4*)(orow + 4 * t4);
 #pragma unroll
@@ -437,6 +506,10 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
           dp = __builtin_amdgcn_mfma_f32_32x32x2f32(c[e], vf[4 * t4 + e], dp, 0, 0, 0);
         }
       }
+    }
+    // (every wavefront reaches the pair sum's barriers; a skipped pair adds zeros)
+    if constexpr (W::SP) f32_pair_sum(smem[(t + 1) & 1][0], wave, lane, hf, s, dp);
+    if (!skip) {
       // element v holds query row r0 + 8 (v / 4) + 4 g + v % 4 of key j
       const bool edge = (kw + 31 >= p.Sk) || (p.causal && r0 < kw + 31) ||
                         (p.window > 0 && r0 + BM - 1 > kw + p.window - 1);
@@ -478,11 +551,11 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
 #pragma unroll
       for (int u2 = 0; u2 < 16; ++u2) {
         const int rr = 8 * (u2 >> 2) + 4 * g + (u2 & 3);
-        float oa[T::DB], qa[T::DB];
-        read_db<T::DB>(Os + rr * T::LD + T::DB * l32, oa);
-        read_db<T::DB>(Qs + rr * T::LD + T::DB * l32, qa);
+        float oa[W::DBw], qa[W::DBw];
+        read_db<W::DBw>(Os + rr * T::LD + doff + W::DBw * l32, oa);
+        read_db<W::DBw>(Qs + rr * T::LD + doff + W::DBw * l32, qa);
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db) {
+        for (int db = 0; db < W::DBw; ++db) {
           dv[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(oa[db], pr[u2], dv[db], 0, 0, 0);
           dk[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[db], ds[u2], dk[db], 0, 0, 0);
         }
@@ -502,8 +575,8 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
     }
   }
 
-  // element v of block db: dim (D/32)(8 (v / 4) + 4 g + v % 4) + db of key j
-  // (row chunks: the unscaled partial sums of chunk rc)
+  // element v of block db: dim doff + (HD/32)(8 (v / 4) + 4 g + v % 4) + db of
+  // key j (row chunks: the unscaled partial sums of chunk rc)
   if (key_ok) {
     const bool part = p.nrc > 1;
     const long po = (long)rc * p.B * p.HKV * p.Sk * D;
@@ -512,10 +585,10 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
     const float ks = part ? 1.f : p.scale;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int m = T::DB * (8 * (v >> 2) + 4 * g + (v & 3));
-      if constexpr (T::DB % 4 == 0) {
+      const int m = doff + W::DBw * (8 * (v >> 2) + 4 * g + (v & 3));
+      if constexpr (W::DBw % 4 == 0) {
 #pragma unroll
-        for (int c4 = 0; c4 < T::DB / 4; ++c4) {
+        for (int c4 = 0; c4 < W::DBw / 4; ++c4) {
           const f32x4 k4 = {dk[4 * c4][v] * ks, dk[4 * c4 + 1][v] * ks,
                             dk[4 * c4 + 2][v] * ks, dk[4 * c4 + 3][v] * ks};
           const f32x4 v4 = {dv[4 * c4][v], dv[4 * c4 + 1][v], dv[4 * c4 + 2][v], dv[4 * c4 + 3][v]};
@@ -524,7 +597,7 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
         }
       } else {
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db) {
+        for (int db = 0; db < W::DBw; ++db) {
           odk[m + db] = dk[db][v] * ks;
           odv[m + db] = dv[db][v];
         }
@@ -535,8 +608,13 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
 
 template <int D>
 static hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((long)p.B * p.H * p.n_qblk), (unsigned)p.nch);
-  if (p.bmask)
+  using W = F32BwdSplit<D>;
+  const long nqb = W::SP ? (p.Sq + W::RW - 1) / W::RW : p.n_qblk;
+  const dim3 grid((unsigned)((long)p.B * p.H * nqb), (unsigned)p.nch);
+  if constexpr (W::SP) {
+    if (p.bmask) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dq_f32_mfma_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, p);
+  } else if (p.bmask)
     hipLaunchKernelGGL((bwd_dq_f32_mfma_kernel<D, true>), grid, dim3(kBwdThreads), 0, stream, p);
   else
     hipLaunchKernelGGL((bwd_dq_f32_mfma_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, p);
@@ -546,8 +624,12 @@ static hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
 template <int D>
 static hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
   // (blockIdx.y: row chunk nrc - 1 - y when p.nrc > 1)
-  const dim3 grid((unsigned)((long)p.B * p.HKV * ((p.Sk + 127) / 128)), (unsigned)p.nrc);
-  if (p.bmask)
+  using W = F32BwdSplit<D>;
+  const dim3 grid((unsigned)((long)p.B * p.HKV * ((p.Sk + W::RW - 1) / W::RW)), (unsigned)p.nrc);
+  if constexpr (W::SP) {
+    if (p.bmask) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dkdv_f32_mfma_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, p);
+  } else if (p.bmask)
     hipLaunchKernelGGL((bwd_dkdv_f32_mfma_kernel<D, true>), grid, dim3(kBwdThreads), 0, stream, p);
   else
     hipLaunchKernelGGL((bwd_dkdv_f32_mfma_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, p);
@@ -560,6 +642,7 @@ hipError_t launch_bwd_f32_mfma_dq(const BwdParams& p, int D, hipStream_t stream)
     case 64: return launch_dq_t<64>(p, stream);
     case 96: return launch_dq_t<96>(p, stream);
     case 128: return launch_dq_t<128>(p, stream);
+    case 256: return launch_dq_t<256>(p, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -570,6 +653,7 @@ hipError_t launch_bwd_f32_mfma_dkdv(const BwdParams& p, int D, hipStream_t strea
     case 64: return launch_dkdv_t<64>(p, stream);
     case 96: return launch_dkdv_t<96>(p, stream);
     case 128: return launch_dkdv_t<128>(p, stream);
+    case 256: return launch_dkdv_t<256>(p, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -77,16 +77,26 @@ CASES += [
     ("bf16", 2, 2, 1, 900, 600, 128, 0, 250),
 ]
 
-# small grids on the per-row kernels (fp32 at D = 16, 48, 80, 256): the rows'
+# small grids on the per-row kernels (fp32 at D = 16, 48, 80): the rows'
 # ranges run in up to eight chunks whose partial sums are added afterwards
 CASES += [
     ("f32", 1, 2, 1, 1024, 1024, 48, 1, 0),      # eight chunks, causal
     ("f32", 1, 2, 2, 600, 900, 16, 0, 100),      # a window alone: ranges up to Sk / Sq
     ("f32", 1, 4, 1, 800, 800, 80, 1, 300),      # causal band of 300
-    ("f32", 1, 2, 1, 600, 700, 256, 0, 0),       # D = 256: two rows per 32-lane group
-    # odd Sq and Sk at D = 256: the last group of each kernel holds one row
+]
+
+# fp32 at D = 256: the fp32 MFMA kernels with the head dims split over
+# wavefront pairs (64 query rows or keys per workgroup; partial scores and dP
+# added through LDS): several tiles, odd Sq and Sk, GQA, windows, dQ key
+# chunks (Sk 3000 over one query tile group) and dK/dV row chunks
+CASES += [
+    ("f32", 1, 2, 1, 600, 700, 256, 0, 0),
     ("f32", 1, 2, 1, 91, 121, 256, 1, 30),
     ("f32", 1, 2, 2, 77, 133, 256, 0, 0),
+    ("f32", 1, 4, 2, 700, 900, 256, 1, 0),       # row chunks of 128 rows
+    ("f32", 1, 1, 1, 200, 3000, 256, 0, 0),      # five key chunks
+    ("f32", 2, 2, 1, 333, 517, 256, 0, 100),
+    ("f32", 1, 2, 1, 1100, 1100, 256, 1, 300),
 ]
 
 # few query tiles on the MFMA kernels: the dQ kernel splits the key axis into

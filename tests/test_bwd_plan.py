@@ -38,9 +38,21 @@ def test_head_dim_routes():
     # ... the per-row kernels when it is small
     p = fa.bwd_plan(1, 1, 1, 256, 256, 48, CUS, dtype="f32")
     assert (p["head_dim"], p["staged"], p["per_row"]) == (48, 0, 1)
-    # fp32 D 256 always per row; 16-bit D 256 always MFMA
-    assert fa.bwd_plan(8, 16, 16, 4096, 4096, 256, CUS, dtype="f32")["per_row"] == 1
+    # D 256 runs MFMA kernels for every type (fp32: the dims split over
+    # wavefront pairs; only a block mask keeps fp32 D 256 on the per-row kernels)
+    assert fa.bwd_plan(8, 16, 16, 4096, 4096, 256, CUS, dtype="f32")["per_row"] == 0
+    assert fa.bwd_plan(1, 1, 1, 128, 128, 256, CUS, dtype="f32")["per_row"] == 0
     assert fa.bwd_plan(1, 1, 1, 128, 128, 256, CUS, dtype="bf16")["per_row"] == 0
+
+
+def test_fp32_d256_chunks_count_64_row_workgroups():
+    # 64 query rows (keys) per workgroup: B1 H4 S2048 has 128 dQ workgroups
+    # (< 512) -> key chunks; 128 dK/dV workgroups against 512 fp32 slots and
+    # a walk of 2048 rows -> 4 row chunks of 512 rows
+    p = fa.bwd_plan(1, 4, 4, 2048, 2048, 256, CUS, causal=True, dtype="f32")
+    assert p["per_row"] == 0 and p["head_dim"] == 256
+    assert (p["key_chunks"], p["keys_per_chunk"]) == (4, 512)
+    assert (p["row_chunks"], p["rows_per_chunk"]) == (4, 512)
 
 
 def test_big_grid_has_no_chunks_small_grid_has():
