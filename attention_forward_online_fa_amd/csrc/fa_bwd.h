@@ -79,12 +79,9 @@ constexpr int bwd_rows_per_group(int D) { return bwd_lanes_per_row(D) == 16 ? 4 
 
 // fp32 inputs at these head dims run the MFMA backward kernels (16, 48 and 80
 // staged into the 32, 64, 96 tiles when the work is large, else the per-row
-// kernels; 256 with its dims split over wavefront pairs, except under a block
-// mask, which keeps the per-row kernels there); 16-bit inputs always run MFMA
-// kernels.
-constexpr bool bwd_f32_mfma(int D, bool masked = false) {
-  return D == 32 || D == 64 || D == 96 || D == 128 || (D == 256 && !masked);
-}
+// kernels; 256 with its dims split over wavefront pairs); 16-bit inputs
+// always run MFMA kernels.
+constexpr bool bwd_f32_mfma(int D) { return D == 32 || D == 64 || D == 96 || D == 128 || D == 256; }
 
 constexpr int kBwdThreads = 256;   // threads per backward workgroup (4 wavefronts)
 constexpr float kLog2e = 1.4426950408889634f;

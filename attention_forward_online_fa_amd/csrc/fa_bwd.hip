@@ -1015,10 +1015,8 @@ static hipError_t sum_parts(const SumJobs& jobs, int njobs, hipStream_t stream) 
 
 template <typename E, int D>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
-  constexpr bool f32_mfma = sizeof(E) == 4 && bwd_f32_mfma(D, true);   // masked or not
+  constexpr bool f32_mfma = sizeof(E) == 4 && bwd_f32_mfma(D);
   constexpr bool b16_mfma = sizeof(E) == 2 && (D == 64 || D == 128 || D == 256);
-  // fp32 at D = 256: the split MFMA kernels without a block mask, else per row
-  const bool f32_split = sizeof(E) == 4 && D == 256 && !p.bmask;
   // (MFMA dQ kernels: blockIdx.y = key chunk when p.nch > 1)
   if constexpr (b16_mfma) {
     const dim3 grid((unsigned)((long)p.B * p.H * p.n_qblk), (unsigned)p.nch);
@@ -1029,9 +1027,6 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
     else
       hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D, false, false>), grid, dim3(kBwdThreads), 0, stream, p);
   } else if constexpr (f32_mfma) {
-    const hipError_t e0 = launch_bwd_f32_mfma_dq(p, D, stream);
-    if (e0 != hipSuccess) return e0;
-  } else if (f32_split) {
     const hipError_t e0 = launch_bwd_f32_mfma_dq(p, D, stream);
     if (e0 != hipSuccess) return e0;
   } else {
@@ -1062,9 +1057,6 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   } else if constexpr (f32_mfma) {
     const hipError_t e0 = launch_bwd_f32_mfma_dkdv(p, D, stream);
     if (e0 != hipSuccess) return e0;
-  } else if (f32_split) {
-    const hipError_t e0 = launch_bwd_f32_mfma_dkdv(p, D, stream);
-    if (e0 != hipSuccess) return e0;
   } else {
     constexpr int R = rows_per_group<D>(), GPB = kBwdThreads / bwd_lanes_per_row(D);
     const long groups = (long)p.B * p.HKV * ((p.Sk + R - 1) / R);
@@ -1084,7 +1076,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   if (p.nch > 1)
     jobs.j[njobs++] = {(const float4*)p.part_q, (float4*)p.dQ, p.scale, (long)p.B * p.H * p.Sq * D / 4,
                        p.nch};
-  const int nparts = b16_mfma || f32_mfma || f32_split ? p.nrc : p.nch;
+  const int nparts = b16_mfma || f32_mfma ? p.nrc : p.nch;
   if (nparts > 1) {
     const long nk4 = (long)p.B * p.HKV * p.Sk * D / 4;
     jobs.j[njobs++] = {(const float4*)p.part_k, (float4*)p.dK, p.scale, nk4, nparts};

@@ -91,11 +91,11 @@ struct BwdPlan {
 // max_row_stride: the largest row stride (elements) of Q, K, V, O, dO;
 // cus: compute units of the device.
 BwdPlan plan_backward(int B, int H, int HKV, int Sq, int Sk, int D, int causal, int window,
-                      int dtype, bool contiguous, long long max_row_stride, int cus, bool masked) {
+                      int dtype, bool contiguous, long long max_row_stride, int cus) {
   BwdPlan pl;
   const long n_qblk = (Sq + 127) / 128;
-  // fp32 at D = 256 (unmasked): MFMA kernels with 64 query rows (keys) per workgroup
-  const bool f32_256 = dtype == FA_F32 && D == 256 && !masked;
+  // fp32 at D = 256: MFMA kernels with 64 query rows (keys) per workgroup
+  const bool f32_256 = dtype == FA_F32 && D == 256;
   const size_t nq = (size_t)B * H * Sq, nk = (size_t)B * HKV * Sk;
   // 16-bit inputs at head dims 16 .. 96 other than 64 run the MFMA kernels of
   // the 64 or 128 tile with the dims from D on held as zeros (they add exact
@@ -122,13 +122,13 @@ BwdPlan plan_backward(int B, int H, int HKV, int Sq, int Sk, int D, int causal, 
   const bool padded = dtype != FA_F32 ? D != DT16 : f32_pad;
   const bool staged = !gen && (padded || !contiguous);
   const int DT = padded ? (dtype != FA_F32 ? DT16 : DTF) : D;
-  // The per-row kernels (fp32 inputs at D = 256 under a block mask, and 16,
-  // 48, 80 unstaged) on grids too small to fill the GPU: each row group's range is cut into nch chunks that run side by side
+  // The per-row kernels (fp32 inputs at D = 16, 48, 80 unstaged) on grids too
+  // small to fill the GPU: each row group's range is cut into nch chunks that run side by side
   // (a causal grid is otherwise bound by its longest rows), their partial
   // sums added up afterwards in chunk order (deterministic). A group's range
   // spans at most `span` + R - 1 keys (query rows): the ranges of its R
   // adjacent rows.
-  const bool per_row = dtype == FA_F32 && !fa::bwd_f32_mfma(DT, masked);
+  const bool per_row = dtype == FA_F32 && !fa::bwd_f32_mfma(DT);
   if (per_row) {
     const int R = fa::bwd_rows_per_group(DT);
     const long groups = (long)B * H * ((Sq + R - 1) / R);
@@ -274,8 +274,7 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
   for (int t = 0; t < 5; ++t) mx = std::max(mx, vs[t][2]);
   const int cus = fa::device_cus();
   if (cus <= 0) return FA_ERR_HIP;
-  const BwdPlan pl = plan_backward(B, H, HKV, Sq, Sk, D, causal, window, dtype, contiguous, mx, cus,
-                                    bm != nullptr);
+  const BwdPlan pl = plan_backward(B, H, HKV, Sq, Sk, D, causal, window, dtype, contiguous, mx, cus);
   const bool gen = pl.gen, staged = pl.staged, per_row = pl.per_row;
   const int DT = pl.DT;
   p.nch = pl.nch;
@@ -418,7 +417,7 @@ extern "C" int fa_bwd_plan(int B, int H, int HKV, int Sq, int Sk, int D, int cau
   const int st = check_bwd(B, H, HKV, Sq, Sk, D, causal, window, dtype);
   if (st != FA_OK) return st;
   if (num_cus < 1) return FA_ERR_SHAPE;
-  const BwdPlan pl = plan_backward(B, H, HKV, Sq, Sk, D, causal, window, dtype, true, D, num_cus, false);
+  const BwdPlan pl = plan_backward(B, H, HKV, Sq, Sk, D, causal, window, dtype, true, D, num_cus);
   const int out[8] = {pl.DT, pl.gen, pl.staged, pl.per_row, pl.nch, pl.chunk_q, pl.nrc, pl.chunk_r};
   for (int t = 0; t < 8; ++t) plan[t] = out[t];
   return FA_OK;

@@ -17,19 +17,18 @@ __device__ __forceinline__ const unsigned char* bwd_mask_row(const BwdParams& p,
 }
 
 // Block masks: the candidates c in [c0, n) with nonzero flags vis(c) go, in
-// order, to list[] as entry(c, flags), until the list is full (kBwdMaxList
-// entries); wave 0 scans 64 candidates per ballot round, with the mask reads
+// order, to list[] as entry(c, flags), until the list is full (Cap entries); wave 0 scans 64 candidates per ballot round, with the mask reads
 // of four rounds in flight at once. Returns the count (uniform) and sets
 // *next to the first candidate not scanned (n once every candidate was). sh
 // is two ints of LDS.
-template <typename Vis, typename Ent>
+template <int Cap = kBwdMaxList, typename Vis, typename Ent>
 __device__ __forceinline__ int bwd_build_list(int c0, int n, unsigned* list, int* sh, int wave,
                                               int lane, Vis vis, Ent entry, int* next) {
   constexpr int kAhead = 4;
   __syncthreads();   // the previous list's readers are done with it
   if (wave == 0) {
     int cnt = 0, c = c0;
-    while (c < n && cnt + 64 <= kBwdMaxList) {
+    while (c < n && cnt + 64 <= Cap) {
       unsigned f[kAhead];
 #pragma unroll
       for (int r = 0; r < kAhead; ++r) {
@@ -38,7 +37,7 @@ __device__ __forceinline__ int bwd_build_list(int c0, int n, unsigned* list, int
       }
 #pragma unroll
       for (int r = 0; r < kAhead; ++r) {
-        if (c >= n || cnt + 64 > kBwdMaxList) break;
+        if (c >= n || cnt + 64 > Cap) break;
         const unsigned long long bal = __ballot(f[r] != 0u);
         if (f[r] != 0u) list[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = entry(c + lane, f[r]);
         cnt += __popcll(bal);

@@ -72,6 +72,9 @@ struct F32BwdSplit {
   static constexpr int DHw = HD / 2;          // score k-steps per wavefront
   static constexpr int DBw = HD / 32;         // output d-blocks per wavefront
   static constexpr int RW = SP ? 64 : 128;    // query rows (dQ) or keys (dK/dV) per workgroup
+  // block-mask list entries held in LDS at once (D = 256: what fits beside
+  // the 130 KiB of tile buffers)
+  static constexpr int LIST = SP ? 4096 : kBwdMaxList;
 };
 
 // Adds the pair's partial score and dP tiles (SP only): element v of s and dp
@@ -104,7 +107,6 @@ __global__ __launch_bounds__(kBwdThreads, D <= 64 ? 2 : 1)
 void bwd_dq_f32_mfma_kernel(BwdParams p) {
   using T = F32BwdTile<D>;
   using W = F32BwdSplit<D>;
-  static_assert(!(W::SP && Msk), "block masks at D = 256 run the per-row kernels");
   static_assert(!W::SP || 4 * 32 * 64 <= T::TILE_F, "the pair sums fit one tile buffer");
   constexpr int BN = T::BN;
   __shared__ __attribute__((aligned(16))) float smem[2][2][T::TILE_F];   // [stage][K, V]
@@ -138,19 +140,19 @@ void bwd_dq_f32_mfma_kernel(BwdParams p) {
   const int t0 = (lo / BN) * BN;
   const int n_cand = hi > lo ? (hi - t0 + BN - 1) / BN : 0;   // key tiles of the range
   // block mask: only the tiles whose mask byte is nonzero, listed in portions
-  __shared__ unsigned tlist[Msk ? kBwdMaxList : 1];
+  __shared__ unsigned tlist[Msk ? W::LIST : 1];
   __shared__ int tsh[2];
   int n_tiles = n_cand, c_next = n_cand;
   const unsigned char* mrow = nullptr;
   auto list_portion = [&](int c0) {
-    return bwd_build_list(
+    return bwd_build_list<W::LIST>(
         c0, n_cand, tlist, tsh, wave, lane,
         [&](int t) { return mrow[(t0 + t * BN) / kBwdMaskK] != 0 ? 1u : 0u; },
         [](int t, unsigned) { return (unsigned)t; },
         &c_next);
   };
   if constexpr (Msk) {
-    mrow = bwd_mask_row(p, b, h, hkv, qblk);
+    mrow = bwd_mask_row(p, b, h, hkv, q0 / kBwdMaskQ);
     n_tiles = list_portion(0);
   }
   auto tile_kt = [&](int t) {   // first key of the t-th tile visited
@@ -345,7 +347,6 @@ __global__ __launch_bounds__(kBwdThreads, D <= 64 && !Msk ? 2 : 1)   // (masked:
 void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
   using T = F32BwdTile<D>;
   using W = F32BwdSplit<D>;
-  static_assert(!(W::SP && Msk), "block masks at D = 256 run the per-row kernels");
   constexpr int BM = T::BN;   // query rows per tile
   __shared__ __attribute__((aligned(16))) float smem[2][2][T::TILE_F];   // [stage][Q, dO]
   __shared__ __attribute__((aligned(16))) float lds_l[2][2][BM];         // [stage][L2, D]
@@ -379,19 +380,21 @@ void bwd_dkdv_f32_mfma_kernel(BwdParams p) {
   const int n_rt = r_hi > r_lo ? (r_hi - rt0 + BM - 1) / BM : 0;
   const int n_cand = n_rt * gh;   // (query head, row tile) pairs
   // block mask: only the pairs whose mask byte is nonzero for one of the
-  // block's two key columns, listed in portions (query head << 22 | row tile
-  // << 2 | a flag per column); a wavefront computes only under its column's flag
-  __shared__ unsigned tlist[Msk ? kBwdMaxList : 1];
+  // block's two key columns (D = 256: its one column, flagged for both row
+  // groups), listed in portions (query head << 22 | row tile << 2 | a flag per
+  // column); a wavefront computes only under its column's flag
+  __shared__ unsigned tlist[Msk ? W::LIST : 1];
   __shared__ int tsh[2];
   const int kb0 = k0 / kBwdMaskK;
   auto pair_flags = [&](int c) {
     const int hl = c / n_rt, r0 = rt0 + (c % n_rt) * BM;
     const unsigned char* m = bwd_mask_row(p, b, hkv * gh + hl, hkv, r0 / kBwdMaskQ);
+    if constexpr (W::SP) return m[kb0] != 0 ? 3u : 0u;
     return (m[kb0] != 0 ? 1u : 0u) | (kb0 + 1 < p.bm_nkb && m[kb0 + 1] != 0 ? 2u : 0u);
   };
   int n_tiles = n_cand, c_next = n_cand;
   auto list_portion = [&](int c0) {
-    return bwd_build_list(
+    return bwd_build_list<W::LIST>(
         c0, n_cand, tlist, tsh, wave, lane, pair_flags,
         [&](int c, unsigned f) { return (unsigned)(c / n_rt) << 22 | (unsigned)(c % n_rt) << 2 | f; },
         &c_next);
@@ -611,10 +614,7 @@ static hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
   using W = F32BwdSplit<D>;
   const long nqb = W::SP ? (p.Sq + W::RW - 1) / W::RW : p.n_qblk;
   const dim3 grid((unsigned)((long)p.B * p.H * nqb), (unsigned)p.nch);
-  if constexpr (W::SP) {
-    if (p.bmask) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dq_f32_mfma_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, p);
-  } else if (p.bmask)
+  if (p.bmask)
     hipLaunchKernelGGL((bwd_dq_f32_mfma_kernel<D, true>), grid, dim3(kBwdThreads), 0, stream, p);
   else
     hipLaunchKernelGGL((bwd_dq_f32_mfma_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, p);
@@ -626,10 +626,7 @@ static hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
   // (blockIdx.y: row chunk nrc - 1 - y when p.nrc > 1)
   using W = F32BwdSplit<D>;
   const dim3 grid((unsigned)((long)p.B * p.HKV * ((p.Sk + W::RW - 1) / W::RW)), (unsigned)p.nrc);
-  if constexpr (W::SP) {
-    if (p.bmask) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_f32_mfma_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, p);
-  } else if (p.bmask)
+  if (p.bmask)
     hipLaunchKernelGGL((bwd_dkdv_f32_mfma_kernel<D, true>), grid, dim3(kBwdThreads), 0, stream, p);
   else
     hipLaunchKernelGGL((bwd_dkdv_f32_mfma_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, p);

@@ -47,9 +47,11 @@ def masked_grads(wl, inp, mask, seed=0):
     return (host64(dq), host64(dk), host64(dv)), dO
 
 
-def check(wl, got, ref):
+def check(wl, got, ref, kv_growth=1.0):
+    # kv_growth widens the dK / dV tolerance where each key sums far more rows
+    # than the cases the base tolerances were set on
     for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
-        scale_r = max(1.0, float(np.abs(r).max()))
+        scale_r = max(1.0, float(np.abs(r).max())) * (kv_growth if name != "dQ" else 1.0)
         err = float(np.abs(g - r).max())
         print(f"  {name}: max|d|={err:.3e} (tol {TOL[wl.dtype] * scale_r:.3e})", flush=True)
         assert np.all(np.isfinite(g)), name
@@ -65,7 +67,8 @@ CASES = [
     ("bf16", 1, 1, 1, 130, 2100, 256, 0, 0, "1", "1"),   # key chunks of the D = 256 dQ kernel
     ("f32", 1, 4, 2, 300, 500, 64, 1, 0, "1", "kv"),
     ("f32", 2, 2, 1, 260, 390, 128, 0, 200, "B", "q"),
-    ("f32", 1, 2, 1, 190, 330, 256, 1, 0, "1", "1"),    # fp32 D = 256: the per-row kernels
+    ("f32", 1, 2, 1, 190, 330, 256, 1, 0, "1", "1"),    # fp32 D = 256: 64-key workgroups, one mask column
+    ("f32", 1, 4, 2, 700, 1000, 256, 0, 300, "B", "kv"),  # with dK/dV row chunks
     # small grids with long row walks: dK/dV row chunks under the mask
     ("bf16", 1, 8, 2, 1100, 1100, 128, 0, 0, "1", "kv"),
     ("f32", 1, 4, 1, 700, 700, 64, 1, 0, "1", "q"),
@@ -88,7 +91,8 @@ def test_masked_backward_matches_oracle(case, density):
 
 
 @pytest.mark.parametrize("dtype,D,Sq", [("bf16", 128, 300), ("f32", 64, 300), ("bf16", 256, 300),
-                                        ("bf16", 128, 1100), ("f32", 64, 1100)])
+                                        ("f32", 256, 300), ("bf16", 128, 1100), ("f32", 64, 1100),
+                                        ("f32", 256, 1100)])
 def test_all_ones_mask_equals_dense_backward(dtype, D, Sq):
     # every block visible: the same gradients as fa_bwd, bit for bit (Sq =
     # 1100: both with dK/dV row chunks)
@@ -120,15 +124,18 @@ def test_unseen_keys_and_empty_rows_get_zero_gradients(dtype):
     check(wl, (dq, dk, dv), ref)
 
 
-def test_dkdv_list_in_portions():
-    # one key block seen by 16 query heads x 625 row tiles = 10000 pairs, more
-    # than a dK/dV workgroup's list holds (8192): the list is built and worked
-    # in two portions. 1024 dK/dV key blocks, so that the grid is too large
-    # for row chunks (and the forward's 2048-tile list still holds the key
-    # axis); only the first 64 keys are visible, so the oracle takes those
-    # alone, and every other key must get dK = dV = 0 exactly
-    Sk = 1024 * 128
-    wl = wl_small("bf16", 1, 16, 1, 40000, Sk, 64, 0, 0, seed=23)
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f32", 256)])
+def test_dkdv_list_in_portions(dtype, D):
+    # one key block seen by 16 query heads x 625 row tiles of 64 rows (fp32:
+    # 1250 of 32) = 10000 (20000) pairs, more than a dK/dV workgroup's list
+    # holds (8192; fp32 D = 256: 4096): the list
+    # is built and worked in portions. 1024 key blocks of 64 keys or more, so
+    # that the grid is too large for row chunks (and the forward's 2048-tile
+    # list still holds the key axis); only the first 64 keys are visible, so
+    # the oracle takes those alone, and every other key must get dK = dV = 0
+    # exactly
+    Sk = 1024 * (128 if dtype == "bf16" else 64)
+    wl = wl_small(dtype, 1, 16, 1, 40000, Sk, D, 0, 0, seed=23)
     inp = W.make_inputs(wl)
     mask = np.zeros((1, 1, -(-40000 // 128), Sk // 64), dtype=np.uint8)
     mask[0, 0, :, 0] = 1
@@ -137,18 +144,25 @@ def test_dkdv_list_in_portions():
     assert np.all(dk[:, :, 64:] == 0) and np.all(dv[:, :, 64:] == 0)
     ref = attention_backward(inp.q, inp.k[:, :, :64], inp.v[:, :, :64], dO, wl.scale(), False, 0,
                              block_mask=mask[:, :, :, :1])
-    check(wl, (dq, dk[:, :, :64], dv[:, :, :64]), ref)
+    # each of the 64 keys sums ~580,000 (query head, row) terms in fp32, whose
+    # rounding error grows like the square root of the term count: fp32 dK
+    # and dV get the base tolerance (set on sums of up to ~4096 terms) times
+    # sqrt(terms / 4096); the bf16 tolerance already covers it
+    terms = 16 * int(mask[0, 0, :, 0].sum()) * 128
+    check(wl, (dq, dk[:, :, :64], dv[:, :, :64]), ref,
+          kv_growth=np.sqrt(terms / 4096) if dtype == "f32" else 1.0)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_dq_list_in_portions(dtype):
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f32", 64), ("f32", 256)])
+def test_dq_list_in_portions(dtype, D):
     # 128 query blocks x 4 heads (no key chunks) over 9000 key tiles (8470
-    # visible): each dQ workgroup's list overflows its 8192 entries and is worked in portions.
+    # visible): each dQ workgroup's list overflows its 8192 entries (fp32 D = 256:
+    # 4096) and is worked in portions.
     # dQ of query block 5 of head 1, non-causal, against the oracle on that
     # block alone (a query row's dQ depends only on its own row and the keys)
     import attention_forward_online_fa_amd as fa
     Sq, Sk = 128 * 128, 9000 * 32
-    wl = wl_small(dtype, 1, 4, 1, Sq, Sk, 64, 0, 0, seed=24)
+    wl = wl_small(dtype, 1, 4, 1, Sq, Sk, D, 0, 0, seed=24)
     inp = W.make_inputs(wl)
     q, k, v = to_device(inp)
     dO, do = grad_output(wl, q, 2)
