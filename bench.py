@@ -162,10 +162,12 @@ def bench_backward(args, wl, inp, q, k, v, torch, fa):
     ms_per_step = wall * 1e3 / args.steps
     per_step = per_step_events(step, stream, 20)
     flops = 2.5 * counted_flops(wl, inp.block_mask)          # 10 D per visible pair
-    # MFMA backward kernels: 16-bit inputs (head dims other than 64, 128 and
-    # 256 on zero-padded copies) and fp32 inputs at D = 32, 64, 96, 128; the
-    # rest (fp32 D = 16, 48, 80, 256) run the per-row VALU kernels
-    if wl.dtype != "f32" or wl.D in (32, 64, 96, 128):
+    # MFMA backward kernels, except where the library's plan picks the per-row
+    # VALU kernels (fp32 at D = 16, 48, 80 on small problems)
+    plan = fa.bwd_plan(wl.B, wl.H, wl.HKV, wl.Sq, wl.Sk, wl.D,
+                       torch.cuda.get_device_properties(0).multi_processor_count,
+                       causal=bool(wl.causal), window=wl.window, dtype=wl.dtype)
+    if not plan["per_row"]:
         bound, peak = "mfma", PEAK_TFLOPS[wl.dtype]
     else:
         bound, peak = "alu", PEAK_VALU_F32

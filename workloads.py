@@ -97,6 +97,9 @@ CONFIGS = [
              amplitude=0.5, check="all", seed_index=8),
     Workload("mha_causal_f32_b4h8_s1024_d32", 4, 8, 8, 1024, 1024, 32, "f32", 1, 0,
              check="all", seed_index=9),
+    # fp32 at head dim 256 (the backward's wavefront-pair split of the dims)
+    Workload("mha_causal_f32_b1h16_s4096_d256", 1, 16, 16, 4096, 4096, 256, "f32", 1, 0,
+             check="sampled", n_random_rows=256, edge_rows=64, seed_index=10),
 ]
 
 # Block-mask granularity (query rows x keys per mask byte).
