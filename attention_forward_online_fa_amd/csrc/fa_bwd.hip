@@ -19,18 +19,19 @@
 // - 16-bit inputs: MFMA kernels (bwd_dq_mfma_kernel, bwd_dkdv_mfma_kernel) at
 //   tile dims 64, 128 and 256; in their general form they read views with
 //   strides and head dims below the tile dim (those dims read as zeros).
-// - fp32 inputs at D = 32, 64, 96, 128: MFMA kernels on v_mfma_f32_32x32x2_f32
-//   (bwd_dq_f32_mfma_kernel, bwd_dkdv_f32_mfma_kernel, in fa_bwd_f32.hip).
-// - fp32 inputs at D = 256, and at D = 16, 48, 80 on small problems (larger
-//   ones are staged into the MFMA kernels of the 32, 64, 96 tiles, the extra
-//   dims zero): the per-row kernels below (bwd_dq_kernel,
-//   bwd_dkdv_kernel), the pages' thread-per-row design mapped to wavefronts on
-//   the VALU: a group of G = 4, 8, 16 or 32 lanes (the fewest that keep D / G
-//   <= 8) owns R consecutive rows of one head (bwd_rows_per_group: 4 with 16
-//   lanes, else 2), query rows in the dQ kernel, key rows in the dK/dV kernel.
-//   A lane holds D / G consecutive elements of each row vector; dot products
-//   reduce over the group with two to four DPP steps (and one lane permute at
-//   G = 32).
+// - fp32 inputs at D = 32, 64, 96, 128, 256: MFMA kernels on
+//   v_mfma_f32_32x32x2_f32 (bwd_dq_f32_mfma_kernel, bwd_dkdv_f32_mfma_kernel,
+//   in fa_bwd_f32.hip; at 256 the head dims split over wavefront pairs).
+// - fp32 inputs at D = 16, 48, 80 on small problems (larger ones are staged
+//   into the MFMA kernels of the 32, 64, 96 tiles, the extra dims zero): the
+//   per-row kernels below (bwd_dq_kernel, bwd_dkdv_kernel), the pages'
+//   thread-per-row design mapped to wavefronts on the VALU: a group of G = 4,
+//   8 or 16 lanes (the fewest that keep D / G <= 8; the kernels also take 32
+//   for wider rows) owns R consecutive rows of one head (bwd_rows_per_group: 4
+//   with 16 lanes, else 2), query rows in the dQ kernel, key rows in the dK/dV
+//   kernel. A lane holds D / G consecutive elements of each row vector; dot
+//   products reduce over the group with two to four DPP steps (and one lane
+//   permute at G = 32).
 // On small grids the per-row kernels run each group's range in chunks
 // (blockIdx.y), and the MFMA dQ kernels the key axis in chunks, whose partial
 // sums sum_parts_kernel adds in chunk order. Under a block mask (the block
